@@ -1,0 +1,251 @@
+"""Seeded synthetic inputs for the tree-verify and partial-KV workloads.
+
+This module only draws random numbers and lays out index structures. It holds
+none of the attention, scoring or selection arithmetic: the GPU path and the
+CPU oracle both receive the arrays built here and nothing else.
+
+Workloads (the pages measure on PG-19 with real LLaMA activations; neither the
+data nor the weights exist here, so Gaussian tensors at the real layer shapes
+stand in for them):
+
+* ``tiny``       fp32, Hq=4, Hkv=1, D=64, L=512, 40-node [1,3,3,3] tree, N(0,1).
+* ``llama8b_20k``  bf16, Hq=32, Hkv=8, D=128, L=20480, tree + 20 four-token
+  chains (T=120), Q ~ N(0,1), K,V ~ N(0,1)/sqrt(128).
+* ``llama8b_100k`` as above with L=102400 (the ultra-long endpoint).
+* ``partial_100k`` the partial-KV draft pass: 4 recent queries, 102400-token
+  cache, 64-token chunks, budget of 64 chunks, 8 chunks per KV head with keys
+  scaled by 3 before rounding.
+* ``llama2_mha_100k`` bf16, Hq=Hkv=32, D=128, L=102400, same 120-query mask.
+
+bf16 tensors are carried as ``np.uint16`` bit patterns (round to nearest even
+from the fp32 draw); fp32 tensors as ``np.float32``.
+
+Page references: the [1,3,3,3] tree and the 4-gram candidates come from the
+TokenSwift tool listing ("How it works") and the ablation table of the
+TokenSwift summary page (tree rows); ``--ngram_topk 20``, ``--gamma 4`` and
+``--retrival_max_budget 4096`` from the TokenSwift-Qwen2.5-7B model card
+("Example using TokenSwift command line").
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+BF16 = "bf16"
+F32 = "f32"
+
+# Constants the pages fix (model card CLI example; summary-page ablation table).
+TREE_SHAPE = (1, 3, 3, 3)   # per-depth top-k of the candidate tree
+NGRAM_TOPK = 20             # retrieved 4-gram candidates
+GAMMA = 4                   # draft length: 4 logits, 4-grams, 4 recent queries
+RETRIEVAL_BUDGET = 4096     # tokens kept in the partial KV cache
+CHUNK = 64                  # tokens per importance chunk (budget = 64 chunks)
+
+
+# --------------------------------------------------------------------------
+# random streams and bf16 rounding
+# --------------------------------------------------------------------------
+def _streams(seed: int, n: int) -> List[np.random.Generator]:
+    return [np.random.Generator(np.random.PCG64(s))
+            for s in np.random.SeedSequence(seed).spawn(n)]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even); returns uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32 (for test tolerances/plots)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+def _encode(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dtype == BF16 else np.ascontiguousarray(x, np.float32)
+
+
+# --------------------------------------------------------------------------
+# draft structures
+# --------------------------------------------------------------------------
+def tree_parents(shape: Sequence[int], rng: Optional[np.random.Generator] = None) -> np.ndarray:
+    """Parent array of the per-depth top-k candidate tree ``shape``.
+
+    Level 0 holds ``shape[0]`` roots; every node of level d has ``shape[d+1]``
+    children. Nodes are numbered level by level (so parent[t] < t). With
+    ``rng`` the order inside each level is shuffled and the parents remapped,
+    so the numbering is not a canonical layout.
+    """
+    levels: List[List[int]] = []   # per level: list of parent *positions in previous level*
+    sizes = []
+    for d, width in enumerate(shape):
+        n_prev = 1 if d == 0 else sizes[-1]
+        lvl = [(-1 if d == 0 else p) for p in range(n_prev) for _ in range(width)]
+        levels.append(lvl)
+        sizes.append(len(lvl))
+    parent = []
+    offset_prev = 0
+    new_pos_prev = None
+    offset = 0
+    for d, lvl in enumerate(levels):
+        n = len(lvl)
+        perm = rng.permutation(n) if rng is not None else np.arange(n)
+        # perm[new_slot] = old index inside the level
+        new_pos = np.empty(n, dtype=np.int64)
+        new_pos[perm] = np.arange(n)
+        level_par = [0] * n
+        for old in range(n):
+            p_old = lvl[old]
+            p = -1 if p_old < 0 else offset_prev + int(new_pos_prev[p_old])
+            level_par[int(new_pos[old])] = p
+        parent.extend(level_par)
+        offset_prev, new_pos_prev = offset, new_pos
+        offset += n
+    return np.asarray(parent, dtype=np.int32)
+
+
+def chain_parents(n_chains: int, length: int, base: int) -> np.ndarray:
+    """``n_chains`` causal chains of ``length`` nodes numbered from ``base``:
+    node base+length*c+j has parent -1 when j == 0 and its predecessor otherwise."""
+    out = np.empty(n_chains * length, dtype=np.int32)
+    for c in range(n_chains):
+        for j in range(length):
+            t = c * length + j
+            out[t] = -1 if j == 0 else base + t - 1
+    return out
+
+
+def tree_plus_chains_parents(rng: np.random.Generator) -> np.ndarray:
+    tree = tree_parents(TREE_SHAPE, rng)
+    chains = chain_parents(NGRAM_TOPK, GAMMA, base=len(tree))
+    return np.concatenate([tree, chains]).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class VerifyCase:
+    name: str
+    dtype: str
+    T: int
+    Hq: int
+    Hkv: int
+    D: int
+    L: int
+    scale: float
+    parent: np.ndarray      # int32 [T]
+    q: np.ndarray           # [T][Hq][D]
+    k_cache: np.ndarray     # [Hkv][L][D]
+    v_cache: np.ndarray
+    k_draft: np.ndarray     # [Hkv][T][D]
+    v_draft: np.ndarray
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def kv_bytes(self) -> int:
+        return 2 * self.k_cache.nbytes
+
+
+@dataclasses.dataclass
+class PartialCase:
+    name: str
+    dtype: str
+    R: int                  # recent queries used for scoring (= draft queries)
+    Hq: int
+    Hkv: int
+    D: int
+    L: int
+    chunk: int
+    k: int                  # chunks kept per KV head
+    scale: float
+    q: np.ndarray           # [R][Hq][D]
+    k_cache: np.ndarray     # [Hkv][L][D]
+    v_cache: np.ndarray
+    k_new: np.ndarray       # [Hkv][R][D]
+    v_new: np.ndarray
+    boosted: np.ndarray     # int32 [Hkv][8] chunk ids whose keys were scaled by 3
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def n_chunks(self) -> int:
+        return self.L // self.chunk
+
+
+def make_verify(name: str, *, dtype: str, Hq: int, Hkv: int, D: int, L: int,
+                seed: int, with_chains: bool, q_std: float = 1.0,
+                kv_std: Optional[float] = None, parent: Optional[np.ndarray] = None) -> VerifyCase:
+    rq, rk, rv, rkd, rvd, rp = _streams(seed, 6)
+    if parent is None:
+        parent = tree_plus_chains_parents(rp) if with_chains else tree_parents(TREE_SHAPE, rp)
+    T = int(len(parent))
+    if kv_std is None:
+        kv_std = 1.0 / np.sqrt(D) if dtype == BF16 else 1.0
+    q = _encode(_normal(rq, (T, Hq, D), q_std), dtype)
+    kc = _encode(_normal(rk, (Hkv, L, D), kv_std), dtype)
+    vc = _encode(_normal(rv, (Hkv, L, D), kv_std), dtype)
+    kd = _encode(_normal(rkd, (Hkv, T, D), kv_std), dtype)
+    vd = _encode(_normal(rvd, (Hkv, T, D), kv_std), dtype)
+    return VerifyCase(name, dtype, T, Hq, Hkv, D, L, float(1.0 / np.sqrt(D)),
+                      np.ascontiguousarray(parent, np.int32), q, kc, vc, kd, vd)
+
+
+def make_partial(name: str = "partial_100k", *, Hq: int = 32, Hkv: int = 8, D: int = 128,
+                 L: int = 102400, R: int = GAMMA, chunk: int = CHUNK,
+                 k: int = RETRIEVAL_BUDGET // CHUNK, n_boost: int = 8, boost: float = 3.0,
+                 seed: int = 3) -> PartialCase:
+    rq, rk, rv, rkn, rvn, rb = _streams(seed, 6)
+    std = 1.0 / np.sqrt(D)
+    n_chunks = L // chunk
+    q = _normal(rq, (R, Hq, D), 1.0)
+    kc = _normal(rk, (Hkv, L, D), std)
+    boosted = np.stack([np.sort(rb.choice(n_chunks, size=n_boost, replace=False))
+                        for _ in range(Hkv)]).astype(np.int32) if n_boost else \
+        np.zeros((Hkv, 0), np.int32)
+    for g in range(Hkv):
+        for c in boosted[g]:
+            kc[g, c * chunk:(c + 1) * chunk, :] *= np.float32(boost)
+    vc = _normal(rv, (Hkv, L, D), std)
+    kn = _normal(rkn, (Hkv, R, D), std)
+    vn = _normal(rvn, (Hkv, R, D), std)
+    return PartialCase(name, BF16, R, Hq, Hkv, D, L, chunk, k, float(1.0 / np.sqrt(D)),
+                       f32_to_bf16_bits(q), f32_to_bf16_bits(kc), f32_to_bf16_bits(vc),
+                       f32_to_bf16_bits(kn), f32_to_bf16_bits(vn), boosted)
+
+
+def workload(name: str, *, L: Optional[int] = None, seed: Optional[int] = None):
+    """The named workloads; ``L`` shrinks the cache for quick tests."""
+    if name == "tiny":
+        return make_verify(name, dtype=F32, Hq=4, Hkv=1, D=64, L=512 if L is None else L,
+                           seed=0 if seed is None else seed, with_chains=False)
+    if name == "llama8b_20k":
+        return make_verify(name, dtype=BF16, Hq=32, Hkv=8, D=128, L=20480 if L is None else L,
+                           seed=1 if seed is None else seed, with_chains=True)
+    if name == "llama8b_100k":
+        return make_verify(name, dtype=BF16, Hq=32, Hkv=8, D=128, L=102400 if L is None else L,
+                           seed=2 if seed is None else seed, with_chains=True)
+    if name == "partial_100k":
+        return make_partial(name, L=102400 if L is None else L, seed=3 if seed is None else seed)
+    if name == "llama2_mha_100k":
+        return make_verify(name, dtype=BF16, Hq=32, Hkv=32, D=128, L=102400 if L is None else L,
+                           seed=4 if seed is None else seed, with_chains=True)
+    raise KeyError(name)
+
+
+WORKLOADS = ("tiny", "llama8b_20k", "llama8b_100k", "partial_100k", "llama2_mha_100k")

@@ -1,0 +1,42 @@
+"""CPU oracle for the tree-verify attention and the partial-KV-cache step.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. The product path (the
+HIP library and its Python binding) never imports, calls or links it, and this
+package imports nothing from the product path.
+
+Everything here is plain numpy in float64: the plain definitions of what the
+fast path computes, with no blocking, splitting or fusion. bf16 inputs arrive
+as uint16 bit patterns and are widened exactly to float64 here.
+
+Functions and the passages they follow (TokenSwift pages):
+
+* ``ancestor_mask``      the tree mask over draft tokens (tool listing, "How it
+                          works": tree-based attention over the candidates).
+* ``verify_attn_ref``     masked softmax attention of the draft queries over
+                          the full cache plus their own ancestors (tool listing,
+                          "How it works": drafts fed to the LLM with the full
+                          KV cache).
+* ``draft_attn_ref``      the same over the gathered partial cache with a
+                          causal chain of new tokens (tool listing, "How it
+                          works": the model with a partial KV cache outputs 4
+                          logits in one forward pass).
+* ``importance_ref``      query-key importance per chunk (summary page,
+                          "Approach": partial cache ranked by query-key
+                          importance).
+* ``topk_ref``            the highest-scoring chunks up to the budget
+                          (model card CLI example: retrieval budget 4096).
+* ``gather_ref``          the partial cache built from the chosen chunks.
+
+Pinned by ``tests/test_oracle_*.py`` (brute force in 50-digit arithmetic,
+reductions to torch's scaled-dot-product attention, closed forms, a rank-count
+definition of top-k). The importance reduction order (max over the grouped
+heads, mean over tokens and recent queries) is a reading of the pages: the
+pages name query-key importance but not the reduction, so that choice is
+pinned only by its own definition.
+"""
+from .attention import ancestor_mask, verify_attn_ref, draft_attn_ref, widen
+from .partial_kv import importance_ref, topk_ref, gather_ref
+
+__all__ = ["ancestor_mask", "verify_attn_ref", "draft_attn_ref", "widen",
+           "importance_ref", "topk_ref", "gather_ref"]
