@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the TokenSwift-style hot path on one MI355X.
+
+One step = one pass of the whole path for one LLaMA3.1-8B-shaped layer
+(32 query heads, 8 KV heads, head_dim 128, bf16) over a 102,400-token cache:
+
+  1. tree-verify attention of 120 draft queries ([1,3,3,3] tree + 20 four-token
+     chains) over the full cache: split-K kernel, then log-sum-exp merge;
+  2. partial-KV refresh: chunk importance from the 4 latest queries ->
+     top-64 of 1600 chunks per KV head -> gather of the 4096-token partial cache;
+  3. the 4-query draft attention over the partial cache.
+
+Inputs are seeded synthetic tensors resident in HBM before timing starts
+(verify inputs: seed 2; partial-KV inputs: seed 3, with 8 chunks per KV head
+carrying 3x keys). Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--cpu-heads H] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per tree-verify step @100K KV (LLaMA3.1-8B layer shape) + % HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="KV heads of the step the CPU oracle runs for the baseline (of 8)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def to_dev(a, dtype, dev):
+    import torch
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_kv_ts_amd import inputs, ops
+
+    dev = torch.device("cuda:0")
+    ops.lib()   # fail loudly if the library is missing
+
+    t0 = time.time()
+    vc = inputs.workload("llama8b_100k")
+    pc = inputs.workload("partial_100k")
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    # ---- device-resident inputs and preallocated outputs -------------------
+    q = to_dev(vc.q, "bf16", dev)
+    kc, vcache = to_dev(vc.k_cache, "bf16", dev), to_dev(vc.v_cache, "bf16", dev)
+    kd, vd = to_dev(vc.k_draft, "bf16", dev), to_dev(vc.v_draft, "bf16", dev)
+    parent = to_dev(vc.parent, "i32", dev)
+    T, Hq, Hkv, D, L = vc.T, vc.Hq, vc.Hkv, vc.D, vc.L
+    S = ops.num_splits(T, Hq, Hkv, D, L, torch.bfloat16)
+    o_part = torch.empty((S, T, Hq, D), dtype=torch.float32, device=dev)
+    l_part = torch.empty((S, T, Hq), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+
+    pq = to_dev(pc.q, "bf16", dev)
+    pk, pv = to_dev(pc.k_cache, "bf16", dev), to_dev(pc.v_cache, "bf16", dev)
+    pkn, pvn = to_dev(pc.k_new, "bf16", dev), to_dev(pc.v_new, "bf16", dev)
+    scores = torch.empty((pc.Hkv, pc.n_chunks), dtype=torch.float32, device=dev)
+    idx = torch.empty((pc.Hkv, pc.k), dtype=torch.int32, device=dev)
+    idx_s = torch.empty((pc.Hkv, pc.k), dtype=torch.float32, device=dev)
+    kp = torch.empty((pc.Hkv, pc.k * pc.chunk, pc.D), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    dout = torch.empty_like(pq)
+    dlse = torch.empty((pc.R, pc.Hq), dtype=torch.float32, device=dev)
+    dws = ops.alloc_workspace(ops.lib().ts_partial_draft_attn_workspace(
+        pc.R, pc.Hq, pc.Hkv, pc.D, pc.k * pc.chunk, ops.TS_BF16, 0), dev)
+
+    names = ["verify_split", "verify_merge", "importance", "topk", "gather", "draft_attn"]
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        ops.tree_verify_attn_partials(q, kc, vcache, kd, vd, parent, scale=vc.scale,
+                                      o_part=o_part, l_part=l_part)
+        rec(1)
+        ops.attn_merge(o_part, l_part, out=out, lse=lse)
+        rec(2)
+        ops.kv_importance_score(pq, pk, pc.chunk, scale=pc.scale, scores=scores)
+        rec(3)
+        ops.kv_topk_select(scores, pc.k, chunk_idx=idx, chunk_score=idx_s)
+        rec(4)
+        ops.kv_gather(pk, pv, idx, pc.chunk, k_part=kp, v_part=vp)
+        rec(5)
+        ops.partial_draft_attn(pq, kp, vp, pkn, pvn, scale=pc.scale, out=dout, lse=dlse,
+                               workspace=dws)
+        rec(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+
+    per = {n: [] for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # us
+    avg = {n: float(np.mean(v)) for n, v in per.items()}
+    med = {n: float(np.median(v)) for n, v in per.items()}
+
+    # ---- roofline of the dominant kernel (verify split-K) -------------------
+    vis = 0
+    par = vc.parent
+    for t in range(T):           # |A(t)| summed over draft rows (the ancestor walk of the mask)
+        a = t
+        while a >= 0:
+            vis += 1
+            a = int(par[a])
+    G = Hq // Hkv
+    pairs = Hq * (T * L + vis)                  # (query row, visible key) pairs
+    flops = 4.0 * D * pairs                     # QK^T and PV, 2 flops per MAC
+    kv_bytes = 2.0 * Hkv * L * D * 2            # K and V of the cache, read once
+    t_split = avg["verify_split"] * 1e-6
+    achieved = flops / t_split / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "kernel": "verify split-K (attn_split)",
+                "algorithmic_flops": flops, "algorithmic_bytes": kv_bytes,
+                "hbm_GBs": round(kv_bytes / t_split / 1e9, 1),
+                "hbm_frac": round(kv_bytes / t_split / 1e9 / HBM_PEAK_GBS, 4)}
+
+    res = {
+        "metric": METRIC,
+        "value": round(ms_per_step * 1e3, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3.1-8b layer, 102400-token bf16 KV cache: tree-verify of 120 drafts "
+                               "([1,3,3,3] tree + 20 4-gram chains) + partial-KV refresh (4 queries, "
+                               "64 of 1600 64-token chunks) + 4-query draft attention",
+                   "T": T, "Hq": Hq, "Hkv": Hkv, "head_dim": D, "kv_len": L, "splits": S,
+                   "chunk": pc.chunk, "topk": pc.k},
+        "verify_us": round(avg["verify_split"] + avg["verify_merge"], 2),
+        "verify_hbm_frac": round(kv_bytes / ((avg["verify_split"] + avg["verify_merge"]) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_us_avg": {n: round(v, 2) for n, v in avg.items()},
+        "kernel_us_median": {n: round(v, 2) for n, v in med.items()},
+        "roofline": roofline,
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(vc, pc, args.cpu_heads)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(vc, pc, heads):
+    """The oracle on `heads` of the 8 KV heads of one step, scaled to the step."""
+    import oracle
+    try:
+        import threadpoolctl
+        blas = threadpoolctl.threadpool_info()
+        threads = max([b.get("num_threads", 1) for b in blas] or [1])
+    except Exception:
+        threads = None
+    cores = len(os.sched_getaffinity(0))
+    hs = list(range(heads))
+    t0 = time.perf_counter()
+    oracle.verify_attn_ref(vc.q, vc.k_cache, vc.v_cache, vc.k_draft, vc.v_draft, vc.parent,
+                           vc.scale, "bf16", heads=hs)
+    s = oracle.importance_ref(pc.q, pc.k_cache, pc.scale, pc.chunk, "bf16", heads=hs)
+    idx, _ = oracle.topk_ref(s[hs], pc.k)
+    kp, vp = oracle.gather_ref(pc.k_cache[hs], pc.v_cache[hs], idx, pc.chunk)
+    G = pc.Hq // pc.Hkv
+    oracle.draft_attn_ref(pc.q[:, :heads * G], kp, vp, pc.k_new[hs], pc.v_new[hs], pc.scale, "bf16")
+    dt = time.perf_counter() - t0
+    return {"value": round(dt * 1e6 * vc.Hkv / heads, 1), "unit": "us", "cores": threads or cores,
+            "host_cores": cores, "kind": "oracle",
+            "sample": f"{heads} of {vc.Hkv} KV heads of one step (verify + importance + top-k + "
+                      f"gather + draft attention), float64 numpy, time x{vc.Hkv / heads:g}"}
+
+
+if __name__ == "__main__":
+    main()

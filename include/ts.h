@@ -1,0 +1,191 @@
+/*
+ * ts.h -- C ABI of the TokenSwift-style verify/draft attention and dynamic
+ * partial-KV-cache kernels for AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute follows the TokenSwift pages:
+ *   - tool listing, "How it works": the drafts (a candidate tree built with
+ *     tree-based attention, plus retrieved 4-grams) are fed to the target
+ *     model with the FULL KV cache; the model with a PARTIAL KV cache and
+ *     three linear heads drafts 4 tokens in one forward pass;
+ *   - summary page, "Approach": the partial KV cache is re-ranked dynamically
+ *     by query-key importance;
+ *   - model card, command-line example: retrieval budget 4096 tokens, gamma 4,
+ *     ngram_topk 20, generation up to 102400 tokens.
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no device memory and keeps no state besides a thread-local
+ *     error message. Scratch space is passed in as `workspace`.
+ *   - Element type `ts_dtype`: TS_BF16 (uint16 bit patterns of bfloat16) or
+ *     TS_F32. Accumulation is always fp32. Outputs of attention are written in
+ *     the input type (bf16 rounded to nearest even); LSE and scores in fp32.
+ *   - Layouts are row-major and dense in the last dimension, e.g. q[T][Hq][D]
+ *     means element (t, h, d) at q + (t*Hq + h)*D + d.
+ *   - GQA: query head h reads KV head h / (Hq/Hkv) (contiguous groups).
+ *   - Tensor pointers must be 16-byte aligned; D must be 64 or 128.
+ *   - Every call validates its arguments on the host and returns a non-zero
+ *     ts_status BEFORE launching anything when they are bad; ts_last_error()
+ *     then describes the problem. On success the work is only enqueued on
+ *     `stream` (asynchronous); faults surface at the caller's next sync.
+ *   - Calls are re-entrant. Two calls that share a workspace must be ordered
+ *     (same stream, or synchronised).
+ */
+#ifndef TS_H_
+#define TS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ts_status {
+  TS_OK = 0,
+  TS_ERR_INVALID_ARG = 1, /* null/misaligned pointer, inconsistent sizes    */
+  TS_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels handle  */
+  TS_ERR_WORKSPACE = 3,   /* workspace smaller than the size query returns  */
+  TS_ERR_HIP = 4          /* a HIP launch failed; message from the runtime  */
+} ts_status;
+
+typedef enum ts_dtype { TS_F32 = 0, TS_BF16 = 1 } ts_dtype;
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* ts_last_error(void);
+
+/* ABI version of this header (bumped on any signature change). */
+int ts_abi_version(void);
+
+#define TS_ABI_VERSION 1
+#define TS_MAX_DRAFT 256 /* max draft tokens T of one verify call */
+
+/* ------------------------------------------------------------------------
+ * Tree-verify attention (tool listing, "How it works": drafts are fed to the
+ * target model with the full KV cache under tree-based attention).
+ *
+ * For draft row t in [0,T), query head h, g = h / (Hq/Hkv):
+ *   A(t) = {t} + ancestors of t along parent[]      (ancestor-or-self mask)
+ *   keys  = cached tokens j in [0, L) of head g  +  draft tokens a in A(t)
+ *   s     = scale * <q[t,h], k>
+ *   out[t,h] = softmax(s) . v          lse[t,h] = ln sum exp(s)   (natural log)
+ *
+ *   q        [T][Hq][D]                  draft queries (already position-encoded)
+ *   k_cache  [Hkv][cache_stride][D]      rows [0, L) are read; cache_stride >= L
+ *   v_cache  same layout as k_cache
+ *   k_draft  [Hkv][T][D]                 K/V of the T drafts (not yet in the cache)
+ *   v_draft  [Hkv][T][D]
+ *   parent   int32 [T] on the device, parent[t] in [-1, t); -1 marks a root, so
+ *            forests (tree + independent 4-gram chains) are allowed. Entries
+ *            outside [-1, t) are treated as -1 (never read out of bounds).
+ *   out      [T][Hq][D]   written in `dtype`
+ *   lse      [T][Hq] fp32, may be NULL
+ *   scale    softmax scale (usually 1/sqrt(D))
+ *   num_splits  0 = library choice; otherwise the number of key ranges the
+ *            work is split into (results agree across choices up to fp32
+ *            rounding). Must match the value given to the size query.
+ *   workspace   >= ts_tree_verify_attn_workspace(...) bytes, 256-byte aligned;
+ *            contents on entry are ignored.
+ * Supported: T in [1, 256], Hq % Hkv == 0, Hq/Hkv <= 16, D in {64, 128}, L >= 0.
+ * ---------------------------------------------------------------------- */
+size_t ts_tree_verify_attn_workspace(int T, int Hq, int Hkv, int D, int64_t L,
+                                     ts_dtype dtype, int num_splits);
+
+ts_status ts_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                              int64_t cache_stride, const void* k_draft, const void* v_draft,
+                              const int32_t* parent, void* out, float* lse,
+                              int T, int Hq, int Hkv, int D, int64_t L, float scale,
+                              ts_dtype dtype, int num_splits,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The two phases of ts_tree_verify_attn, for callers that merge partial
+ * results themselves (e.g. partials computed on several devices, each over
+ * its own slice of the cache -- merging across devices is the same log-sum-
+ * exp rule as merging across splits).
+ *
+ * ts_tree_verify_attn_partials writes, for every split s in [0, n_splits):
+ *   o_part [n_splits][T][Hq][D] fp32   softmax(s restricted to split s) . v
+ *   l_part [n_splits][T][Hq]    fp32   ln sum exp(s) over split s (-inf if empty)
+ * with n_splits = ts_tree_verify_attn_num_splits(...). Split s covers a
+ * contiguous range of cached tokens; the draft tokens belong to the last split.
+ * ts_attn_merge combines `n_parts` such partials:
+ *   lse = ln sum_s exp(l_part[s]);  out = sum_s exp(l_part[s] - lse) * o_part[s]. */
+int ts_tree_verify_attn_num_splits(int T, int Hq, int Hkv, int D, int64_t L,
+                                   ts_dtype dtype, int num_splits);
+
+ts_status ts_tree_verify_attn_partials(const void* q, const void* k_cache, const void* v_cache,
+                                       int64_t cache_stride, const void* k_draft,
+                                       const void* v_draft, const int32_t* parent,
+                                       float* o_part, float* l_part,
+                                       int T, int Hq, int Hkv, int D, int64_t L, float scale,
+                                       ts_dtype dtype, int num_splits, hipStream_t stream);
+
+ts_status ts_attn_merge(const float* o_part, const float* l_part, int n_parts,
+                        int rows, int D, void* out, float* lse, ts_dtype dtype,
+                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Chunk importance (summary page, "Approach": the partial cache is ranked by
+ * query-key importance). For KV head g and chunk c = tokens [c*chunk, (c+1)*chunk):
+ *   u[r, j]     = max over query heads h of group g of  scale * <q_recent[r,h], k[g,j]>
+ *   scores[g,c] = mean over r in [0,R) and j in chunk c of u[r, j]
+ * (max over the grouped heads, mean over tokens and recent queries: the pages
+ * name the importance but not its reduction; this is the reading used.)
+ *
+ *   q_recent [R][Hq][D]            the R most recent queries (R = gamma = 4)
+ *   k_cache  [Hkv][cache_stride][D] rows [0, L) read; V is never read
+ *   scores   [Hkv][L/chunk] fp32
+ * Supported: L % chunk == 0, chunk in [1, 4096], R*(Hq/Hkv) <= 64, Hq/Hkv in
+ * {1,2,4,8,16}, D in {64,128}.
+ * ---------------------------------------------------------------------- */
+ts_status ts_kv_importance_score(const void* q_recent, const void* k_cache, int64_t cache_stride,
+                                 float* scores, int R, int Hq, int Hkv, int D, int64_t L,
+                                 int chunk, float scale, ts_dtype dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Top-k chunk selection (model card CLI: retrieval budget 4096 tokens =
+ * k chunks of `chunk` tokens). Per KV head independently: the k chunks of
+ * highest score, ties broken toward the lower chunk index, written in
+ * ASCENDING chunk index (so a gathered cache keeps time order).
+ *   scores      [Hkv][n_chunks] fp32 (NaN not allowed)
+ *   chunk_idx   [Hkv][k] int32 out
+ *   chunk_score [Hkv][k] fp32 out, may be NULL (scores of the chosen chunks)
+ * Supported: 1 <= k <= n_chunks <= 65536. No workspace.
+ * ---------------------------------------------------------------------- */
+ts_status ts_kv_topk_select(const float* scores, int Hkv, int n_chunks, int k,
+                            int32_t* chunk_idx, float* chunk_score, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Gather of the chosen chunks into a partial cache (summary page, "Approach").
+ *   k_part[g][i*chunk + u][:] = k_cache[g][chunk_idx[g][i]*chunk + u][:]
+ *   (and the same for V), bit-exact copies.
+ *   k_part, v_part [Hkv][k*chunk][D]. An index outside [0, L/chunk) writes
+ *   zeros for that chunk (never reads out of bounds).
+ * Supported: L % chunk == 0, chunk*D*elem_size a multiple of 16 bytes.
+ * ---------------------------------------------------------------------- */
+ts_status ts_kv_gather(const void* k_cache, const void* v_cache, int64_t cache_stride,
+                       const int32_t* chunk_idx, int Hkv, int k, int chunk, int D, int64_t L,
+                       void* k_part, void* v_part, ts_dtype dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Draft attention over the partial cache (tool listing, "How it works": the
+ * target model with a partial KV cache drafts 4 tokens in one forward pass).
+ * Tq new tokens attend to all P gathered tokens and causally among
+ * themselves: exactly ts_tree_verify_attn with the chain parent[t] = t-1.
+ *   q [Tq][Hq][D]; k_part, v_part [Hkv][P][D]; k_new, v_new [Hkv][Tq][D];
+ *   out [Tq][Hq][D]; lse [Tq][Hq] fp32 (may be NULL).
+ * Supported: as ts_tree_verify_attn with T = Tq.
+ * ---------------------------------------------------------------------- */
+size_t ts_partial_draft_attn_workspace(int Tq, int Hq, int Hkv, int D, int64_t P,
+                                       ts_dtype dtype, int num_splits);
+
+ts_status ts_partial_draft_attn(const void* q, const void* k_part, const void* v_part,
+                                const void* k_new, const void* v_new, void* out, float* lse,
+                                int Tq, int Hq, int Hkv, int D, int64_t P, float scale,
+                                ts_dtype dtype, int num_splits,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TS_H_ */

@@ -1,0 +1,277 @@
+// C ABI of the library: argument validation, work planning, launches.
+// Nothing here allocates device memory or synchronises; every check runs on
+// the host before the first HIP call, so a rejected call has no side effect.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ts_status fail(ts_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ts_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TS_OK;
+  return fail(TS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(ts_dtype d) { return d == TS_BF16 ? 2 : 4; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Rows of one workgroup of the matrix-core kernel (see attn_mfma.hip).
+constexpr int kMfmaRows = 256;
+constexpr int kValuRows = 16;
+// MI355X: 256 compute units. Target roughly this many workgroups of the
+// matrix-core kernel (one per CU) and four per CU for the vector-ALU kernel.
+constexpr int kCUs = 256;
+
+ts_status check_attn_shape(const char* fn, int T, int Hq, int Hkv, int D, int64_t L,
+                           ts_dtype dtype, int num_splits) {
+  if (dtype != TS_F32 && dtype != TS_BF16) return fail(TS_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (T < 1 || T > TS_MAX_DRAFT) return fail(TS_ERR_UNSUPPORTED, "%s: T=%d outside [1, %d]", fn, T, TS_MAX_DRAFT);
+  if (Hq < 1 || Hkv < 1) return fail(TS_ERR_INVALID_ARG, "%s: Hq=%d Hkv=%d must be >= 1", fn, Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(TS_ERR_INVALID_ARG, "%s: Hq=%d not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (Hq / Hkv > 16) return fail(TS_ERR_UNSUPPORTED, "%s: group size Hq/Hkv=%d > 16", fn, Hq / Hkv);
+  if (Hkv > 65535) return fail(TS_ERR_UNSUPPORTED, "%s: Hkv=%d > 65535", fn, Hkv);
+  if (D != 64 && D != 128) return fail(TS_ERR_UNSUPPORTED, "%s: D=%d (supported: 64, 128)", fn, D);
+  if (L < 0) return fail(TS_ERR_INVALID_ARG, "%s: L=%lld < 0", fn, (long long)L);
+  if (L > (int64_t)1 << 30) return fail(TS_ERR_UNSUPPORTED, "%s: L=%lld > 2^30", fn, (long long)L);
+  if (num_splits < 0 || num_splits > 65535) return fail(TS_ERR_INVALID_ARG, "%s: num_splits=%d", fn, num_splits);
+  return TS_OK;
+}
+
+}  // namespace
+
+namespace ts {
+
+AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype, int num_splits) {
+  AttnPlan p{};
+  const int G = Hq / Hkv;
+  p.rows_per_head = T * G;
+  p.path = kPathValu;
+  (void)D;
+  (void)dtype;
+  p.rows_per_group = p.path == kPathMfma ? kMfmaRows : kValuRows;
+  p.n_rowgroups = (p.rows_per_head + p.rows_per_group - 1) / p.rows_per_group;
+  p.n_cache_tiles = (int)((L + kTile - 1) / kTile);
+  p.n_draft_tiles = (T + kTile - 1) / kTile;
+  p.n_virtual = p.n_cache_tiles + p.n_draft_tiles;
+  int s = num_splits;
+  if (s <= 0) {
+    const int per_cu = p.path == kPathMfma ? 1 : 4;
+    const int64_t groups = (int64_t)Hkv * p.n_rowgroups;
+    s = (int)((kCUs * per_cu + groups - 1) / groups);
+    if (s < 1) s = 1;
+  }
+  if (s > p.n_virtual) s = p.n_virtual;
+  p.tiles_per_split = (p.n_virtual + s - 1) / s;
+  p.n_splits = (p.n_virtual + p.tiles_per_split - 1) / p.tiles_per_split;
+  return p;
+}
+
+}  // namespace ts
+
+using namespace ts;
+
+extern "C" {
+
+const char* ts_last_error(void) { return g_last_error.c_str(); }
+
+int ts_abi_version(void) { return TS_ABI_VERSION; }
+
+int ts_tree_verify_attn_num_splits(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype,
+                                   int num_splits) {
+  if (check_attn_shape("ts_tree_verify_attn_num_splits", T, Hq, Hkv, D, L, dtype, num_splits) != TS_OK)
+    return -1;
+  return plan_attention(T, Hq, Hkv, D, L, dtype, num_splits).n_splits;
+}
+
+size_t ts_tree_verify_attn_workspace(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype,
+                                     int num_splits) {
+  if (check_attn_shape("ts_tree_verify_attn_workspace", T, Hq, Hkv, D, L, dtype, num_splits) != TS_OK)
+    return 0;
+  const AttnPlan p = plan_attention(T, Hq, Hkv, D, L, dtype, num_splits);
+  const size_t rows = (size_t)T * Hq;
+  return align_up((size_t)p.n_splits * rows * D * sizeof(float)) +
+         align_up((size_t)p.n_splits * rows * sizeof(float));
+}
+
+static ts_status attn_common(const char* fn, const void* q, const void* kc, const void* vc,
+                             int64_t cache_stride, const void* kd, const void* vd,
+                             const int32_t* parent, bool need_parent, float* o_part, float* l_part,
+                             int T, int Hq, int Hkv, int D, int64_t L, float scale,
+                             ts_dtype dtype, int num_splits, hipStream_t stream) {
+  ts_status st = check_attn_shape(fn, T, Hq, Hkv, D, L, dtype, num_splits);
+  if (st != TS_OK) return st;
+  if (!q || !kd || !vd || !o_part || !l_part) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (L > 0 && (!kc || !vc)) return fail(TS_ERR_INVALID_ARG, "%s: null cache pointer with L=%lld", fn, (long long)L);
+  if (need_parent && !parent) return fail(TS_ERR_INVALID_ARG, "%s: parent is null", fn);
+  if (!aligned16(q) || !aligned16(kd) || !aligned16(vd) || !aligned16(o_part) ||
+      (L > 0 && (!aligned16(kc) || !aligned16(vc))))
+    return fail(TS_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (((uintptr_t)l_part & 3u) != 0) return fail(TS_ERR_INVALID_ARG, "%s: l_part misaligned", fn);
+  if (cache_stride < L) return fail(TS_ERR_INVALID_ARG, "%s: cache_stride=%lld < L=%lld", fn, (long long)cache_stride, (long long)L);
+  if (!std::isfinite(scale) || scale == 0.f) return fail(TS_ERR_INVALID_ARG, "%s: scale must be finite and non-zero", fn);
+
+  AttnArgs a{};
+  a.q = q; a.kc = kc; a.vc = vc; a.cache_stride = cache_stride; a.kd = kd; a.vd = vd;
+  a.parent = parent; a.o_part = o_part; a.l_part = l_part;
+  a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D; a.L = L;
+  a.scale_log2 = scale * kLog2e;
+  a.plan = plan_attention(T, Hq, Hkv, D, L, dtype, num_splits);
+  hipError_t e = a.plan.path == kPathMfma ? launch_attn_split_mfma(a, stream)
+                                          : launch_attn_split_valu(a, dtype, stream);
+  return from_hip(e, fn);
+}
+
+ts_status ts_tree_verify_attn_partials(const void* q, const void* k_cache, const void* v_cache,
+                                       int64_t cache_stride, const void* k_draft,
+                                       const void* v_draft, const int32_t* parent,
+                                       float* o_part, float* l_part, int T, int Hq, int Hkv,
+                                       int D, int64_t L, float scale, ts_dtype dtype,
+                                       int num_splits, hipStream_t stream) {
+  return attn_common("ts_tree_verify_attn_partials", q, k_cache, v_cache, cache_stride, k_draft,
+                     v_draft, parent, true, o_part, l_part, T, Hq, Hkv, D, L, scale, dtype,
+                     num_splits, stream);
+}
+
+ts_status ts_attn_merge(const float* o_part, const float* l_part, int n_parts, int rows, int D,
+                        void* out, float* lse, ts_dtype dtype, hipStream_t stream) {
+  const char* fn = "ts_attn_merge";
+  if (dtype != TS_F32 && dtype != TS_BF16) return fail(TS_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (!o_part || !l_part || !out) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (n_parts < 1 || rows < 1) return fail(TS_ERR_INVALID_ARG, "%s: n_parts=%d rows=%d must be >= 1", fn, n_parts, rows);
+  if (D != 64 && D != 128) return fail(TS_ERR_UNSUPPORTED, "%s: D=%d (supported: 64, 128)", fn, D);
+  if (!aligned16(o_part) || ((uintptr_t)out & 7u) != 0)
+    return fail(TS_ERR_INVALID_ARG, "%s: o_part must be 16-byte and out 8-byte aligned", fn);
+  return from_hip(launch_attn_merge(o_part, l_part, n_parts, rows, D, out, lse, dtype, stream), fn);
+}
+
+static ts_status verify_like(const char* fn, const void* q, const void* kc, const void* vc,
+                             int64_t cache_stride, const void* kd, const void* vd,
+                             const int32_t* parent, bool need_parent, void* out, float* lse,
+                             int T, int Hq, int Hkv, int D, int64_t L, float scale,
+                             ts_dtype dtype, int num_splits, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  ts_status st = check_attn_shape(fn, T, Hq, Hkv, D, L, dtype, num_splits);
+  if (st != TS_OK) return st;
+  if (!out) return fail(TS_ERR_INVALID_ARG, "%s: out is null", fn);
+  if (!aligned16(out)) return fail(TS_ERR_INVALID_ARG, "%s: out must be 16-byte aligned", fn);
+  if (lse && ((uintptr_t)lse & 3u)) return fail(TS_ERR_INVALID_ARG, "%s: lse misaligned", fn);
+  const size_t need = ts_tree_verify_attn_workspace(T, Hq, Hkv, D, L, dtype, num_splits);
+  if (!workspace) return fail(TS_ERR_INVALID_ARG, "%s: workspace is null", fn);
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return fail(TS_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  if (workspace_bytes < need)
+    return fail(TS_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
+  const AttnPlan p = plan_attention(T, Hq, Hkv, D, L, dtype, num_splits);
+  const size_t rows = (size_t)T * Hq;
+  float* o_part = static_cast<float*>(workspace);
+  float* l_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           align_up((size_t)p.n_splits * rows * D * sizeof(float)));
+  st = attn_common(fn, q, kc, vc, cache_stride, kd, vd, parent, need_parent, o_part, l_part, T,
+                   Hq, Hkv, D, L, scale, dtype, num_splits, stream);
+  if (st != TS_OK) return st;
+  return from_hip(launch_attn_merge(o_part, l_part, p.n_splits, (int)rows, D, out, lse, dtype, stream), fn);
+}
+
+ts_status ts_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                              int64_t cache_stride, const void* k_draft, const void* v_draft,
+                              const int32_t* parent, void* out, float* lse, int T, int Hq,
+                              int Hkv, int D, int64_t L, float scale, ts_dtype dtype,
+                              int num_splits, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  return verify_like("ts_tree_verify_attn", q, k_cache, v_cache, cache_stride, k_draft, v_draft,
+                     parent, true, out, lse, T, Hq, Hkv, D, L, scale, dtype, num_splits,
+                     workspace, workspace_bytes, stream);
+}
+
+size_t ts_partial_draft_attn_workspace(int Tq, int Hq, int Hkv, int D, int64_t P, ts_dtype dtype,
+                                       int num_splits) {
+  return ts_tree_verify_attn_workspace(Tq, Hq, Hkv, D, P, dtype, num_splits);
+}
+
+ts_status ts_partial_draft_attn(const void* q, const void* k_part, const void* v_part,
+                                const void* k_new, const void* v_new, void* out, float* lse,
+                                int Tq, int Hq, int Hkv, int D, int64_t P, float scale,
+                                ts_dtype dtype, int num_splits, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return verify_like("ts_partial_draft_attn", q, k_part, v_part, P, k_new, v_new, nullptr, false,
+                     out, lse, Tq, Hq, Hkv, D, P, scale, dtype, num_splits, workspace,
+                     workspace_bytes, stream);
+}
+
+ts_status ts_kv_importance_score(const void* q_recent, const void* k_cache, int64_t cache_stride,
+                                 float* scores, int R, int Hq, int Hkv, int D, int64_t L,
+                                 int chunk, float scale, ts_dtype dtype, hipStream_t stream) {
+  const char* fn = "ts_kv_importance_score";
+  if (dtype != TS_F32 && dtype != TS_BF16) return fail(TS_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (!q_recent || !k_cache || !scores) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned16(q_recent) || !aligned16(k_cache) || ((uintptr_t)scores & 3u))
+    return fail(TS_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (R < 1 || Hq < 1 || Hkv < 1) return fail(TS_ERR_INVALID_ARG, "%s: R, Hq, Hkv must be >= 1", fn);
+  if (Hq % Hkv) return fail(TS_ERR_INVALID_ARG, "%s: Hq=%d not a multiple of Hkv=%d", fn, Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G > 16 || (G & (G - 1))) return fail(TS_ERR_UNSUPPORTED, "%s: group size %d not a power of two <= 16", fn, G);
+  if (R * G > 64) return fail(TS_ERR_UNSUPPORTED, "%s: R*G=%d > 64", fn, R * G);
+  if (Hkv > 65535) return fail(TS_ERR_UNSUPPORTED, "%s: Hkv=%d > 65535", fn, Hkv);
+  if (D != 64 && D != 128) return fail(TS_ERR_UNSUPPORTED, "%s: D=%d (supported: 64, 128)", fn, D);
+  if (chunk < 1 || chunk > 4096) return fail(TS_ERR_UNSUPPORTED, "%s: chunk=%d outside [1, 4096]", fn, chunk);
+  if (L < 0) return fail(TS_ERR_INVALID_ARG, "%s: L < 0", fn);
+  if (L % chunk) return fail(TS_ERR_UNSUPPORTED, "%s: L=%lld not a multiple of chunk=%d", fn, (long long)L, chunk);
+  if (L / chunk > (1 << 24)) return fail(TS_ERR_UNSUPPORTED, "%s: too many chunks", fn);
+  if (cache_stride < L) return fail(TS_ERR_INVALID_ARG, "%s: cache_stride < L", fn);
+  if (!std::isfinite(scale)) return fail(TS_ERR_INVALID_ARG, "%s: scale not finite", fn);
+  return from_hip(launch_importance(q_recent, k_cache, cache_stride, scores, R, Hq, Hkv, D, L,
+                                    chunk, scale, dtype, stream), fn);
+}
+
+ts_status ts_kv_topk_select(const float* scores, int Hkv, int n_chunks, int k,
+                            int32_t* chunk_idx, float* chunk_score, hipStream_t stream) {
+  const char* fn = "ts_kv_topk_select";
+  if (!scores || !chunk_idx) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (((uintptr_t)scores & 3u) || ((uintptr_t)chunk_idx & 3u) || ((uintptr_t)chunk_score & 3u))
+    return fail(TS_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  if (Hkv < 1 || Hkv > 65535) return fail(TS_ERR_INVALID_ARG, "%s: Hkv=%d", fn, Hkv);
+  if (n_chunks < 1 || n_chunks > 65536) return fail(TS_ERR_UNSUPPORTED, "%s: n_chunks=%d outside [1, 65536]", fn, n_chunks);
+  if (k < 1 || k > n_chunks) return fail(TS_ERR_INVALID_ARG, "%s: k=%d outside [1, n_chunks=%d]", fn, k, n_chunks);
+  return from_hip(launch_topk(scores, Hkv, n_chunks, k, chunk_idx, chunk_score, stream), fn);
+}
+
+ts_status ts_kv_gather(const void* k_cache, const void* v_cache, int64_t cache_stride,
+                       const int32_t* chunk_idx, int Hkv, int k, int chunk, int D, int64_t L,
+                       void* k_part, void* v_part, ts_dtype dtype, hipStream_t stream) {
+  const char* fn = "ts_kv_gather";
+  if (dtype != TS_F32 && dtype != TS_BF16) return fail(TS_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (!k_cache || !v_cache || !chunk_idx || !k_part || !v_part)
+    return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_part) || !aligned16(v_part) ||
+      ((uintptr_t)chunk_idx & 3u))
+    return fail(TS_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (Hkv < 1 || Hkv > 65535 || k < 1 || chunk < 1 || D < 1) return fail(TS_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (L < 0 || L % chunk) return fail(TS_ERR_UNSUPPORTED, "%s: L=%lld not a multiple of chunk=%d", fn, (long long)L, chunk);
+  if (cache_stride < L) return fail(TS_ERR_INVALID_ARG, "%s: cache_stride < L", fn);
+  if (((int64_t)chunk * D * elem_size(dtype)) % 16) return fail(TS_ERR_UNSUPPORTED, "%s: chunk*D*elem not a multiple of 16 bytes", fn);
+  if (((int64_t)cache_stride * D * elem_size(dtype)) % 16) return fail(TS_ERR_UNSUPPORTED, "%s: cache head stride not a multiple of 16 bytes", fn);
+  if (L / chunk > 2147483647LL) return fail(TS_ERR_UNSUPPORTED, "%s: too many chunks", fn);
+  return from_hip(launch_gather(k_cache, v_cache, cache_stride, chunk_idx, Hkv, k, chunk, D, L,
+                                k_part, v_part, elem_size(dtype), stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Shared device helpers and the host-side launch interface of the kernels.
+// gfx950 (CDNA4) only: 64-wide wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ts.h"
+
+namespace ts {
+
+constexpr int kWave = 64;
+constexpr int kTile = 64;          // keys per attention tile
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+typedef uint16_t bf16_t;           // bf16 bit pattern
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(bf16_t, h);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static float load(const float* p) { return *p; }
+  __device__ static void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ static float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ static void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// Load 8 consecutive elements (16 B for bf16, 2x16 B for fp32) as floats.
+__device__ __forceinline__ void load8(const bf16_t* p, float* o) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float* o) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+  o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Ancestor-or-self bitmask of the drafts, built in LDS from parent[]:
+// bit a of anc[t*words + a/32] is set iff a is t or an ancestor of t.
+// Entries of parent[] outside [-1, t) end the walk (treated as roots), so the
+// walk is bounded by t steps and never leaves [0, T). With parent == nullptr
+// the drafts form one causal chain (parent[t] = t - 1).
+__device__ __forceinline__ void build_ancestor_mask(const int32_t* parent, int T, int words,
+                                                    uint32_t* anc, int tid, int nthreads) {
+  for (int i = tid; i < T * words; i += nthreads) anc[i] = 0u;
+  __syncthreads();
+  for (int t = tid; t < T; t += nthreads) {
+    uint32_t* row = anc + t * words;
+    if (parent == nullptr) {
+      for (int w = 0; w < words; ++w) {
+        int lo = w * 32;
+        uint32_t bits = 0u;
+        if (t >= lo + 31) bits = 0xffffffffu;
+        else if (t >= lo) bits = (t - lo == 31) ? 0xffffffffu : ((1u << (t - lo + 1)) - 1u);
+        row[w] = bits;
+      }
+    } else {
+      int a = t;
+      while (a >= 0) {
+        row[a >> 5] |= 1u << (a & 31);
+        int p = parent[a];
+        a = (p >= 0 && p < a) ? p : -1;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// ----------------------------------------------------------------------------
+// Work decomposition of one masked split-K attention call.
+// ----------------------------------------------------------------------------
+enum AttnPath { kPathValu = 0, kPathMfma = 1 };
+
+struct AttnPlan {
+  int path;
+  int rows_per_head;    // T * G
+  int rows_per_group;   // rows of one workgroup
+  int n_rowgroups;
+  int n_cache_tiles;    // ceil(L / kTile)
+  int n_draft_tiles;    // ceil(T / kTile)
+  int n_virtual;        // cache tiles then draft tiles
+  int tiles_per_split;
+  int n_splits;
+};
+
+struct AttnArgs {
+  const void* q;            // [T][Hq][D]
+  const void* kc;           // [Hkv][cache_stride][D]
+  const void* vc;
+  int64_t cache_stride;
+  const void* kd;           // [Hkv][T][D]
+  const void* vd;
+  const int32_t* parent;    // [T] or nullptr = causal chain
+  float* o_part;            // [S][T][Hq][D]
+  float* l_part;            // [S][T][Hq]
+  int T, Hq, Hkv, G, D;
+  int64_t L;
+  float scale_log2;         // scale * log2(e)
+  AttnPlan plan;
+};
+
+AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype, int num_splits);
+
+// Launchers (return the hipGetLastError() of the launch).
+hipError_t launch_attn_split_valu(const AttnArgs& a, ts_dtype dtype, hipStream_t s);
+hipError_t launch_attn_split_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_merge(const float* o_part, const float* l_part, int n_parts, int rows,
+                             int D, void* out, float* lse, ts_dtype dtype, hipStream_t s);
+hipError_t launch_importance(const void* q, const void* kc, int64_t stride, float* scores,
+                             int R, int Hq, int Hkv, int D, int64_t L, int chunk, float scale,
+                             ts_dtype dtype, hipStream_t s);
+hipError_t launch_topk(const float* scores, int Hkv, int n, int k, int32_t* idx, float* val,
+                       hipStream_t s);
+hipError_t launch_gather(const void* kc, const void* vc, int64_t stride, const int32_t* idx,
+                         int Hkv, int k, int chunk, int D, int64_t L, void* kp, void* vp,
+                         int elem_bytes, hipStream_t s);
+
+}  // namespace ts

@@ -55,9 +55,14 @@ def _streams(seed: int, n: int) -> List[np.random.Generator]:
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16 (nearest, ties to even); returns uint16 bit patterns."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    if not np.isfinite(x).all():
+        raise ValueError("only finite values are rounded here")
+    u = x.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)          # finite inputs: u + 0x8000 < 2^32
+    lsb += np.uint32(0x7FFF)
+    lsb += u
+    lsb >>= np.uint32(16)
+    return lsb.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

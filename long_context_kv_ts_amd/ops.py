@@ -1,0 +1,327 @@
+"""Thin Python binding of ``libts.so`` (the C ABI declared in ``include/ts.h``).
+
+Argument marshalling only: torch tensors supply device memory, shapes and the
+current HIP stream; every step of the computation runs in the library's
+kernels. There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+
+Entry points (same names as the C functions, without the ``ts_`` prefix where
+noted): ``tree_verify_attn``, ``tree_verify_attn_partials``, ``attn_merge``,
+``kv_importance_score``, ``kv_topk_select``, ``kv_gather``,
+``partial_draft_attn``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libts.so")
+_lib = None
+
+TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_WORKSPACE, TS_ERR_HIP = range(5)
+TS_F32, TS_BF16 = 0, 1
+
+_c_void_p, _c_int, _c_i64, _c_f, _c_size = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                            ctypes.c_float, ctypes.c_size_t)
+
+# name -> (restype, argtypes); must mirror include/ts.h
+SIGNATURES = {
+    "ts_last_error": (ctypes.c_char_p, []),
+    "ts_abi_version": (_c_int, []),
+    "ts_tree_verify_attn_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int]),
+    "ts_tree_verify_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_void_p, _c_void_p,
+                                     _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                                     _c_i64, _c_f, _c_int, _c_int, _c_void_p, _c_size, _c_void_p]),
+    "ts_tree_verify_attn_num_splits": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int]),
+    "ts_tree_verify_attn_partials": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_void_p,
+                                              _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                              _c_int, _c_int, _c_int, _c_i64, _c_f, _c_int, _c_int,
+                                              _c_void_p]),
+    "ts_attn_merge": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                               _c_int, _c_void_p]),
+    "ts_kv_importance_score": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int,
+                                        _c_int, _c_int, _c_i64, _c_int, _c_f, _c_int, _c_void_p]),
+    "ts_kv_topk_select": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
+    "ts_kv_gather": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                              _c_i64, _c_void_p, _c_void_p, _c_int, _c_void_p]),
+    "ts_partial_draft_attn_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int]),
+    "ts_partial_draft_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                       _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_i64,
+                                       _c_f, _c_int, _c_int, _c_void_p, _c_size, _c_void_p]),
+}
+
+
+class TsError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[ts status {status}] {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libts.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m long_context_kv_ts_amd.build`")
+        l = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _check(status: int) -> None:
+    if status != TS_OK:
+        raise TsError(status, lib().ts_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TS_BF16
+    if t.dtype == torch.float32:
+        return TS_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: Optional[torch.Tensor], name: str, dim: int, dtype=None, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _cache_stride(t: torch.Tensor, name: str) -> int:
+    """Row stride (in tokens) of a [Hkv][stride][D] cache view whose last two
+    dims are dense; lets callers pass cache[:, :L] of a larger allocation."""
+    Hkv, L, D = t.shape
+    if t.stride(2) != 1 or (L > 1 and t.stride(1) != D):
+        raise ValueError(f"{name} must be dense in its last two dims")
+    if Hkv > 1 and t.stride(0) % D:
+        raise ValueError(f"{name} head stride must be a multiple of D")
+    return t.stride(0) // D if Hkv > 1 else max(L, 1)
+
+
+def _contig(t: torch.Tensor, name: str) -> None:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# workspace
+# ---------------------------------------------------------------------------
+def verify_workspace_bytes(T: int, Hq: int, Hkv: int, D: int, L: int, dtype: torch.dtype,
+                           num_splits: int = 0) -> int:
+    code = TS_BF16 if dtype == torch.bfloat16 else TS_F32
+    n = lib().ts_tree_verify_attn_workspace(T, Hq, Hkv, D, L, code, num_splits)
+    if n == 0:
+        raise TsError(TS_ERR_INVALID_ARG, lib().ts_last_error().decode())
+    return int(n)
+
+
+def num_splits(T: int, Hq: int, Hkv: int, D: int, L: int, dtype: torch.dtype, num_splits: int = 0) -> int:
+    code = TS_BF16 if dtype == torch.bfloat16 else TS_F32
+    n = lib().ts_tree_verify_attn_num_splits(T, Hq, Hkv, D, L, code, num_splits)
+    if n < 0:
+        raise TsError(TS_ERR_INVALID_ARG, lib().ts_last_error().decode())
+    return int(n)
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 256-byte-aligned blocks
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def tree_verify_attn(q, k_cache, v_cache, k_draft, v_draft, parent, *, scale=None, out=None,
+                     lse=None, want_lse=True, num_splits: int = 0,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """ts_tree_verify_attn. q [T][Hq][D]; caches [Hkv][L][D] (a prefix view of a
+    larger cache is allowed); drafts [Hkv][T][D]; parent int32 [T] on the GPU."""
+    _need(q, "q", 3)
+    dev = q.device
+    T, Hq, D = q.shape
+    _need(k_cache, "k_cache", 3, q.dtype, dev)
+    _need(v_cache, "v_cache", 3, q.dtype, dev)
+    _need(k_draft, "k_draft", 3, q.dtype, dev)
+    _need(v_draft, "v_draft", 3, q.dtype, dev)
+    _need(parent, "parent", 1, torch.int32, dev)
+    Hkv, L, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if tuple(k_draft.shape) != (Hkv, T, D) or tuple(v_draft.shape) != (Hkv, T, D):
+        raise ValueError(f"drafts must be [{Hkv}][{T}][{D}]")
+    if parent.shape[0] != T:
+        raise ValueError("parent must have T entries")
+    for n, t in (("q", q), ("k_draft", k_draft), ("v_draft", v_draft), ("parent", parent)):
+        _contig(t, n)
+    stride = _cache_stride(k_cache, "k_cache")
+    if _cache_stride(v_cache, "v_cache") != stride:
+        raise ValueError("k_cache and v_cache must share the row stride")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    need = verify_workspace_bytes(T, Hq, Hkv, D, L, q.dtype, num_splits)
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    _check(lib().ts_tree_verify_attn(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stride, k_draft.data_ptr(),
+        v_draft.data_ptr(), parent.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, T, Hq, Hkv, D, L, float(scale), code,
+        num_splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, lse
+
+
+def tree_verify_attn_partials(q, k_cache, v_cache, k_draft, v_draft, parent, *, scale=None,
+                              o_part=None, l_part=None, num_splits: int = 0):
+    """ts_tree_verify_attn_partials -> (o_part [S][T][Hq][D] fp32, l_part [S][T][Hq] fp32)."""
+    _need(q, "q", 3)
+    dev = q.device
+    T, Hq, D = q.shape
+    Hkv, L, _ = k_cache.shape
+    _contig(q, "q")
+    stride = _cache_stride(k_cache, "k_cache")
+    S = globals()["num_splits"](T, Hq, Hkv, D, L, q.dtype, num_splits)
+    if o_part is None:
+        o_part = torch.empty((S, T, Hq, D), dtype=torch.float32, device=dev)
+    if l_part is None:
+        l_part = torch.empty((S, T, Hq), dtype=torch.float32, device=dev)
+    if o_part.numel() < S * T * Hq * D or l_part.numel() < S * T * Hq:
+        raise ValueError("partial buffers too small")
+    _check(lib().ts_tree_verify_attn_partials(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stride, k_draft.data_ptr(),
+        v_draft.data_ptr(), parent.data_ptr(), o_part.data_ptr(), l_part.data_ptr(), T, Hq, Hkv,
+        D, L, float(1.0 / math.sqrt(D) if scale is None else scale), _dtype_code(q), num_splits,
+        _stream(dev)))
+    return o_part, l_part
+
+
+def attn_merge(o_part, l_part, *, out_dtype=torch.bfloat16, out=None, lse=None):
+    """ts_attn_merge over the leading (parts) dim: o_part [S][..][D], l_part [S][..]."""
+    _contig(o_part, "o_part")
+    _contig(l_part, "l_part")
+    S = o_part.shape[0]
+    D = o_part.shape[-1]
+    rows = o_part[0].numel() // D
+    if l_part.numel() != S * rows:
+        raise ValueError("l_part does not match o_part")
+    dev = o_part.device
+    if out is None:
+        out = torch.empty(o_part.shape[1:], dtype=out_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(l_part.shape[1:], dtype=torch.float32, device=dev)
+    _check(lib().ts_attn_merge(o_part.data_ptr(), l_part.data_ptr(), S, rows, D, out.data_ptr(),
+                               lse.data_ptr(), _dtype_code(out), _stream(dev)))
+    return out, lse
+
+
+def kv_importance_score(q_recent, k_cache, chunk: int, *, scale=None, scores=None):
+    """ts_kv_importance_score -> scores [Hkv][L/chunk] fp32."""
+    _need(q_recent, "q_recent", 3)
+    dev = q_recent.device
+    _need(k_cache, "k_cache", 3, q_recent.dtype, dev)
+    _contig(q_recent, "q_recent")
+    R, Hq, D = q_recent.shape
+    Hkv, L, _ = k_cache.shape
+    stride = _cache_stride(k_cache, "k_cache")
+    if scores is None:
+        scores = torch.empty((Hkv, L // chunk), dtype=torch.float32, device=dev)
+    _check(lib().ts_kv_importance_score(
+        q_recent.data_ptr(), k_cache.data_ptr(), stride, scores.data_ptr(), R, Hq, Hkv, D, L,
+        chunk, float(1.0 / math.sqrt(D) if scale is None else scale), _dtype_code(q_recent),
+        _stream(dev)))
+    return scores
+
+
+def kv_topk_select(scores, k: int, *, chunk_idx=None, chunk_score=None, want_scores=True):
+    """ts_kv_topk_select -> (chunk_idx int32 [Hkv][k] ascending, chunk_score fp32 [Hkv][k])."""
+    _need(scores, "scores", 2, torch.float32)
+    _contig(scores, "scores")
+    Hkv, n = scores.shape
+    dev = scores.device
+    if chunk_idx is None:
+        chunk_idx = torch.empty((Hkv, k), dtype=torch.int32, device=dev)
+    if chunk_score is None and want_scores:
+        chunk_score = torch.empty((Hkv, k), dtype=torch.float32, device=dev)
+    _check(lib().ts_kv_topk_select(scores.data_ptr(), Hkv, n, k, chunk_idx.data_ptr(),
+                                   chunk_score.data_ptr() if chunk_score is not None else None,
+                                   _stream(dev)))
+    return chunk_idx, chunk_score
+
+
+def kv_gather(k_cache, v_cache, chunk_idx, chunk: int, *, k_part=None, v_part=None):
+    """ts_kv_gather -> (k_part, v_part) [Hkv][k*chunk][D]."""
+    _need(k_cache, "k_cache", 3)
+    dev = k_cache.device
+    _need(v_cache, "v_cache", 3, k_cache.dtype, dev)
+    _need(chunk_idx, "chunk_idx", 2, torch.int32, dev)
+    _contig(chunk_idx, "chunk_idx")
+    Hkv, L, D = k_cache.shape
+    k = chunk_idx.shape[1]
+    stride = _cache_stride(k_cache, "k_cache")
+    if _cache_stride(v_cache, "v_cache") != stride:
+        raise ValueError("k_cache and v_cache must share the row stride")
+    if k_part is None:
+        k_part = torch.empty((Hkv, k * chunk, D), dtype=k_cache.dtype, device=dev)
+    if v_part is None:
+        v_part = torch.empty((Hkv, k * chunk, D), dtype=k_cache.dtype, device=dev)
+    _check(lib().ts_kv_gather(k_cache.data_ptr(), v_cache.data_ptr(), stride, chunk_idx.data_ptr(),
+                              Hkv, k, chunk, D, L, k_part.data_ptr(), v_part.data_ptr(),
+                              _dtype_code(k_cache), _stream(dev)))
+    return k_part, v_part
+
+
+def partial_draft_attn(q, k_part, v_part, k_new, v_new, *, scale=None, out=None, lse=None,
+                       want_lse=True, num_splits: int = 0, workspace=None):
+    """ts_partial_draft_attn: q [Tq][Hq][D] over partial cache [Hkv][P][D] plus
+    the Tq new tokens [Hkv][Tq][D] under a causal chain."""
+    _need(q, "q", 3)
+    dev = q.device
+    Tq, Hq, D = q.shape
+    for n, t in (("k_part", k_part), ("v_part", v_part), ("k_new", k_new), ("v_new", v_new)):
+        _need(t, n, 3, q.dtype, dev)
+        _contig(t, n)
+    _contig(q, "q")
+    Hkv, P, _ = k_part.shape
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=dev)
+    need = int(lib().ts_partial_draft_attn_workspace(Tq, Hq, Hkv, D, P, code, num_splits))
+    if need == 0:
+        raise TsError(TS_ERR_INVALID_ARG, lib().ts_last_error().decode())
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    _check(lib().ts_partial_draft_attn(
+        q.data_ptr(), k_part.data_ptr(), v_part.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+        out.data_ptr(), lse.data_ptr() if lse is not None else None, Tq, Hq, Hkv, D, P,
+        float(1.0 / math.sqrt(D) if scale is None else scale), code, num_splits,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, lse

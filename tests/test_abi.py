@@ -1,0 +1,167 @@
+"""The C ABI on the host: the library loads, exports every function the header
+declares with the argument count the binding uses, and rejects bad arguments
+before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_kv_ts_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ts.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ops.library_path()),
+                                reason="libts.so not built (run __graft_entry__.build())")
+
+F, B = ops.TS_F32, ops.TS_BF16
+P = 0x10000          # a 256-byte-aligned fake device address; never dereferenced
+MIS = P + 8          # misaligned
+
+
+def _header_prototypes():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    protos = {}
+    for m in re.finditer(r"\b(ts_\w+)\s*\(([^;{]*?)\)\s*;", text):
+        name, args = m.group(1), m.group(2).strip()
+        n = 0 if args in ("", "void") else args.count(",") + 1
+        protos[name] = n
+    return protos
+
+
+def test_every_declared_function_is_exported_and_bound():
+    protos = _header_prototypes()
+    assert len(protos) >= 12
+    lib = ops.lib()
+    for name, nargs in protos.items():
+        assert hasattr(lib, name), f"{name} not exported"
+        assert name in ops.SIGNATURES, f"{name} not bound in ops.py"
+        assert len(ops.SIGNATURES[name][1]) == nargs, f"{name}: binding has wrong arg count"
+    assert set(ops.SIGNATURES) == set(protos)
+    assert lib.ts_abi_version() == 1
+
+
+def _verify(**kw):
+    a = dict(q=P, kc=P, vc=P, stride=1024, kd=P, vd=P, parent=P, out=P, lse=P, T=120, Hq=32,
+             Hkv=8, D=128, L=1024, scale=0.088, dtype=B, ns=0, ws=P, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return ops.lib().ts_tree_verify_attn(a["q"], a["kc"], a["vc"], a["stride"], a["kd"], a["vd"],
+                                         a["parent"], a["out"], a["lse"], a["T"], a["Hq"], a["Hkv"],
+                                         a["D"], a["L"], a["scale"], a["dtype"], a["ns"], a["ws"],
+                                         a["wsb"], a["stream"])
+
+
+def _err():
+    return ops.lib().ts_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(T=0), ops.TS_ERR_UNSUPPORTED, "T=0"),
+    (dict(T=257), ops.TS_ERR_UNSUPPORTED, "T=257"),
+    (dict(Hq=30), ops.TS_ERR_INVALID_ARG, "multiple"),
+    (dict(Hq=32 * 17, Hkv=1), ops.TS_ERR_UNSUPPORTED, "group size"),
+    (dict(D=96), ops.TS_ERR_UNSUPPORTED, "D=96"),
+    (dict(L=-1), ops.TS_ERR_INVALID_ARG, "L=-1"),
+    (dict(stride=100), ops.TS_ERR_INVALID_ARG, "cache_stride"),
+    (dict(q=None), ops.TS_ERR_INVALID_ARG, "null"),
+    (dict(parent=None), ops.TS_ERR_INVALID_ARG, "parent"),
+    (dict(out=None), ops.TS_ERR_INVALID_ARG, "out"),
+    (dict(q=MIS), ops.TS_ERR_INVALID_ARG, "aligned"),
+    (dict(kc=MIS), ops.TS_ERR_INVALID_ARG, "aligned"),
+    (dict(ws=None), ops.TS_ERR_INVALID_ARG, "workspace"),
+    (dict(ws=P + 16), ops.TS_ERR_INVALID_ARG, "256-byte"),
+    (dict(wsb=1024), ops.TS_ERR_WORKSPACE, "required"),
+    (dict(dtype=7), ops.TS_ERR_INVALID_ARG, "dtype"),
+    (dict(scale=float("nan")), ops.TS_ERR_INVALID_ARG, "scale"),
+    (dict(ns=-2), ops.TS_ERR_INVALID_ARG, "num_splits"),
+])
+def test_verify_rejects(kw, status, needle):
+    assert _verify(**kw) == status
+    msg = _err()
+    assert "ts_tree_verify_attn" in msg and needle in msg, msg
+
+
+def test_workspace_query():
+    lib = ops.lib()
+    w1 = lib.ts_tree_verify_attn_workspace(120, 32, 8, 128, 20480, B, 0)
+    w2 = lib.ts_tree_verify_attn_workspace(120, 32, 8, 128, 102400, B, 0)
+    assert w1 > 0 and w2 > 0
+    for L in (0, 1, 63, 64, 65, 20480):
+        for ns in (0, 1, 3, 16):
+            S = lib.ts_tree_verify_attn_num_splits(120, 32, 8, 128, L, B, ns)
+            assert S >= 1
+            if ns:
+                assert S <= ns
+            w = lib.ts_tree_verify_attn_workspace(120, 32, 8, 128, L, B, ns)
+            assert w >= S * 120 * 32 * 129 * 4
+            assert w % 256 == 0
+    assert lib.ts_tree_verify_attn_workspace(0, 32, 8, 128, 10, B, 0) == 0
+    assert lib.ts_tree_verify_attn_num_splits(0, 32, 8, 128, 10, B, 0) == -1
+    assert lib.ts_partial_draft_attn_workspace(4, 32, 8, 128, 4096, B, 0) > 0
+
+
+def test_partials_and_merge_reject():
+    lib = ops.lib()
+    st = lib.ts_tree_verify_attn_partials(P, P, P, 64, P, P, None, P, P, 4, 4, 1, 64, 64, 0.1, F, 0, None)
+    assert st == ops.TS_ERR_INVALID_ARG and "parent" in _err()
+    assert lib.ts_attn_merge(P, P, 0, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_attn_merge(P, P, 2, 10, 100, P, P, B, None) == ops.TS_ERR_UNSUPPORTED
+    assert lib.ts_attn_merge(None, P, 2, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_attn_merge(MIS, P, 2, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
+
+
+def test_draft_attn_rejects():
+    lib = ops.lib()
+    st = lib.ts_partial_draft_attn(P, P, P, P, P, P, P, 0, 32, 8, 128, 4096, 0.1, B, 0, P, 1 << 30, None)
+    assert st == ops.TS_ERR_UNSUPPORTED and "ts_partial_draft_attn" in _err()
+    st = lib.ts_partial_draft_attn(P, P, P, P, P, P, P, 4, 32, 8, 128, 4096, 0.1, B, 0, P, 16, None)
+    assert st == ops.TS_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(L=1000), ops.TS_ERR_UNSUPPORTED),          # not a multiple of chunk
+    (dict(chunk=0), ops.TS_ERR_UNSUPPORTED),
+    (dict(R=17), ops.TS_ERR_UNSUPPORTED),            # R*G > 64
+    (dict(Hq=24), ops.TS_ERR_UNSUPPORTED),           # G = 3 not a power of two
+    (dict(D=80), ops.TS_ERR_UNSUPPORTED),
+    (dict(q=None), ops.TS_ERR_INVALID_ARG),
+    (dict(k=MIS), ops.TS_ERR_INVALID_ARG),
+    (dict(stride=64), ops.TS_ERR_INVALID_ARG),
+])
+def test_importance_rejects(args, status):
+    a = dict(q=P, k=P, stride=4096, scores=P, R=4, Hq=32, Hkv=8, D=128, L=4096, chunk=64, scale=0.1, dtype=B)
+    a.update(args)
+    st = ops.lib().ts_kv_importance_score(a["q"], a["k"], a["stride"], a["scores"], a["R"], a["Hq"],
+                                          a["Hkv"], a["D"], a["L"], a["chunk"], a["scale"], a["dtype"], None)
+    assert st == status
+    assert "ts_kv_importance_score" in _err()
+
+
+def test_topk_rejects():
+    lib = ops.lib()
+    assert lib.ts_kv_topk_select(P, 8, 1600, 0, P, None, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_kv_topk_select(P, 8, 1600, 1601, P, None, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_kv_topk_select(P, 8, 70000, 64, P, None, None) == ops.TS_ERR_UNSUPPORTED
+    assert lib.ts_kv_topk_select(None, 8, 1600, 64, P, None, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_kv_topk_select(P, 0, 1600, 64, P, None, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_kv_topk_select(P + 2, 8, 1600, 64, P, None, None) == ops.TS_ERR_INVALID_ARG
+
+
+def test_gather_rejects():
+    lib = ops.lib()
+    assert lib.ts_kv_gather(P, P, 4096, P, 8, 64, 64, 128, 4000, P, P, B, None) == ops.TS_ERR_UNSUPPORTED
+    assert lib.ts_kv_gather(P, P, 100, P, 8, 64, 64, 128, 4096, P, P, B, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_kv_gather(P, P, 4096, None, 8, 64, 64, 128, 4096, P, P, B, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_kv_gather(P, MIS, 4096, P, 8, 64, 64, 128, 4096, P, P, B, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_kv_gather(P, P, 4096, P, 8, 64, 1, 4, 4096, P, P, B, None) == ops.TS_ERR_UNSUPPORTED
+    assert lib.ts_kv_gather(P, P, 4096, P, 8, 64, 64, 128, 4096, P, P, 9, None) == ops.TS_ERR_INVALID_ARG
+    assert "ts_kv_gather" in _err()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ops, "_lib", None)
+    monkeypatch.setattr(ops, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        ops.lib()

@@ -1,0 +1,209 @@
+"""GPU parity of ts_tree_verify_attn (and its split/merge phases) against the
+CPU oracle, element by element, on the seeded workloads at full size and on
+edge cases. Calls go through the C ABI (long_context_kv_ts_amd.ops)."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_kv_ts_amd import inputs, ops
+import oracle
+from gpu_util import check_attn, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_verify(c, num_splits=0, stride_pad=0):
+    dt = c.dtype
+    kc, vc = c.k_cache, c.v_cache
+    if stride_pad:
+        # the cache as a prefix view of a larger allocation (capacity L + pad)
+        Hkv, L, D = kc.shape
+        big_k = np.zeros((Hkv, L + stride_pad, D), kc.dtype)
+        big_v = np.zeros((Hkv, L + stride_pad, D), vc.dtype)
+        big_k[:, :L] = kc
+        big_v[:, :L] = vc
+        big_k[:, L:] = 0x7FC0 if dt == "bf16" else np.float32(np.nan)   # NaN past L: must never be read
+        big_v[:, L:] = 0x7FC0 if dt == "bf16" else np.float32(np.nan)
+        kd_, vd_ = to_dev(big_k, dt)[:, :L], to_dev(big_v, dt)[:, :L]
+    else:
+        kd_, vd_ = to_dev(kc, dt), to_dev(vc, dt)
+    out, lse = ops.tree_verify_attn(to_dev(c.q, dt), kd_, vd_, to_dev(c.k_draft, dt),
+                                    to_dev(c.v_draft, dt), to_dev(c.parent, "i32"),
+                                    scale=c.scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+_cache = {}
+
+
+def workload_with_ref(name, **kw):
+    key = (name, tuple(sorted(kw.items())))
+    if key not in _cache:
+        c = inputs.workload(name, **kw)
+        ref = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, c.parent,
+                                     c.scale, c.dtype)
+        _cache.clear()
+        _cache[key] = (c, ref)
+    return _cache[key]
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama8b_20k", "llama8b_100k", "llama2_mha_100k"])
+def test_verify_full_size(name):
+    say(f"[verify full] {name}")
+    c, (ro, rl) = workload_with_ref(name)
+    out, lse = run_verify(c)
+    check_attn(out, lse, ro, rl, c.dtype, name)
+
+
+@pytest.mark.parametrize("ns", [1, 3, 7, 40])
+def test_split_count_invariance(ns):
+    say(f"[splits] llama8b_20k L=4000 num_splits={ns}")
+    c, (ro, rl) = workload_with_ref("llama8b_20k", L=4000)
+    out, lse = run_verify(c, num_splits=ns)
+    check_attn(out, lse, ro, rl, c.dtype, f"splits={ns}")
+
+
+@pytest.mark.parametrize("L", [0, 1, 63, 64, 65, 1000, 64 * 37 + 13])
+def test_ragged_and_empty_cache(L):
+    say(f"[ragged] L={L}")
+    c = inputs.make_verify("ragged", dtype="bf16", Hq=8, Hkv=2, D=128, L=L, seed=100 + L, with_chains=True)
+    ro, rl = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, c.parent, c.scale, "bf16")
+    out, lse = run_verify(c)
+    check_attn(out, lse, ro, rl, "bf16", f"L={L}")
+
+
+def test_cache_prefix_view_never_reads_past_L():
+    say("[stride] cache view with capacity L+100 (NaN past L)")
+    c = inputs.make_verify("stride", dtype="bf16", Hq=8, Hkv=4, D=128, L=777, seed=7, with_chains=True)
+    ro, rl = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, c.parent, c.scale, "bf16")
+    out, lse = run_verify(c, stride_pad=100)
+    check_attn(out, lse, ro, rl, "bf16", "prefix view")
+
+
+@pytest.mark.parametrize("shape", [
+    dict(dtype="bf16", Hq=4, Hkv=4, D=128),     # MHA, one row per token
+    dict(dtype="bf16", Hq=16, Hkv=2, D=64),     # G=8, D=64
+    dict(dtype="f32", Hq=8, Hkv=2, D=128),
+    dict(dtype="f32", Hq=16, Hkv=1, D=64),      # G=16
+])
+def test_head_shapes(shape):
+    say(f"[shapes] {shape}")
+    c = inputs.make_verify("shape", L=2100, seed=11, with_chains=True, **shape)
+    ro, rl = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, c.parent, c.scale, c.dtype)
+    out, lse = run_verify(c)
+    check_attn(out, lse, ro, rl, c.dtype, str(shape))
+
+
+@pytest.mark.parametrize("T", [1, 2, 64, 65, 256])
+def test_draft_counts(T):
+    say(f"[T] T={T}")
+    rng = np.random.default_rng(T)
+    parent = np.array([-1 if t == 0 or rng.random() < 0.2 else int(rng.integers(max(0, t - 9), t))
+                       for t in range(T)], np.int32)
+    c = inputs.make_verify("T", dtype="bf16", Hq=8, Hkv=2, D=128, L=500, seed=T, with_chains=False, parent=parent)
+    ro, rl = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, c.parent, c.scale, "bf16")
+    out, lse = run_verify(c)
+    check_attn(out, lse, ro, rl, "bf16", f"T={T}")
+
+
+def test_deep_chain_256():
+    say("[T] one causal chain of 256 drafts")
+    parent = np.arange(-1, 255, dtype=np.int32)
+    c = inputs.make_verify("chain", dtype="bf16", Hq=4, Hkv=1, D=128, L=300, seed=3, with_chains=False, parent=parent)
+    ro, rl = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, c.parent, c.scale, "bf16")
+    out, lse = run_verify(c)
+    check_attn(out, lse, ro, rl, "bf16", "chain256")
+
+
+def test_out_of_range_parents_are_roots():
+    say("[parent] out-of-range entries")
+    c = inputs.make_verify("badparent", dtype="bf16", Hq=8, Hkv=2, D=128, L=200, seed=9, with_chains=True)
+    bad = c.parent.copy()
+    bad[5] = 7          # not < t
+    bad[9] = -5
+    bad[50] = 10_000
+    bad[60] = 60        # self
+    clean = bad.copy()
+    for t in range(len(bad)):
+        if not (-1 <= bad[t] < t):
+            clean[t] = -1
+    ro, rl = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, clean, c.scale, "bf16")
+    c.parent = bad
+    out, lse = run_verify(c)
+    check_attn(out, lse, ro, rl, "bf16", "bad parents")
+
+
+# ---------------------------------------------------------------------------
+# structured full-size pins
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["llama8b_100k", "llama2_mha_100k"])
+def test_zero_keys_count_every_visible_key(name):
+    """All keys zero: every logit is exactly 0, so lse[t,h] = ln(L + |A(t)|).
+    At L = 102400 one key more or less moves lse by ~1e-5 (~10 fp32 ulp)."""
+    say(f"[zero keys] {name}")
+    c = inputs.workload(name)
+    c.k_cache[:] = 0
+    c.k_draft[:] = 0
+    out, lse = run_verify(c)
+    vis = oracle.ancestor_mask(c.parent).sum(1)
+    expect = np.log(c.L + vis.astype(np.float64))[:, None]
+    err = np.abs(to_host(lse) - expect).max()
+    say(f"  max|lse - ln(L+|A(t)|)| = {err:.3e} (1/(L+1) = {1 / (c.L + 1):.3e})")
+    assert err < 3e-6
+    # and the output is the mean of the visible values (checked on head 0 of each group)
+    ro, rl = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, c.parent,
+                                    c.scale, c.dtype, heads=[0])
+    G = c.G
+    check_attn(out[:, :G], lse[:, :G], ro[:, :G], rl[:, :G], "bf16", "zero keys head 0")
+
+
+def test_dominant_drafts_show_the_exact_ancestor_pattern():
+    """Prefix keys 0; draft keys and queries along one axis with logit ~20; draft
+    values one-hot per draft. The output is then ~ the mean of the one-hot
+    vectors of A(t), which exposes the mask row by row at full size."""
+    say("[dominant drafts] llama8b_100k")
+    c = inputs.workload("llama8b_100k")
+    T, D = c.T, c.D
+    c.k_cache[:] = 0
+    one = inputs.f32_to_bf16_bits(np.float32(1.0))
+    c.k_draft[:] = 0
+    c.k_draft[:, :, 0] = inputs.f32_to_bf16_bits(np.float32(2.0))
+    c.q[:] = 0
+    c.q[:, :, 0] = inputs.f32_to_bf16_bits(np.float32(10.0 * np.sqrt(D)))
+    c.v_draft[:] = 0
+    for a in range(T):
+        c.v_draft[:, a, a % D] = one
+    out, lse = run_verify(c)
+    ro, rl = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, c.parent,
+                                    c.scale, c.dtype)
+    check_attn(out, lse, ro, rl, "bf16", "dominant drafts")
+    vis = oracle.ancestor_mask(c.parent)
+    got = to_host(out)
+    for t in range(T):
+        n = vis[t].sum()
+        seen = got[t, :, :T] > 0.5 / n
+        np.testing.assert_array_equal(seen, np.broadcast_to(vis[t], seen.shape), err_msg=f"row {t}")
+
+
+# ---------------------------------------------------------------------------
+# the two phases separately
+# ---------------------------------------------------------------------------
+def test_partials_then_merge_equal_single_call():
+    say("[phases] partials + merge")
+    c, (ro, rl) = workload_with_ref("llama8b_20k", L=5000)
+    dt = c.dtype
+    args = (to_dev(c.q, dt), to_dev(c.k_cache, dt), to_dev(c.v_cache, dt), to_dev(c.k_draft, dt),
+            to_dev(c.v_draft, dt), to_dev(c.parent, "i32"))
+    o_part, l_part = ops.tree_verify_attn_partials(*args, scale=c.scale, num_splits=5)
+    out, lse = ops.attn_merge(o_part, l_part, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    check_attn(out, lse, ro, rl, "bf16", "partials+merge")
+    # each split's partial is itself attention over its key range: merging any
+    # two halves of the partial list with the same rule gives the same result
+    S = o_part.shape[0]
+    a_o, a_l = ops.attn_merge(o_part[: S // 2].contiguous(), l_part[: S // 2].contiguous(), out_dtype=torch.float32)
+    b_o, b_l = ops.attn_merge(o_part[S // 2:].contiguous(), l_part[S // 2:].contiguous(), out_dtype=torch.float32)
+    out2, lse2 = ops.attn_merge(torch.stack([a_o, b_o]), torch.stack([a_l, b_l]), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    check_attn(out2, lse2, ro, rl, "bf16", "merge of merges")
