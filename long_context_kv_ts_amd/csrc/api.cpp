@@ -64,9 +64,10 @@ AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype
   AttnPlan p{};
   const int G = Hq / Hkv;
   p.rows_per_head = T * G;
-  p.path = kPathValu;
-  (void)D;
-  (void)dtype;
+  // Matrix cores where the grouped query rows of a KV head fill at least one
+  // 32-row MFMA block; the vector-ALU kernel otherwise (and for fp32).
+  p.path = (dtype == TS_BF16 && (D == 128 || D == 64) && p.rows_per_head >= 32) ? kPathMfma
+                                                                                 : kPathValu;
   p.rows_per_group = p.path == kPathMfma ? kMfmaRows : kValuRows;
   p.n_rowgroups = (p.rows_per_head + p.rows_per_group - 1) / p.rows_per_group;
   p.n_cache_tiles = (int)((L + kTile - 1) / kTile);

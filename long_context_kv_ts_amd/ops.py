@@ -115,6 +115,8 @@ def _cache_stride(t: torch.Tensor, name: str) -> int:
     """Row stride (in tokens) of a [Hkv][stride][D] cache view whose last two
     dims are dense; lets callers pass cache[:, :L] of a larger allocation."""
     Hkv, L, D = t.shape
+    if t.numel() == 0:
+        return L
     if t.stride(2) != 1 or (L > 1 and t.stride(1) != D):
         raise ValueError(f"{name} must be dense in its last two dims")
     if Hkv > 1 and t.stride(0) % D:
