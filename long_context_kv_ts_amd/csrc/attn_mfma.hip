@@ -9,27 +9,30 @@
 //
 // Scores are computed transposed, S^T = K . Q^T (A = K tile from LDS, B = Q
 // held in registers), so each lane's accumulator values all belong to ONE
-// query row (row = lane % 32 of the block, 16 keys per 32-key block, the other
-// 16 in lane ^ 32). Row max/sum are then per-lane with one cross-half
-// exchange, and the output O^T = V^T . P^T again gives every lane one row, so
-// rescaling O is a per-lane multiply. P^T reuses the score registers
-// directly as the B operand: the order of the reduction over keys is free, so
-// the V^T operand is read in the matching key order. V^T is produced while
-// staging (4x8 register transposes) into an LDS layout where that order is
-// contiguous: column k' = 32*kb + 16*hh + 8*h + e holds key
-// 32*kb + 16*hh + 8*(e/4) + 4*h + e%4.
+// query row (row = lane % 32, 16 keys of a 32-key block; the other 16 are in
+// lane ^ 32). Row max/sum are then per-lane with one cross-half exchange, and
+// the output O^T = V^T . P^T again gives every lane one row, so rescaling O is
+// a per-lane multiply. P^T reuses the score registers directly as the B
+// operand: the reduction order over keys is free, so the V^T operand is read
+// in the key order the scores arrive in -- k-slot 8*h + 4*r + e of a 16-key
+// chunk is key 16*hh + 8*r + 4*h + e.
+//
+// K and V tiles (64 keys) stream from HBM straight into LDS with 16-byte
+// global_load_lds_dwordx4 (no staging registers) through a 3-stage ring, so
+// two tiles are in flight while one is computed; one barrier per tile. Both
+// tiles are stored row-major with 16-byte chunks XOR-swizzled per row (K:
+// chunk ^ row%16, V: chunk ^ 4*(row%4)): the K operand reads (16 rows, one
+// chunk) and the transposing ds_read_b64_tr_b16 reads of V^T (4 rows x 32
+// bytes per 16 lanes) are both free of bank conflicts. Rows past the valid
+// keys re-read the last valid row (finite data, masked scores).
 //
 // Softmax in base 2 on fp32 scores (exact bf16 products, fp32 sums); scale is
 // applied in fp32 after the product. The running max is only raised when a new
 // score exceeds it by more than 2^8 ("lazy rescale"), which keeps every
 // probability <= 256 and makes rescaling of the accumulators rare. The
 // probabilities are rounded to bf16 for the PV product; the row sum uses the
-// unrounded values.
-//
-// K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
-// i+1 are issued before the tile-i products and written to the other buffer
-// after them; one barrier per tile. Tiles past the cache are the draft K/V,
-// masked by the ancestor-or-self bitmask built in LDS from parent[].
+// unrounded values. Tiles past the cache are the draft K/V, masked by the
+// ancestor-or-self bitmask built in LDS from parent[].
 #include "common.h"
 
 namespace ts {
@@ -44,107 +47,66 @@ constexpr int kNB = 1;                       // 32-row blocks per wave
 constexpr int kRowsPerGroup = kWaves * kNB * 32;
 constexpr float kLazy = 8.0f;                // log2 headroom before a rescale
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+#define TS_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr int kStages = 3;
+
 template <int D> struct Layout {
   static constexpr int KS = D / 16;                  // k-steps of QK^T
   static constexpr int DB = D / 32;                  // 32-wide column blocks of O
-  static constexpr int kRow = D + 8;                 // K tile row stride (bf16): +16 B
-  static constexpr int vRow = kTile + 8;             // V^T row stride (bf16): 144 B
-  static constexpr int kElems = kTile * kRow;
-  static constexpr int vElems = D * vRow;
-  static constexpr int vUnits = 2 * 8 * (D / 8);     // (key group, key half, 8-dim block) units of V
-  static constexpr int kChunks = kTile * D / 8;      // 16-byte chunks of a K tile
-  static constexpr int kThreadsK = kThreads - vUnits;
-  static constexpr int kPer = (kChunks + kThreadsK - 1) / kThreadsK;
-  static constexpr int nStage = kPer > 4 ? kPer : 4;
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int tileElems = kTile * D;        // one K or V tile, unpadded
+  static constexpr int loadsPerTensor = kTile * D * 2 / 1024;   // 1 KB per wave-wide load
+  static constexpr int loadsPerWave = 2 * loadsPerTensor / kWaves;
+  static constexpr int rowsPerLoad = 1024 / (D * 2);
 };
 
-__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) {   // {a.lo, b.lo}
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) {   // {a.hi, b.hi}
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+// Physical 16-byte chunk of logical chunk c in row r.
+template <int D> __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & (Layout<D>::CH - 1)); }
+template <int D> __device__ __forceinline__ int v_chunk(int r, int c) {
+  return c ^ ((4 * (r & 3)) & (Layout<D>::CH - 1));
 }
 
+// One wave-wide 16-byte-per-lane load from global memory straight into LDS:
+// lane l's bytes land at dst + 16*l (dst is wave-uniform, passed in M0).
+// Written as asm with no outputs so that the compiler does not guard every
+// later LDS read with a wait for ALL outstanding loads; completion is instead
+// awaited explicitly (vmcnt) before the barrier that publishes a tile. Loads
+// the compiler does not count only make its own waits stricter.
+__device__ __forceinline__ void lds_dma16(const bf16_t* src, bf16_t* dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TS_LDS(void, dst))));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+// Issue this wave's share of the direct-to-LDS loads of one K/V tile.
 template <int D>
-struct Stage {
-  uint4 r[Layout<D>::nStage];   // V: 4 keys x 16 B  |  K: kPer chunks of 16 B
-};
-
-// V staging unit u: key group kg = u % 8 (= (kb, hh, h) of the V^T column
-// order), key half eh = (u / 8) % 2, 8-dim block db = u / 16. It covers keys
-// 32*kb + 16*hh + 4*h + 8*eh + i, i < 4, i.e. V^T columns kg*8 + eh*4 + i.
-__device__ __forceinline__ int v_unit_key(int u, int i) {
-  const int kg = u & 7, eh = (u >> 3) & 1;
-  return 32 * (kg >> 2) + 16 * ((kg >> 1) & 1) + 4 * (kg & 1) + 8 * eh + i;
-}
-
-// Issue the global loads of one tile into registers (zeros past nvalid).
-template <int D>
-__device__ __forceinline__ void stage_load(Stage<D>& st, const bf16_t* kb, const bf16_t* vb,
-                                           int nvalid, int tid) {
+__device__ __forceinline__ void issue_tile(const bf16_t* kb, const bf16_t* vb, int nvalid,
+                                           bf16_t* Kst, bf16_t* Vst, int wave, int lane) {
   using Ly = Layout<D>;
-  if (tid < Ly::vUnits) {
-    const int db = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = v_unit_key(tid, i);
-      st.r[i] = key < nvalid ? *reinterpret_cast<const uint4*>(vb + (int64_t)key * D + db * 8)
-                             : make_uint4(0u, 0u, 0u, 0u);
-    }
-  } else {
-    const int kt = tid - Ly::vUnits;
-#pragma unroll
-    for (int n = 0; n < Ly::kPer; ++n) {
-      const int j = kt + n * Ly::kThreadsK;          // chunk: key j/(D/8), 8-dim block j%(D/8)
-      const int key = j / (D / 8), c8 = j % (D / 8);
-      st.r[n] = (j < Ly::kChunks && key < nvalid)
-                    ? *reinterpret_cast<const uint4*>(kb + (int64_t)key * D + c8 * 8)
-                    : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-}
-
-// Write staged registers into an LDS buffer: K row-major, V transposed
-// (4x8 register transpose, 8-byte stores).
-template <int D>
-__device__ __forceinline__ void stage_store(const Stage<D>& st, bf16_t* Ks, bf16_t* Vt, int tid) {
-  using Ly = Layout<D>;
-  if (tid < Ly::vUnits) {
-    const int kg = tid & 7, eh = (tid >> 3) & 1, db = tid >> 4;
-    uint32_t w[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w[i][0] = st.r[i].x; w[i][1] = st.r[i].y; w[i][2] = st.r[i].z; w[i][3] = st.r[i].w;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int src = j >> 1;
-      uint2 o;
-      if (j & 1) {
-        o.x = perm_hi(w[0][src], w[1][src]); o.y = perm_hi(w[2][src], w[3][src]);
-      } else {
-        o.x = perm_lo(w[0][src], w[1][src]); o.y = perm_lo(w[2][src], w[3][src]);
-      }
-      *reinterpret_cast<uint2*>(Vt + (db * 8 + j) * Ly::vRow + kg * 8 + eh * 4) = o;
-    }
-  } else {
-    const int kt = tid - Ly::vUnits;
-#pragma unroll
-    for (int n = 0; n < Ly::kPer; ++n) {
-      const int j = kt + n * Ly::kThreadsK;
-      if (j < Ly::kChunks) {
-        const int key = j / (D / 8), c8 = j % (D / 8);
-        *reinterpret_cast<uint4*>(Ks + key * Ly::kRow + c8 * 8) = st.r[n];
-      }
-    }
+  for (int n = 0; n < Ly::loadsPerWave; ++n) {
+    const int q = wave * Ly::loadsPerWave + n;               // 0 .. 2*loadsPerTensor-1
+    const bool isv = q >= Ly::loadsPerTensor;
+    const int m = isv ? q - Ly::loadsPerTensor : q;          // 1 KB block of the tile
+    const int r = m * Ly::rowsPerLoad + lane / Ly::CH;       // tile row this lane fills
+    const int pc = lane % Ly::CH;                            // physical chunk it fills
+    const int c = isv ? v_chunk<D>(r, pc) : k_chunk<D>(r, pc);   // xor: its own inverse
+    const int rr = min(r, nvalid - 1);
+    const bf16_t* src = (isv ? vb : kb) + (int64_t)rr * D + c * 8;
+    bf16_t* dst = (isv ? Vst : Kst) + m * 512;
+    lds_dma16(src, dst);
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a) {
   using Ly = Layout<D>;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][Ly::kElems];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][Ly::vElems];
+  __shared__ __attribute__((aligned(1024))) bf16_t KVs[kStages][2][Ly::tileElems];
   __shared__ uint32_t anc[TS_MAX_DRAFT * (TS_MAX_DRAFT / 32)];
 
   const AttnPlan& pl = a.plan;
@@ -164,33 +126,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   const int G = a.G, T = a.T, Hq = a.Hq;
   const float c = a.scale_log2;
 
-  // ---- Q operand (B of S^T = K Q^T): lane holds row col of each block ------
-  bf16x8_t qf[kNB][Ly::KS];
-  bool row_ok[kNB];
-  int row_t[kNB], row_h[kNB];
-#pragma unroll
-  for (int b = 0; b < kNB; ++b) {
-    const int row = rg * kRowsPerGroup + wave * (kNB * 32) + b * 32 + col;
-    row_ok[b] = row < pl.rows_per_head;
-    row_t[b] = row_ok[b] ? row / G : 0;
-    row_h[b] = g * G + (row_ok[b] ? row % G : 0);
-    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + ((int64_t)row_t[b] * Hq + row_h[b]) * D;
-#pragma unroll
-    for (int ks = 0; ks < Ly::KS; ++ks) {
-      uint4 u = row_ok[b] ? *reinterpret_cast<const uint4*>(qp + ks * 16 + half * 8)
-                          : make_uint4(0u, 0u, 0u, 0u);
-      qf[b][ks] = __builtin_bit_cast(bf16x8_t, u);
-    }
-  }
-  // waves whose row blocks are all padding skip the products
-  const bool wave_active = rg * kRowsPerGroup + wave * (kNB * 32) < pl.rows_per_head;
-
   const int vt0 = split * pl.tiles_per_split;
   const int vt1 = min(vt0 + pl.tiles_per_split, pl.n_virtual);
-  const int words = (T + 31) >> 5;
-  if (vt1 > pl.n_cache_tiles) build_ancestor_mask(a.parent, T, words, anc, tid, kThreads);
 
-  auto tile_ptrs = [&](int vt, const bf16_t*& kb, const bf16_t*& vb, int& key0, int& nvalid) {
+  auto tile_src = [&](int vt, const bf16_t*& kb, const bf16_t*& vb, int& key0, int& nvalid) {
     const bool draft = vt >= pl.n_cache_tiles;
     key0 = draft ? (vt - pl.n_cache_tiles) * kTile : vt * kTile;
     nvalid = draft ? min(kTile, T - key0) : (int)min((int64_t)kTile, a.L - key0);
@@ -199,139 +138,158 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
     vb = draft ? static_cast<const bf16_t*>(a.vd) + ((int64_t)g * T + key0) * D
                : static_cast<const bf16_t*>(a.vc) + ((int64_t)g * a.cache_stride + key0) * D;
   };
-
-  f32x16_t O[kNB][Ly::DB];
-  float m[kNB], lsum[kNB];
-#pragma unroll
-  for (int b = 0; b < kNB; ++b) {
-    m[b] = -INFINITY;
-    lsum[b] = 0.f;
-#pragma unroll
-    for (int db = 0; db < Ly::DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) O[b][db][i] = 0.f;
-  }
-
-  Stage<D> st;
-  {
+  auto issue = [&](int vt, int stage) {
     const bf16_t *kb, *vb;
     int key0, nvalid;
-    tile_ptrs(vt0, kb, vb, key0, nvalid);
-    stage_load<D>(st, kb, vb, nvalid, tid);
-    stage_store<D>(st, Ks[0], Vt[0], tid);
+    tile_src(vt, kb, vb, key0, nvalid);
+    issue_tile<D>(kb, vb, nvalid, KVs[stage][0], KVs[stage][1], wave, lane);
+  };
+  // the first tile starts streaming before anything else
+  issue(vt0, 0);
+
+  // ---- Q operand (B of S^T = K Q^T): lane holds row `col` of the block -----
+  bf16x8_t qf[Ly::KS];
+  const int row = rg * kRowsPerGroup + wave * 32 + col;
+  const bool row_ok = row < pl.rows_per_head;
+  const int row_t = row_ok ? row / G : 0;
+  const int row_h = g * G + (row_ok ? row % G : 0);
+  {
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + ((int64_t)row_t * Hq + row_h) * D;
+#pragma unroll
+    for (int ks = 0; ks < Ly::KS; ++ks) {
+      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16 + half * 8)
+                       : make_uint4(0u, 0u, 0u, 0u);
+      qf[ks] = __builtin_bit_cast(bf16x8_t, u);
+    }
+    // Wait for Q here, once: the compiler would otherwise place its wait at the
+    // first use inside the tile loop, where it would run every iteration and
+    // drain the prefetched tiles too.
+#pragma unroll
+    for (int ks = 0; ks < Ly::KS; ++ks) asm volatile("" : : "v"(qf[ks]));
   }
-  __syncthreads();
+  if (vt0 + 1 < vt1) issue(vt0 + 1, 1);
+  // waves whose rows are all padding skip the products
+  const bool wave_active = rg * kRowsPerGroup + wave * 32 < pl.rows_per_head;
+
+  const int words = (T + 31) >> 5;
+  if (vt1 > pl.n_cache_tiles) build_ancestor_mask(a.parent, T, words, anc, tid, kThreads);
+
+  f32x16_t O[Ly::DB];
+#pragma unroll
+  for (int db = 0; db < Ly::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
 
   for (int vt = vt0; vt < vt1; ++vt) {
-    const int cur = (vt - vt0) & 1;
-    if (vt + 1 < vt1) {
-      const bf16_t *kb, *vb;
-      int key0, nvalid;
-      tile_ptrs(vt + 1, kb, vb, key0, nvalid);
-      stage_load<D>(st, kb, vb, nvalid, tid);
-    }
+    const int i = vt - vt0;
+    const int cur = i % kStages;
+    // this wave's loads of tile vt are the oldest outstanding; the next tile's
+    // (if issued) may stay in flight
+    if (vt + 1 < vt1) __builtin_amdgcn_s_waitcnt(0x0F70 | Ly::loadsPerWave);   // vmcnt(loadsPerWave)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                                   // vmcnt(0)
+    __syncthreads();   // tile vt visible to all; stage (i+2)%3 no longer read
+    if (vt + 2 < vt1) issue(vt + 2, (i + 2) % kStages);
+
     if (wave_active) {
       const bool draft = vt >= pl.n_cache_tiles;
       const int key0 = draft ? (vt - pl.n_cache_tiles) * kTile : vt * kTile;
       const int nvalid = draft ? min(kTile, T - key0) : (int)min((int64_t)kTile, a.L - key0);
-      const bf16_t* Kc = Ks[cur];
-      const bf16_t* Vc = Vt[cur];
+      const bf16_t* Kc = KVs[cur][0];
+      const bf16_t* Vc = KVs[cur][1];
 
       // One 32-key block at a time: S^T block, mask, softmax update, PV.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        f32x16_t S[kNB];
+        f32x16_t S;
 #pragma unroll
-        for (int b = 0; b < kNB; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) S[b][i] = 0.f;
+        for (int e = 0; e < 16; ++e) S[e] = 0.f;
+        const int kr = 32 * kb + col;                       // K row read by this lane
 #pragma unroll
         for (int ks = 0; ks < Ly::KS; ++ks) {
           const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-              Kc + (32 * kb + col) * Ly::kRow + ks * 16 + half * 8);
-#pragma unroll
-          for (int b = 0; b < kNB; ++b)
-            S[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[b][ks], S[b], 0, 0, 0);
+              Kc + kr * D + k_chunk<D>(kr, 2 * ks + half) * 8);
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S, 0, 0, 0);
         }
 
         // mask: ragged cache tail, draft ancestor bits
         if (draft || nvalid < kTile) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-#pragma unroll
-            for (int b = 0; b < kNB; ++b) {
-              bool ok = key < nvalid;
-              if (draft) {
-                const int kk = key0 + key;
-                ok = ok && row_ok[b] && ((anc[row_t[b] * words + (kk >> 5)] >> (kk & 31)) & 1u);
-              }
-              if (!ok) S[b][i] = -INFINITY;
+          for (int e = 0; e < 16; ++e) {
+            const int key = 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3);
+            bool ok = key < nvalid;
+            if (draft) {
+              const int kk = key0 + key;
+              ok = ok && row_ok && ((anc[row_t * words + (kk >> 5)] >> (kk & 31)) & 1u);
             }
+            if (!ok) S[e] = -INFINITY;
           }
         }
 
         // online softmax (base 2, lazy rescale)
-        bf16x8_t P[kNB][2];
+        float mx = S[0];
 #pragma unroll
-        for (int b = 0; b < kNB; ++b) {
-          float mx = S[b][0];
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;          // same for lanes l, l^32
+        const bool need = mx > m + kLazy;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+          // need implies mx finite; exp2(-inf) = 0 clears a row that had no key yet
+          const float alpha = need ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
+          m = need ? mx : m;
+          lsum *= alpha;
 #pragma unroll
-          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[b][i]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;        // same for lanes l, l^32
-          const bool need = mx > m[b] + kLazy;
-          if (__builtin_amdgcn_ballot_w64(need) != 0) {
-            // need implies mx finite; exp2(-inf) = 0 clears a row that had no key yet
-            const float alpha = need ? __builtin_amdgcn_exp2f(m[b] - mx) : 1.f;
-            m[b] = need ? mx : m[b];
-            lsum[b] *= alpha;
+          for (int db = 0; db < Ly::DB; ++db)
 #pragma unroll
-            for (int db = 0; db < Ly::DB; ++db)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) O[b][db][i] *= alpha;
-          }
-          // finite stand-in for a row with no key yet: exp2(-inf) = 0 for masked scores
-          const float nmb = -fmaxf(m[b], -3.0e38f);
-          float ls = 0.f;
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            bf16x8_t pv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              // v_exp_f32 directly: results below 2^-126 of the running max flush to 0
-              const float p = __builtin_amdgcn_exp2f(fmaf(S[b][8 * hh + e], c, nmb));
-              ls += p;
-              pv[e] = static_cast<__bf16>(p);
-            }
-            P[b][hh] = pv;
-          }
-          lsum[b] += ls;
+            for (int e = 0; e < 16; ++e) O[db][e] *= alpha;
         }
+        // finite stand-in for a row with no key yet: exp2(-inf) = 0 for masked scores
+        const float nmb = -fmaxf(m, -3.0e38f);
+        bf16x8_t P[2];
+        float ls = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            // v_exp_f32 directly: results below 2^-126 of the running max flush to 0
+            const float p = __builtin_amdgcn_exp2f(fmaf(S[8 * hh + e], c, nmb));
+            ls += p;
+            P[hh][e] = static_cast<__bf16>(p);
+          }
+        }
+        lsum += ls;
 
-        // O^T += V^T P^T over this block's 32 keys (two 16-key k-chunks)
+        // O^T += V^T P^T over this block's 32 keys (two 16-key chunks). The
+        // V^T operand of lane l: dim 32*db + l%32, keys 16*hh + 8*r + 4*h + e,
+        // fetched by two transposing reads (r = 0, 1) of 4 keys each.
+        const int vrow0 = 32 * kb + 4 * half + ((lane & 15) >> 2);
+        const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
           for (int db = 0; db < Ly::DB; ++db) {
-            const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(
-                Vc + (32 * db + col) * Ly::vRow + 32 * kb + 16 * hh + half * 8);
+            s16x4_t part[2];
 #pragma unroll
-            for (int b = 0; b < kNB; ++b)
-              O[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[b][hh], O[b][db], 0, 0, 0);
+            for (int r = 0; r < 2; ++r) {
+              const int vr = vrow0 + 16 * hh + 8 * r;
+              const int d = 32 * db + vdim;
+              const bf16_t* vp = Vc + vr * D + v_chunk<D>(vr, d >> 3) * 8 + (d & 7);
+              part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TS_LDS(s16x4_t, vp));
+            }
+            const s16x4_t lo = part[0], hi = part[1];
+            const bf16x8_t vf = __builtin_bit_cast(
+                bf16x8_t, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                                      hi[0], hi[1], hi[2], hi[3]});
+            O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[hh], O[db], 0, 0, 0);
           }
         }
       }
     }
-    if (vt + 1 < vt1) stage_store<D>(st, Ks[cur ^ 1], Vt[cur ^ 1], tid);
-    __syncthreads();
   }
 
   // ---- epilogue: normalise and write the split's partial ---------------------
-#pragma unroll
-  for (int b = 0; b < kNB; ++b) {
-    const float ltot = lsum[b] + __shfl_xor(lsum[b], 32, kWave);
-    if (!row_ok[b]) continue;
-    const int64_t orow = ((int64_t)split * T + row_t[b]) * Hq + row_h[b];
+  const float ltot = lsum + __shfl_xor(lsum, 32, kWave);
+  if (row_ok) {
+    const int64_t orow = ((int64_t)split * T + row_t) * Hq + row_h;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     float* op = a.o_part + orow * D;
 #pragma unroll
@@ -339,11 +297,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = 32 * db + 8 * q4 + 4 * half;
-        float4 v = make_float4(O[b][db][4 * q4] * inv, O[b][db][4 * q4 + 1] * inv,
-                               O[b][db][4 * q4 + 2] * inv, O[b][db][4 * q4 + 3] * inv);
+        float4 v = make_float4(O[db][4 * q4] * inv, O[db][4 * q4 + 1] * inv,
+                               O[db][4 * q4 + 2] * inv, O[db][4 * q4 + 3] * inv);
         *reinterpret_cast<float4*>(op + d) = v;
       }
-    if (half == 0) a.l_part[orow] = ltot > 0.f ? (m[b] + log2f(ltot)) * kLn2 : -INFINITY;
+    if (half == 0) a.l_part[orow] = ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
   }
 }
 
