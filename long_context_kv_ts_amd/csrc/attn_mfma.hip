@@ -69,38 +69,34 @@ template <int D> __device__ __forceinline__ int v_chunk(int r, int c) {
 }
 
 // One wave-wide 16-byte-per-lane load from global memory straight into LDS:
-// lane l's bytes land at dst + 16*l (dst is wave-uniform, passed in M0).
-// Written as asm with no outputs so that the compiler does not guard every
-// later LDS read with a wait for ALL outstanding loads; completion is instead
-// awaited explicitly (vmcnt) before the barrier that publishes a tile. Loads
-// the compiler does not count only make its own waits stricter.
-__device__ __forceinline__ void lds_dma16(const bf16_t* src, bf16_t* dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TS_LDS(void, dst))));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+// lane l reads base + voff (base uniform, in SGPRs) and its 16 bytes land at
+// lds + 16*l (lds uniform, passed in M0). Written as asm with no outputs so
+// that the compiler does not guard every later LDS read with a wait for ALL
+// outstanding loads; completion is instead awaited explicitly (vmcnt) before
+// the barrier that publishes a tile. Loads the compiler does not count only
+// make its own waits stricter.
+__device__ __forceinline__ void lds_dma16(const bf16_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(src), "s"(lds)
+               : "v"(voff), "s"(base), "s"(lds)
                : "memory", "m0");
 }
 
-// Issue this wave's share of the direct-to-LDS loads of one K/V tile.
+// Per-lane byte offset, within a tile, of the row/chunk that load n of wave w
+// fills. Load q = w*loadsPerWave + n covers 1 KB block m = q % loadsPerTensor
+// of K (waves in the first half) or of V (second half); lane l fills row
+// m*rowsPerLoad + l/CH, physical chunk l%CH, so it reads the logical chunk
+// that the row's swizzle maps there. Rows past nvalid re-read row nvalid-1.
 template <int D>
-__device__ __forceinline__ void issue_tile(const bf16_t* kb, const bf16_t* vb, int nvalid,
-                                           bf16_t* Kst, bf16_t* Vst, int wave, int lane) {
+__device__ __forceinline__ uint32_t dma_offset(int wave, int n, int lane, int nvalid) {
   using Ly = Layout<D>;
-#pragma unroll
-  for (int n = 0; n < Ly::loadsPerWave; ++n) {
-    const int q = wave * Ly::loadsPerWave + n;               // 0 .. 2*loadsPerTensor-1
-    const bool isv = q >= Ly::loadsPerTensor;
-    const int m = isv ? q - Ly::loadsPerTensor : q;          // 1 KB block of the tile
-    const int r = m * Ly::rowsPerLoad + lane / Ly::CH;       // tile row this lane fills
-    const int pc = lane % Ly::CH;                            // physical chunk it fills
-    const int c = isv ? v_chunk<D>(r, pc) : k_chunk<D>(r, pc);   // xor: its own inverse
-    const int rr = min(r, nvalid - 1);
-    const bf16_t* src = (isv ? vb : kb) + (int64_t)rr * D + c * 8;
-    bf16_t* dst = (isv ? Vst : Kst) + m * 512;
-    lds_dma16(src, dst);
-  }
+  const int q = wave * Ly::loadsPerWave + n;
+  const bool isv = q >= Ly::loadsPerTensor;
+  const int mblk = isv ? q - Ly::loadsPerTensor : q;
+  const int r = mblk * Ly::rowsPerLoad + lane / Ly::CH;
+  const int pc = lane % Ly::CH;
+  const int c = isv ? v_chunk<D>(r, pc) : k_chunk<D>(r, pc);   // xor: its own inverse
+  return (uint32_t)((min(r, nvalid - 1) * D + c * 8) * 2);
 }
 
 template <int D>
@@ -121,7 +117,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   if (unit >= n_units) return;
   const int split = unit % pl.n_splits, g = unit / pl.n_splits;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps wave math scalar
   const int col = lane & 31, half = lane >> 5;
   const int G = a.G, T = a.T, Hq = a.Hq;
   const float c = a.scale_log2;
@@ -129,20 +126,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   const int vt0 = split * pl.tiles_per_split;
   const int vt1 = min(vt0 + pl.tiles_per_split, pl.n_virtual);
 
-  auto tile_src = [&](int vt, const bf16_t*& kb, const bf16_t*& vb, int& key0, int& nvalid) {
-    const bool draft = vt >= pl.n_cache_tiles;
-    key0 = draft ? (vt - pl.n_cache_tiles) * kTile : vt * kTile;
-    nvalid = draft ? min(kTile, T - key0) : (int)min((int64_t)kTile, a.L - key0);
-    kb = draft ? static_cast<const bf16_t*>(a.kd) + ((int64_t)g * T + key0) * D
-               : static_cast<const bf16_t*>(a.kc) + ((int64_t)g * a.cache_stride + key0) * D;
-    vb = draft ? static_cast<const bf16_t*>(a.vd) + ((int64_t)g * T + key0) * D
-               : static_cast<const bf16_t*>(a.vc) + ((int64_t)g * a.cache_stride + key0) * D;
-  };
+  // This wave streams K (first half of the waves) or V (second half).
+  const bool wave_v = wave * Ly::loadsPerWave >= Ly::loadsPerTensor;
+  const bf16_t* cache_base =
+      static_cast<const bf16_t*>(wave_v ? a.vc : a.kc) + (int64_t)g * a.cache_stride * D;
+  const bf16_t* draft_base = static_cast<const bf16_t*>(wave_v ? a.vd : a.kd) + (int64_t)g * T * D;
+  uint32_t off_full[Ly::loadsPerWave];
+#pragma unroll
+  for (int n = 0; n < Ly::loadsPerWave; ++n) off_full[n] = dma_offset<D>(wave, n, lane, kTile);
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TS_LDS(void, &KVs[0][0][0])));
   auto issue = [&](int vt, int stage) {
-    const bf16_t *kb, *vb;
-    int key0, nvalid;
-    tile_src(vt, kb, vb, key0, nvalid);
-    issue_tile<D>(kb, vb, nvalid, KVs[stage][0], KVs[stage][1], wave, lane);
+    const bool draft = vt >= pl.n_cache_tiles;
+    const int key0 = draft ? (vt - pl.n_cache_tiles) * kTile : vt * kTile;
+    const int nvalid = draft ? min(kTile, T - key0) : (int)min((int64_t)kTile, a.L - key0);
+    const bf16_t* base = (draft ? draft_base : cache_base) + (int64_t)key0 * D;
+    auto lds_of = [&](int n) {
+      const int q = wave * Ly::loadsPerWave + n;
+      const int mblk = q >= Ly::loadsPerTensor ? q - Ly::loadsPerTensor : q;
+      return lds_base + (uint32_t)(((stage * 2 + (wave_v ? 1 : 0)) * Ly::tileElems + mblk * 512) * 2);
+    };
+    if (__builtin_expect(nvalid == kTile, 1)) {
+#pragma unroll
+      for (int n = 0; n < Ly::loadsPerWave; ++n) lds_dma16(base, off_full[n], lds_of(n));
+    } else {
+#pragma unroll
+      for (int n = 0; n < Ly::loadsPerWave; ++n)
+        lds_dma16(base, dma_offset<D>(wave, n, lane, nvalid), lds_of(n));
+    }
   };
   // the first tile starts streaming before anything else
   issue(vt0, 0);
