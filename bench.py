@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=2,
                     help="KV heads of the step the CPU oracle runs for the baseline (of 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step instead of eager launches")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -66,6 +69,14 @@ def main():
     from long_context_kv_ts_amd import inputs, ops
 
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": src.numel() * 2, "bytes_written": dst.numel() * 2}))
+        return
     ops.lib()   # fail loudly if the library is missing
 
     t0 = time.time()
@@ -122,14 +133,39 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    # With --graph the step is replayed as one HIP graph (nothing in it
+    # allocates or clears memory); by default the launches are eager.
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # timed region 1: K steps, wall clock between two syncs
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
+
+    # timed region 2: the same K steps launched eagerly with HIP events between
+    # the kernels (on torch's current stream, which every call launches on):
+    # per-kernel durations for the roofline
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t2) * 1e3 / args.steps
 
     per = {n: [] for n in names}
     for ev in events:
@@ -154,7 +190,7 @@ def main():
     achieved = flops / t_split / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None, "kernel": "verify split-K (attn_split)",
+                "traffic": measured_traffic(), "kernel": "verify split-K (attn_split_mfma_kernel)",
                 "algorithmic_flops": flops, "algorithmic_bytes": kv_bytes,
                 "hbm_GBs": round(kv_bytes / t_split / 1e9, 1),
                 "hbm_frac": round(kv_bytes / t_split / 1e9 / HBM_PEAK_GBS, 4)}
@@ -177,6 +213,8 @@ def main():
                                "64 of 1600 64-token chunks) + 4-query draft attention",
                    "T": T, "Hq": Hq, "Hkv": Hkv, "head_dim": D, "kv_len": L, "splits": S,
                    "chunk": pc.chunk, "topk": pc.k},
+        "timing": "graph replay of the step" if graph is not None else "eager launches",
+        "eager_ms_per_step": round(eager_ms, 4),
         "verify_us": round(avg["verify_split"] + avg["verify_merge"], 2),
         "verify_hbm_frac": round(kv_bytes / ((avg["verify_split"] + avg["verify_merge"]) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_us_avg": {n: round(v, 2) for n, v in avg.items()},
@@ -187,6 +225,33 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(vc, pc, args.cpu_heads)
     print(json.dumps(res), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_split_102400_hbm_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "long_context_kv_ts_amd", "csrc", f) for f in ("attn_mfma.hip", "common.h")]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the verify split kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by what the same counters read
+    for a plain copy of known size; None if the kernel source has changed since."""
+    try:
+        kv = dict(line.split("=", 1) for line in open(TRAFFIC_FILE) if "=" in line and not line.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return round(float(kv["fetch_kib"]) * float(kv["fetch_scale"]) * 1024
+                     + float(kv["write_kib"]) * float(kv["write_scale"]) * 1024)
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(vc, pc, heads):

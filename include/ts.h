@@ -3,12 +3,13 @@
  * partial-KV-cache kernels for AMD Instinct MI355X (gfx950).
  *
  * What the calls compute follows the TokenSwift pages:
- *   - tool listing, "How it works": the drafts (a candidate tree built with
- *     tree-based attention, plus retrieved 4-grams) are fed to the target
- *     model with the FULL KV cache; the model with a PARTIAL KV cache and
- *     three linear heads drafts 4 tokens in one forward pass;
- *   - summary page, "Approach": the partial KV cache is re-ranked dynamically
- *     by query-key importance;
+ *   - tool listing, "How it works": verification runs the target model once
+ *     over all drafts (a candidate tree plus retrieved 4-grams) against the
+ *     COMPLETE KV cache, each draft seeing only its own tree ancestors;
+ *     drafting runs the target model itself, with a small set of extra linear
+ *     heads, over a REDUCED (partial) KV cache and proposes 4 tokens per pass;
+ *   - summary page, "Approach": the reduced cache is re-selected during
+ *     generation by how strongly queries attend to its keys;
  *   - model card, command-line example: retrieval budget 4096 tokens, gamma 4,
  *     ngram_topk 20, generation up to 102400 tokens.
  *
@@ -61,8 +62,9 @@ int ts_abi_version(void);
 #define TS_MAX_DRAFT 256 /* max draft tokens T of one verify call */
 
 /* ------------------------------------------------------------------------
- * Tree-verify attention (tool listing, "How it works": drafts are fed to the
- * target model with the full KV cache under tree-based attention).
+ * Tree-verify attention (tool listing, "How it works": one verification pass
+ * of the target model over all drafts against the complete cache, with the
+ * tree mask).
  *
  * For draft row t in [0,T), query head h, g = h / (Hq/Hkv):
  *   A(t) = {t} + ancestors of t along parent[]      (ancestor-or-self mask)
@@ -125,8 +127,9 @@ ts_status ts_attn_merge(const float* o_part, const float* l_part, int n_parts,
                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Chunk importance (summary page, "Approach": the partial cache is ranked by
- * query-key importance). For KV head g and chunk c = tokens [c*chunk, (c+1)*chunk):
+ * Chunk importance (summary page, "Approach": the reduced cache is chosen by
+ * how strongly queries attend to its keys). For KV head g and chunk
+ * c = tokens [c*chunk, (c+1)*chunk):
  *   u[r, j]     = max over query heads h of group g of  scale * <q_recent[r,h], k[g,j]>
  *   scores[g,c] = mean over r in [0,R) and j in chunk c of u[r, j]
  * (max over the grouped heads, mean over tokens and recent queries: the pages
@@ -168,8 +171,9 @@ ts_status ts_kv_gather(const void* k_cache, const void* v_cache, int64_t cache_s
                        void* k_part, void* v_part, ts_dtype dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Draft attention over the partial cache (tool listing, "How it works": the
- * target model with a partial KV cache drafts 4 tokens in one forward pass).
+ * Draft attention over the partial cache (tool listing, "How it works":
+ * drafting runs the target model itself over the reduced cache, proposing
+ * 4 tokens per pass).
  * Tq new tokens attend to all P gathered tokens and causally among
  * themselves: exactly ts_tree_verify_attn with the chain parent[t] = t-1.
  *   q [Tq][Hq][D]; k_part, v_part [Hkv][P][D]; k_new, v_new [Hkv][Tq][D];

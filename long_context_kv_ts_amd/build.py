@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libts.so")
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_merge.hip",
+SOURCES = ["api.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_small.hip", "attn_merge.hip",
            "importance.hip", "topk.hip", "gather.hip"]
 
 

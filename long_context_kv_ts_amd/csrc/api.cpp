@@ -64,18 +64,22 @@ AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype
   AttnPlan p{};
   const int G = Hq / Hkv;
   p.rows_per_head = T * G;
-  // Matrix cores where the grouped query rows of a KV head fill at least one
-  // 32-row MFMA block; the vector-ALU kernel otherwise (and for fp32).
-  p.path = (dtype == TS_BF16 && (D == 128 || D == 64) && p.rows_per_head >= 32) ? kPathMfma
-                                                                                 : kPathValu;
-  p.rows_per_group = p.path == kPathMfma ? kMfmaRows : kValuRows;
+  // bf16: matrix cores. KV heads with more than 16 grouped query rows use the
+  // 256-row / 32-row-block kernel; up to 16 rows (one 16x16 MFMA tile) the
+  // wave-per-split kernel. fp32: vector ALUs.
+  if (dtype == TS_BF16) p.path = p.rows_per_head > 16 ? kPathMfma : kPathSmall;
+  else p.path = kPathValu;
+  (void)D;
+  p.rows_per_group = p.path == kPathMfma ? kMfmaRows : p.path == kPathSmall ? 16 : kValuRows;
   p.n_rowgroups = (p.rows_per_head + p.rows_per_group - 1) / p.rows_per_group;
   p.n_cache_tiles = (int)((L + kTile - 1) / kTile);
   p.n_draft_tiles = (T + kTile - 1) / kTile;
   p.n_virtual = p.n_cache_tiles + p.n_draft_tiles;
   int s = num_splits;
   if (s <= 0) {
-    const int per_cu = p.path == kPathMfma ? 1 : 4;
+    // workgroups per CU the launch aims for: matrix-core kernel 1 (it holds a
+    // whole CU), small kernel 8 waves (each wave a split), vector-ALU kernel 4
+    const int per_cu = p.path == kPathMfma ? 1 : p.path == kPathSmall ? 8 : 4;
     const int64_t groups = (int64_t)Hkv * p.n_rowgroups;
     s = (int)((kCUs * per_cu + groups - 1) / groups);
     if (s < 1) s = 1;
@@ -136,8 +140,9 @@ static ts_status attn_common(const char* fn, const void* q, const void* kc, cons
   a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D; a.L = L;
   a.scale_log2 = scale * kLog2e;
   a.plan = plan_attention(T, Hq, Hkv, D, L, dtype, num_splits);
-  hipError_t e = a.plan.path == kPathMfma ? launch_attn_split_mfma(a, stream)
-                                          : launch_attn_split_valu(a, dtype, stream);
+  hipError_t e = a.plan.path == kPathMfma    ? launch_attn_split_mfma(a, stream)
+                 : a.plan.path == kPathSmall ? launch_attn_split_small(a, stream)
+                                             : launch_attn_split_valu(a, dtype, stream);
   return from_hip(e, fn);
 }
 

@@ -98,7 +98,7 @@ __device__ __forceinline__ void build_ancestor_mask(const int32_t* parent, int T
 // ----------------------------------------------------------------------------
 // Work decomposition of one masked split-K attention call.
 // ----------------------------------------------------------------------------
-enum AttnPath { kPathValu = 0, kPathMfma = 1 };
+enum AttnPath { kPathValu = 0, kPathMfma = 1, kPathSmall = 2 };
 
 struct AttnPlan {
   int path;
@@ -133,6 +133,7 @@ AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype
 // Launchers (return the hipGetLastError() of the launch).
 hipError_t launch_attn_split_valu(const AttnArgs& a, ts_dtype dtype, hipStream_t s);
 hipError_t launch_attn_split_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_split_small(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const float* o_part, const float* l_part, int n_parts, int rows,
                              int D, void* out, float* lse, ts_dtype dtype, hipStream_t s);
 hipError_t launch_importance(const void* q, const void* kc, int64_t stride, float* scores,

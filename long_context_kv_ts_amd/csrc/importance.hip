@@ -133,16 +133,87 @@ __global__ __launch_bounds__(256) void importance_mfma_kernel(
   }
 }
 
+// 64-token chunks: the whole chunk's K (16 KB) is requested before any
+// product, so each wave keeps 16 loads in flight instead of walking the chunk
+// one 16-key block at a time.
+template <int D, int NRB>
+__global__ __launch_bounds__(256) void importance_mfma64_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, int64_t stride,
+    float* __restrict__ scores, int R, int Hq, int Hkv, float scale, int n_chunks) {
+  constexpr int KS = D / 32, CHUNK = 64, NKB = CHUNK / 16;
+  const int g = blockIdx.y, G = Hq / Hkv, rows = R * G;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+
+  bf16x8_t qb[NRB][KS];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int row = rb * 16 + col;
+    const bool valid = row < rows;
+    const int r = valid ? row / G : 0, h = g * G + (valid ? row % G : 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 u = valid ? *reinterpret_cast<const uint4*>(q + ((int64_t)r * Hq + h) * D + ks * 32 + quad * 8)
+                            : make_uint4(0u, 0u, 0u, 0u);
+      qb[rb][ks] = __builtin_bit_cast(bf16x8_t, u);
+    }
+  }
+  const float inv = 1.f / (float)(CHUNK * R);
+  const int waves_total = gridDim.x * 4;
+  for (int c = blockIdx.x * 4 + wave; c < n_chunks; c += waves_total) {
+    const bf16_t* base = kc + ((int64_t)g * stride + (int64_t)c * CHUNK) * D;
+    bf16x8_t ka[NKB][KS];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[kb][ks] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(base + (int64_t)(kb * 16 + col) * D + ks * 32 + quad * 8));
+    float tot = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][ks], qb[rb][ks], s, 0, 0, 0);
+        // s[i]: key 16*kb + 4*quad + i, query row rb*16 + col; max over the G
+        // heads of a recent query = max over G adjacent columns (lanes)
+        const int row = rb * 16 + col;
+        const bool head0 = (row % G) == 0 && row < rows;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = s[i] * scale;
+          for (int o = 1; o < G; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+          tot += head0 ? v : 0.f;
+        }
+      }
+    }
+    tot = wave_sum(tot);
+    if (lane == 0) scores[(int64_t)g * n_chunks + c] = tot * inv;
+  }
+}
+
 template <int D>
 hipError_t launch_mfma(const bf16_t* q, const bf16_t* kc, int64_t stride, float* scores, int R,
                        int Hq, int Hkv, int chunk, float scale, int n_chunks, hipStream_t s) {
   const int rows = R * (Hq / Hkv);
   // enough waves to keep ~64 KB of K loads in flight per CU; each wave strides
   // over chunks of its KV head
+  // one chunk per wave (waves stride over chunks only past 65535 workgroups)
   int blocks_x = (n_chunks + 3) / 4;
-  const int max_blocks_x = (2048 + Hkv - 1) / Hkv;
-  if (blocks_x > max_blocks_x) blocks_x = max_blocks_x;
+  if (blocks_x > 65535) blocks_x = 65535;
   dim3 grid(blocks_x, Hkv);
+  if (chunk == 64) {
+    if (rows <= 16)
+      importance_mfma64_kernel<D, 1><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, scale, n_chunks);
+    else if (rows <= 32)
+      importance_mfma64_kernel<D, 2><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, scale, n_chunks);
+    else
+      importance_mfma64_kernel<D, 4><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, scale, n_chunks);
+    return hipGetLastError();
+  }
   if (rows <= 16)
     importance_mfma_kernel<D, 1><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, chunk, scale, n_chunks);
   else if (rows <= 32)

@@ -1,12 +1,18 @@
-// Top-k chunk selection per KV head by radix select, then stream compaction.
+// Top-k chunk selection per KV head.
 //
-// Scores map to order-preserving 32-bit keys (larger score -> larger key).
-// Four 8-bit radix passes over LDS histograms find the exact key of the k-th
-// largest element; `need` = how many elements equal to that key are kept.
-// Among equal keys the lower chunk index wins, and the chosen chunks are
-// written in ascending index order: both fall out of one exclusive prefix
-// sum over the chunks in index order. One 256-thread workgroup per KV head;
-// every thread owns a contiguous run of chunk indices.
+// Scores map to order-preserving 32-bit keys (larger score -> larger key; -0
+// and +0 share a key). Ties go to the lower chunk index and the chosen chunks
+// are written in ascending index order.
+//
+// n <= 4096 (the partial-KV workloads: 1600 chunks of 64 tokens at 100K):
+//   one 1024-thread workgroup per KV head sorts the unique 64-bit keys
+//   (score key << 32 | ~index) descending with a bitonic network in LDS; the
+//   first k are the selection, which a second bitonic sort orders by index.
+// larger n: four 8-bit radix passes over LDS histograms find the exact key of
+//   the k-th largest element and how many of the elements equal to it are
+//   kept; one exclusive prefix sum over the chunks in index order then both
+//   breaks ties toward lower indices and writes the result in index order
+//   (256 threads, each owning a contiguous run of chunk indices).
 #include "common.h"
 
 namespace ts {
@@ -107,11 +113,78 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   }
 }
 
+// Bitonic sort of N (power of two) 64-bit keys in LDS; descending if `desc`.
+// Pair i of a stage is (lo, lo + stride) with lo = 2i - i % stride.
+__device__ __forceinline__ void bitonic_sort(uint64_t* v, int N, bool desc, int tid, int nthreads) {
+  for (int size = 2; size <= N; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (N >> 1); i += nthreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = ((lo & size) == 0) != desc;     // ascending run?
+        const uint64_t a = v[lo], b = v[hi];
+        if ((a > b) == up) {
+          v[lo] = b;
+          v[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+constexpr int kSortMax = 4096;
+constexpr int kSortThreads = 1024;
+
+__global__ __launch_bounds__(kSortThreads) void topk_sort_kernel(const float* __restrict__ scores,
+                                                                 int n, int k,
+                                                                 int32_t* __restrict__ idx_out,
+                                                                 float* __restrict__ val_out) {
+  __shared__ uint64_t v[kSortMax];
+  const int tid = threadIdx.x, g = blockIdx.x;
+  const float* s = scores + (int64_t)g * n;
+  int N = 2;
+  while (N < n) N <<= 1;
+  // padding sorts last: every real key has a non-zero high word
+  for (int i = tid; i < N; i += kSortThreads)
+    v[i] = i < n ? ((uint64_t)order_key(s[i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i) : 0ull;
+  __syncthreads();
+  bitonic_sort(v, N, true, tid, kSortThreads);
+  // the first k, re-keyed by index (index << 32 | score key), sorted ascending
+  int K = 2;
+  while (K < k) K <<= 1;
+  uint64_t w[kSortMax / kSortThreads];
+  int cnt = 0;
+  for (int i = tid; i < K; i += kSortThreads) {
+    uint64_t x = ~0ull;
+    if (i < k) {
+      const uint64_t y = v[i];
+      x = ((uint64_t)(0xFFFFFFFFu - (uint32_t)y) << 32) | (y >> 32);
+    }
+    w[cnt++] = x;
+  }
+  __syncthreads();
+  cnt = 0;
+  for (int i = tid; i < K; i += kSortThreads) v[i] = w[cnt++];
+  __syncthreads();
+  bitonic_sort(v, K, false, tid, kSortThreads);
+  for (int i = tid; i < k; i += kSortThreads) {
+    const uint64_t x = v[i];
+    idx_out[(int64_t)g * k + i] = (int32_t)(x >> 32);
+    if (val_out) {
+      const uint32_t key = (uint32_t)x;
+      const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+      val_out[(int64_t)g * k + i] = __uint_as_float(u);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float* scores, int Hkv, int n, int k, int32_t* idx, float* val,
                        hipStream_t s) {
-  topk_kernel<<<Hkv, kThreads, 0, s>>>(scores, n, k, idx, val);
+  if (n <= kSortMax) topk_sort_kernel<<<Hkv, kSortThreads, 0, s>>>(scores, n, k, idx, val);
+  else topk_kernel<<<Hkv, kThreads, 0, s>>>(scores, n, k, idx, val);
   return hipGetLastError();
 }
 

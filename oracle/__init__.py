@@ -12,18 +12,19 @@ as uint16 bit patterns and are widened exactly to float64 here.
 Functions and the passages they follow (TokenSwift pages):
 
 * ``ancestor_mask``      the tree mask over draft tokens (tool listing, "How it
-                          works": tree-based attention over the candidates).
+                          works": candidates are organised as a tree and
+                          attend along it).
 * ``verify_attn_ref``     masked softmax attention of the draft queries over
-                          the full cache plus their own ancestors (tool listing,
-                          "How it works": drafts fed to the LLM with the full
-                          KV cache).
+                          the whole cache plus their own ancestors (tool
+                          listing, "How it works": the target model checks all
+                          drafts in one pass against its complete cache).
 * ``draft_attn_ref``      the same over the gathered partial cache with a
                           causal chain of new tokens (tool listing, "How it
-                          works": the model with a partial KV cache outputs 4
-                          logits in one forward pass).
+                          works": drafting runs the target model itself on a
+                          reduced cache).
 * ``importance_ref``      query-key importance per chunk (summary page,
-                          "Approach": partial cache ranked by query-key
-                          importance).
+                          "Approach": the reduced cache is re-selected by how
+                          strongly queries attend to its keys).
 * ``topk_ref``            the highest-scoring chunks up to the budget
                           (model card CLI example: retrieval budget 4096).
 * ``gather_ref``          the partial cache built from the chosen chunks.

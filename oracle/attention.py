@@ -2,9 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
-What is computed (TokenSwift tool listing, "How it works"): the draft tokens
-are fed to the target model with the full KV cache; tree-based attention lets
-every candidate see only its own ancestors among the drafts. With
+What is computed (TokenSwift tool listing, "How it works"): verification runs
+the target model once over all draft tokens against its complete KV cache, and
+the tree mask lets every candidate see, among the drafts, only itself and its
+ancestors. With
 ``A(t) = {t} U ancestors(t)`` along ``parent[]``, for draft row t and query
 head h of KV group g = h // G:
 

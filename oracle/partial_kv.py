@@ -2,9 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
-The TokenSwift summary page ("Approach") keeps a partial KV cache that is
-re-ranked by query-key importance; the model card CLI example fixes the
-retrieval budget at 4096 tokens. The pages give no formula, so these readings
+The TokenSwift summary page ("Approach") drafts over a reduced KV cache that
+is re-selected as generation proceeds, by how strongly queries attend to its
+keys; the model card CLI example sets that budget to 4096 tokens. The pages give no formula, so these readings
 hold (each is a plain definition, not an algorithm):
 
 * importance of chunk c of KV head g (tokens c*chunk .. c*chunk+chunk-1),

@@ -1,0 +1,60 @@
+"""The whole step captured in a HIP graph and replayed: every replay must
+reproduce the eager results bit for bit (the kernels are deterministic and
+nothing in the step allocates or clears memory)."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_kv_ts_amd import inputs, ops
+from gpu_util import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager():
+    say("[graph] verify + partial-KV step, 3 replays")
+    dev = torch.device("cuda:0")
+    c = inputs.make_verify("graph", dtype="bf16", Hq=32, Hkv=8, D=128, L=5000, seed=21, with_chains=True)
+    p = inputs.make_partial(L=8192, seed=22)
+    q, kc, vc, kd, vd = (to_dev(x, "bf16") for x in (c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft))
+    par = to_dev(c.parent, "i32")
+    pq, pk, pv, pkn, pvn = (to_dev(x, "bf16") for x in (p.q, p.k_cache, p.v_cache, p.k_new, p.v_new))
+    S = ops.num_splits(c.T, c.Hq, c.Hkv, c.D, c.L, torch.bfloat16)
+    o_part = torch.empty((S, c.T, c.Hq, c.D), dtype=torch.float32, device=dev)
+    l_part = torch.empty((S, c.T, c.Hq), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((c.T, c.Hq), dtype=torch.float32, device=dev)
+    scores = torch.empty((p.Hkv, p.n_chunks), dtype=torch.float32, device=dev)
+    idx = torch.empty((p.Hkv, p.k), dtype=torch.int32, device=dev)
+    val = torch.empty((p.Hkv, p.k), dtype=torch.float32, device=dev)
+    kp = torch.empty((p.Hkv, p.k * p.chunk, p.D), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    dout = torch.empty_like(pq)
+    dlse = torch.empty((p.R, p.Hq), dtype=torch.float32, device=dev)
+    ws = ops.alloc_workspace(ops.lib().ts_partial_draft_attn_workspace(p.R, p.Hq, p.Hkv, p.D, p.k * p.chunk,
+                                                                       ops.TS_BF16, 0), dev)
+
+    def step():
+        ops.tree_verify_attn_partials(q, kc, vc, kd, vd, par, scale=c.scale, o_part=o_part, l_part=l_part)
+        ops.attn_merge(o_part, l_part, out=out, lse=lse)
+        ops.kv_importance_score(pq, pk, p.chunk, scale=p.scale, scores=scores)
+        ops.kv_topk_select(scores, p.k, chunk_idx=idx, chunk_score=val)
+        ops.kv_gather(pk, pv, idx, p.chunk, k_part=kp, v_part=vp)
+        ops.partial_draft_attn(pq, kp, vp, pkn, pvn, scale=p.scale, out=dout, lse=dlse, workspace=ws)
+
+    results = (out, lse, scores, idx, val, kp, vp, dout, dlse)
+    step()
+    torch.cuda.synchronize()
+    eager = [r.clone() for r in results]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for r in results:
+            r.zero_()                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("out", "lse", "scores", "idx", "val", "kp", "vp", "dout", "dlse"), results, eager):
+            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), f"replay {rep}: {name}"

@@ -150,3 +150,20 @@ def test_draft_attention_shapes(shape):
     torch.cuda.synchronize()
     ro, rl = oracle.draft_attn_ref(q, kp, vp, kn, vn, D ** -0.5, "bf16")
     check_attn(out, lse, ro, rl, "bf16", str(shape))
+
+
+@pytest.mark.parametrize("Tq,Hq,Hkv,D,P", [(4, 32, 8, 128, 4096), (4, 32, 8, 128, 1000), (1, 8, 2, 128, 777),
+                                          (3, 16, 4, 64, 300), (16, 16, 16, 128, 2100), (2, 4, 4, 128, 64)])
+def test_small_row_kernel_shapes(Tq, Hq, Hkv, D, P):
+    """KV heads with at most 16 grouped rows (wave-per-split kernel), ragged lengths."""
+    say(f"[small rows] Tq={Tq} Hq={Hq} Hkv={Hkv} D={D} P={P}")
+    rng = np.random.default_rng(Tq * 1000 + P)
+    f = lambda *s, sd=1.0: inputs.f32_to_bf16_bits((rng.standard_normal(s) * sd).astype(np.float32))
+    q, kp, vp = f(Tq, Hq, D), f(Hkv, P, D, sd=D ** -0.5), f(Hkv, P, D, sd=D ** -0.5)
+    kn, vn = f(Hkv, Tq, D, sd=D ** -0.5), f(Hkv, Tq, D, sd=D ** -0.5)
+    for ns in (0, 3):
+        out, lse = ops.partial_draft_attn(*(to_dev(a, "bf16") for a in (q, kp, vp, kn, vn)), scale=D ** -0.5,
+                                          num_splits=ns)
+        torch.cuda.synchronize()
+        ro, rl = oracle.draft_attn_ref(q, kp, vp, kn, vn, D ** -0.5, "bf16")
+        check_attn(out, lse, ro, rl, "bf16", f"splits={ns}")
