@@ -34,11 +34,8 @@ int elem_size(ts_dtype d) { return d == TS_BF16 ? 2 : 4; }
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Rows of one workgroup of the matrix-core kernel (see attn_mfma.hip).
-constexpr int kMfmaRows = 256;
 constexpr int kValuRows = 16;
-// MI355X: 256 compute units. Target roughly this many workgroups of the
-// matrix-core kernel (one per CU) and four per CU for the vector-ALU kernel.
+// MI355X: 256 compute units.
 constexpr int kCUs = 256;
 
 ts_status check_attn_shape(const char* fn, int T, int Hq, int Hkv, int D, int64_t L,
@@ -70,16 +67,17 @@ AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype
   if (dtype == TS_BF16) p.path = p.rows_per_head > 16 ? kPathMfma : kPathSmall;
   else p.path = kPathValu;
   (void)D;
-  p.rows_per_group = p.path == kPathMfma ? kMfmaRows : p.path == kPathSmall ? 16 : kValuRows;
+  p.rows_per_group = p.path == kPathMfma ? mfma_rows_per_group() : p.path == kPathSmall ? 16 : kValuRows;
   p.n_rowgroups = (p.rows_per_head + p.rows_per_group - 1) / p.rows_per_group;
-  p.n_cache_tiles = (int)((L + kTile - 1) / kTile);
-  p.n_draft_tiles = (T + kTile - 1) / kTile;
+  p.tile = p.path == kPathMfma ? mfma_tile_keys() : kTile;
+  p.n_cache_tiles = (int)((L + p.tile - 1) / p.tile);
+  p.n_draft_tiles = (T + p.tile - 1) / p.tile;
   p.n_virtual = p.n_cache_tiles + p.n_draft_tiles;
   int s = num_splits;
   if (s <= 0) {
-    // workgroups per CU the launch aims for: matrix-core kernel 1 (it holds a
-    // whole CU), small kernel 8 waves (each wave a split), vector-ALU kernel 4
-    const int per_cu = p.path == kPathMfma ? 1 : p.path == kPathSmall ? 8 : 4;
+    // workgroups per CU the launch aims for: as many matrix-core workgroups as
+    // fit a CU, 8 waves of the small kernel (each wave a split), 4 vector-ALU
+    const int per_cu = p.path == kPathMfma ? mfma_groups_per_cu() : p.path == kPathSmall ? 8 : 4;
     const int64_t groups = (int64_t)Hkv * p.n_rowgroups;
     s = (int)((kCUs * per_cu + groups - 1) / groups);
     if (s < 1) s = 1;

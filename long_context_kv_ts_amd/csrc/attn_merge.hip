@@ -5,17 +5,20 @@
 // o_s is each split's softmax-normalised output and l_s its natural-log
 // normaliser (-inf for a split that saw no key of the row).
 //
-// One workgroup per output row. The splits are spread over NG groups of D/4
-// threads (each thread owns 4 columns), so every thread issues only S/NG
-// independent 16-byte loads instead of walking all S splits one round trip at
-// a time. Each group keeps its own running max; the groups' partial sums meet
-// in LDS, rescaled to the common max.
+// One wave per output row, four rows per 256-thread workgroup. The wave's
+// lanes form 64/(D/4) split groups of D/4 lanes (each lane owns 4 columns);
+// a lane first issues the loads of a batch of its splits, then folds them
+// into a running max/sum, so several 16-byte loads are in flight per lane.
+// The groups' partial results are combined with lane exchanges: no LDS and no
+// barrier.
 #include "common.h"
 
 namespace ts {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / kWave;
+constexpr int kBatch = 8;
 
 template <typename Tout, int D>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(const float* __restrict__ o_part,
@@ -23,56 +26,66 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(const float* __res
                                                               int S, int rows,
                                                               Tout* __restrict__ out,
                                                               float* __restrict__ lse) {
-  constexpr int C4 = D / 4;              // threads per split group (one float4 each)
-  constexpr int NG = kThreads / C4;      // split groups
-  __shared__ float4 acc_s[NG][C4];
-  __shared__ float m_s[NG], w_s[NG];
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const int gi = tid / C4, c = tid % C4;
+  constexpr int C4 = D / 4;              // lanes per split group (one float4 each)
+  constexpr int NG = kWave / C4;         // split groups per wave
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;               // whole wave leaves; no barrier follows
+  const int gi = lane / C4, c = lane % C4;
 
-  // each group merges its splits (s = gi, gi+NG, ...) with its own running max
   float m = -INFINITY, ws = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int s = gi; s < S; s += NG) {
-    const int64_t pr = (int64_t)s * rows + row;
-    const float ls = l_part[pr];
-    const float4 o = *reinterpret_cast<const float4*>(o_part + pr * D + 4 * c);
-    if (ls == -INFINITY) continue;
-    const float mn = fmaxf(m, ls);
-    const float a = __expf(m - mn);          // m = -inf: 0
-    const float w = __expf(ls - mn);
-    ws = ws * a + w;
-    acc.x = acc.x * a + w * o.x; acc.y = acc.y * a + w * o.y;
-    acc.z = acc.z * a + w * o.z; acc.w = acc.w * a + w * o.w;
-    m = mn;
-  }
-  acc_s[gi][c] = acc;
-  if (c == 0) { m_s[gi] = m; w_s[gi] = ws; }
-  __syncthreads();
-  if (gi == 0) {
-    float M = -INFINITY;
+  for (int s0 = gi; s0 < S; s0 += NG * kBatch) {
+    float lb[kBatch];
+    float4 ob[kBatch];
 #pragma unroll
-    for (int k = 0; k < NG; ++k) M = fmaxf(M, m_s[k]);
-    float wt = 0.f;
-    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int k = 0; k < NG; ++k) {
-        if (m_s[k] == -INFINITY) continue;
-        const float f = __expf(m_s[k] - M);
-        wt += w_s[k] * f;
-        const float4 a = acc_s[k][c];
-        t.x += a.x * f; t.y += a.y * f; t.z += a.z * f; t.w += a.w * f;
+    for (int b = 0; b < kBatch; ++b) {
+      const int s = s0 + b * NG;
+      lb[b] = -INFINITY;
+      ob[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s < S) {
+        const int64_t pr = (int64_t)s * rows + row;
+        lb[b] = l_part[pr];
+        ob[b] = *reinterpret_cast<const float4*>(o_part + pr * D + 4 * c);
       }
     }
-    const float inv = wt > 0.f ? 1.f / wt : 0.f;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const float ls = lb[b];
+      if (ls == -INFINITY) continue;     // empty split (or past S)
+      const float mn = fmaxf(m, ls);
+      const float a = __expf(m - mn);    // m = -inf: 0
+      const float w = __expf(ls - mn);
+      const float4 o = ob[b];
+      ws = ws * a + w;
+      acc.x = acc.x * a + w * o.x; acc.y = acc.y * a + w * o.y;
+      acc.z = acc.z * a + w * o.z; acc.w = acc.w * a + w * o.w;
+      m = mn;
+    }
+  }
+  // combine the split groups: lanes c, c + C4, ... hold the same columns
+#pragma unroll
+  for (int off = C4; off < kWave; off <<= 1) {
+    const float m2 = __shfl_xor(m, off, kWave), w2 = __shfl_xor(ws, off, kWave);
+    float4 a2;
+    a2.x = __shfl_xor(acc.x, off, kWave); a2.y = __shfl_xor(acc.y, off, kWave);
+    a2.z = __shfl_xor(acc.z, off, kWave); a2.w = __shfl_xor(acc.w, off, kWave);
+    const float M = fmaxf(m, m2);
+    const float f1 = M == -INFINITY ? 0.f : __expf(m - M);
+    const float f2 = M == -INFINITY ? 0.f : __expf(m2 - M);
+    ws = ws * f1 + w2 * f2;
+    acc.x = acc.x * f1 + a2.x * f2; acc.y = acc.y * f1 + a2.y * f2;
+    acc.z = acc.z * f1 + a2.z * f2; acc.w = acc.w * f1 + a2.w * f2;
+    m = M;
+  }
+  if (gi == 0) {
+    const float inv = ws > 0.f ? 1.f / ws : 0.f;
     Tout* op = out + (int64_t)row * D + 4 * c;
-    Elem<Tout>::store(op + 0, t.x * inv);
-    Elem<Tout>::store(op + 1, t.y * inv);
-    Elem<Tout>::store(op + 2, t.z * inv);
-    Elem<Tout>::store(op + 3, t.w * inv);
-    if (lse != nullptr && c == 0) lse[row] = wt > 0.f ? M + logf(wt) : -INFINITY;
+    Elem<Tout>::store(op + 0, acc.x * inv);
+    Elem<Tout>::store(op + 1, acc.y * inv);
+    Elem<Tout>::store(op + 2, acc.z * inv);
+    Elem<Tout>::store(op + 3, acc.w * inv);
+    if (lse != nullptr && c == 0) lse[row] = ws > 0.f ? m + logf(ws) : -INFINITY;
   }
 }
 
@@ -80,16 +93,17 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(const float* __res
 
 hipError_t launch_attn_merge(const float* o_part, const float* l_part, int n_parts, int rows,
                              int D, void* out, float* lse, ts_dtype dtype, hipStream_t s) {
+  const int grid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (dtype == TS_BF16) {
     if (D == 128)
-      attn_merge_kernel<bf16_t, 128><<<rows, kThreads, 0, s>>>(o_part, l_part, n_parts, rows, static_cast<bf16_t*>(out), lse);
+      attn_merge_kernel<bf16_t, 128><<<grid, kThreads, 0, s>>>(o_part, l_part, n_parts, rows, static_cast<bf16_t*>(out), lse);
     else
-      attn_merge_kernel<bf16_t, 64><<<rows, kThreads, 0, s>>>(o_part, l_part, n_parts, rows, static_cast<bf16_t*>(out), lse);
+      attn_merge_kernel<bf16_t, 64><<<grid, kThreads, 0, s>>>(o_part, l_part, n_parts, rows, static_cast<bf16_t*>(out), lse);
   } else {
     if (D == 128)
-      attn_merge_kernel<float, 128><<<rows, kThreads, 0, s>>>(o_part, l_part, n_parts, rows, static_cast<float*>(out), lse);
+      attn_merge_kernel<float, 128><<<grid, kThreads, 0, s>>>(o_part, l_part, n_parts, rows, static_cast<float*>(out), lse);
     else
-      attn_merge_kernel<float, 64><<<rows, kThreads, 0, s>>>(o_part, l_part, n_parts, rows, static_cast<float*>(out), lse);
+      attn_merge_kernel<float, 64><<<grid, kThreads, 0, s>>>(o_part, l_part, n_parts, rows, static_cast<float*>(out), lse);
   }
   return hipGetLastError();
 }

@@ -99,6 +99,17 @@ __device__ __forceinline__ uint32_t dma_offset(int wave, int n, int lane, int nv
   return (uint32_t)((min(r, nvalid - 1) * D + c * 8) * 2);
 }
 
+// v_permlane32_swap(x, x) returns (x[l], x[l+32]) in lanes 0-31 and (x[l-32], x[l])
+// in lanes 32-63: combining the pair gives lane l and lane l^32 without LDS.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a) {
   using Ly = Layout<D>;
@@ -240,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
         float mx = S[0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;          // same for lanes l, l^32
+        mx = max_xor32(mx) * c;                                  // same for lanes l, l^32
         const bool need = mx > m + kLazy;
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
           // need implies mx finite; exp2(-inf) = 0 clears a row that had no key yet
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   }
 
   // ---- epilogue: normalise and write the split's partial ---------------------
-  const float ltot = lsum + __shfl_xor(lsum, 32, kWave);
+  const float ltot = sum_xor32(lsum);
   if (row_ok) {
     const int64_t orow = ((int64_t)split * T + row_t) * Hq + row_h;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
@@ -318,6 +329,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
 }  // namespace
 
 int mfma_rows_per_group() { return kRowsPerGroup; }
+int mfma_tile_keys() { return kTile; }
+int mfma_groups_per_cu() { return 1; }
 
 hipError_t launch_attn_split_mfma(const AttnArgs& a, hipStream_t s) {
   const int R = a.plan.n_rowgroups;

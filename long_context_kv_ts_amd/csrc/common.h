@@ -102,11 +102,12 @@ enum AttnPath { kPathValu = 0, kPathMfma = 1, kPathSmall = 2 };
 
 struct AttnPlan {
   int path;
+  int tile;             // keys per tile of the chosen kernel
   int rows_per_head;    // T * G
   int rows_per_group;   // rows of one workgroup
   int n_rowgroups;
-  int n_cache_tiles;    // ceil(L / kTile)
-  int n_draft_tiles;    // ceil(T / kTile)
+  int n_cache_tiles;    // ceil(L / tile)
+  int n_draft_tiles;    // ceil(T / tile)
   int n_virtual;        // cache tiles then draft tiles
   int tiles_per_split;
   int n_splits;
@@ -129,6 +130,11 @@ struct AttnArgs {
 };
 
 AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype, int num_splits);
+
+// Work decomposition of the matrix-core kernel (defined next to it).
+int mfma_rows_per_group();
+int mfma_groups_per_cu();
+int mfma_tile_keys();
 
 // Launchers (return the hipGetLastError() of the launch).
 hipError_t launch_attn_split_valu(const AttnArgs& a, ts_dtype dtype, hipStream_t s);

@@ -10,6 +10,7 @@ namespace ts {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBatch = 4;
 
 __global__ __launch_bounds__(kThreads) void gather_kernel(
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc, int64_t head_bytes,
@@ -26,7 +27,18 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
     return;
   }
   const uint4* s4 = reinterpret_cast<const uint4*>(src + (int64_t)g * head_bytes + (int64_t)c * chunk_bytes);
-  for (int64_t j = threadIdx.x; j < n16; j += kThreads) d4[j] = s4[j];
+  // full batches: all loads issued before the stores (a 64x128 bf16 chunk is
+  // exactly one batch), then a plain tail
+  const int n = (int)n16;
+  int j = threadIdx.x;
+  for (; j + (kBatch - 1) * kThreads < n; j += kBatch * kThreads) {
+    uint4 b[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) b[u] = s4[j + u * kThreads];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) d4[j + u * kThreads] = b[u];
+  }
+  for (; j < n; j += kThreads) d4[j] = s4[j];
 }
 
 }  // namespace

@@ -85,7 +85,8 @@ def test_partial_step_full(L):
 def test_topk_ties_and_edges():
     say("[topk] ties, k = n, k = 1")
     rng = np.random.default_rng(0)
-    for n, k in ((1600, 64), (1600, 1600), (1600, 1), (7, 3), (65536, 64), (5000, 4096)):
+    for n, k in ((1600, 64), (1600, 1600), (1600, 1), (7, 3), (65536, 64), (5000, 4096),
+                 (4096, 64), (4096, 65), (1024, 64), (1025, 33), (64, 64), (2048, 63)):
         s = np.round(rng.standard_normal((3, n)), 2).astype(np.float32)   # many exact ties
         s[1] = 0.5                                                        # all equal
         s[2, ::3] = -0.0
@@ -94,6 +95,8 @@ def test_topk_ties_and_edges():
         torch.cuda.synchronize()
         ref_idx, ref_val = oracle.topk_ref(s.astype(np.float64), k)
         np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx, err_msg=f"n={n} k={k}")
+        np.testing.assert_array_equal(val.cpu().numpy(), np.take_along_axis(s, ref_idx, 1),
+                                      err_msg=f"values n={n} k={k}")
 
 
 def test_topk_negative_and_infinite_scores():
