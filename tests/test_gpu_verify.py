@@ -56,12 +56,21 @@ def test_verify_full_size(name):
     check_attn(out, lse, ro, rl, c.dtype, name)
 
 
-@pytest.mark.parametrize("ns", [1, 3, 7, 40])
+@pytest.mark.parametrize("ns", [1, 3, 7, 40, 65])
 def test_split_count_invariance(ns):
     say(f"[splits] llama8b_20k L=4000 num_splits={ns}")
     c, (ro, rl) = workload_with_ref("llama8b_20k", L=4000)
     out, lse = run_verify(c, num_splits=ns)
     check_attn(out, lse, ro, rl, c.dtype, f"splits={ns}")
+
+
+def test_many_splits():
+    """More than 128 partials per row: the merge spreads one row over 16 waves."""
+    say("[splits] llama8b_20k L=12000 num_splits=200")
+    c, (ro, rl) = workload_with_ref("llama8b_20k", L=12000)
+    assert ops.num_splits(c.T, c.Hq, c.Hkv, c.D, c.L, torch.bfloat16, 200) > 128
+    out, lse = run_verify(c, num_splits=200)
+    check_attn(out, lse, ro, rl, c.dtype, "splits=200")
 
 
 @pytest.mark.parametrize("L", [0, 1, 63, 64, 65, 1000, 64 * 37 + 13])
