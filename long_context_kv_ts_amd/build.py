@@ -22,6 +22,11 @@ LIB = os.path.join(PKG, "libts.so")
 ARCH = "gfx950"
 SOURCES = ["api.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_small.hip", "attn_merge.hip",
            "importance.hip", "topk.hip", "gather.hip"]
+# Per-source extra flags. The matrix-core verify kernel never produces or
+# consumes NaN (masked scores are -inf, every exp2 argument is finite or -inf),
+# so it is built without NaN semantics: maxima of matrix-core results then need
+# no quieting instruction and fuse into v_max3_f32.
+EXTRA_FLAGS = {"attn_mfma.hip": ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:
@@ -40,7 +45,7 @@ def _flags():
 def _compile(src: str, hipcc: str) -> str:
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc, *_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc, *_flags(), *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -3,78 +3,82 @@
 // Work unit: (row group of 256 query rows, split, KV head). A row is a
 // (draft token t, query head h) pair of the KV head's group, row = t*G + h%G,
 // so the G grouped heads of one KV head share every K/V tile: 120 drafts x 4
-// heads = 480 rows per KV head for a LLaMA3.1-8B layer. Eight waves (two per
-// SIMD, so one wave's matrix products overlap the other's softmax), each owns
-// one block of 32 rows; all eight read the same K/V tile from LDS.
+// heads = 480 rows per KV head for a LLaMA3.1-8B layer. Eight waves, two per
+// SIMD, each own one block of 32 rows; all eight read the same K/V tile from
+// LDS.
 //
 // Scores are computed transposed, S^T = K . Q^T (A = K tile from LDS, B = Q
 // held in registers), so each lane's accumulator values all belong to ONE
-// query row (row = lane % 32, 16 keys of a 32-key block; the other 16 are in
-// lane ^ 32). Row max/sum are then per-lane with one cross-half exchange, and
-// the output O^T = V^T . P^T again gives every lane one row, so rescaling O is
-// a per-lane multiply. P^T reuses the score registers directly as the B
-// operand: the reduction order over keys is free, so the V^T operand is read
-// in the key order the scores arrive in -- k-slot 8*h + 4*r + e of a 16-key
-// chunk is key 16*hh + 8*r + 4*h + e.
+// query row (row = lane % 32, 16 keys of a 32-key tile; the other 16 are in
+// lane ^ 32). Row max/sum are then per-lane with one cross-half exchange
+// (v_permlane32_swap), and O^T = V^T . P^T again gives every lane one row, so
+// rescaling O is a per-lane multiply. P^T reuses the score registers directly
+// as the B operand: the reduction order over keys is free, so the V^T operand
+// is read in the key order the scores arrive in -- k-slot 8*h + 4*r + e of a
+// 16-key chunk is key 16*hh + 8*r + 4*h + e.
 //
-// K and V tiles (64 keys) stream from HBM straight into LDS with 16-byte
-// global_load_lds_dwordx4 (no staging registers) through a 3-stage ring, so
-// two tiles are in flight while one is computed; one barrier per tile. Both
-// tiles are stored row-major with 16-byte chunks XOR-swizzled per row (K:
-// chunk ^ row%16, V: chunk ^ 4*(row%4)): the K operand reads (16 rows, one
-// chunk) and the transposing ds_read_b64_tr_b16 reads of V^T (4 rows x 32
-// bytes per 16 lanes) are both free of bank conflicts. Rows past the valid
-// keys re-read the last valid row (finite data, masked scores).
+// Schedule. A single wave can neither issue vector-ALU work nor matrix
+// products at the SIMD's full rate, and the softmax of a 32x32 block costs
+// about as many issue cycles as its 16 products, so each wave is
+// software-pipelined over 32-key tiles: iteration j issues QK^T(j+1) and
+// PV(j-1) on the matrix cores interleaved with the softmax of tile j on the
+// vector ALUs, and the two waves of a SIMD fill each other's gaps. The K and
+// V^T operands of the next iteration are read from LDS right after the
+// products that last used their registers.
+//
+// Tiles stream from HBM straight into LDS with 16-byte global_load_lds_dwordx4
+// (no staging registers) through a 7-stage ring, three tiles ahead of the one
+// being published. K tiles of all stages come first, then the V tiles, so
+// every operand read is a per-lane base plus an immediate offset. Rows are
+// stored with 16-byte chunks XOR-swizzled per row (K: chunk ^ row%16, V:
+// chunk ^ 4*(row%4)), which keeps the K operand reads (32 rows, one chunk)
+// and the transposing ds_read_b64_tr_b16 reads of V^T free of bank conflicts.
+// The ring's depth lets the steady-state barrier skip the LDS drain: the stage
+// it hands to the next load was last read two iterations earlier, and those
+// reads were consumed by products before the barrier. Tiles past the last
+// full cache tile (a ragged tail, the drafts) are masked and form a suffix of
+// the split; they run unpipelined after it.
 //
 // Softmax in base 2 on fp32 scores (exact bf16 products, fp32 sums); scale is
 // applied in fp32 after the product. The running max is only raised when a new
 // score exceeds it by more than 2^8 ("lazy rescale"), which keeps every
 // probability <= 256 and makes rescaling of the accumulators rare. The
 // probabilities are rounded to bf16 for the PV product; the row sum uses the
-// unrounded values. Tiles past the cache are the draft K/V, masked by the
-// ancestor-or-self bitmask built in LDS from parent[].
+// unrounded values. Draft tiles are masked by the ancestor-or-self bitmask
+// built in LDS from parent[] (a 32-key tile is one word of a row's mask).
 #include "common.h"
+#include <type_traits>
 
 namespace ts {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-constexpr int kThreads = 512;
-constexpr int kWaves = 8;                    // 2 waves per SIMD: MFMA of one overlaps softmax of the other
-constexpr int kNB = 1;                       // 32-row blocks per wave
-constexpr int kRowsPerGroup = kWaves * kNB * 32;
-constexpr float kLazy = 8.0f;                // log2 headroom before a rescale
-
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define TS_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int kStages = 3;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kRowsPerGroup = kWaves * 32;
+constexpr int kKeys = 32;
+constexpr int kStages = 7;
+constexpr float kLazy = 8.0f;
 
 template <int D> struct Layout {
-  static constexpr int KS = D / 16;                  // k-steps of QK^T
-  static constexpr int DB = D / 32;                  // 32-wide column blocks of O
-  static constexpr int CH = D / 8;                   // 16-byte chunks per row
-  static constexpr int tileElems = kTile * D;        // one K or V tile, unpadded
-  static constexpr int loadsPerTensor = kTile * D * 2 / 1024;   // 1 KB per wave-wide load
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int CH = D / 8;
+  static constexpr int tileElems = kKeys * D;
+  static constexpr int loadsPerTensor = kKeys * D * 2 / 1024;
   static constexpr int loadsPerWave = 2 * loadsPerTensor / kWaves;
   static constexpr int rowsPerLoad = 1024 / (D * 2);
 };
 
-// Physical 16-byte chunk of logical chunk c in row r.
 template <int D> __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & (Layout<D>::CH - 1)); }
 template <int D> __device__ __forceinline__ int v_chunk(int r, int c) {
   return c ^ ((4 * (r & 3)) & (Layout<D>::CH - 1));
 }
 
-// One wave-wide 16-byte-per-lane load from global memory straight into LDS:
-// lane l reads base + voff (base uniform, in SGPRs) and its 16 bytes land at
-// lds + 16*l (lds uniform, passed in M0). Written as asm with no outputs so
-// that the compiler does not guard every later LDS read with a wait for ALL
-// outstanding loads; completion is instead awaited explicitly (vmcnt) before
-// the barrier that publishes a tile. Loads the compiler does not count only
-// make its own waits stricter.
 __device__ __forceinline__ void lds_dma16(const bf16_t* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
@@ -82,11 +86,6 @@ __device__ __forceinline__ void lds_dma16(const bf16_t* base, uint32_t voff, uin
                : "memory", "m0");
 }
 
-// Per-lane byte offset, within a tile, of the row/chunk that load n of wave w
-// fills. Load q = w*loadsPerWave + n covers 1 KB block m = q % loadsPerTensor
-// of K (waves in the first half) or of V (second half); lane l fills row
-// m*rowsPerLoad + l/CH, physical chunk l%CH, so it reads the logical chunk
-// that the row's swizzle maps there. Rows past nvalid re-read row nvalid-1.
 template <int D>
 __device__ __forceinline__ uint32_t dma_offset(int wave, int n, int lane, int nvalid) {
   using Ly = Layout<D>;
@@ -95,12 +94,10 @@ __device__ __forceinline__ uint32_t dma_offset(int wave, int n, int lane, int nv
   const int mblk = isv ? q - Ly::loadsPerTensor : q;
   const int r = mblk * Ly::rowsPerLoad + lane / Ly::CH;
   const int pc = lane % Ly::CH;
-  const int c = isv ? v_chunk<D>(r, pc) : k_chunk<D>(r, pc);   // xor: its own inverse
+  const int c = isv ? v_chunk<D>(r, pc) : k_chunk<D>(r, pc);
   return (uint32_t)((min(r, nvalid - 1) * D + c * 8) * 2);
 }
 
-// v_permlane32_swap(x, x) returns (x[l], x[l+32]) in lanes 0-31 and (x[l-32], x[l])
-// in lanes 32-63: combining the pair gives lane l and lane l^32 without LDS.
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -110,16 +107,18 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+template <bool B> using Flag = std::integral_constant<bool, B>;
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a) {
   using Ly = Layout<D>;
-  __shared__ __attribute__((aligned(1024))) bf16_t KVs[kStages][2][Ly::tileElems];
+  // K tiles of every stage, then V tiles: operand reads are a per-lane base
+  // plus an immediate (stage * tile bytes + row offsets), all below 64 KB
+  __shared__ __attribute__((aligned(1024))) bf16_t Ks[kStages][Ly::tileElems];
+  __shared__ __attribute__((aligned(1024))) bf16_t Vs[kStages][Ly::tileElems];
   __shared__ uint32_t anc[TS_MAX_DRAFT * (TS_MAX_DRAFT / 32)];
 
   const AttnPlan& pl = a.plan;
-  // XCD-aware order: workgroups i and i+8 run on the same XCD (L2). The row
-  // groups of one (split, head) unit -- which read the same K/V tiles -- are
-  // placed 8 ids apart.
   const int R = pl.n_rowgroups;
   const int id = blockIdx.x;
   const int unit = (id / (8 * R)) * 8 + (id % 8);
@@ -129,34 +128,43 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   const int split = unit % pl.n_splits, g = unit / pl.n_splits;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps wave math scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int G = a.G, T = a.T, Hq = a.Hq;
   const float c = a.scale_log2;
 
   const int vt0 = split * pl.tiles_per_split;
   const int vt1 = min(vt0 + pl.tiles_per_split, pl.n_virtual);
+  const int nb = vt1 - vt0;
 
-  // This wave streams K (first half of the waves) or V (second half).
   const bool wave_v = wave * Ly::loadsPerWave >= Ly::loadsPerTensor;
   const bf16_t* cache_base =
       static_cast<const bf16_t*>(wave_v ? a.vc : a.kc) + (int64_t)g * a.cache_stride * D;
   const bf16_t* draft_base = static_cast<const bf16_t*>(wave_v ? a.vd : a.kd) + (int64_t)g * T * D;
   uint32_t off_full[Ly::loadsPerWave];
 #pragma unroll
-  for (int n = 0; n < Ly::loadsPerWave; ++n) off_full[n] = dma_offset<D>(wave, n, lane, kTile);
-  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TS_LDS(void, &KVs[0][0][0])));
-  auto issue = [&](int vt, int stage) {
+  for (int n = 0; n < Ly::loadsPerWave; ++n) off_full[n] = dma_offset<D>(wave, n, lane, kKeys);
+  const uint32_t k_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TS_LDS(void, &Ks[0][0])));
+  const uint32_t v_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TS_LDS(void, &Vs[0][0])));
+  constexpr uint32_t kTileBytes = Ly::tileElems * 2;
+  const uint32_t my_lds = wave_v ? v_lds : k_lds;     // this wave's DMA destination tensor
+  auto tile_keys = [&](int vt, int& key0, int& nvalid) {
     const bool draft = vt >= pl.n_cache_tiles;
-    const int key0 = draft ? (vt - pl.n_cache_tiles) * kTile : vt * kTile;
-    const int nvalid = draft ? min(kTile, T - key0) : (int)min((int64_t)kTile, a.L - key0);
+    key0 = draft ? (vt - pl.n_cache_tiles) * kKeys : vt * kKeys;
+    nvalid = draft ? min(kKeys, T - key0) : (int)min((int64_t)kKeys, a.L - key0);
+    return draft;
+  };
+  auto issue = [&](int j) {          // tile j of this split -> stage j % kStages
+    int key0, nvalid;
+    const bool draft = tile_keys(vt0 + j, key0, nvalid);
     const bf16_t* base = (draft ? draft_base : cache_base) + (int64_t)key0 * D;
+    const uint32_t sb = my_lds + (uint32_t)(j % kStages) * kTileBytes;
     auto lds_of = [&](int n) {
       const int q = wave * Ly::loadsPerWave + n;
       const int mblk = q >= Ly::loadsPerTensor ? q - Ly::loadsPerTensor : q;
-      return lds_base + (uint32_t)(((stage * 2 + (wave_v ? 1 : 0)) * Ly::tileElems + mblk * 512) * 2);
+      return sb + (uint32_t)(mblk * 1024);
     };
-    if (__builtin_expect(nvalid == kTile, 1)) {
+    if (__builtin_expect(nvalid == kKeys, 1)) {
 #pragma unroll
       for (int n = 0; n < Ly::loadsPerWave; ++n) lds_dma16(base, off_full[n], lds_of(n));
     } else {
@@ -165,10 +173,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
         lds_dma16(base, dma_offset<D>(wave, n, lane, nvalid), lds_of(n));
     }
   };
-  // the first tile starts streaming before anything else
-  issue(vt0, 0);
+  // tiles [0, issued) of this split have been issued (uniform)
+  int issued = 0;
+  auto issue_upto = [&](int limit) {    // issue the next tile if it is <= limit
+    if (issued < nb && issued <= limit) {
+      issue(issued);
+      ++issued;
+    }
+  };
+  // wait until tile j has landed; younger tiles may stay in flight
+  auto wait_for = [&](int j) {
+    const int after = issued - 1 - j;
+    if (after >= 4) __builtin_amdgcn_s_waitcnt(0x0F70 | (4 * Ly::loadsPerWave));
+    else if (after == 3) __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * Ly::loadsPerWave));
+    else if (after == 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * Ly::loadsPerWave));
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | Ly::loadsPerWave);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
 
-  // ---- Q operand (B of S^T = K Q^T): lane holds row `col` of the block -----
+  // ---- Q operand: lane holds row `col` of this wave's 32-row block -----------
   bf16x8_t qf[Ly::KS];
   const int row = rg * kRowsPerGroup + wave * 32 + col;
   const bool row_ok = row < pl.rows_per_head;
@@ -177,23 +200,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   {
     const bf16_t* qp = static_cast<const bf16_t*>(a.q) + ((int64_t)row_t * Hq + row_h) * D;
 #pragma unroll
-    for (int ks = 0; ks < Ly::KS; ++ks) {
-      uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qp + ks * 16 + half * 8)
-                       : make_uint4(0u, 0u, 0u, 0u);
-      qf[ks] = __builtin_bit_cast(bf16x8_t, u);
-    }
-    // Wait for Q here, once: the compiler would otherwise place its wait at the
-    // first use inside the tile loop, where it would run every iteration and
-    // drain the prefetched tiles too.
+    for (int ks = 0; ks < Ly::KS; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + ks * 16 + half * 8));
 #pragma unroll
     for (int ks = 0; ks < Ly::KS; ++ks) asm volatile("" : : "v"(qf[ks]));
   }
-  if (vt0 + 1 < vt1) issue(vt0 + 1, 1);
-  // waves whose rows are all padding skip the products
-  const bool wave_active = rg * kRowsPerGroup + wave * 32 < pl.rows_per_head;
+  // tiles 0..4 start streaming (Q has already landed)
+  for (int j = 0; j < 5; ++j) issue_upto(j);
 
   const int words = (T + 31) >> 5;
   if (vt1 > pl.n_cache_tiles) build_ancestor_mask(a.parent, T, words, anc, tid, kThreads);
+
+  // per-lane LDS addresses of the operand reads in stage 0
+  uint32_t koff[Ly::KS], voff[Ly::DB];
+  {
+    const int vrow0 = 4 * half + ((lane & 15) >> 2);
+    const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int ks = 0; ks < Ly::KS; ++ks) koff[ks] = k_lds + (uint32_t)((col * D + k_chunk<D>(col, 2 * ks + half) * 8) * 2);
+#pragma unroll
+    for (int db = 0; db < Ly::DB; ++db) {
+      const int d = 32 * db + vdim;
+      voff[db] = v_lds + (uint32_t)((vrow0 * D + v_chunk<D>(vrow0, d >> 3) * 8 + (d & 7)) * 2);
+    }
+    // opaque to the compiler: the stage and row offsets then fold into the
+    // instructions' immediate field instead of being added per read
+#pragma unroll
+    for (int ks = 0; ks < Ly::KS; ++ks) asm volatile("" : "+v"(koff[ks]));
+#pragma unroll
+    for (int db = 0; db < Ly::DB; ++db) asm volatile("" : "+v"(voff[db]));
+  }
 
   f32x16_t O[Ly::DB];
 #pragma unroll
@@ -201,113 +237,213 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
 #pragma unroll
     for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
   float m = -INFINITY, lsum = 0.f;
+  f32x16_t S;
+  bf16x8_t P[2];
+  bf16x8_t Kf[Ly::KS];
+  bf16x8_t Vf[2][Ly::DB];
 
-  for (int vt = vt0; vt < vt1; ++vt) {
-    const int i = vt - vt0;
-    const int cur = i % kStages;
-    // this wave's loads of tile vt are the oldest outstanding; the next tile's
-    // (if issued) may stay in flight
-    if (vt + 1 < vt1) __builtin_amdgcn_s_waitcnt(0x0F70 | Ly::loadsPerWave);   // vmcnt(loadsPerWave)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                                   // vmcnt(0)
-    __syncthreads();   // tile vt visible to all; stage (i+2)%3 no longer read
-    if (vt + 2 < vt1) issue(vt + 2, (i + 2) % kStages);
-
-    if (wave_active) {
-      const bool draft = vt >= pl.n_cache_tiles;
-      const int key0 = draft ? (vt - pl.n_cache_tiles) * kTile : vt * kTile;
-      const int nvalid = draft ? min(kTile, T - key0) : (int)min((int64_t)kTile, a.L - key0);
-      const bf16_t* Kc = KVs[cur][0];
-      const bf16_t* Vc = KVs[cur][1];
-
-      // One 32-key block at a time: S^T block, mask, softmax update, PV.
+  auto read_k_at = [&](uint32_t so) {          // so: stage offset in bytes
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16_t S;
+    for (int ks = 0; ks < Ly::KS; ++ks)
+      Kf[ks] = *reinterpret_cast<__attribute__((address_space(3))) bf16x8_t*>(koff[ks] + so);
+  };
+  auto read_v_at = [&](uint32_t so) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) S[e] = 0.f;
-        const int kr = 32 * kb + col;                       // K row read by this lane
+    for (int db = 0; db < Ly::DB; ++db) {
+      __attribute__((address_space(3))) s16x4_t* vp =
+          reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(voff[db] + so);
 #pragma unroll
-        for (int ks = 0; ks < Ly::KS; ++ks) {
-          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-              Kc + kr * D + k_chunk<D>(kr, 2 * ks + half) * 8);
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S, 0, 0, 0);
-        }
-
-        // mask: ragged cache tail, draft ancestor bits
-        if (draft || nvalid < kTile) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3);
-            bool ok = key < nvalid;
-            if (draft) {
-              const int kk = key0 + key;
-              ok = ok && row_ok && ((anc[row_t * words + (kk >> 5)] >> (kk & 31)) & 1u);
-            }
-            if (!ok) S[e] = -INFINITY;
-          }
-        }
-
-        // online softmax (base 2, lazy rescale)
-        float mx = S[0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[e]);
-        mx = max_xor32(mx) * c;                                  // same for lanes l, l^32
-        const bool need = mx > m + kLazy;
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
-          // need implies mx finite; exp2(-inf) = 0 clears a row that had no key yet
-          const float alpha = need ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
-          m = need ? mx : m;
-          lsum *= alpha;
-#pragma unroll
-          for (int db = 0; db < Ly::DB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) O[db][e] *= alpha;
-        }
-        // finite stand-in for a row with no key yet: exp2(-inf) = 0 for masked scores
-        const float nmb = -fmaxf(m, -3.0e38f);
-        bf16x8_t P[2];
-        float ls = 0.f;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            // v_exp_f32 directly: results below 2^-126 of the running max flush to 0
-            const float p = __builtin_amdgcn_exp2f(fmaf(S[8 * hh + e], c, nmb));
-            ls += p;
-            P[hh][e] = static_cast<__bf16>(p);
-          }
-        }
-        lsum += ls;
-
-        // O^T += V^T P^T over this block's 32 keys (two 16-key chunks). The
-        // V^T operand of lane l: dim 32*db + l%32, keys 16*hh + 8*r + 4*h + e,
-        // fetched by two transposing reads (r = 0, 1) of 4 keys each.
-        const int vrow0 = 32 * kb + 4 * half + ((lane & 15) >> 2);
-        const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int db = 0; db < Ly::DB; ++db) {
-            s16x4_t part[2];
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-              const int vr = vrow0 + 16 * hh + 8 * r;
-              const int d = 32 * db + vdim;
-              const bf16_t* vp = Vc + vr * D + v_chunk<D>(vr, d >> 3) * 8 + (d & 7);
-              part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TS_LDS(s16x4_t, vp));
-            }
-            const s16x4_t lo = part[0], hi = part[1];
-            const bf16x8_t vf = __builtin_bit_cast(
-                bf16x8_t, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
-                                                                      hi[0], hi[1], hi[2], hi[3]});
-            O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[hh], O[db], 0, 0, 0);
-          }
-        }
+      for (int hh = 0; hh < 2; ++hh) {
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vp + (16 * hh) * D / 4);
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vp + (16 * hh + 8) * D / 4);
+        Vf[hh][db] = __builtin_bit_cast(
+            bf16x8_t, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                                  hi[0], hi[1], hi[2], hi[3]});
       }
     }
+  };
+  auto read_k = [&](int j) { read_k_at((uint32_t)(j % kStages) * kTileBytes); };
+  auto read_v = [&](int j) { read_v_at((uint32_t)(j % kStages) * kTileBytes); };
+  auto qk = [&](f32x16_t& Sx) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Sx[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < Ly::KS; ++ks) Sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Kf[ks], qf[ks], Sx, 0, 0, 0);
+  };
+  auto pv = [&](const bf16x8_t* Px) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int db = 0; db < Ly::DB; ++db)
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Vf[hh][db], Px[hh], O[db], 0, 0, 0);
+  };
+  // softmax of one 32x32 score block; returns whether O must be scaled by *alpha
+  auto softmax = [&](auto masked, f32x16_t Sx, bf16x8_t* Px, float* alpha, int j) -> bool {
+    if constexpr (decltype(masked)::value) {
+      int key0, nvalid;
+      const bool draft = tile_keys(vt0 + j, key0, nvalid);
+      uint32_t bits = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+      if (draft) bits &= row_ok ? anc[row_t * words + (key0 >> 5)] : 0u;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = 8 * (e >> 2) + 4 * half + (e & 3);
+        Sx[e] = ((bits >> key) & 1u) ? Sx[e] : -INFINITY;
+      }
+    }
+    float t2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float t = fmaxf(fmaxf(Sx[8 * i], Sx[8 * i + 1]), Sx[8 * i + 2]);
+      t = fmaxf(fmaxf(t, Sx[8 * i + 3]), Sx[8 * i + 4]);
+      t = fmaxf(fmaxf(t, Sx[8 * i + 5]), Sx[8 * i + 6]);
+      t2[i] = fmaxf(t, Sx[8 * i + 7]);
+    }
+    float mx = fmaxf(t2[0], t2[1]);
+    mx = max_xor32(mx) * c;
+    const bool need = mx > m + kLazy;
+    *alpha = need ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
+    m = need ? mx : m;
+    const float nmb = -fmaxf(m, -3.0e38f);
+    float pe[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(Sx[e], c, nmb));
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Px[hh][e] = static_cast<__bf16>(pe[8 * hh + e]);
+    float s4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s4[i] = (pe[4 * i] + pe[4 * i + 1]) + (pe[4 * i + 2] + pe[4 * i + 3]);
+    lsum = lsum * *alpha + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
+    return __builtin_amdgcn_ballot_w64(need) != 0;
+  };
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int db = 0; db < Ly::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) O[db][e] *= alpha;
+  };
+
+  // Tiles past the last full cache tile (ragged cache tail, drafts) are masked;
+  // they form a suffix of the split and run after the pipelined prefix.
+  const int full_tiles = (int)(a.L / kKeys);
+  const int nb_u = max(0, min(nb, full_tiles - vt0));
+
+  // Pipelined iteration j over unmasked tiles. On entry: S = S(j), Kf = K(j+1)
+  // (if j+1 < nb_u), Vf = V(j-1) and P = P(j-1) (if j >= 1).
+  auto iter = [&](auto prev, auto next, int j) {
+    constexpr bool kPrev = decltype(prev)::value, kNext = decltype(next)::value;
+    // publish tile j+2, start tile j+5
+    wait_for(j + 2);
+    __syncthreads();                    // every wave is past iteration j-1: tile j-1 is free
+    issue_upto(j + 5);
+    f32x16_t Sn;
+    if constexpr (kNext) qk(Sn);
+    if constexpr (kPrev) pv(P);
+    read_k(j + 2);                      // past the split's end this reads a stale stage: unused
+    read_v(j);
+    float al;
+    bf16x8_t Pn[2];
+    const bool rs = softmax(Flag<false>{}, S, Pn, &al, j);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 15; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);
+    asm volatile("" : : "v"(Pn[0]), "v"(Pn[1]), "v"(lsum), "v"(m));
+    if (rs) rescale(al);
+    P[0] = Pn[0]; P[1] = Pn[1];
+    if constexpr (kNext) S = Sn;
+  };
+
+  // Steady-state iteration j (1 <= j, j + 5 < nb_u), stage U = j % kStages known
+  // at compile time: tiles j+2..j+4 are in flight, tile j+5 is a full cache
+  // tile. The barrier needs no LDS drain: the stage it recycles (tile j-2) was
+  // last read two iterations ago and those reads were consumed by products.
+  const bf16_t* cache_next = cache_base + (int64_t)(vt0 + 5) * kKeys * D;   // tile 5 onwards
+  auto fast = [&](auto ust, int j) {
+    constexpr int U = decltype(ust)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * Ly::loadsPerWave));        // tile j+2 landed
+    asm volatile("s_barrier" : : : "memory");
+    {
+      const bf16_t* base = cache_next + (int64_t)j * kKeys * D;         // tile j+5
+      const uint32_t sb = my_lds + (uint32_t)(((U + 5) % kStages) * kTileBytes);
+#pragma unroll
+      for (int n = 0; n < Ly::loadsPerWave; ++n) {
+        const int q = wave * Ly::loadsPerWave + n;
+        const int mblk = q >= Ly::loadsPerTensor ? q - Ly::loadsPerTensor : q;
+        lds_dma16(base, off_full[n], sb + (uint32_t)(mblk * 1024));
+      }
+    }
+    f32x16_t Sn;
+    qk(Sn);
+    pv(P);
+    read_k_at((uint32_t)(((U + 2) % kStages) * kTileBytes));
+    read_v_at((uint32_t)(U * kTileBytes));
+    float al;
+    bf16x8_t Pn[2];
+    const bool rs = softmax(Flag<false>{}, S, Pn, &al, j);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    asm volatile("" : : "v"(Pn[0]), "v"(Pn[1]), "v"(lsum), "v"(m));
+    if (rs) rescale(al);
+    P[0] = Pn[0]; P[1] = Pn[1];
+    S = Sn;
+  };
+
+  if (nb_u > 0) {
+    // publish tiles 0 and 1 (tiles up to 4 are in flight)
+    wait_for(1);
+    __syncthreads();
+    read_k(0);
+    qk(S);
+    if (nb_u > 1) read_k(1);
+    if (nb_u == 1) iter(Flag<false>{}, Flag<false>{}, 0);
+    else {
+      iter(Flag<false>{}, Flag<true>{}, 0);
+      int j = 1;
+      for (; j + kStages <= nb_u - 5; j += kStages) {       // j % kStages == 1
+        fast(std::integral_constant<int, 1>{}, j);
+        fast(std::integral_constant<int, 2>{}, j + 1);
+        fast(std::integral_constant<int, 3>{}, j + 2);
+        fast(std::integral_constant<int, 4>{}, j + 3);
+        fast(std::integral_constant<int, 5>{}, j + 4);
+        fast(std::integral_constant<int, 6>{}, j + 5);
+        fast(std::integral_constant<int, 0>{}, j + 6);
+        issued = j + kStages + 5;
+      }
+      for (; j < nb_u - 1; ++j) iter(Flag<true>{}, Flag<true>{}, j);
+      iter(Flag<true>{}, Flag<false>{}, nb_u - 1);
+    }
+    pv(P);                              // PV of the last pipelined tile (Vf = V(nb_u - 1))
+  }
+  // masked suffix, one tile at a time
+  for (int j = nb_u; j < nb; ++j) {
+    wait_for(j);
+    __syncthreads();                    // tile j visible; every wave is past tile j - 1
+    issue_upto(j + 4);
+    read_k(j);
+    qk(S);
+    float al;
+    if (softmax(Flag<true>{}, S, P, &al, j)) rescale(al);
+    read_v(j);
+    pv(P);
   }
 
-  // ---- epilogue: normalise and write the split's partial ---------------------
+  // ---- epilogue ---------------------------------------------------------------
   const float ltot = sum_xor32(lsum);
   if (row_ok) {
     const int64_t orow = ((int64_t)split * T + row_t) * Hq + row_h;
@@ -329,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
 }  // namespace
 
 int mfma_rows_per_group() { return kRowsPerGroup; }
-int mfma_tile_keys() { return kTile; }
+int mfma_tile_keys() { return kKeys; }
 int mfma_groups_per_cu() { return 1; }
 
 hipError_t launch_attn_split_mfma(const AttnArgs& a, hipStream_t s) {
