@@ -28,6 +28,12 @@ Functions and the passages they follow (TokenSwift pages):
 * ``topk_ref``            the highest-scoring chunks up to the budget
                           (model card CLI example: retrieval budget 4096).
 * ``gather_ref``          the partial cache built from the chosen chunks.
+* ``accept_ref``          the longest valid draft path, one picked at random
+                          among equals (tool listing, "How it works": drafts
+                          are checked for an exact match with the target's
+                          tokens and one of the longest is chosen at random).
+* ``commit_ref``          the KV cache updated with the accepted drafts (same
+                          passage).
 
 Pinned by ``tests/test_oracle_*.py`` (brute force in 50-digit arithmetic,
 reductions to torch's scaled-dot-product attention, closed forms, a rank-count
@@ -38,6 +44,7 @@ pinned only by its own definition.
 """
 from .attention import ancestor_mask, verify_attn_ref, draft_attn_ref, widen
 from .partial_kv import importance_ref, topk_ref, gather_ref
+from .accept import accept_ref, commit_ref
 
 __all__ = ["ancestor_mask", "verify_attn_ref", "draft_attn_ref", "widen",
-           "importance_ref", "topk_ref", "gather_ref"]
+           "importance_ref", "topk_ref", "gather_ref", "accept_ref", "commit_ref"]
