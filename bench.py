@@ -222,9 +222,51 @@ def main():
         "roofline": roofline,
     }
 
+    res["accept_commit_us"] = time_accept_commit(vc, dev, args.steps)
+
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(vc, pc, args.cpu_heads)
     print(json.dumps(res), flush=True)
+
+
+def time_accept_commit(vc, dev, reps):
+    """Acceptance + KV commit after the step (its own figure, not part of the
+    step's value): the verify forest with the target agreeing along one
+    4-token tree path, 8 KV heads of bf16 K/V rows committed."""
+    import torch
+    from long_context_kv_ts_amd import ops
+    parent = vc.parent.astype(np.int32)
+    T = len(parent)
+    draft = (np.arange(T) + 1000).astype(np.int32)
+    target = np.full(T + 1, -5, np.int32)
+    leaf = max(t for t in range(T) if t < 40 and not (parent == t).any())
+    path = []
+    a = leaf
+    while a >= 0:
+        path.append(a)
+        a = int(parent[a])
+    path = path[::-1]
+    target[0] = draft[path[0]]
+    for i in range(1, len(path)):
+        target[path[i - 1] + 1] = draft[path[i]]
+    L = 4096
+    kc = torch.zeros((vc.Hkv, L + T, vc.D), dtype=torch.bfloat16, device=dev)
+    vcc = torch.zeros_like(kc)
+    kd = torch.ones((vc.Hkv, T, vc.D), dtype=torch.bfloat16, device=dev)
+    vd = torch.ones_like(kd)
+    pt, dt, tt = (torch.from_numpy(x).to(dev) for x in (parent, draft, target))
+    n, pth, bonus = ops.accept_commit(pt, dt, tt, 7, kc, vcc, L, kd, vd)
+    for _ in range(3):
+        ops.accept_commit(pt, dt, tt, 7, kc, vcc, L, kd, vd, n_accepted=n, path=pth, bonus=bonus)
+    torch.cuda.synchronize()
+    assert int(n.item()) == len(path)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ops.accept_commit(pt, dt, tt, 7, kc, vcc, L, kd, vd, n_accepted=n, path=pth, bonus=bonus)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / reps, 2)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_split_102400_hbm_traffic.txt")

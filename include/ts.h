@@ -189,6 +189,37 @@ ts_status ts_partial_draft_attn(const void* q, const void* k_part, const void* v
                                 ts_dtype dtype, int num_splits,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Acceptance and KV-cache commit (tool listing, "How it works": the drafts are
+ * checked for an exact match with the target model's tokens, one of the
+ * longest valid drafts is chosen at random, and the KV cache is updated).
+ *
+ *   parent      int32 [T] on the device, the draft forest of the verify call
+ *               (entries outside [-1, t) count as roots)
+ *   draft_tok   int32 [T] the drafts' tokens
+ *   target_tok  int32 [T+1]: [0] the target's token for the position after
+ *               the committed context, [t+1] its token for the position after
+ *               draft t (from the verify pass at row t)
+ *   rand_u32    a uniform random number drawn by the caller
+ *   A root is valid when draft_tok[root] == target_tok[0]; a node a with
+ *   parent p when its parent is valid and draft_tok[a] == target_tok[p+1].
+ *   Among the valid nodes of greatest depth, in index order, number
+ *   rand_u32 % count is chosen; n = its depth + 1 (0 if no root is valid).
+ *   Written (device, int32): *n_accepted = n; path[0..n) = the chosen root
+ *   path root first, path[n..T) = -1; *bonus = target_tok[last + 1]
+ *   (target_tok[0] when n = 0).
+ *   Commit: k_cache[g][L+i][:] = k_draft[g][path[i]][:] for i < n, every KV
+ *   head g, and the same for V (bit-exact copies).
+ *   k_cache, v_cache [Hkv][cache_stride][D]; k_draft, v_draft [Hkv][T][D].
+ * Requires L + T <= cache_stride (room for the longest possible path).
+ * Supported: T in [1, 256], D in {64, 128}. No workspace.
+ * ---------------------------------------------------------------------- */
+ts_status ts_accept_commit(const int32_t* parent, const int32_t* draft_tok, const int32_t* target_tok,
+                           uint32_t rand_u32, int T, void* k_cache, void* v_cache, int64_t cache_stride,
+                           int64_t L, const void* k_draft, const void* v_draft, int Hkv, int D,
+                           ts_dtype dtype, int32_t* n_accepted, int32_t* path, int32_t* bonus,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -278,4 +278,30 @@ ts_status ts_kv_gather(const void* k_cache, const void* v_cache, int64_t cache_s
                                 k_part, v_part, elem_size(dtype), stream), fn);
 }
 
+ts_status ts_accept_commit(const int32_t* parent, const int32_t* draft_tok, const int32_t* target_tok,
+                           uint32_t rand_u32, int T, void* k_cache, void* v_cache, int64_t cache_stride,
+                           int64_t L, const void* k_draft, const void* v_draft, int Hkv, int D,
+                           ts_dtype dtype, int32_t* n_accepted, int32_t* path, int32_t* bonus,
+                           hipStream_t stream) {
+  const char* fn = "ts_accept_commit";
+  if (dtype != TS_F32 && dtype != TS_BF16) return fail(TS_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (!parent || !draft_tok || !target_tok || !k_cache || !v_cache || !k_draft || !v_draft ||
+      !n_accepted || !path || !bonus)
+    return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_draft) || !aligned16(v_draft) ||
+      ((uintptr_t)parent & 3u) || ((uintptr_t)draft_tok & 3u) || ((uintptr_t)target_tok & 3u) ||
+      ((uintptr_t)n_accepted & 3u) || ((uintptr_t)path & 3u) || ((uintptr_t)bonus & 3u))
+    return fail(TS_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned (int32 arrays 4-byte)", fn);
+  if (T < 1 || T > TS_MAX_DRAFT) return fail(TS_ERR_INVALID_ARG, "%s: T=%d outside [1, %d]", fn, T, TS_MAX_DRAFT);
+  if (Hkv < 1 || Hkv > 65535) return fail(TS_ERR_INVALID_ARG, "%s: Hkv=%d", fn, Hkv);
+  if (D != 64 && D != 128) return fail(TS_ERR_UNSUPPORTED, "%s: D=%d (64 or 128)", fn, D);
+  if (L < 0) return fail(TS_ERR_INVALID_ARG, "%s: L=%lld < 0", fn, (long long)L);
+  if (cache_stride < L + T)
+    return fail(TS_ERR_INVALID_ARG, "%s: cache_stride=%lld leaves no room for %d rows after L=%lld", fn,
+                (long long)cache_stride, T, (long long)L);
+  return from_hip(launch_accept_commit(parent, draft_tok, target_tok, rand_u32, T, k_cache, v_cache,
+                                       cache_stride, L, k_draft, v_draft, Hkv, D, elem_size(dtype),
+                                       n_accepted, path, bonus, stream), fn);
+}
+
 }  // extern "C"

@@ -150,5 +150,10 @@ hipError_t launch_topk(const float* scores, int Hkv, int n, int k, int32_t* idx,
 hipError_t launch_gather(const void* kc, const void* vc, int64_t stride, const int32_t* idx,
                          int Hkv, int k, int chunk, int D, int64_t L, void* kp, void* vp,
                          int elem_bytes, hipStream_t s);
+hipError_t launch_accept_commit(const int32_t* parent, const int32_t* draft_tok,
+                                const int32_t* target_tok, uint32_t rand_u32, int T, void* kc,
+                                void* vc, int64_t stride, int64_t L, const void* kd, const void* vd,
+                                int Hkv, int D, int elem_bytes, int32_t* n_out, int32_t* path_out,
+                                int32_t* bonus_out, hipStream_t s);
 
 }  // namespace ts

@@ -48,6 +48,9 @@ SIGNATURES = {
     "ts_kv_topk_select": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "ts_kv_gather": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int, _c_int, _c_int,
                               _c_i64, _c_void_p, _c_void_p, _c_int, _c_void_p]),
+    "ts_accept_commit": (_c_int, [_c_void_p, _c_void_p, _c_void_p, ctypes.c_uint32, _c_int, _c_void_p,
+                                  _c_void_p, _c_i64, _c_i64, _c_void_p, _c_void_p, _c_int, _c_int,
+                                  _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "ts_partial_draft_attn_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int]),
     "ts_partial_draft_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                        _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_i64,
@@ -297,6 +300,47 @@ def kv_gather(k_cache, v_cache, chunk_idx, chunk: int, *, k_part=None, v_part=No
                               Hkv, k, chunk, D, L, k_part.data_ptr(), v_part.data_ptr(),
                               _dtype_code(k_cache), _stream(dev)))
     return k_part, v_part
+
+
+def accept_commit(parent, draft_tok, target_tok, rand_u32: int, k_cache, v_cache, L: int,
+                  k_draft, v_draft, *, n_accepted=None, path=None, bonus=None):
+    """ts_accept_commit -> (n_accepted [1], path [T], bonus [1]) int32 device tensors.
+
+    k_cache, v_cache: [Hkv][capacity][D] (rows L .. L+n-1 are written in place;
+    capacity >= L + T); k_draft, v_draft: [Hkv][T][D]; parent, draft_tok [T],
+    target_tok [T+1] int32 on the device."""
+    dev = k_cache.device
+    for n, t, dims in (("parent", parent, 1), ("draft_tok", draft_tok, 1), ("target_tok", target_tok, 1)):
+        _need(t, n, dims, torch.int32, dev)
+        _contig(t, n)
+    _need(k_cache, "k_cache", 3)
+    _need(v_cache, "v_cache", 3, k_cache.dtype, dev)
+    for n, t in (("k_draft", k_draft), ("v_draft", v_draft)):
+        _need(t, n, 3, k_cache.dtype, dev)
+        _contig(t, n)
+    T = parent.shape[0]
+    if draft_tok.shape[0] != T or target_tok.shape[0] != T + 1:
+        raise ValueError("draft_tok must have T entries and target_tok T+1")
+    Hkv, cap, D = k_cache.shape
+    if k_draft.shape != (Hkv, T, D) or v_draft.shape != (Hkv, T, D):
+        raise ValueError("k_draft / v_draft must be [Hkv][T][D]")
+    stride = _cache_stride(k_cache, "k_cache")
+    if _cache_stride(v_cache, "v_cache") != stride:
+        raise ValueError("k_cache and v_cache must share the row stride")
+    if cap < L + T:
+        raise ValueError(f"cache capacity {cap} < L + T = {L + T}")
+    if n_accepted is None:
+        n_accepted = torch.empty(1, dtype=torch.int32, device=dev)
+    if path is None:
+        path = torch.empty(T, dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib().ts_accept_commit(parent.data_ptr(), draft_tok.data_ptr(), target_tok.data_ptr(),
+                                  int(rand_u32) & 0xFFFFFFFF, T, k_cache.data_ptr(), v_cache.data_ptr(),
+                                  stride, int(L), k_draft.data_ptr(), v_draft.data_ptr(), Hkv, D,
+                                  _dtype_code(k_cache), n_accepted.data_ptr(), path.data_ptr(),
+                                  bonus.data_ptr(), _stream(dev)))
+    return n_accepted, path, bonus
 
 
 def partial_draft_attn(q, k_part, v_part, k_new, v_new, *, scale=None, out=None, lse=None,

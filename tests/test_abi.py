@@ -160,6 +160,30 @@ def test_gather_rejects():
     assert "ts_kv_gather" in _err()
 
 
+def test_accept_commit_rejects():
+    lib = ops.lib()
+    ok = (P, P, P, 7, 120, P, P, 102400 + 120, 102400, P, P, 8, 128, B, P, P, P, None)
+
+    def call(**kw):
+        names = ["parent", "draft", "target", "rand", "T", "kc", "vc", "stride", "L", "kd", "vd",
+                 "Hkv", "D", "dtype", "n", "path", "bonus", "stream"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return lib.ts_accept_commit(*[args[n] for n in names])
+
+    assert call(T=0) == ops.TS_ERR_INVALID_ARG
+    assert call(T=257) == ops.TS_ERR_INVALID_ARG
+    assert call(D=96) == ops.TS_ERR_UNSUPPORTED
+    assert call(stride=102400 + 119) == ops.TS_ERR_INVALID_ARG      # no room for T rows after L
+    assert call(L=-1) == ops.TS_ERR_INVALID_ARG
+    assert call(target=None) == ops.TS_ERR_INVALID_ARG
+    assert call(kc=MIS) == ops.TS_ERR_INVALID_ARG
+    assert call(path=P + 2) == ops.TS_ERR_INVALID_ARG
+    assert call(dtype=9) == ops.TS_ERR_INVALID_ARG
+    assert call(Hkv=0) == ops.TS_ERR_INVALID_ARG
+    assert "ts_accept_commit" in _err()
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "_lib", None)
     monkeypatch.setattr(ops, "_LIB_PATH", str(tmp_path / "missing.so"))

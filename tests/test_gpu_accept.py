@@ -1,0 +1,133 @@
+"""GPU parity of ts_accept_commit (acceptance of the verified drafts and the
+KV-cache commit) against the oracle: bit-exact on n, the path, the bonus token
+and every cache row, including the rows that must stay untouched."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, say, to_dev
+from long_context_kv_ts_amd import inputs, ops
+from oracle import accept_ref, commit_ref
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "accept_example.json")
+
+
+def _bits(shape, rng, dtype):
+    if dtype == "bf16":
+        return rng.integers(0, 0x7F00, size=shape).astype(np.uint16)     # finite bf16 patterns
+    return rng.standard_normal(shape).astype(np.float32)
+
+
+def run_case(parent, draft, target, rand, *, Hkv=2, D=128, L=37, extra=5, dtype="bf16", seed=0,
+             label=""):
+    parent = np.asarray(parent, np.int32)
+    draft = np.asarray(draft, np.int32)
+    target = np.asarray(target, np.int32)
+    T = len(parent)
+    rng = np.random.default_rng(seed)
+    cap = L + T + extra
+    kc, vc = _bits((Hkv, cap, D), rng, dtype), _bits((Hkv, cap, D), rng, dtype)
+    kd, vd = _bits((Hkv, T, D), rng, dtype), _bits((Hkv, T, D), rng, dtype)
+    dkc, dvc = to_dev(kc, dtype), to_dev(vc, dtype)
+    n, path, bonus = ops.accept_commit(to_dev(parent, "i32"), to_dev(draft, "i32"), to_dev(target, "i32"),
+                                       rand, dkc, dvc, L, to_dev(kd, dtype), to_dev(vd, dtype))
+    torch.cuda.synchronize()
+    rn, rpath, rbonus = accept_ref(parent, draft, target, rand)
+    gn, gpath, gbonus = int(n.item()), path.cpu().numpy(), int(bonus.item())
+    say(f"  {label}: n={gn} path={gpath[:gn].tolist()} bonus={gbonus}")
+    assert gn == rn, f"{label}: n {gn} != {rn}"
+    assert gpath[:gn].tolist() == rpath and (gpath[gn:] == -1).all(), f"{label}: path"
+    assert gbonus == rbonus, f"{label}: bonus"
+    rk, rv = commit_ref(kc, vc, L, kd, vd, rpath)
+    view = (lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)) if dtype == "bf16" else \
+        (lambda t: t.cpu().numpy())
+    assert np.array_equal(view(dkc), rk) and np.array_equal(view(dvc), rv), f"{label}: cache rows"
+    return gn
+
+
+def test_hand_worked_example():
+    say("[accept] tests/golden/accept_example.json")
+    ex = json.load(open(GOLDEN))
+    for i, case in enumerate(ex["cases"]):
+        tgt = list(ex["target_tok"])
+        if "target0" in case:
+            tgt[0] = case["target0"]
+        n = run_case(ex["parent"], ex["draft_tok"], tgt, case["rand"], label=f"case {i}", seed=i)
+        assert n == case["n"]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_forests(seed):
+    """Small vocabularies make many paths valid and many ties."""
+    rng = np.random.default_rng(100 + seed)
+    T = int(rng.integers(1, 257))
+    parent = np.array([int(rng.integers(-1, t)) if t else -1 for t in range(T)], np.int32)
+    vocab = int(rng.integers(2, 4))
+    draft = rng.integers(0, vocab, T).astype(np.int32)
+    target = rng.integers(0, vocab, T + 1).astype(np.int32)
+    for rand in (0, int(rng.integers(0, 2**32))):
+        run_case(parent, draft, target, rand, D=(64, 128)[seed % 2], dtype=("bf16", "f32")[seed % 3 == 0],
+                 seed=seed, label=f"T={T} seed={seed} rand={rand}")
+
+
+def test_verify_forest_with_planted_paths():
+    """The [1,3,3,3] tree + 20 four-token chains of the verify workload; the
+    target agrees with the drafts along one tree path and two chains, so the
+    longest paths tie and the random number picks between them."""
+    c = inputs.make_verify("acc", dtype="f32", Hq=1, Hkv=1, D=64, L=0, seed=2, with_chains=True)
+    parent = c.parent.astype(np.int32)
+    T = len(parent)
+    draft = (np.arange(T) + 1000).astype(np.int32)
+    target = np.full(T + 1, -5, np.int32)
+
+    def root_path(t):
+        p = []
+        while t >= 0:
+            p.append(t)
+            t = int(parent[t])
+        return p[::-1]
+
+    leaves = [t for t in range(T) if not (parent == t).any()]
+    tree_leaf = max(t for t in leaves if len(root_path(t)) == 4 and root_path(t)[0] == 0)
+    chain_leaves = [t for t in leaves if root_path(t)[0] != 0][:2]
+    planted = [tree_leaf] + chain_leaves
+    for leaf in planted:                              # the three roots carry the target's token
+        draft[root_path(leaf)[0]] = 7
+    target[0] = 7
+    for leaf in planted:
+        p = root_path(leaf)
+        for i in range(1, len(p)):
+            target[p[i - 1] + 1] = draft[p[i]]
+        target[leaf + 1] = 900 + leaf
+    ns = {run_case(parent, draft, target, r, Hkv=8, L=1000, label=f"planted rand={r}") for r in range(3)}
+    assert ns == {4}
+
+
+def test_single_draft_and_full_chain():
+    say("[accept] T=1 and a 256-token chain")
+    run_case([-1], [5], [5, 6], 0, label="T=1 match")
+    run_case([-1], [5], [4, 6], 0, label="T=1 no match")
+    # parent entries outside [-1, t) count as roots, as in the attention mask
+    run_case([-1, 5, -7, 1, 3, 0], [4, 4, 4, 9, 4, 9], [4, 9, 4, 4, 4, 4, 4], 1, label="bad parents")
+    T = 256
+    draft = np.arange(T, dtype=np.int32) * 3
+    target = np.concatenate([draft, [42]]).astype(np.int32)
+    assert run_case(np.arange(-1, T - 1), draft, target, 99, L=0, extra=0, label="chain 256") == T
+
+
+def test_full_size_cache():
+    """LLaMA3.1-8B layer: 8 KV heads, 102,400 cached tokens, bf16; the commit
+    writes only rows L..L+n-1 (the comparison covers the whole cache)."""
+    say("[accept] 102400-token cache")
+    c = inputs.make_verify("acc", dtype="f32", Hq=1, Hkv=1, D=64, L=0, seed=2, with_chains=True)
+    parent = c.parent.astype(np.int32)
+    T = len(parent)
+    rng = np.random.default_rng(5)
+    draft = rng.integers(0, 2, T).astype(np.int32)
+    target = rng.integers(0, 2, T + 1).astype(np.int32)
+    run_case(parent, draft, target, 3, Hkv=8, D=128, L=102400, extra=0, label="100K")
