@@ -34,6 +34,9 @@ Functions and the passages they follow (TokenSwift pages):
                           tokens and one of the longest is chosen at random).
 * ``commit_ref``          the KV cache updated with the accepted drafts (same
                           passage).
+* ``build_tree_ref``      the candidate tree from the per-position logits
+                          (tool listing, "How it works"; tree shapes from the
+                          summary page's ablation table).
 
 Pinned by ``tests/test_oracle_*.py`` (brute force in 50-digit arithmetic,
 reductions to torch's scaled-dot-product attention, closed forms, a rank-count
@@ -45,6 +48,8 @@ pinned only by its own definition.
 from .attention import ancestor_mask, verify_attn_ref, draft_attn_ref, widen
 from .partial_kv import importance_ref, topk_ref, gather_ref
 from .accept import accept_ref, commit_ref
+from .tree import build_tree_ref
 
 __all__ = ["ancestor_mask", "verify_attn_ref", "draft_attn_ref", "widen",
-           "importance_ref", "topk_ref", "gather_ref", "accept_ref", "commit_ref"]
+           "importance_ref", "topk_ref", "gather_ref", "accept_ref", "commit_ref",
+           "build_tree_ref"]
