@@ -223,6 +223,7 @@ def main():
     }
 
     res["accept_commit_us"] = time_accept_commit(vc, dev, args.steps)
+    res["draft_tree_us"] = time_draft_tree(dev, args.steps)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(vc, pc, args.cpu_heads)
@@ -264,6 +265,27 @@ def time_accept_commit(vc, dev, reps):
     e0.record()
     for _ in range(reps):
         ops.accept_commit(pt, dt, tt, 7, kc, vcc, L, kd, vd, n_accepted=n, path=pth, bonus=bonus)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+
+
+def time_draft_tree(dev, reps):
+    """Candidate tree [1,3,3,3] from 4 positions' fp32 logits over the
+    LLaMA3.1 vocabulary of 128,256 tokens (its own figure, not part of value)."""
+    import torch
+    from long_context_kv_ts_amd import ops
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    logits = torch.randn((4, 128256), device=dev, generator=g)
+    parent, tok, cand = ops.build_draft_tree(logits, [1, 3, 3, 3])
+    for _ in range(3):
+        ops.build_draft_tree(logits, [1, 3, 3, 3], parent=parent, draft_tok=tok, cand=cand)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ops.build_draft_tree(logits, [1, 3, 3, 3], parent=parent, draft_tok=tok, cand=cand)
     e1.record()
     torch.cuda.synchronize()
     return round(e0.elapsed_time(e1) * 1e3 / reps, 2)

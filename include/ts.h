@@ -190,6 +190,33 @@ ts_status ts_partial_draft_attn(const void* q, const void* k_part, const void* v
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Candidate tree of draft tokens from the per-position logits (tool listing,
+ * "How it works": one pass yields logits for the next positions and the
+ * candidates are organised as a tree; the summary page's ablation table uses
+ * the shapes [1,3,3,3], [3,3,3,3] and [1,9,9,9]).
+ *
+ *   logits  [P][V] in `dtype` (TS_F32 or TS_BF16), position d in row d; NaN
+ *           not allowed
+ *   shape   HOST array of `depth` ints: k_d candidates at depth d
+ *   Depth d's candidates are the k_d highest logits of row d, equal logits
+ *   ranked by lower token id. The tree is the product of the depths: each
+ *   node of depth d has k_{d+1} children. Nodes are numbered breadth-first,
+ *   inside a depth in lexicographic order of the candidate ranks along the
+ *   root path, so parent[t] < t and the result feeds ts_tree_verify_attn
+ *   (which takes T <= 256) directly.
+ *   Written (device, int32): parent [T] (-1 for depth-0 nodes), draft_tok [T]
+ *   (the node's candidate token), cand [depth][16] if not NULL (ranked
+ *   candidates, -1 past k_d).
+ * T = ts_draft_tree_nodes(shape, depth) = sum_d k_0*..*k_d.
+ * Supported: depth in [1, 8], k_d in [1, 16], k_d <= V, T <= 1024, P >= depth.
+ * ---------------------------------------------------------------------- */
+int ts_draft_tree_nodes(const int32_t* shape, int depth);   /* -1 if unsupported */
+
+ts_status ts_build_draft_tree(const void* logits, int P, int V, const int32_t* shape, int depth,
+                              int32_t* parent, int32_t* draft_tok, int32_t* cand, ts_dtype dtype,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Acceptance and KV-cache commit (tool listing, "How it works": the drafts are
  * checked for an exact match with the target model's tokens, one of the
  * longest valid drafts is chosen at random, and the KV cache is updated).

@@ -278,6 +278,56 @@ ts_status ts_kv_gather(const void* k_cache, const void* v_cache, int64_t cache_s
                                 k_part, v_part, elem_size(dtype), stream), fn);
 }
 
+// Node count of a tree shape, or -1 (with ts_last_error) if the shape is not supported.
+static int tree_shape(const char* fn, const int32_t* shape, int depth, TreeShape* out) {
+  if (!shape) { fail(TS_ERR_INVALID_ARG, "%s: shape is null", fn); return -1; }
+  if (depth < 1 || depth > kTreeMaxDepth) {
+    fail(TS_ERR_UNSUPPORTED, "%s: depth=%d outside [1, %d]", fn, depth, kTreeMaxDepth);
+    return -1;
+  }
+  TreeShape sh{};
+  int64_t total = 0, n = 1;
+  for (int d = 0; d < depth; ++d) {
+    if (shape[d] < 1 || shape[d] > kTreeMaxK) {
+      fail(TS_ERR_UNSUPPORTED, "%s: shape[%d]=%d outside [1, %d]", fn, d, shape[d], kTreeMaxK);
+      return -1;
+    }
+    n *= shape[d];
+    if (total + n > kTreeMaxNodes) {
+      fail(TS_ERR_UNSUPPORTED, "%s: more than %d nodes", fn, kTreeMaxNodes);
+      return -1;
+    }
+    sh.k[d] = shape[d];
+    sh.n[d] = (int)n;
+    sh.off[d] = (int)total;
+    total += n;
+  }
+  if (out) *out = sh;
+  return (int)total;
+}
+
+int ts_draft_tree_nodes(const int32_t* shape, int depth) {
+  return tree_shape("ts_draft_tree_nodes", shape, depth, nullptr);
+}
+
+ts_status ts_build_draft_tree(const void* logits, int P, int V, const int32_t* shape, int depth,
+                              int32_t* parent, int32_t* draft_tok, int32_t* cand, ts_dtype dtype,
+                              hipStream_t stream) {
+  const char* fn = "ts_build_draft_tree";
+  if (dtype != TS_F32 && dtype != TS_BF16) return fail(TS_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (!logits || !parent || !draft_tok) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (((uintptr_t)logits % elem_size(dtype)) || ((uintptr_t)parent & 3u) || ((uintptr_t)draft_tok & 3u) ||
+      ((uintptr_t)cand & 3u))
+    return fail(TS_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  TreeShape sh;
+  if (tree_shape(fn, shape, depth, &sh) < 0) return TS_ERR_UNSUPPORTED;
+  if (P < depth) return fail(TS_ERR_INVALID_ARG, "%s: P=%d positions for depth %d", fn, P, depth);
+  if (V < 1) return fail(TS_ERR_INVALID_ARG, "%s: V=%d", fn, V);
+  for (int d = 0; d < depth; ++d)
+    if (shape[d] > V) return fail(TS_ERR_INVALID_ARG, "%s: shape[%d]=%d > V=%d", fn, d, shape[d], V);
+  return from_hip(launch_build_tree(logits, V, sh, depth, parent, draft_tok, cand, dtype, stream), fn);
+}
+
 ts_status ts_accept_commit(const int32_t* parent, const int32_t* draft_tok, const int32_t* target_tok,
                            uint32_t rand_u32, int T, void* k_cache, void* v_cache, int64_t cache_stride,
                            int64_t L, const void* k_draft, const void* v_draft, int Hkv, int D,

@@ -48,6 +48,9 @@ SIGNATURES = {
     "ts_kv_topk_select": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "ts_kv_gather": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int, _c_int, _c_int,
                               _c_i64, _c_void_p, _c_void_p, _c_int, _c_void_p]),
+    "ts_draft_tree_nodes": (_c_int, [_c_void_p, _c_int]),
+    "ts_build_draft_tree": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                     _c_void_p, _c_int, _c_void_p]),
     "ts_accept_commit": (_c_int, [_c_void_p, _c_void_p, _c_void_p, ctypes.c_uint32, _c_int, _c_void_p,
                                   _c_void_p, _c_i64, _c_i64, _c_void_p, _c_void_p, _c_int, _c_int,
                                   _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
@@ -300,6 +303,37 @@ def kv_gather(k_cache, v_cache, chunk_idx, chunk: int, *, k_part=None, v_part=No
                               Hkv, k, chunk, D, L, k_part.data_ptr(), v_part.data_ptr(),
                               _dtype_code(k_cache), _stream(dev)))
     return k_part, v_part
+
+
+def draft_tree_nodes(shape) -> int:
+    """ts_draft_tree_nodes: node count of a tree shape [k_0, k_1, ...]."""
+    arr = (ctypes.c_int32 * len(shape))(*[int(k) for k in shape])
+    n = lib().ts_draft_tree_nodes(ctypes.cast(arr, ctypes.c_void_p), len(shape))
+    if n < 0:
+        raise TsError(TS_ERR_UNSUPPORTED, lib().ts_last_error().decode())
+    return int(n)
+
+
+def build_draft_tree(logits, shape, *, parent=None, draft_tok=None, cand=None):
+    """ts_build_draft_tree -> (parent [T], draft_tok [T], cand [depth][16]) int32 device tensors.
+
+    logits: [P][V] float32 or bfloat16 on the device; shape: host list of k_d."""
+    _need(logits, "logits", 2)
+    _contig(logits, "logits")
+    dev = logits.device
+    P, V = logits.shape
+    T = draft_tree_nodes(shape)
+    if parent is None:
+        parent = torch.empty(T, dtype=torch.int32, device=dev)
+    if draft_tok is None:
+        draft_tok = torch.empty(T, dtype=torch.int32, device=dev)
+    if cand is None:
+        cand = torch.empty((len(shape), 16), dtype=torch.int32, device=dev)
+    arr = (ctypes.c_int32 * len(shape))(*[int(k) for k in shape])
+    _check(lib().ts_build_draft_tree(logits.data_ptr(), P, V, ctypes.cast(arr, ctypes.c_void_p), len(shape),
+                                     parent.data_ptr(), draft_tok.data_ptr(), cand.data_ptr(),
+                                     _dtype_code(logits), _stream(dev)))
+    return parent, draft_tok, cand
 
 
 def accept_commit(parent, draft_tok, target_tok, rand_u32: int, k_cache, v_cache, L: int,

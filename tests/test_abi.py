@@ -184,6 +184,28 @@ def test_accept_commit_rejects():
     assert "ts_accept_commit" in _err()
 
 
+def test_draft_tree_rejects():
+    import ctypes
+    lib = ops.lib()
+    shape = (ctypes.c_int32 * 4)(1, 3, 3, 3)
+    sp = ctypes.cast(shape, ctypes.c_void_p)
+    assert lib.ts_draft_tree_nodes(sp, 4) == 40
+    assert lib.ts_draft_tree_nodes(sp, 0) == -1
+    assert lib.ts_draft_tree_nodes(None, 4) == -1
+    big = (ctypes.c_int32 * 4)(16, 16, 16, 16)
+    assert lib.ts_draft_tree_nodes(ctypes.cast(big, ctypes.c_void_p), 4) == -1    # > 1024 nodes
+    nine = (ctypes.c_int32 * 4)(1, 9, 9, 9)
+    assert lib.ts_draft_tree_nodes(ctypes.cast(nine, ctypes.c_void_p), 4) == 820
+    assert lib.ts_build_draft_tree(P, 3, 128256, sp, 4, P, P, None, F, None) == ops.TS_ERR_INVALID_ARG   # P < depth
+    assert lib.ts_build_draft_tree(P, 4, 2, sp, 4, P, P, None, F, None) == ops.TS_ERR_INVALID_ARG        # k > V
+    assert lib.ts_build_draft_tree(None, 4, 128256, sp, 4, P, P, None, F, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_build_draft_tree(P, 4, 128256, sp, 4, P + 2, P, None, F, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_build_draft_tree(P, 4, 128256, sp, 4, P, P, None, 9, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_build_draft_tree(P, 4, 128256, ctypes.cast(big, ctypes.c_void_p), 4, P, P, None, F,
+                                   None) == ops.TS_ERR_UNSUPPORTED
+    assert "ts_build_draft_tree" in _err()
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "_lib", None)
     monkeypatch.setattr(ops, "_LIB_PATH", str(tmp_path / "missing.so"))

@@ -1,0 +1,79 @@
+"""GPU parity of ts_build_draft_tree (candidate tree from per-position logits)
+against the oracle: bit-exact parent[], draft tokens and ranked candidates."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import say, to_dev
+from long_context_kv_ts_amd import inputs, ops
+from oracle import build_tree_ref, widen
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tree_example.json")
+VOCAB = 128256            # LLaMA3.1 vocabulary
+
+
+def check(logits_host, shape, dtype, label):
+    lg = to_dev(logits_host, dtype)
+    parent, tok, cand = ops.build_draft_tree(lg, shape)
+    torch.cuda.synchronize()
+    ref_logits = widen(logits_host, dtype)
+    rp, rt, rc = build_tree_ref(ref_logits, shape)
+    gp, gt, gc = parent.cpu().numpy(), tok.cpu().numpy(), cand.cpu().numpy()
+    say(f"  {label}: T={len(rp)} cand[0]={gc[0, :shape[0]].tolist()}")
+    assert np.array_equal(gp, rp), f"{label}: parent"
+    assert np.array_equal(gt, rt), f"{label}: draft tokens"
+    for d, k in enumerate(shape):
+        assert gc[d, :k].tolist() == rc[d].tolist() and (gc[d, k:] == -1).all(), f"{label}: cand[{d}]"
+    return parent, tok
+
+
+def test_hand_worked_example():
+    ex = json.load(open(GOLDEN))
+    check(np.array(ex["logits"], np.float32), ex["shape"], "f32", "golden")
+
+
+@pytest.mark.parametrize("shape", [[1, 3, 3, 3], [3, 3, 3, 3], [1, 9, 9, 9]])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_pages_shapes_full_vocabulary(shape, dtype):
+    """The ablation table's tree shapes over a 128,256-token vocabulary; bf16
+    logits carry many exact ties."""
+    rng = np.random.default_rng(len(shape) * 10 + shape[1])
+    logits = (rng.standard_normal((4, VOCAB)) * 3).astype(np.float32)
+    if dtype == "bf16":
+        logits = inputs.f32_to_bf16_bits(logits)
+    check(logits, shape, dtype, f"{shape} {dtype}")
+
+
+def test_ties_and_small_vocabularies():
+    rng = np.random.default_rng(7)
+    for V in (1, 3, 16, 17, 1000, 1025):
+        P = 5
+        logits = np.round(rng.standard_normal((P, V)), 0).astype(np.float32)   # heavy ties
+        logits[:, ::7] = -0.0
+        shape = [int(min(V, k)) for k in rng.integers(1, 17, P)]
+        while sum(int(np.prod(shape[:d + 1])) for d in range(len(shape))) > 1024:
+            shape = shape[:-1]
+        check(logits, shape, "f32", f"V={V} shape={shape}")
+
+
+def test_tree_feeds_verify():
+    """The [1,3,3,3] tree built on the GPU is a valid parent[] for the verify
+    call: its attention matches the oracle's on that forest."""
+    from gpu_util import check_attn
+    from oracle import verify_attn_ref
+    rng = np.random.default_rng(9)
+    logits = rng.standard_normal((4, 5000)).astype(np.float32)
+    parent, _ = check(logits, [1, 3, 3, 3], "f32", "tree for verify")
+    c = inputs.make_verify("tree", dtype="bf16", Hq=8, Hkv=2, D=128, L=700, seed=11, with_chains=False)
+    par = parent.cpu().numpy().astype(np.int32)
+    assert len(par) == c.T
+    out, lse = ops.tree_verify_attn(to_dev(c.q, "bf16"), to_dev(c.k_cache, "bf16"), to_dev(c.v_cache, "bf16"),
+                                    to_dev(c.k_draft, "bf16"), to_dev(c.v_draft, "bf16"), parent, scale=c.scale)
+    torch.cuda.synchronize()
+    ro, rl = verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, par, c.scale, "bf16")
+    check_attn(out, lse, ro, rl, "bf16", "verify on the built tree")
