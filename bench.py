@@ -278,14 +278,15 @@ def time_draft_tree(dev, reps):
     g = torch.Generator(device=dev)
     g.manual_seed(4)
     logits = torch.randn((4, 128256), device=dev, generator=g)
-    parent, tok, cand = ops.build_draft_tree(logits, [1, 3, 3, 3])
+    ws = ops.alloc_workspace(int(ops.lib().ts_build_draft_tree_workspace(128256, 4)), dev)
+    parent, tok, cand = ops.build_draft_tree(logits, [1, 3, 3, 3], workspace=ws)
     for _ in range(3):
-        ops.build_draft_tree(logits, [1, 3, 3, 3], parent=parent, draft_tok=tok, cand=cand)
+        ops.build_draft_tree(logits, [1, 3, 3, 3], parent=parent, draft_tok=tok, cand=cand, workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        ops.build_draft_tree(logits, [1, 3, 3, 3], parent=parent, draft_tok=tok, cand=cand)
+        ops.build_draft_tree(logits, [1, 3, 3, 3], parent=parent, draft_tok=tok, cand=cand, workspace=ws)
     e1.record()
     torch.cuda.synchronize()
     return round(e0.elapsed_time(e1) * 1e3 / reps, 2)

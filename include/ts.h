@@ -207,14 +207,18 @@ ts_status ts_partial_draft_attn(const void* q, const void* k_part, const void* v
  *   Written (device, int32): parent [T] (-1 for depth-0 nodes), draft_tok [T]
  *   (the node's candidate token), cand [depth][16] if not NULL (ranked
  *   candidates, -1 past k_d).
- * T = ts_draft_tree_nodes(shape, depth) = sum_d k_0*..*k_d.
+ * T = ts_draft_tree_nodes(shape, depth) = sum_d k_0*..*k_d. Workspace: at least
+ * ts_build_draft_tree_workspace(V, depth) bytes, contents ignored on entry.
  * Supported: depth in [1, 8], k_d in [1, 16], k_d <= V, T <= 1024, P >= depth.
  * ---------------------------------------------------------------------- */
 int ts_draft_tree_nodes(const int32_t* shape, int depth);   /* -1 if unsupported */
 
+/* Scratch for the per-slice candidates (<= 64 KiB), 256-byte aligned; 0 on bad sizes. */
+size_t ts_build_draft_tree_workspace(int V, int depth);
+
 ts_status ts_build_draft_tree(const void* logits, int P, int V, const int32_t* shape, int depth,
                               int32_t* parent, int32_t* draft_tok, int32_t* cand, ts_dtype dtype,
-                              hipStream_t stream);
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Acceptance and KV-cache commit (tool listing, "How it works": the drafts are

@@ -10,7 +10,8 @@
 //
 // One workgroup per (KV head, K or V). With at most 256 drafts the acceptance
 // is a few hundred integer operations, so every workgroup computes it itself
-// (thread t walks node t's ancestors) and then copies its own head's rows:
+// (the forest and tokens are staged in LDS, thread t walks node t's ancestors
+// there) and then copies its own head's rows:
 // no workgroup waits for another. Workgroup (0, 0) also writes n, the path
 // and the bonus token.
 #include "common.h"
@@ -28,19 +29,28 @@ __global__ __launch_bounds__(kThreads) void accept_commit_kernel(
     const uint8_t* __restrict__ kd, const uint8_t* __restrict__ vd, int row_bytes,
     int32_t* __restrict__ n_out, int32_t* __restrict__ path_out, int32_t* __restrict__ bonus_out) {
   __shared__ int s_path[TS_MAX_DRAFT];
+  __shared__ int s_par[TS_MAX_DRAFT], s_draft[TS_MAX_DRAFT], s_tgt[TS_MAX_DRAFT + 1];
   __shared__ int s_best[kWavesA], s_cnt[kWavesA];
   __shared__ int s_last;
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t >> 6;
 
+  // the forest and its tokens in LDS (the root walks below chase parents)
+  if (t < T) {
+    const int p = parent[t];
+    s_par[t] = (p < -1 || p >= t) ? -1 : p;
+    s_draft[t] = draft_tok[t];
+  }
+  if (t < T) s_tgt[t] = target_tok[t];
+  if (t == 0) s_tgt[T] = target_tok[T];    // T may equal the block size
+  __syncthreads();
   // depth of node t if its root path is valid, else -1 (the walk ends: parents decrease)
   int depth = -1;
   if (t < T) {
     bool ok = true;
     int d = 0, a = t;
     while (a >= 0) {
-      int p = parent[a];
-      if (p < -1 || p >= a) p = -1;
-      ok = ok && draft_tok[a] == target_tok[p + 1];
+      const int p = s_par[a];
+      ok = ok && s_draft[a] == s_tgt[p + 1];
       d += p >= 0;
       a = p;
     }
@@ -76,8 +86,7 @@ __global__ __launch_bounds__(kThreads) void accept_commit_kernel(
     int a = s_last;
     for (int i = n - 1; i >= 0; --i) {
       s_path[i] = a;
-      const int p = parent[a];
-      a = (p >= -1 && p < a) ? p : -1;
+      a = s_par[a];
     }
   }
   __syncthreads();
@@ -85,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void accept_commit_kernel(
     if (t < T) path_out[t] = t < n ? s_path[t] : -1;
     if (t == 0) {
       *n_out = n;
-      *bonus_out = n > 0 ? target_tok[s_last + 1] : target_tok[0];
+      *bonus_out = n > 0 ? s_tgt[s_last + 1] : s_tgt[0];
     }
   }
 

@@ -310,9 +310,14 @@ int ts_draft_tree_nodes(const int32_t* shape, int depth) {
   return tree_shape("ts_draft_tree_nodes", shape, depth, nullptr);
 }
 
+size_t ts_build_draft_tree_workspace(int V, int depth) {
+  if (V < 1 || depth < 1 || depth > kTreeMaxDepth) return 0;
+  return align_up((size_t)depth * tree_slices(V) * kTreeMaxK * sizeof(uint64_t));
+}
+
 ts_status ts_build_draft_tree(const void* logits, int P, int V, const int32_t* shape, int depth,
                               int32_t* parent, int32_t* draft_tok, int32_t* cand, ts_dtype dtype,
-                              hipStream_t stream) {
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "ts_build_draft_tree";
   if (dtype != TS_F32 && dtype != TS_BF16) return fail(TS_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
   if (!logits || !parent || !draft_tok) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
@@ -325,7 +330,11 @@ ts_status ts_build_draft_tree(const void* logits, int P, int V, const int32_t* s
   if (V < 1) return fail(TS_ERR_INVALID_ARG, "%s: V=%d", fn, V);
   for (int d = 0; d < depth; ++d)
     if (shape[d] > V) return fail(TS_ERR_INVALID_ARG, "%s: shape[%d]=%d > V=%d", fn, d, shape[d], V);
-  return from_hip(launch_build_tree(logits, V, sh, depth, parent, draft_tok, cand, dtype, stream), fn);
+  if (!workspace || ((uintptr_t)workspace & 255u)) return fail(TS_ERR_INVALID_ARG, "%s: workspace null or not 256-byte aligned", fn);
+  if (workspace_bytes < ts_build_draft_tree_workspace(V, depth))
+    return fail(TS_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes,
+                ts_build_draft_tree_workspace(V, depth));
+  return from_hip(launch_build_tree(logits, V, sh, depth, parent, draft_tok, cand, workspace, dtype, stream), fn);
 }
 
 ts_status ts_accept_commit(const int32_t* parent, const int32_t* draft_tok, const int32_t* target_tok,

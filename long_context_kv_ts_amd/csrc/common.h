@@ -161,9 +161,10 @@ struct TreeShape {
   int n[kTreeMaxDepth];
   int off[kTreeMaxDepth];
 };
+int tree_slices(int V);    // vocabulary slices per position (workspace rows)
 hipError_t launch_build_tree(const void* logits, int V, const TreeShape& shape, int depth,
-                             int32_t* parent, int32_t* draft_tok, int32_t* cand, ts_dtype dtype,
-                             hipStream_t s);
+                             int32_t* parent, int32_t* draft_tok, int32_t* cand, void* workspace,
+                             ts_dtype dtype, hipStream_t s);
 
 hipError_t launch_accept_commit(const int32_t* parent, const int32_t* draft_tok,
                                 const int32_t* target_tok, uint32_t rand_u32, int T, void* kc,

@@ -8,17 +8,20 @@
 // parent q / k_d inside depth d-1, so every depth's nodes can be written
 // knowing only that depth's candidates.
 //
-// One 1024-thread workgroup per depth: each thread keeps its own top-k of
-// 64-bit keys (order-preserving logit key << 32 | ~token id, so larger is
-// better and ties go to the lower id) while it strides over the vocabulary;
-// the block then extracts the k best in k rounds of a block-wide max; finally
-// the workgroup writes its depth's nodes.
+// Candidates are ranked by 64-bit keys (order-preserving logit key << 32 |
+// ~token id: larger is better, equal logits go to the lower id); keys are
+// unique. Two launches:
+//   1. grid (slices, depth): each 256-thread workgroup scans one slice of its
+//      row (16-byte loads), keeps a per-thread top-KL list, and extracts its
+//      slice's k best keys into the workspace in k rounds of a block max;
+//   2. grid (depth): each workgroup merges its row's slice candidates the same
+//      way and writes the ranked candidates and its depth's nodes.
 #include "common.h"
 
 namespace ts {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
 constexpr int kWavesT = kThreads / kWave;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -26,6 +29,37 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+__device__ __forceinline__ uint64_t make_key(float f, int i) {
+  return ((uint64_t)order_key(f) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+__device__ __forceinline__ int key_token(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+
+// Per-thread descending list of the KL largest keys seen (0 = empty slot).
+template <int KL> struct TopList {
+  uint64_t v[KL];
+  __device__ void init() {
+#pragma unroll
+    for (int j = 0; j < KL; ++j) v[j] = 0ull;
+  }
+  __device__ void offer(uint64_t key) {
+    if (key > v[KL - 1]) {
+      uint64_t x = key;                  // insertion by compare-exchange down the list
+#pragma unroll
+      for (int j = 0; j < KL; ++j) {
+        const uint64_t hi = x > v[j] ? x : v[j];
+        x = x > v[j] ? v[j] : x;
+        v[j] = hi;
+      }
+    }
+  }
+  __device__ void pop() {
+#pragma unroll
+    for (int j = 0; j < KL - 1; ++j) v[j] = v[j + 1];
+    v[KL - 1] = 0ull;
+  }
+};
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
 #pragma unroll
@@ -36,72 +70,112 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
   return x;
 }
 
-template <typename Tin>
-__global__ __launch_bounds__(kThreads) void build_tree_kernel(const Tin* __restrict__ logits, int V,
-                                                              TreeShape shape,
-                                                              int32_t* __restrict__ parent,
-                                                              int32_t* __restrict__ draft_tok,
-                                                              int32_t* __restrict__ cand_out) {
-  __shared__ uint64_t s_wmax[kWavesT];
-  __shared__ int32_t s_cand[kTreeMaxK];
-  const int d = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int k = shape.k[d];
-  const Tin* row = logits + (int64_t)d * V;
-
-  // per-thread top-kTreeMaxK, descending; 0 is below every real key
-  uint64_t top[kTreeMaxK];
-#pragma unroll
-  for (int j = 0; j < kTreeMaxK; ++j) top[j] = 0ull;
-  for (int i = tid; i < V; i += kThreads) {
-    const uint64_t key = ((uint64_t)order_key(Elem<Tin>::load(row + i)) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i);
-    if (key > top[kTreeMaxK - 1]) {
-      uint64_t x = key;                  // insertion by compare-exchange down the list
-#pragma unroll
-      for (int j = 0; j < kTreeMaxK; ++j) {
-        const uint64_t hi = x > top[j] ? x : top[j];
-        x = x > top[j] ? top[j] : x;
-        top[j] = hi;
-      }
-    }
-  }
-  // k rounds: the best remaining head wins and its owner pops it
+// k rounds of a block-wide max over the threads' list heads; the owner of the
+// winner pops it. Writes the k winners (0 when the block has run out) to out[].
+template <int KL>
+__device__ void block_extract(TopList<KL>& top, int k, uint64_t* s_wmax, uint64_t* out) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   for (int r = 0; r < k; ++r) {
-    const uint64_t m = wave_max_u64(top[0]);
+    const uint64_t m = wave_max_u64(top.v[0]);
     if (lane == 0) s_wmax[wave] = m;
     __syncthreads();
     uint64_t best = s_wmax[0];
 #pragma unroll
     for (int w = 1; w < kWavesT; ++w) best = s_wmax[w] > best ? s_wmax[w] : best;
-    if (top[0] == best && best != 0ull) {     // keys are unique: exactly one owner
-#pragma unroll
-      for (int j = 0; j < kTreeMaxK - 1; ++j) top[j] = top[j + 1];
-      top[kTreeMaxK - 1] = 0ull;
-    }
-    if (tid == 0) s_cand[r] = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
+    if (best != 0ull && top.v[0] == best) top.pop();   // keys are unique: one owner
+    if (threadIdx.x == 0) out[r] = best;
     __syncthreads();
   }
-  if (cand_out != nullptr && tid < kTreeMaxK) cand_out[d * kTreeMaxK + tid] = tid < k ? s_cand[tid] : -1;
+}
 
-  // this depth's nodes
+template <typename Tin, int KL>
+__global__ __launch_bounds__(kThreads) void tree_slice_kernel(const Tin* __restrict__ logits, int V,
+                                                              int slice, TreeShape shape,
+                                                              uint64_t* __restrict__ ws) {
+  __shared__ uint64_t s_wmax[kWavesT];
+  __shared__ uint64_t s_out[kTreeMaxK];
+  const int b = blockIdx.x, d = blockIdx.y, nb = gridDim.x, tid = threadIdx.x;
+  const int k = shape.k[d];
+  const Tin* row = logits + (int64_t)d * V;
+  const int i0 = b * slice, i1 = min(V, i0 + slice);
+  TopList<KL> top;
+  top.init();
+  // 16-byte loads over the slice's aligned middle, element loads at its edges
+  constexpr int kPer = 16 / sizeof(Tin);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(row + i0);
+  const int head = min(i1 - i0, (int)(((16 - (base & 15)) & 15) / sizeof(Tin)));
+  const bool vec = (base % sizeof(Tin)) == 0;
+  const int a0 = vec ? i0 + head : i1;
+  const int nvec = vec ? (i1 - a0) / kPer : 0;
+  for (int v = tid; v < nvec; v += kThreads) {
+    const uint4 u = reinterpret_cast<const uint4*>(row + a0)[v];
+    Tin e[kPer];
+    __builtin_memcpy(e, &u, 16);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) top.offer(make_key(Elem<Tin>::load(&e[q]), a0 + v * kPer + q));
+  }
+  for (int i = i0 + tid; i < a0; i += kThreads) top.offer(make_key(Elem<Tin>::load(row + i), i));
+  for (int i = a0 + nvec * kPer + tid; i < i1; i += kThreads) top.offer(make_key(Elem<Tin>::load(row + i), i));
+  block_extract<KL>(top, k, s_wmax, s_out);
+  if (tid < k) ws[((int64_t)d * nb + b) * kTreeMaxK + tid] = s_out[tid];
+}
+
+template <int KL>
+__global__ __launch_bounds__(kThreads) void tree_merge_kernel(const uint64_t* __restrict__ ws, int nb,
+                                                              TreeShape shape,
+                                                              int32_t* __restrict__ parent,
+                                                              int32_t* __restrict__ draft_tok,
+                                                              int32_t* __restrict__ cand_out) {
+  __shared__ uint64_t s_wmax[kWavesT];
+  __shared__ uint64_t s_out[kTreeMaxK];
+  const int d = blockIdx.x, tid = threadIdx.x;
+  const int k = shape.k[d];
+  TopList<KL> top;
+  top.init();
+  const uint64_t* w = ws + (int64_t)d * nb * kTreeMaxK;
+  for (int e = tid; e < nb * k; e += kThreads) top.offer(w[(e / k) * kTreeMaxK + (e % k)]);
+  block_extract<KL>(top, k, s_wmax, s_out);
+  if (cand_out != nullptr && tid < kTreeMaxK) cand_out[d * kTreeMaxK + tid] = tid < k ? key_token(s_out[tid]) : -1;
   const int off = shape.off[d], n = shape.n[d];
   const int poff = d > 0 ? shape.off[d - 1] : 0;
   for (int q = tid; q < n; q += kThreads) {
     parent[off + q] = d > 0 ? poff + q / k : -1;
-    draft_tok[off + q] = s_cand[q % k];
+    draft_tok[off + q] = key_token(s_out[q % k]);
   }
+}
+
+template <int KL>
+void launch_kl(const void* logits, int V, const TreeShape& shape, int depth, int nb, int slice,
+               uint64_t* ws, int32_t* parent, int32_t* draft_tok, int32_t* cand, ts_dtype dtype,
+               hipStream_t s) {
+  dim3 g1(nb, depth);
+  if (dtype == TS_BF16)
+    tree_slice_kernel<bf16_t, KL><<<g1, kThreads, 0, s>>>(static_cast<const bf16_t*>(logits), V, slice, shape, ws);
+  else
+    tree_slice_kernel<float, KL><<<g1, kThreads, 0, s>>>(static_cast<const float*>(logits), V, slice, shape, ws);
+  tree_merge_kernel<KL><<<depth, kThreads, 0, s>>>(ws, nb, shape, parent, draft_tok, cand);
 }
 
 }  // namespace
 
+int tree_slices(int V) {
+  // about 4096 logits per workgroup, at most 64 slices per position
+  int nb = (V + 4095) / 4096;
+  return nb < 1 ? 1 : nb > 64 ? 64 : nb;
+}
+
 hipError_t launch_build_tree(const void* logits, int V, const TreeShape& shape, int depth,
-                             int32_t* parent, int32_t* draft_tok, int32_t* cand, ts_dtype dtype,
-                             hipStream_t s) {
-  if (dtype == TS_BF16)
-    build_tree_kernel<bf16_t><<<depth, kThreads, 0, s>>>(static_cast<const bf16_t*>(logits), V, shape,
-                                                        parent, draft_tok, cand);
-  else
-    build_tree_kernel<float><<<depth, kThreads, 0, s>>>(static_cast<const float*>(logits), V, shape,
-                                                       parent, draft_tok, cand);
+                             int32_t* parent, int32_t* draft_tok, int32_t* cand, void* workspace,
+                             ts_dtype dtype, hipStream_t s) {
+  const int nb = tree_slices(V);
+  const int slice = (V + nb - 1) / nb;
+  int kmax = 1;
+  for (int d = 0; d < depth; ++d) kmax = shape.k[d] > kmax ? shape.k[d] : kmax;
+  uint64_t* ws = static_cast<uint64_t*>(workspace);
+  // a thread's list only needs the most keys one workgroup can extract
+  if (kmax <= 4) launch_kl<4>(logits, V, shape, depth, nb, slice, ws, parent, draft_tok, cand, dtype, s);
+  else if (kmax <= 8) launch_kl<8>(logits, V, shape, depth, nb, slice, ws, parent, draft_tok, cand, dtype, s);
+  else launch_kl<16>(logits, V, shape, depth, nb, slice, ws, parent, draft_tok, cand, dtype, s);
   return hipGetLastError();
 }
 

@@ -49,8 +49,9 @@ SIGNATURES = {
     "ts_kv_gather": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int, _c_int, _c_int,
                               _c_i64, _c_void_p, _c_void_p, _c_int, _c_void_p]),
     "ts_draft_tree_nodes": (_c_int, [_c_void_p, _c_int]),
+    "ts_build_draft_tree_workspace": (_c_size, [_c_int, _c_int]),
     "ts_build_draft_tree": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p,
-                                     _c_void_p, _c_int, _c_void_p]),
+                                     _c_void_p, _c_int, _c_void_p, _c_size, _c_void_p]),
     "ts_accept_commit": (_c_int, [_c_void_p, _c_void_p, _c_void_p, ctypes.c_uint32, _c_int, _c_void_p,
                                   _c_void_p, _c_i64, _c_i64, _c_void_p, _c_void_p, _c_int, _c_int,
                                   _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
@@ -314,7 +315,7 @@ def draft_tree_nodes(shape) -> int:
     return int(n)
 
 
-def build_draft_tree(logits, shape, *, parent=None, draft_tok=None, cand=None):
+def build_draft_tree(logits, shape, *, parent=None, draft_tok=None, cand=None, workspace=None):
     """ts_build_draft_tree -> (parent [T], draft_tok [T], cand [depth][16]) int32 device tensors.
 
     logits: [P][V] float32 or bfloat16 on the device; shape: host list of k_d."""
@@ -329,10 +330,13 @@ def build_draft_tree(logits, shape, *, parent=None, draft_tok=None, cand=None):
         draft_tok = torch.empty(T, dtype=torch.int32, device=dev)
     if cand is None:
         cand = torch.empty((len(shape), 16), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(int(lib().ts_build_draft_tree_workspace(V, len(shape))), dev)
     arr = (ctypes.c_int32 * len(shape))(*[int(k) for k in shape])
     _check(lib().ts_build_draft_tree(logits.data_ptr(), P, V, ctypes.cast(arr, ctypes.c_void_p), len(shape),
                                      parent.data_ptr(), draft_tok.data_ptr(), cand.data_ptr(),
-                                     _dtype_code(logits), _stream(dev)))
+                                     _dtype_code(logits), workspace.data_ptr(), workspace.numel(),
+                                     _stream(dev)))
     return parent, draft_tok, cand
 
 

@@ -196,13 +196,16 @@ def test_draft_tree_rejects():
     assert lib.ts_draft_tree_nodes(ctypes.cast(big, ctypes.c_void_p), 4) == -1    # > 1024 nodes
     nine = (ctypes.c_int32 * 4)(1, 9, 9, 9)
     assert lib.ts_draft_tree_nodes(ctypes.cast(nine, ctypes.c_void_p), 4) == 820
-    assert lib.ts_build_draft_tree(P, 3, 128256, sp, 4, P, P, None, F, None) == ops.TS_ERR_INVALID_ARG   # P < depth
-    assert lib.ts_build_draft_tree(P, 4, 2, sp, 4, P, P, None, F, None) == ops.TS_ERR_INVALID_ARG        # k > V
-    assert lib.ts_build_draft_tree(None, 4, 128256, sp, 4, P, P, None, F, None) == ops.TS_ERR_INVALID_ARG
-    assert lib.ts_build_draft_tree(P, 4, 128256, sp, 4, P + 2, P, None, F, None) == ops.TS_ERR_INVALID_ARG
-    assert lib.ts_build_draft_tree(P, 4, 128256, sp, 4, P, P, None, 9, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_build_draft_tree(P, 3, 128256, sp, 4, P, P, None, F, P, 1 << 20, None) == ops.TS_ERR_INVALID_ARG   # P < depth
+    assert lib.ts_build_draft_tree(P, 4, 2, sp, 4, P, P, None, F, P, 1 << 20, None) == ops.TS_ERR_INVALID_ARG        # k > V
+    assert lib.ts_build_draft_tree(None, 4, 128256, sp, 4, P, P, None, F, P, 1 << 20, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_build_draft_tree(P, 4, 128256, sp, 4, P + 2, P, None, F, P, 1 << 20, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_build_draft_tree(P, 4, 128256, sp, 4, P, P, None, 9, P, 1 << 20, None) == ops.TS_ERR_INVALID_ARG
     assert lib.ts_build_draft_tree(P, 4, 128256, ctypes.cast(big, ctypes.c_void_p), 4, P, P, None, F,
-                                   None) == ops.TS_ERR_UNSUPPORTED
+                                   P, 1 << 20, None) == ops.TS_ERR_UNSUPPORTED
+    assert lib.ts_build_draft_tree_workspace(128256, 4) == 4 * 32 * 16 * 8
+    assert lib.ts_build_draft_tree(P, 4, 128256, sp, 4, P, P, None, F, P, 1024, None) == ops.TS_ERR_WORKSPACE
+    assert lib.ts_build_draft_tree(P, 4, 128256, sp, 4, P, P, None, F, P + 8, 1 << 20, None) == ops.TS_ERR_INVALID_ARG
     assert "ts_build_draft_tree" in _err()
 
 

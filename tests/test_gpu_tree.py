@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import say, to_dev
+from gpu_util import DEV as DEV_T, say, to_dev
 from long_context_kv_ts_amd import inputs, ops
 from oracle import build_tree_ref, widen
 
@@ -77,3 +77,27 @@ def test_tree_feeds_verify():
     torch.cuda.synchronize()
     ro, rl = verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, par, c.scale, "bf16")
     check_attn(out, lse, ro, rl, "bf16", "verify on the built tree")
+
+
+def test_many_slices_and_reused_workspace():
+    """Vocabularies that split into several slices (ragged last slice, odd
+    slice starts for bf16, the 64-slice cap above 262,144 tokens), with one
+    workspace reused across calls and filled with garbage beforehand."""
+    rng = np.random.default_rng(21)
+    ws = ops.alloc_workspace(int(ops.lib().ts_build_draft_tree_workspace(300001, 4)), DEV_T)
+    ws.fill_(0xFF)
+    for V, dtype in ((4097, "f32"), (8195, "bf16"), (128257, "bf16"), (300001, "f32")):
+        logits = (rng.standard_normal((4, V)) * 2).astype(np.float32)
+        # the best tokens of a row sit at both ends and on slice edges
+        logits[:, [0, V - 1, V // 2]] = 50.0
+        if dtype == "bf16":
+            logits = inputs.f32_to_bf16_bits(logits)
+        lg = to_dev(logits, dtype)
+        shape = [3, 4, 2, 5]
+        parent, tok, cand = ops.build_draft_tree(lg, shape, workspace=ws)
+        torch.cuda.synchronize()
+        rp, rt, rc = build_tree_ref(widen(logits, dtype), shape)
+        say(f"  V={V} {dtype}: cand[0]={cand[0, :3].tolist()}")
+        assert np.array_equal(parent.cpu().numpy(), rp) and np.array_equal(tok.cpu().numpy(), rt), f"V={V}"
+        for d, k in enumerate(shape):
+            assert cand[d, :k].cpu().tolist() == rc[d].tolist(), f"V={V} cand[{d}]"
