@@ -37,10 +37,14 @@ Functions and the passages they follow (TokenSwift pages):
 * ``build_tree_ref``      the candidate tree from the per-position logits
                           (tool listing, "How it works"; tree shapes from the
                           summary page's ablation table).
+* ``sample_ref``          the target's token per verified position: windowed
+                          repetition penalty, temperature, min-p, and a draw
+                          from the caller's uniform (model card CLI example;
+                          summary page, "Approach" and ablation table).
 
 Pinned by ``tests/test_oracle_*.py`` (brute force in 50-digit arithmetic,
 reductions to torch's scaled-dot-product attention, closed forms, a rank-count
-definition of top-k). The importance reduction order (max over the grouped
+definition of top-k, hand-worked examples, scipy's softmax for the sampler). The importance reduction order (max over the grouped
 heads, mean over tokens and recent queries) is a reading of the pages: the
 pages name query-key importance but not the reduction, so that choice is
 pinned only by its own definition.
@@ -49,7 +53,8 @@ from .attention import ancestor_mask, verify_attn_ref, draft_attn_ref, widen
 from .partial_kv import importance_ref, topk_ref, gather_ref
 from .accept import accept_ref, commit_ref
 from .tree import build_tree_ref
+from .sample import sample_ref
 
 __all__ = ["ancestor_mask", "verify_attn_ref", "draft_attn_ref", "widen",
            "importance_ref", "topk_ref", "gather_ref", "accept_ref", "commit_ref",
-           "build_tree_ref"]
+           "build_tree_ref", "sample_ref"]
