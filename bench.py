@@ -224,6 +224,7 @@ def main():
 
     res["accept_commit_us"] = time_accept_commit(vc, dev, args.steps)
     res["draft_tree_us"] = time_draft_tree(dev, args.steps)
+    res["sample_us"] = time_sample(dev, args.steps)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(vc, pc, args.cpu_heads)
@@ -287,6 +288,32 @@ def time_draft_tree(dev, reps):
     e0.record()
     for _ in range(reps):
         ops.build_draft_tree(logits, [1, 3, 3, 3], parent=parent, draft_tok=tok, cand=cand, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+
+
+def time_sample(dev, reps):
+    """Target tokens for the 121 verify rows over the LLaMA3.1 vocabulary:
+    fp32 logits [121][128256], penalty 1.2 over 1024 tokens, temperature 1,
+    min-p 0.1 (its own figure, not part of value)."""
+    import torch
+    from long_context_kv_ts_amd import inputs, ops
+    c = inputs.make_sample(dtype="f32")
+    logits = torch.from_numpy(c.logits).to(dev)
+    hist, parent, dtok = (torch.from_numpy(a).to(dev) for a in (c.hist, c.parent, c.draft_tok))
+    u = torch.from_numpy(c.u).to(dev)
+    ws = ops.alloc_workspace(int(ops.lib().ts_sample_workspace(c.R, c.V)), dev)
+    tok = torch.empty(c.R, dtype=torch.int32, device=dev)
+    kw = dict(hist=hist, parent=parent, draft_tok=dtok, window=inputs.PENALTY_WINDOW, penalty=inputs.PENALTY,
+              temperature=inputs.TEMPERATURE, min_p=inputs.MIN_P, u=u, tok=tok, workspace=ws)
+    for _ in range(3):
+        ops.sample_tokens(logits, **kw)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ops.sample_tokens(logits, **kw)
     e1.record()
     torch.cuda.synchronize()
     return round(e0.elapsed_time(e1) * 1e3 / reps, 2)

@@ -251,6 +251,47 @@ ts_status ts_accept_commit(const int32_t* parent, const int32_t* draft_tok, cons
                            ts_dtype dtype, int32_t* n_accepted, int32_t* path, int32_t* bonus,
                            hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Target-token sampling with the windowed contextual penalty (model card CLI
+ * example: min-p, temperature, a penalty over a window of recent tokens; the
+ * summary page's "Approach" and ablation table: penalty theta over the last W
+ * tokens). Produces the target tokens that ts_accept_commit checks drafts
+ * against.
+ *
+ *   logits     [R][V] fp32 or bf16 (dtype), R = T + 1: row 0 for the position
+ *              after the committed context, row t+1 for the position after
+ *              draft t. Values may be -inf, not NaN or +inf; every row needs
+ *              one finite value.
+ *   hist       int32 [n_hist] on the device: the most recent committed tokens,
+ *              oldest first (only the last `window` are read); NULL iff n_hist = 0
+ *   parent, draft_tok  int32 [T] on the device, the draft forest (entries of
+ *              parent outside [-1, t) count as roots); NULL iff T = 0
+ *   window     W >= 0. Row r's window is the last W tokens of hist followed,
+ *              for r > 0, by the draft tokens on the root path of draft r-1.
+ *              Window ids outside [0, V) are ignored.
+ *   penalty    theta > 0: a windowed token's logit x becomes x / theta if
+ *              x > 0, else x * theta (once per token, however often it recurs)
+ *   temperature  tau >= 0; 0 = greedy: the lowest id with the largest
+ *              penalised logit
+ *   min_p      in [0, 1]: token i is kept when p_i >= min_p * max p, where
+ *              p = softmax(penalised / tau); 0 keeps every token
+ *   u          fp32 [R] on the device, uniforms in [0, 1) drawn by the caller
+ *              (may be NULL when tau = 0)
+ *   tok        int32 [R] out: the smallest kept id whose cumulative kept
+ *              probability (id order) exceeds u[r]; when rounding leaves
+ *              u[r] at or past the end, the last kept id
+ * Supported: V in [1, 1048576], T in [0, 256]. Workspace: at least
+ * ts_sample_workspace(R, V) bytes (272 bytes per row and 4096 logits),
+ * 256-byte aligned, contents ignored on entry.
+ * ---------------------------------------------------------------------- */
+size_t ts_sample_workspace(int R, int V);   /* 0 on bad sizes */
+
+ts_status ts_sample_tokens(const void* logits, int R, int V, const int32_t* hist, int n_hist,
+                           const int32_t* parent, const int32_t* draft_tok, int T, int window,
+                           float penalty, float temperature, float min_p, const float* u,
+                           int32_t* tok, ts_dtype dtype, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,7 +14,7 @@
 // there) and then copies its own head's rows:
 // no workgroup waits for another. Workgroup (0, 0) also writes n, the path
 // and the bonus token.
-#include "common.h"
+#include "decode.h"
 
 namespace ts {
 namespace {

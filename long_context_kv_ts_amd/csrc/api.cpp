@@ -6,7 +6,7 @@
 #include <cstdio>
 #include <string>
 
-#include "common.h"
+#include "decode.h"
 
 namespace {
 
@@ -361,6 +361,61 @@ ts_status ts_accept_commit(const int32_t* parent, const int32_t* draft_tok, cons
   return from_hip(launch_accept_commit(parent, draft_tok, target_tok, rand_u32, T, k_cache, v_cache,
                                        cache_stride, L, k_draft, v_draft, Hkv, D, elem_size(dtype),
                                        n_accepted, path, bonus, stream), fn);
+}
+
+size_t ts_sample_workspace(int R, int V) {
+  if (R < 1 || R > TS_MAX_DRAFT + 1 || V < 1 || V > kSampleSub * kSampleMaxSubs) return 0;
+  return align_up(sample_workspace_bytes(R, V));
+}
+
+ts_status ts_sample_tokens(const void* logits, int R, int V, const int32_t* hist, int n_hist,
+                           const int32_t* parent, const int32_t* draft_tok, int T, int window,
+                           float penalty, float temperature, float min_p, const float* u,
+                           int32_t* tok, ts_dtype dtype, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  const char* fn = "ts_sample_tokens";
+  if (dtype != TS_F32 && dtype != TS_BF16) return fail(TS_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (T < 0 || T > TS_MAX_DRAFT) return fail(TS_ERR_INVALID_ARG, "%s: T=%d outside [0, %d]", fn, T, TS_MAX_DRAFT);
+  if (R != T + 1) return fail(TS_ERR_INVALID_ARG, "%s: R=%d rows for T=%d drafts (R = T + 1)", fn, R, T);
+  if (V < 1 || V > kSampleSub * kSampleMaxSubs)
+    return fail(TS_ERR_UNSUPPORTED, "%s: V=%d outside [1, %d]", fn, V, kSampleSub * kSampleMaxSubs);
+  if (n_hist < 0 || window < 0) return fail(TS_ERR_INVALID_ARG, "%s: n_hist=%d window=%d", fn, n_hist, window);
+  if (!logits || !tok || (n_hist > 0 && !hist) || (T > 0 && (!parent || !draft_tok)) ||
+      (temperature > 0.0f && !u))
+    return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (((uintptr_t)logits % elem_size(dtype)) || ((uintptr_t)hist & 3u) || ((uintptr_t)parent & 3u) ||
+      ((uintptr_t)draft_tok & 3u) || ((uintptr_t)u & 3u) || ((uintptr_t)tok & 3u))
+    return fail(TS_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  if (!(penalty > 0.0f) || !std::isfinite(penalty)) return fail(TS_ERR_INVALID_ARG, "%s: penalty=%g", fn, penalty);
+  if (!(temperature >= 0.0f) || !std::isfinite(temperature))
+    return fail(TS_ERR_INVALID_ARG, "%s: temperature=%g", fn, temperature);
+  if (!(min_p >= 0.0f && min_p <= 1.0f)) return fail(TS_ERR_INVALID_ARG, "%s: min_p=%g outside [0, 1]", fn, min_p);
+  if (!workspace || ((uintptr_t)workspace & 255u)) return fail(TS_ERR_INVALID_ARG, "%s: workspace null or not 256-byte aligned", fn);
+  const size_t need = ts_sample_workspace(R, V);
+  if (workspace_bytes < need) return fail(TS_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  SampleArgs a{};
+  a.logits = logits;
+  a.R = R;
+  a.V = V;
+  a.hist = hist;
+  a.n_hist = n_hist;
+  a.parent = parent;
+  a.draft_tok = draft_tok;
+  a.T = T;
+  a.window = window;
+  a.theta = penalty;
+  // greedy keeps s2 = 0; a tiny temperature saturates at a finite scale so that 0 * s2 stays 0
+  a.s2 = temperature > 0.0f ? (float)std::fmin(1.4426950408889634 / (double)temperature, 1e30) : 0.0f;
+  // greedy: the cut sits at the maximum, so the kept tokens are the maxima
+  a.cut = temperature == 0.0f ? 0.0f
+          : min_p > 0.0f      ? (float)((double)temperature * std::log((double)min_p))
+                              : -INFINITY;
+  a.u = u;
+  a.tok = tok;
+  a.nb = sample_subslices(V);
+  a.sub = static_cast<SampleSub*>(workspace);
+  a.cand = reinterpret_cast<SampleCand*>(a.sub + (size_t)R * a.nb);
+  return from_hip(launch_sample(a, dtype, stream), fn);
 }
 
 }  // extern "C"

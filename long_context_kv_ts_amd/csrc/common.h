@@ -150,26 +150,5 @@ hipError_t launch_topk(const float* scores, int Hkv, int n, int k, int32_t* idx,
 hipError_t launch_gather(const void* kc, const void* vc, int64_t stride, const int32_t* idx,
                          int Hkv, int k, int chunk, int D, int64_t L, void* kp, void* vp,
                          int elem_bytes, hipStream_t s);
-// Candidate tree of draft tokens (shape [k_0..k_{depth-1}]): per depth d the
-// number of candidates k[d], the node count n[d] = k[0]*..*k[d] and the first
-// node index off[d] (breadth-first numbering).
-constexpr int kTreeMaxDepth = 8;
-constexpr int kTreeMaxK = 16;
-constexpr int kTreeMaxNodes = 1024;
-struct TreeShape {
-  int k[kTreeMaxDepth];
-  int n[kTreeMaxDepth];
-  int off[kTreeMaxDepth];
-};
-int tree_slices(int V);    // vocabulary slices per position (workspace rows)
-hipError_t launch_build_tree(const void* logits, int V, const TreeShape& shape, int depth,
-                             int32_t* parent, int32_t* draft_tok, int32_t* cand, void* workspace,
-                             ts_dtype dtype, hipStream_t s);
-
-hipError_t launch_accept_commit(const int32_t* parent, const int32_t* draft_tok,
-                                const int32_t* target_tok, uint32_t rand_u32, int T, void* kc,
-                                void* vc, int64_t stride, int64_t L, const void* kd, const void* vd,
-                                int Hkv, int D, int elem_bytes, int32_t* n_out, int32_t* path_out,
-                                int32_t* bonus_out, hipStream_t s);
 
 }  // namespace ts

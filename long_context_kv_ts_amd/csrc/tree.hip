@@ -16,7 +16,7 @@
 //      slice's k best keys into the workspace in k rounds of a block max;
 //   2. grid (depth): each workgroup merges its row's slice candidates the same
 //      way and writes the ranked candidates and its depth's nodes.
-#include "common.h"
+#include "decode.h"
 
 namespace ts {
 namespace {

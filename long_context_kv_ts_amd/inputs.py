@@ -16,6 +16,11 @@ stand in for them):
   cache, 64-token chunks, budget of 64 chunks, 8 chunks per KV head with keys
   scaled by 3 before rounding.
 * ``llama2_mha_100k`` bf16, Hq=Hkv=32, D=128, L=102400, same 120-query mask.
+* ``make_sample``  target-token sampling over the verify rows: logits
+  [121][128256] ~ N(0, 3^2) with 64 "hot" token ids raised by 8 in every row
+  (so that a handful of tokens pass min-p 0.1 and the repetition penalty
+  changes draws), 4096 committed tokens half drawn from the hot ids, draft
+  tokens from the hot ids on the tree + chains forest, u ~ U[0, 1) in fp32.
 
 bf16 tensors are carried as ``np.uint16`` bit patterns (round to nearest even
 from the fp32 draw); fp32 tensors as ``np.float32``.
@@ -42,6 +47,11 @@ NGRAM_TOPK = 20             # retrieved 4-gram candidates
 GAMMA = 4                   # draft length: 4 logits, 4-grams, 4 recent queries
 RETRIEVAL_BUDGET = 4096     # tokens kept in the partial KV cache
 CHUNK = 64                  # tokens per importance chunk (budget = 64 chunks)
+MIN_P = 0.1                 # sampling: min-p
+TEMPERATURE = 1.0           # sampling: temperature
+PENALTY = 1.2               # contextual penalty theta
+PENALTY_WINDOW = 1024       # contextual penalty window W (tokens)
+VOCAB = 128256              # LLaMA3.1 vocabulary
 
 
 # --------------------------------------------------------------------------
@@ -232,6 +242,38 @@ def make_partial(name: str = "partial_100k", *, Hq: int = 32, Hkv: int = 8, D: i
     return PartialCase(name, BF16, R, Hq, Hkv, D, L, chunk, k, float(1.0 / np.sqrt(D)),
                        f32_to_bf16_bits(q), f32_to_bf16_bits(kc), f32_to_bf16_bits(vc),
                        f32_to_bf16_bits(kn), f32_to_bf16_bits(vn), boosted)
+
+
+@dataclasses.dataclass
+class SampleCase:
+    name: str
+    dtype: str
+    R: int
+    V: int
+    logits: np.ndarray       # [R][V] fp32, or bf16 bit patterns
+    hist: np.ndarray         # int32 [n_hist] committed tokens, oldest first
+    parent: np.ndarray       # int32 [T], T = R - 1
+    draft_tok: np.ndarray    # int32 [T]
+    u: np.ndarray            # fp32 [R] uniforms in [0, 1)
+
+
+def make_sample(name: str = "sample_llama8b", *, dtype: str = F32, V: int = VOCAB, n_hist: int = 4096,
+                parent: Optional[np.ndarray] = None, logit_std: float = 3.0, n_hot: int = 64,
+                hot_boost: float = 8.0, seed: int = 5) -> SampleCase:
+    rl, rh, rd, ru, rp, rhot = _streams(seed, 6)
+    if parent is None:
+        parent = tree_plus_chains_parents(rp)
+    T = int(len(parent))
+    R = T + 1
+    x = _normal(rl, (R, V), logit_std)
+    hot = rhot.choice(V, size=min(n_hot, V), replace=False)
+    x[:, hot] += np.float32(hot_boost)
+    from_hot = rh.random(n_hist) < 0.5
+    hist = np.where(from_hot, rh.choice(hot, n_hist), rh.integers(0, V, n_hist)).astype(np.int32)
+    draft_tok = rd.choice(hot, size=T).astype(np.int32)
+    u = ru.random(R, dtype=np.float32)
+    return SampleCase(name, dtype, R, V, _encode(x, dtype), hist,
+                      np.ascontiguousarray(parent, np.int32), draft_tok, u)
 
 
 def workload(name: str, *, L: Optional[int] = None, seed: Optional[int] = None):

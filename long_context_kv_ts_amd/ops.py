@@ -55,6 +55,10 @@ SIGNATURES = {
     "ts_accept_commit": (_c_int, [_c_void_p, _c_void_p, _c_void_p, ctypes.c_uint32, _c_int, _c_void_p,
                                   _c_void_p, _c_i64, _c_i64, _c_void_p, _c_void_p, _c_int, _c_int,
                                   _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "ts_sample_workspace": (_c_size, [_c_int, _c_int]),
+    "ts_sample_tokens": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_int,
+                                  _c_int, ctypes.c_float, ctypes.c_float, ctypes.c_float, _c_void_p,
+                                  _c_void_p, _c_int, _c_void_p, _c_size, _c_void_p]),
     "ts_partial_draft_attn_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int]),
     "ts_partial_draft_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                        _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_i64,
@@ -379,6 +383,47 @@ def accept_commit(parent, draft_tok, target_tok, rand_u32: int, k_cache, v_cache
                                   _dtype_code(k_cache), n_accepted.data_ptr(), path.data_ptr(),
                                   bonus.data_ptr(), _stream(dev)))
     return n_accepted, path, bonus
+
+
+def sample_tokens(logits, *, hist=None, parent=None, draft_tok=None, window: int = 1024,
+                  penalty: float = 1.2, temperature: float = 1.0, min_p: float = 0.1, u=None,
+                  tok=None, workspace=None):
+    """ts_sample_tokens -> tok [R] int32: the target's token for each of the
+    R = T + 1 verified positions of logits [R][V] (row 0 after the committed
+    context, row t+1 after draft t), with the windowed repetition penalty,
+    temperature, min-p and the caller's uniforms u [R] (fp32, device)."""
+    _need(logits, "logits", 2)
+    _contig(logits, "logits")
+    dev = logits.device
+    R, V = logits.shape
+    T = 0
+    if parent is not None or draft_tok is not None:
+        for n, t in (("parent", parent), ("draft_tok", draft_tok)):
+            _need(t, n, 1, torch.int32, dev)
+            _contig(t, n)
+        T = parent.shape[0]
+        if draft_tok.shape[0] != T:
+            raise ValueError("parent and draft_tok must have T entries")
+    n_hist = 0
+    if hist is not None:
+        _need(hist, "hist", 1, torch.int32, dev)
+        _contig(hist, "hist")
+        n_hist = hist.shape[0]
+    if temperature > 0:
+        _need(u, "u", 1, torch.float32, dev)
+        _contig(u, "u")
+        if u.shape[0] != R:
+            raise ValueError("u must have one uniform per row")
+    if tok is None:
+        tok = torch.empty(R, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(int(lib().ts_sample_workspace(R, V)), dev)
+    ptr = lambda t: t.data_ptr() if t is not None and t.numel() else None
+    _check(lib().ts_sample_tokens(logits.data_ptr(), R, V, ptr(hist), n_hist, ptr(parent), ptr(draft_tok), T,
+                                  int(window), float(penalty), float(temperature), float(min_p),
+                                  ptr(u) if temperature > 0 else None, tok.data_ptr(), _dtype_code(logits),
+                                  workspace.data_ptr(), workspace.numel(), _stream(dev)))
+    return tok
 
 
 def partial_draft_attn(q, k_part, v_part, k_new, v_new, *, scale=None, out=None, lse=None,

@@ -78,7 +78,10 @@ def sample_row(x, tokens, theta, temperature, min_p, u):
     tok = min(idx, last_kept)
     # how far the draw and the filter sit from a decision boundary
     u_margin = float(np.min(np.abs(cdf[keep] - u)))
-    keep_margin = float(np.min(np.abs((y - y.max()) - np.log(min_p)))) if min_p > 0 else np.inf
+    # tokens at the maximum are kept whatever min_p is, so they sit at no boundary
+    below = y < y.max()
+    keep_margin = float(np.min(np.abs((y[below] - y.max()) - np.log(min_p)), initial=np.inf)) \
+        if min_p > 0 else np.inf
     return tok, {"greedy": False, "z": z, "q": q, "keep": keep, "cdf": cdf,
                  "u_margin": u_margin, "keep_margin": keep_margin}
 

@@ -209,6 +209,37 @@ def test_draft_tree_rejects():
     assert "ts_build_draft_tree" in _err()
 
 
+def test_sample_rejects():
+    """Argument checks of ts_sample_tokens; none of these calls launches anything."""
+    lib = ops.lib()
+    ws = lib.ts_sample_workspace(121, 128256)
+    assert ws >= 121 * 32 * (16 + 32 * 8) and ws % 256 == 0
+    assert lib.ts_sample_workspace(0, 100) == 0 and lib.ts_sample_workspace(1, (1 << 20) + 1) == 0
+
+    def call(logits=P, R=121, V=128256, hist=P, n_hist=4096, parent=P, draft=P, T=120, window=1024,
+             penalty=1.2, temp=1.0, min_p=0.1, u=P, tok=P, dtype=F, wsp=P, wsb=1 << 20):
+        return lib.ts_sample_tokens(logits, R, V, hist, n_hist, parent, draft, T, window, penalty, temp,
+                                    min_p, u, tok, dtype, wsp, wsb, None)
+    bad = ops.TS_ERR_INVALID_ARG
+    assert call(R=120) == bad                                   # R != T + 1
+    assert call(T=257, R=258) == bad
+    assert call(V=(1 << 20) + 1) == ops.TS_ERR_UNSUPPORTED
+    assert call(V=0) == ops.TS_ERR_UNSUPPORTED
+    assert call(logits=None) == bad
+    assert call(hist=None) == bad                               # n_hist > 0
+    assert call(parent=None) == bad                             # T > 0
+    assert call(u=None) == bad                                  # temperature > 0
+    assert call(tok=P + 2) == bad
+    assert call(window=-1) == bad and call(n_hist=-1) == bad
+    assert call(penalty=0.0) == bad and call(penalty=float("inf")) == bad
+    assert call(temp=-1.0) == bad and call(temp=float("nan")) == bad
+    assert call(min_p=1.5) == bad and call(min_p=-0.1) == bad
+    assert call(dtype=7) == bad
+    assert call(wsp=P + 16) == bad
+    assert call(wsb=ws - 4) == ops.TS_ERR_WORKSPACE
+    assert "ts_sample_tokens" in _err()
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "_lib", None)
     monkeypatch.setattr(ops, "_LIB_PATH", str(tmp_path / "missing.so"))

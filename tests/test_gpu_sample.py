@@ -1,0 +1,157 @@
+"""GPU parity of ts_sample_tokens (target-token sampling with the windowed
+repetition penalty, temperature and min-p) against the oracle.
+
+The sampled token is an integer decided by floating point: the GPU sums the
+kept weights in fp32 in its own order, the oracle in fp64. So a row must match
+the oracle exactly whenever its draw u sits more than 1e-4 (of the kept mass)
+from a cumulative boundary and no logit sits within 1e-4 of the min-p cut;
+closer to a boundary, the GPU's token must still be a valid draw within 2e-5
+of it (either neighbour of the boundary). Greedy rows must match exactly
+unless the two best penalised logits are within 1e-6 relative."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, say, to_dev
+from long_context_kv_ts_amd import inputs, ops
+from oracle import sample_ref, widen
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "sample_example.json")
+EXACT_MARGIN = 1e-4
+VALID_TOL = 2e-5
+
+
+def _i32(a):
+    a = np.asarray(a, np.int32)
+    return to_dev(a, "i32") if a.size else None
+
+
+def run(logits, dtype, hist, parent, draft, *, window, penalty, temperature, min_p, u, label,
+        workspace=None):
+    R = logits.shape[0]
+    u = np.asarray(u, np.float32)
+    tok = ops.sample_tokens(to_dev(logits, dtype), hist=_i32(hist), parent=_i32(parent) if len(parent) else None,
+                            draft_tok=_i32(draft) if len(draft) else None, window=window, penalty=penalty,
+                            temperature=temperature, min_p=min_p, u=to_dev(u, "f32"), workspace=workspace)
+    torch.cuda.synchronize()
+    got = tok.cpu().numpy()
+    ref, diags = sample_ref(widen(logits, dtype), hist, parent if len(parent) else None, draft,
+                            window=window, penalty=penalty, temperature=temperature, min_p=min_p,
+                            u=u.astype(np.float64))
+    near = 0
+    for r in range(R):
+        g, e, d = int(got[r]), int(ref[r]), diags[r]
+        if d["greedy"]:
+            z = d["z"]
+            if g != e:
+                assert 0 <= g < len(z) and z[g] >= z.max() - 1e-6 * abs(z.max()), f"{label} row {r}: {g} != {e}"
+                near += 1
+            continue
+        if d["u_margin"] > EXACT_MARGIN and d["keep_margin"] > EXACT_MARGIN:
+            assert g == e, f"{label} row {r}: token {g} != oracle {e} (u={u[r]})"
+            continue
+        near += 1
+        assert 0 <= g < len(d["q"]), f"{label} row {r}: token {g} out of range"
+        q, cdf = d["q"], d["cdf"]
+        lo, hi = cdf[g] - q[g], cdf[g]
+        y = d["z"] / temperature
+        border = abs((y[g] - y.max()) - np.log(min_p)) < VALID_TOL if min_p > 0 else False
+        assert (q[g] > 0 or border) and lo - VALID_TOL <= u[r] < hi + VALID_TOL, \
+            f"{label} row {r}: token {g} (oracle {e}) is not a draw at u={u[r]} (cdf {lo}..{hi})"
+    say(f"  {label}: {R} rows, {near} near a boundary, tokens {got[:6].tolist()}...")
+    return got
+
+
+def test_hand_worked_example():
+    ex = json.load(open(GOLDEN))
+    x = np.array(ex["logits"], np.float32)
+    kw = dict(window=ex["window"], penalty=ex["penalty"], min_p=ex["min_p"])
+    g = run(x, "f32", ex["hist"], ex["parent"], ex["draft_tok"], temperature=0.0, u=[0.5] * 3,
+            label="golden greedy", **kw)
+    assert g.tolist() == ex["greedy"]
+    for d in ex["draws"]:
+        g = run(x, "f32", ex["hist"], ex["parent"], ex["draft_tok"], temperature=1.0, u=d["u"],
+                label=f"golden u={d['u']}", **kw)
+        assert g.tolist() == d["tok"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_verify_rows_full_vocabulary(dtype):
+    """The pages' settings (min-p 0.1, temperature 1, theta 1.2, W 1024) on the
+    121 rows of the tree + chains verify pass over the LLaMA3.1 vocabulary."""
+    c = inputs.make_sample(dtype=dtype)
+    run(c.logits, dtype, c.hist, c.parent, c.draft_tok, window=inputs.PENALTY_WINDOW, penalty=inputs.PENALTY,
+        temperature=inputs.TEMPERATURE, min_p=inputs.MIN_P, u=c.u, label=f"121x128256 {dtype}")
+
+
+@pytest.mark.parametrize("window,penalty,temperature,min_p", [
+    (1024, 1.2, 0.0, 0.1),        # greedy
+    (0, 1.2, 1.0, 0.1),           # no window
+    (1024, 1.0, 1.0, 0.1),        # no penalty
+    (1024, 1.2, 1.0, 0.0),        # min-p off: every token kept
+    (20, 1.2, 0.5, 0.05),         # the ablation's shortest window
+    (2048, 1.2, 1.5, 0.2),        # and its longest
+    (1024, 1.2, 1.0, 1.0),        # only the maximum survives
+    (1024, 1.2, 1e-3, 0.1),       # near-greedy
+])
+def test_knobs(window, penalty, temperature, min_p):
+    c = inputs.make_sample(dtype="bf16", seed=6)
+    run(c.logits, "bf16", c.hist, c.parent, c.draft_tok, window=window, penalty=penalty,
+        temperature=temperature, min_p=min_p, u=c.u, label=f"W={window} theta={penalty} tau={temperature} "
+                                                          f"min_p={min_p}")
+
+
+@pytest.mark.parametrize("V", [1, 3, 7, 9, 4095, 4096, 4097, 8200, 128257])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_vocabularies_and_edges(V, dtype):
+    """Vocabularies around the 4096-logit slices, odd row lengths (misaligned
+    rows), window ids outside [0, V), -inf logits, u = 0 and u just below 1."""
+    rng = np.random.default_rng(V)
+    parent = np.array([-1, 0, 1, -1, 3], np.int32)
+    draft = rng.integers(0, V, 5).astype(np.int32)
+    hist = np.concatenate([rng.integers(0, V, 300), [-5, V + 3, V]]).astype(np.int32)
+    x = (rng.standard_normal((6, V)) * 2).astype(np.float32)
+    if V > 2:
+        x[1, ::3] = -np.inf
+        x[2, 1:] = -np.inf
+    if dtype == "bf16":
+        fin = np.isfinite(x)
+        b = inputs.f32_to_bf16_bits(np.where(fin, x, 0))
+        b[~fin] = 0xFF80                                   # bf16 -inf
+        x = b
+    u = rng.random(6, dtype=np.float32)
+    u[0], u[3] = 0.0, np.float32(np.nextafter(np.float32(1), np.float32(0)))
+    for tau, mp in ((1.0, 0.1), (0.7, 0.0), (0.0, 0.1)):
+        run(x, dtype, hist, parent, draft, window=64, penalty=1.3, temperature=tau, min_p=mp, u=u,
+            label=f"V={V} {dtype} tau={tau} min_p={mp}")
+
+
+def test_single_row_no_drafts_no_history():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((1, 50000)) * 3).astype(np.float32)
+    for u in (0.0, 0.25, 0.999):
+        run(x, "f32", [], [], [], window=1024, penalty=1.2, temperature=1.0, min_p=0.1, u=[u],
+            label=f"T=0 u={u}")
+
+
+def test_deep_chain_window_from_the_path():
+    """A 256-draft chain with W = 64: late rows' windows hold only draft tokens."""
+    T = 256
+    parent = np.arange(-1, T - 1, dtype=np.int32)
+    c = inputs.make_sample(dtype="f32", V=5000, parent=parent, n_hot=40, seed=8)
+    run(c.logits, "f32", c.hist, c.parent, c.draft_tok, window=64, penalty=1.5, temperature=1.0,
+        min_p=0.05, u=c.u, label="chain 256, W=64")
+
+
+def test_reused_workspace_with_garbage():
+    ws = ops.alloc_workspace(int(ops.lib().ts_sample_workspace(257, 300000)), DEV)
+    ws.fill_(0x7F)
+    for V, dtype, seed in ((300000, "f32", 1), (128256, "bf16", 2), (1000, "f32", 3)):
+        c = inputs.make_sample(dtype=dtype, V=V, seed=seed)
+        run(c.logits, dtype, c.hist, c.parent, c.draft_tok, window=1024, penalty=1.2, temperature=1.0,
+            min_p=0.1, u=c.u, label=f"shared workspace V={V}", workspace=ws)
