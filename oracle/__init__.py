@@ -41,6 +41,10 @@ Functions and the passages they follow (TokenSwift pages):
                           repetition penalty, temperature, min-p, and a draw
                           from the caller's uniform (model card CLI example;
                           summary page, "Approach" and ablation table).
+* ``ngram_table``, ``ngram_update``, ``retrieve_ref``  the 4-gram table of the
+                          committed text and the top-k 4-grams for a first
+                          token (tool listing, "How it works"; model card CLI
+                          example: top-k 20).
 
 Pinned by ``tests/test_oracle_*.py`` (brute force in 50-digit arithmetic,
 reductions to torch's scaled-dot-product attention, closed forms, a rank-count
@@ -54,7 +58,8 @@ from .partial_kv import importance_ref, topk_ref, gather_ref
 from .accept import accept_ref, commit_ref
 from .tree import build_tree_ref
 from .sample import sample_ref
+from .ngram import ngram_table, ngram_update, retrieve_ref
 
 __all__ = ["ancestor_mask", "verify_attn_ref", "draft_attn_ref", "widen",
            "importance_ref", "topk_ref", "gather_ref", "accept_ref", "commit_ref",
-           "build_tree_ref", "sample_ref"]
+           "build_tree_ref", "sample_ref", "ngram_table", "ngram_update", "retrieve_ref"]
