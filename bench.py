@@ -225,6 +225,7 @@ def main():
     res["accept_commit_us"] = time_accept_commit(vc, dev, args.steps)
     res["draft_tree_us"] = time_draft_tree(dev, args.steps)
     res["sample_us"] = time_sample(dev, args.steps)
+    res["ngram_us"] = time_ngram(dev, args.steps)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(vc, pc, args.cpu_heads)
@@ -314,6 +315,37 @@ def time_sample(dev, reps):
     e0.record()
     for _ in range(reps):
         ops.sample_tokens(logits, **kw)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+
+
+def time_ngram(dev, reps):
+    """One step of the 4-gram table after 102,400 committed tokens: add the
+    5 tokens of a verification and retrieve the 20 best 4-grams for a first
+    token (its own figure, not part of value)."""
+    import torch
+    from long_context_kv_ts_amd import inputs, ops
+    text = inputs.make_text(102400 + 5 * (reps + 8))
+    tokens = torch.from_numpy(text).to(dev)
+    table = ops.NgramTable(dev, capacity_log2=18, max_entries=131072)
+    table.update(tokens, 0, 102400)
+    first = torch.zeros(1, dtype=torch.int32, device=dev)            # the most frequent token id
+    ws = ops.alloc_workspace(int(ops.lib().ts_ngram_retrieve_workspace(table.max_entries, 20)), dev)
+    out = (torch.empty((20, 4), dtype=torch.int32, device=dev), torch.empty(20, dtype=torch.int32, device=dev),
+           torch.empty(1, dtype=torch.int32, device=dev))
+    n = 102400
+    for _ in range(3):
+        table.update(tokens, n, n + 5)
+        table.retrieve(first, 20, out_tok=out[0], out_count=out[1], n_found=out[2], workspace=ws)
+        n += 5
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        table.update(tokens, n, n + 5)
+        table.retrieve(first, 20, out_tok=out[0], out_count=out[1], n_found=out[2], workspace=ws)
+        n += 5
     e1.record()
     torch.cuda.synchronize()
     return round(e0.elapsed_time(e1) * 1e3 / reps, 2)

@@ -292,6 +292,49 @@ ts_status ts_sample_tokens(const void* logits, int R, int V, const int32_t* hist
                            int32_t* tok, ts_dtype dtype, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * 4-gram table of the committed text and top-k retrieval (tool listing, "How
+ * it works": top-k candidate 4-grams become draft tokens and the n-gram table
+ * is updated after verification; model card CLI example: top-k 20).
+ *
+ * The table is one device buffer of ts_ngram_table_bytes(capacity_log2,
+ * max_entries) bytes, 256-byte aligned, owned by the caller and set up by
+ * ts_ngram_init. It begins with a ts_ngram_header (copy it back to inspect):
+ * min(n_entries, max_entries) distinct 4-grams are stored, and `dropped`
+ * counts 4-grams that found no room (then retrieval misses them).
+ * Supported: capacity_log2 in [4, 24], max_entries in [1, 262144] and at most
+ * the capacity (keep the capacity at least twice the distinct 4-grams).
+ *
+ * ts_ngram_update: adds the 4-grams tokens[p-3 .. p] for p in [from, to), p >= 3,
+ * each with its count and the last p it ended at. `tokens` is the committed
+ * text on the device (int32, at least `to` entries): after a verification,
+ * append the accepted drafts and the bonus token and call with the old and new
+ * lengths. 0 <= from <= to <= 2^31 - 1.
+ *
+ * ts_ngram_retrieve: the 4-grams whose first token is *first_tok (a device
+ * int32, e.g. the root of the candidate tree), ranked by count then by last
+ * position, both descending; the best k (k in [1, 64]) go to out_tok [k][4]
+ * (rows past the matches are -1), their counts to out_count [k] (nullable, 0
+ * past the matches) and how many there are to *n_found (nullable). max_entries
+ * must be the table's. Workspace: ts_ngram_retrieve_workspace(max_entries, k)
+ * bytes, 256-byte aligned.
+ * Calls on one table must not overlap (order them on one stream).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t capacity_log2;
+  int32_t max_entries;
+  int32_t n_entries;
+  int32_t dropped;
+} ts_ngram_header;
+
+size_t ts_ngram_table_bytes(int capacity_log2, int max_entries);   /* 0 if unsupported */
+ts_status ts_ngram_init(void* table, size_t table_bytes, int capacity_log2, int max_entries, hipStream_t stream);
+ts_status ts_ngram_update(void* table, const int32_t* tokens, int64_t from, int64_t to, hipStream_t stream);
+size_t ts_ngram_retrieve_workspace(int max_entries, int k);        /* 0 if unsupported */
+ts_status ts_ngram_retrieve(const void* table, int max_entries, const int32_t* first_tok, int k,
+                            int32_t* out_tok, int32_t* out_count, int32_t* n_found, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -418,4 +418,58 @@ ts_status ts_sample_tokens(const void* logits, int R, int V, const int32_t* hist
   return from_hip(launch_sample(a, dtype, stream), fn);
 }
 
+static_assert(sizeof(ts_ngram_header) == sizeof(NgramHeader), "header layouts agree");
+
+size_t ts_ngram_table_bytes(int capacity_log2, int max_entries) {
+  if (capacity_log2 < 4 || capacity_log2 > kNgramMaxCapacityLog2 || max_entries < 1 ||
+      max_entries > kNgramMaxEntries || max_entries > (1 << capacity_log2))
+    return 0;
+  return align_up(ngram_table_bytes(capacity_log2, max_entries));
+}
+
+ts_status ts_ngram_init(void* table, size_t table_bytes, int capacity_log2, int max_entries, hipStream_t stream) {
+  const char* fn = "ts_ngram_init";
+  const size_t need = ts_ngram_table_bytes(capacity_log2, max_entries);
+  if (need == 0)
+    return fail(TS_ERR_UNSUPPORTED, "%s: capacity_log2=%d max_entries=%d (capacity_log2 in [4, %d], max_entries in "
+                "[1, %d] and at most the capacity)", fn, capacity_log2, max_entries, kNgramMaxCapacityLog2,
+                kNgramMaxEntries);
+  if (!table || ((uintptr_t)table & 255u)) return fail(TS_ERR_INVALID_ARG, "%s: table null or not 256-byte aligned", fn);
+  if (table_bytes < need) return fail(TS_ERR_WORKSPACE, "%s: table %zu < %zu bytes", fn, table_bytes, need);
+  return from_hip(launch_ngram_init(ngram_view(table, capacity_log2), capacity_log2, max_entries, stream), fn);
+}
+
+ts_status ts_ngram_update(void* table, const int32_t* tokens, int64_t from, int64_t to, hipStream_t stream) {
+  const char* fn = "ts_ngram_update";
+  if (!table || ((uintptr_t)table & 255u)) return fail(TS_ERR_INVALID_ARG, "%s: table null or not 256-byte aligned", fn);
+  if (from < 0 || to < from || to > 2147483647LL)
+    return fail(TS_ERR_INVALID_ARG, "%s: from=%lld to=%lld", fn, (long long)from, (long long)to);
+  if (to > 3 && (!tokens || ((uintptr_t)tokens & 3u)))
+    return fail(TS_ERR_INVALID_ARG, "%s: tokens null or misaligned", fn);
+  return from_hip(launch_ngram_update(table, tokens, from, to, stream), fn);
+}
+
+size_t ts_ngram_retrieve_workspace(int max_entries, int k) {
+  if (max_entries < 1 || max_entries > kNgramMaxEntries || k < 1 || k > kNgramMaxK) return 0;
+  return align_up(ngram_retrieve_workspace_bytes(max_entries, k));
+}
+
+ts_status ts_ngram_retrieve(const void* table, int max_entries, const int32_t* first_tok, int k,
+                            int32_t* out_tok, int32_t* out_count, int32_t* n_found, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "ts_ngram_retrieve";
+  if (max_entries < 1 || max_entries > kNgramMaxEntries || k < 1 || k > kNgramMaxK)
+    return fail(TS_ERR_UNSUPPORTED, "%s: max_entries=%d k=%d (max_entries in [1, %d], k in [1, %d])", fn,
+                max_entries, k, kNgramMaxEntries, kNgramMaxK);
+  if (!table || ((uintptr_t)table & 255u)) return fail(TS_ERR_INVALID_ARG, "%s: table null or not 256-byte aligned", fn);
+  if (!first_tok || !out_tok || ((uintptr_t)first_tok & 3u) || ((uintptr_t)out_tok & 3u) ||
+      ((uintptr_t)out_count & 3u) || ((uintptr_t)n_found & 3u))
+    return fail(TS_ERR_INVALID_ARG, "%s: null or misaligned pointer", fn);
+  if (!workspace || ((uintptr_t)workspace & 255u)) return fail(TS_ERR_INVALID_ARG, "%s: workspace null or not 256-byte aligned", fn);
+  const size_t need = ts_ngram_retrieve_workspace(max_entries, k);
+  if (workspace_bytes < need) return fail(TS_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  return from_hip(launch_ngram_retrieve(const_cast<void*>(table), max_entries, first_tok, k, out_tok, out_count,
+                                        n_found, workspace, stream), fn);
+}
+
 }  // extern "C"

@@ -66,4 +66,42 @@ int sample_subslices(int V);
 size_t sample_workspace_bytes(int R, int V);
 hipError_t launch_sample(const SampleArgs& a, ts_dtype dtype, hipStream_t s);
 
+// 4-gram table of the committed text: header, slots (entry id or -1), entries.
+struct NgramEntry {
+  int32_t tok[4];
+  int32_t count;                         // 0: an entry that was never published
+  int32_t last;                          // last position at which the 4-gram ended
+};
+struct NgramHeader {                     // the first bytes of the table (same layout as ts_ngram_header)
+  int32_t capacity_log2;
+  int32_t max_entries;
+  int32_t n_entries;                     // entries allocated (may pass max_entries: then dropped counts)
+  int32_t dropped;                       // 4-grams that found no room
+};
+struct NgramView {
+  NgramHeader* hdr;
+  int32_t* slots;                        // [1 << capacity_log2]
+  NgramEntry* entries;                   // [max_entries]
+};
+constexpr int kNgramHeaderBytes = 256;
+constexpr int kNgramMaxCapacityLog2 = 24;
+constexpr int kNgramMaxEntries = 262144; // 64 scan workgroups of 4096 entries
+constexpr int kNgramMaxK = 64;
+size_t ngram_table_bytes(int capacity_log2, int max_entries);
+// The layout of a table of capacity 2^capacity_log2 (host and device).
+__host__ __device__ inline NgramView ngram_view(void* table, int capacity_log2) {
+  char* b = static_cast<char*>(table);
+  NgramView v;
+  v.hdr = reinterpret_cast<NgramHeader*>(b);
+  v.slots = reinterpret_cast<int32_t*>(b + kNgramHeaderBytes);
+  v.entries = reinterpret_cast<NgramEntry*>(b + kNgramHeaderBytes + ((size_t(4) << capacity_log2) + 255) / 256 * 256);
+  return v;
+}
+size_t ngram_retrieve_workspace_bytes(int max_entries, int k);
+hipError_t launch_ngram_init(NgramView t, int capacity_log2, int max_entries, hipStream_t s);
+// These two read the table's layout from its header on the device.
+hipError_t launch_ngram_update(void* table, const int32_t* tokens, int64_t from, int64_t to, hipStream_t s);
+hipError_t launch_ngram_retrieve(void* table, int max_entries, const int32_t* first_tok, int k, int32_t* out_tok,
+                                 int32_t* out_count, int32_t* n_found, void* workspace, hipStream_t s);
+
 }  // namespace ts

@@ -21,6 +21,9 @@ stand in for them):
   (so that a handful of tokens pass min-p 0.1 and the repetition penalty
   changes draws), 4096 committed tokens half drawn from the hot ids, draft
   tokens from the hot ids on the tree + chains forest, u ~ U[0, 1) in fp32.
+* ``make_text``    a committed text for the 4-gram table: Zipf(1.2) token ids
+  over the vocabulary, with 30% of the 32-token blocks copied from earlier in
+  the text.
 
 bf16 tensors are carried as ``np.uint16`` bit patterns (round to nearest even
 from the fp32 draw); fp32 tensors as ``np.float32``.
@@ -274,6 +277,26 @@ def make_sample(name: str = "sample_llama8b", *, dtype: str = F32, V: int = VOCA
     u = ru.random(R, dtype=np.float32)
     return SampleCase(name, dtype, R, V, _encode(x, dtype), hist,
                       np.ascontiguousarray(parent, np.int32), draft_tok, u)
+
+
+def make_text(n: int, *, V: int = VOCAB, zipf: float = 1.2, copy_prob: float = 0.3, block: int = 32,
+              seed: int = 7) -> np.ndarray:
+    """A committed text of n tokens: Zipf-distributed ids (id = rank - 1, past V
+    folded back), and with probability `copy_prob` a 32-token block copied
+    from an earlier place in the text (the repetition that 4-gram retrieval
+    reuses)."""
+    rz, rc = _streams(seed, 2)
+    out = np.empty(n, np.int32)
+    pos = 0
+    while pos < n:
+        m = min(block, n - pos)
+        if pos >= block and rc.random() < copy_prob:
+            src = int(rc.integers(0, pos - m + 1))
+            out[pos:pos + m] = out[src:src + m]
+        else:
+            out[pos:pos + m] = (rz.zipf(zipf, m) - 1) % V
+        pos += m
+    return out
 
 
 def workload(name: str, *, L: Optional[int] = None, seed: Optional[int] = None):

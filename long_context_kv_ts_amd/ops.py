@@ -59,6 +59,12 @@ SIGNATURES = {
     "ts_sample_tokens": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_int,
                                   _c_int, ctypes.c_float, ctypes.c_float, ctypes.c_float, _c_void_p,
                                   _c_void_p, _c_int, _c_void_p, _c_size, _c_void_p]),
+    "ts_ngram_table_bytes": (_c_size, [_c_int, _c_int]),
+    "ts_ngram_init": (_c_int, [_c_void_p, _c_size, _c_int, _c_int, _c_void_p]),
+    "ts_ngram_update": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_i64, _c_void_p]),
+    "ts_ngram_retrieve_workspace": (_c_size, [_c_int, _c_int]),
+    "ts_ngram_retrieve": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_void_p, _c_size, _c_void_p]),
     "ts_partial_draft_attn_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int]),
     "ts_partial_draft_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                        _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_i64,
@@ -424,6 +430,57 @@ def sample_tokens(logits, *, hist=None, parent=None, draft_tok=None, window: int
                                   ptr(u) if temperature > 0 else None, tok.data_ptr(), _dtype_code(logits),
                                   workspace.data_ptr(), workspace.numel(), _stream(dev)))
     return tok
+
+
+class NgramTable:
+    """The 4-gram table of the committed text (ts_ngram_*), in one device buffer.
+
+    update(tokens, start, end) adds the 4-grams ending at positions start..end-1
+    of the committed text `tokens` (int32, device); retrieve(first_tok, k) gives
+    the k 4-grams starting with the device int32 first_tok[0], ranked by count
+    then recency."""
+
+    def __init__(self, device, capacity_log2: int = 18, max_entries: int = 131072):
+        nbytes = int(lib().ts_ngram_table_bytes(capacity_log2, max_entries))
+        if nbytes == 0:
+            raise TsError(TS_ERR_UNSUPPORTED, f"capacity_log2={capacity_log2} max_entries={max_entries}")
+        self.device = torch.device(device)
+        self.capacity_log2, self.max_entries = capacity_log2, max_entries
+        self.buf = alloc_workspace(nbytes, self.device)
+        self.reset()
+
+    def reset(self):
+        _check(lib().ts_ngram_init(self.buf.data_ptr(), self.buf.numel(), self.capacity_log2, self.max_entries,
+                                   _stream(self.device)))
+
+    def update(self, tokens, start: int, end: int):
+        _need(tokens, "tokens", 1, torch.int32, self.device)
+        _contig(tokens, "tokens")
+        if end > tokens.shape[0]:
+            raise ValueError(f"end={end} past the {tokens.shape[0]} tokens")
+        _check(lib().ts_ngram_update(self.buf.data_ptr(), tokens.data_ptr(), int(start), int(end),
+                                     _stream(self.device)))
+
+    def retrieve(self, first_tok, k: int = 20, *, out_tok=None, out_count=None, n_found=None, workspace=None):
+        _need(first_tok, "first_tok", 1, torch.int32, self.device)
+        dev = self.device
+        if out_tok is None:
+            out_tok = torch.empty((k, 4), dtype=torch.int32, device=dev)
+        if out_count is None:
+            out_count = torch.empty(k, dtype=torch.int32, device=dev)
+        if n_found is None:
+            n_found = torch.empty(1, dtype=torch.int32, device=dev)
+        if workspace is None:
+            workspace = alloc_workspace(int(lib().ts_ngram_retrieve_workspace(self.max_entries, k)), dev)
+        _check(lib().ts_ngram_retrieve(self.buf.data_ptr(), self.max_entries, first_tok.data_ptr(), int(k),
+                                       out_tok.data_ptr(), out_count.data_ptr(), n_found.data_ptr(),
+                                       workspace.data_ptr(), workspace.numel(), _stream(dev)))
+        return out_tok, out_count, n_found
+
+    def header(self) -> dict:
+        """The table's header (synchronises the stream)."""
+        h = self.buf[:16].view(torch.int32).cpu().tolist()
+        return dict(capacity_log2=h[0], max_entries=h[1], n_entries=h[2], dropped=h[3])
 
 
 def partial_draft_attn(q, k_part, v_part, k_new, v_new, *, scale=None, out=None, lse=None,

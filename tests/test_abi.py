@@ -240,6 +240,29 @@ def test_sample_rejects():
     assert "ts_sample_tokens" in _err()
 
 
+def test_ngram_rejects():
+    lib = ops.lib()
+    nb = lib.ts_ngram_table_bytes(18, 131072)
+    assert nb >= 256 + 4 * (1 << 18) + 24 * 131072 and nb % 256 == 0
+    assert lib.ts_ngram_table_bytes(3, 8) == 0 and lib.ts_ngram_table_bytes(25, 8) == 0
+    assert lib.ts_ngram_table_bytes(10, 2048) == 0                       # more entries than slots
+    assert lib.ts_ngram_table_bytes(20, 262145) == 0
+    assert lib.ts_ngram_init(P, nb, 18, 131072 * 3, None) == ops.TS_ERR_UNSUPPORTED
+    assert lib.ts_ngram_init(P + 16, nb, 18, 131072, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_ngram_init(P, nb - 256, 18, 131072, None) == ops.TS_ERR_WORKSPACE
+    assert lib.ts_ngram_update(None, P, 0, 10, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_ngram_update(P, P, 5, 4, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_ngram_update(P, None, 0, 10, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_ngram_update(P, P, 0, 1 << 31, None) == ops.TS_ERR_INVALID_ARG
+    ws = lib.ts_ngram_retrieve_workspace(131072, 20)
+    assert ws > 0 and lib.ts_ngram_retrieve_workspace(131072, 65) == 0
+    assert lib.ts_ngram_retrieve(P, 131072, P, 0, P, P, P, P, ws, None) == ops.TS_ERR_UNSUPPORTED
+    assert lib.ts_ngram_retrieve(P, 131072, P, 65, P, P, P, P, 1 << 20, None) == ops.TS_ERR_UNSUPPORTED
+    assert lib.ts_ngram_retrieve(P, 131072, None, 20, P, P, P, P, ws, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_ngram_retrieve(P, 131072, P, 20, P, P, P, P, ws - 4, None) == ops.TS_ERR_WORKSPACE
+    assert "ts_ngram_retrieve" in _err()
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "_lib", None)
     monkeypatch.setattr(ops, "_LIB_PATH", str(tmp_path / "missing.so"))
