@@ -59,7 +59,7 @@ const char* ts_last_error(void);
 int ts_abi_version(void);
 
 #define TS_ABI_VERSION 1
-#define TS_MAX_DRAFT 256 /* max draft tokens T of one verify call */
+#define TS_MAX_DRAFT 1024 /* max draft tokens T of one verify call */
 
 /* ------------------------------------------------------------------------
  * Tree-verify attention (tool listing, "How it works": one verification pass
@@ -88,7 +88,7 @@ int ts_abi_version(void);
  *            rounding). Must match the value given to the size query.
  *   workspace   >= ts_tree_verify_attn_workspace(...) bytes, 256-byte aligned;
  *            contents on entry are ignored.
- * Supported: T in [1, 256], Hq % Hkv == 0, Hq/Hkv <= 16, D in {64, 128}, L >= 0.
+ * Supported: T in [1, 1024], Hq % Hkv == 0, Hq/Hkv <= 16, D in {64, 128}, L >= 0.
  * ---------------------------------------------------------------------- */
 size_t ts_tree_verify_attn_workspace(int T, int Hq, int Hkv, int D, int64_t L,
                                      ts_dtype dtype, int num_splits);
@@ -203,7 +203,7 @@ ts_status ts_partial_draft_attn(const void* q, const void* k_part, const void* v
  *   node of depth d has k_{d+1} children. Nodes are numbered breadth-first,
  *   inside a depth in lexicographic order of the candidate ranks along the
  *   root path, so parent[t] < t and the result feeds ts_tree_verify_attn
- *   (which takes T <= 256) directly.
+ *   (which takes T <= 1024) directly.
  *   Written (device, int32): parent [T] (-1 for depth-0 nodes), draft_tok [T]
  *   (the node's candidate token), cand [depth][16] if not NULL (ranked
  *   candidates, -1 past k_d).
@@ -243,7 +243,7 @@ ts_status ts_build_draft_tree(const void* logits, int P, int V, const int32_t* s
  *   head g, and the same for V (bit-exact copies).
  *   k_cache, v_cache [Hkv][cache_stride][D]; k_draft, v_draft [Hkv][T][D].
  * Requires L + T <= cache_stride (room for the longest possible path).
- * Supported: T in [1, 256], D in {64, 128}. No workspace.
+ * Supported: T in [1, 1024], D in {64, 128}. No workspace.
  * ---------------------------------------------------------------------- */
 ts_status ts_accept_commit(const int32_t* parent, const int32_t* draft_tok, const int32_t* target_tok,
                            uint32_t rand_u32, int T, void* k_cache, void* v_cache, int64_t cache_stride,
@@ -280,7 +280,7 @@ ts_status ts_accept_commit(const int32_t* parent, const int32_t* draft_tok, cons
  *   tok        int32 [R] out: the smallest kept id whose cumulative kept
  *              probability (id order) exceeds u[r]; when rounding leaves
  *              u[r] at or past the end, the last kept id
- * Supported: V in [1, 1048576], T in [0, 256]. Workspace: at least
+ * Supported: V in [1, 1048576], T in [0, 1024]. Workspace: at least
  * ts_sample_workspace(R, V) bytes (272 bytes per row and 4096 logits),
  * 256-byte aligned, contents ignored on entry.
  * ---------------------------------------------------------------------- */

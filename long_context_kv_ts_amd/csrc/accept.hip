@@ -8,7 +8,7 @@
 // length, ordered by their last node's index, number rand % count is accepted;
 // its K/V rows move from the draft buffers into cache rows L .. L+n-1.
 //
-// One workgroup per (KV head, K or V). With at most 256 drafts the acceptance
+// One workgroup per (KV head, K or V). With at most 1024 drafts the acceptance
 // is a few hundred integer operations, so every workgroup computes it itself
 // (the forest and tokens are staged in LDS, thread t walks node t's ancestors
 // there) and then copies its own head's rows:
@@ -19,7 +19,7 @@
 namespace ts {
 namespace {
 
-constexpr int kThreads = 256;     // one thread per draft (TS_MAX_DRAFT)
+constexpr int kThreads = TS_MAX_DRAFT;     // one thread per draft
 constexpr int kWavesA = kThreads / kWave;
 
 __global__ __launch_bounds__(kThreads) void accept_commit_kernel(

@@ -116,7 +116,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   // plus an immediate (stage * tile bytes + row offsets), all below 64 KB
   __shared__ __attribute__((aligned(1024))) bf16_t Ks[kStages][Ly::tileElems];
   __shared__ __attribute__((aligned(1024))) bf16_t Vs[kStages][Ly::tileElems];
-  __shared__ uint32_t anc[TS_MAX_DRAFT * (TS_MAX_DRAFT / 32)];
+  // ancestor rows of this row group's drafts (at most 256 of them) and the staged forest
+  __shared__ uint32_t anc[kRowsPerGroup * (TS_MAX_DRAFT / 32)];
+  __shared__ int32_t s_par[TS_MAX_DRAFT];
 
   const AttnPlan& pl = a.plan;
   const int R = pl.n_rowgroups;
@@ -209,7 +211,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   for (int j = 0; j < 5; ++j) issue_upto(j);
 
   const int words = (T + 31) >> 5;
-  if (vt1 > pl.n_cache_tiles) build_ancestor_mask(a.parent, T, words, anc, tid, kThreads);
+  int t_lo, t_hi;
+  draft_rows_of(rg * kRowsPerGroup, min(pl.rows_per_head, (rg + 1) * kRowsPerGroup), G, T, t_lo, t_hi);
+  if (vt1 > pl.n_cache_tiles) build_ancestor_rows(a.parent, words, t_lo, t_hi, anc, s_par, tid, kThreads);
 
   // per-lane LDS addresses of the operand reads in stage 0
   uint32_t koff[Ly::KS], voff[Ly::DB];
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
       int key0, nvalid;
       const bool draft = tile_keys(vt0 + j, key0, nvalid);
       uint32_t bits = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
-      if (draft) bits &= row_ok ? anc[row_t * words + (key0 >> 5)] : 0u;
+      if (draft) bits &= row_ok ? anc[(row_t - t_lo) * words + (key0 >> 5)] : 0u;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = 8 * (e >> 2) + 4 * half + (e & 3);

@@ -29,6 +29,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define TS_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 constexpr int kThreads = 256;      // 4 independent waves
+constexpr int kSmallMaxDrafts = 16;  // this path serves heads of at most 16 query rows
 constexpr float kLazy = 8.0f;
 
 template <int D> struct SLayout {
@@ -56,7 +57,9 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void attn_split_small_kernel(AttnArgs a) {
   using Ly = SLayout<D>;
   __shared__ __attribute__((aligned(1024))) bf16_t Vs[4][Ly::tileElems];
-  __shared__ uint32_t anc[TS_MAX_DRAFT * (TS_MAX_DRAFT / 32)];
+  // at most 16 query rows per head reach this kernel, so at most 16 drafts: one mask word each
+  __shared__ uint32_t anc[kSmallMaxDrafts];
+  __shared__ int32_t s_par[kSmallMaxDrafts];
 
   const AttnPlan& pl = a.plan;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -69,8 +72,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_small_kernel(AttnArgs a) 
   // the mask is needed by the wave(s) whose range reaches the drafts
   const int last_split = min(blockIdx.x * 4 + 3, pl.n_splits - 1);
   const bool block_has_draft = (last_split + 1) * pl.tiles_per_split > pl.n_cache_tiles;
-  const int words = (T + 31) >> 5;
-  if (block_has_draft) build_ancestor_mask(a.parent, T, words, anc, tid, kThreads);
+  const int words = (T + 31) >> 5;                 // 1
+  if (block_has_draft) build_ancestor_rows(a.parent, words, 0, T, anc, s_par, tid, kThreads);
   if (split >= pl.n_splits) return;
 
   const int vt0 = split * pl.tiles_per_split;
@@ -219,6 +222,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_small_kernel(AttnArgs a) 
 }  // namespace
 
 hipError_t launch_attn_split_small(const AttnArgs& a, hipStream_t s) {
+  if (a.T > kSmallMaxDrafts || a.plan.rows_per_head > 16) return hipErrorInvalidValue;   // the plan never sends these
   dim3 grid((a.plan.n_splits + 3) / 4, a.Hkv);
   if (a.D == 128) attn_split_small_kernel<128><<<grid, kThreads, 0, s>>>(a);
   else attn_split_small_kernel<64><<<grid, kThreads, 0, s>>>(a);

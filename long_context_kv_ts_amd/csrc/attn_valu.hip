@@ -24,7 +24,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_valu_kernel(AttnArgs a) {
   __shared__ float Vs[kTile][D];
   __shared__ float Qs[kRows][D];
   __shared__ float Ps[kRows][kTile];
-  __shared__ uint32_t anc[TS_MAX_DRAFT * (TS_MAX_DRAFT / 32)];
+  __shared__ uint32_t anc[kRows * (TS_MAX_DRAFT / 32)];   // this workgroup's drafts (<= kRows)
+  __shared__ int32_t s_par[TS_MAX_DRAFT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rg = blockIdx.x, split = blockIdx.y, g = blockIdx.z;
@@ -45,7 +46,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_valu_kernel(AttnArgs a) {
   const int vt0 = split * pl.tiles_per_split;
   const int vt1 = min(vt0 + pl.tiles_per_split, pl.n_virtual);
   const int words = (T + 31) >> 5;
-  if (vt1 > pl.n_cache_tiles) build_ancestor_mask(a.parent, T, words, anc, tid, kThreads);
+  int t_lo, t_hi;
+  draft_rows_of(row0, min(pl.rows_per_head, row0 + kRows), G, T, t_lo, t_hi);
+  if (vt1 > pl.n_cache_tiles) build_ancestor_rows(a.parent, words, t_lo, t_hi, anc, s_par, tid, kThreads);
 
   float m[4], l[4], acc[4][DL];
 #pragma unroll
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_valu_kernel(AttnArgs a) {
       bool ok = lane < nvalid && row < pl.rows_per_head;
       if (draft && ok) {
         const int t = row / G, key = key0 + lane;
-        ok = (anc[t * words + (key >> 5)] >> (key & 31)) & 1u;
+        ok = (anc[(t - t_lo) * words + (key >> 5)] >> (key & 31)) & 1u;
       }
       s = ok ? s : -INFINITY;
       const float mt = wave_max(s);

@@ -64,17 +64,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Ancestor-or-self bitmask of the drafts, built in LDS from parent[]:
-// bit a of anc[t*words + a/32] is set iff a is t or an ancestor of t.
-// Entries of parent[] outside [-1, t) end the walk (treated as roots), so the
-// walk is bounded by t steps and never leaves [0, T). With parent == nullptr
-// the drafts form one causal chain (parent[t] = t - 1).
-__device__ __forceinline__ void build_ancestor_mask(const int32_t* parent, int T, int words,
-                                                    uint32_t* anc, int tid, int nthreads) {
-  for (int i = tid; i < T * words; i += nthreads) anc[i] = 0u;
+// Ancestor-or-self bitmask rows of the drafts t in [t_lo, t_hi), built in LDS:
+// bit a of anc[(t - t_lo) * words + a/32] is set iff a is t or an ancestor of
+// t. parent[0 .. t_hi) is first staged in LDS (s_par), so each walk chases
+// parents there. Entries of parent[] outside [-1, t) end the walk (treated as
+// roots), so a walk takes at most t steps and never leaves [0, T). With
+// parent == nullptr the drafts form one causal chain (parent[t] = t - 1) and
+// s_par is not used. Rows a workgroup does not own are never built.
+__device__ __forceinline__ void build_ancestor_rows(const int32_t* parent, int words, int t_lo, int t_hi,
+                                                    uint32_t* anc, int32_t* s_par, int tid, int nthreads) {
+  const int n = t_hi - t_lo;
+  for (int i = tid; i < n * words; i += nthreads) anc[i] = 0u;
+  if (parent != nullptr)
+    for (int t = tid; t < t_hi; t += nthreads) s_par[t] = parent[t];
   __syncthreads();
-  for (int t = tid; t < T; t += nthreads) {
-    uint32_t* row = anc + t * words;
+  for (int t = t_lo + tid; t < t_hi; t += nthreads) {
+    uint32_t* row = anc + (t - t_lo) * words;
     if (parent == nullptr) {
       for (int w = 0; w < words; ++w) {
         int lo = w * 32;
@@ -87,12 +92,18 @@ __device__ __forceinline__ void build_ancestor_mask(const int32_t* parent, int T
       int a = t;
       while (a >= 0) {
         row[a >> 5] |= 1u << (a & 31);
-        int p = parent[a];
+        int p = s_par[a];
         a = (p >= 0 && p < a) ? p : -1;
       }
     }
   }
   __syncthreads();
+}
+
+// Draft rows [t_lo, t_hi) behind query rows [row0, row1) of one KV head (row = t * G + h).
+__device__ __forceinline__ void draft_rows_of(int row0, int row1, int G, int T, int& t_lo, int& t_hi) {
+  t_lo = row0 / G;
+  t_hi = row1 > row0 ? min(T, (row1 - 1) / G + 1) : t_lo;
 }
 
 // ----------------------------------------------------------------------------

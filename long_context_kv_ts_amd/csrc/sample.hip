@@ -57,21 +57,26 @@ struct PickLds {
 };
 
 // The window loads of one thread, issued ahead of the logits: the forest
-// entry tid and up to 4 of the last min(n_hist, W) committed tokens.
+// entries tid + 256 k and up to 4 of the last min(n_hist, W) committed tokens.
 constexpr int kHistRegs = 4;
+constexpr int kDraftRegs = TS_MAX_DRAFT / kThreads;   // forest entries a thread stages
 struct WindowRegs {
-  int par, dtok;
+  int par[kDraftRegs], dtok[kDraftRegs];
   int hist[kHistRegs];
 };
 
 __device__ __forceinline__ void window_prefetch(const SampleArgs& a, int r, WindowRegs& w) {
   const int tid = threadIdx.x;
   const bool walk = r > 0 && a.window > 0;
-  w.par = -1;
-  w.dtok = 0;
-  if (walk && tid < a.T) {                      // T <= kThreads
-    w.par = a.parent[tid];
-    w.dtok = a.draft_tok[tid];
+#pragma unroll
+  for (int k = 0; k < kDraftRegs; ++k) {
+    const int t = tid + k * kThreads;
+    w.par[k] = -1;
+    w.dtok[k] = 0;
+    if (walk && t < a.T) {
+      w.par[k] = a.parent[t];
+      w.dtok[k] = a.draft_tok[t];
+    }
   }
   const int nh = min(a.n_hist, a.window);
   const int h0 = a.n_hist - nh;
@@ -90,9 +95,13 @@ __device__ void mark_window(const SampleArgs& a, int r, int i0, int i1, Lds& s, 
   const int nw = (i1 - i0 + 31) >> 5;
   for (int k = tid; k < nw; k += kThreads) s.bits[k] = 0u;
   const bool walk = r > 0 && a.window > 0;
-  if (walk && tid < a.T) {
-    s.par[tid] = w.par;
-    s.dtok[tid] = w.dtok;
+#pragma unroll
+  for (int k = 0; k < kDraftRegs; ++k) {
+    const int t = tid + k * kThreads;
+    if (walk && t < a.T) {
+      s.par[t] = w.par[k];
+      s.dtok[t] = w.dtok[k];
+    }
   }
   __syncthreads();
   if (walk && tid == 0) {

@@ -144,8 +144,10 @@ def chain_parents(n_chains: int, length: int, base: int) -> np.ndarray:
     return out
 
 
-def tree_plus_chains_parents(rng: np.random.Generator) -> np.ndarray:
-    tree = tree_parents(TREE_SHAPE, rng)
+def tree_plus_chains_parents(rng: np.random.Generator, shape: Sequence[int] = TREE_SHAPE) -> np.ndarray:
+    """The candidate tree `shape` (shuffled within levels) followed by the
+    4-gram chains; [1,9,9,9] gives 820 + 80 = 900 drafts."""
+    tree = tree_parents(shape, rng)
     chains = chain_parents(NGRAM_TOPK, GAMMA, base=len(tree))
     return np.concatenate([tree, chains]).astype(np.int32)
 

@@ -59,7 +59,7 @@ def _err():
 
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(T=0), ops.TS_ERR_UNSUPPORTED, "T=0"),
-    (dict(T=257), ops.TS_ERR_UNSUPPORTED, "T=257"),
+    (dict(T=1025), ops.TS_ERR_UNSUPPORTED, "T=1025"),
     (dict(Hq=30), ops.TS_ERR_INVALID_ARG, "multiple"),
     (dict(Hq=32 * 17, Hkv=1), ops.TS_ERR_UNSUPPORTED, "group size"),
     (dict(D=96), ops.TS_ERR_UNSUPPORTED, "D=96"),
@@ -172,7 +172,7 @@ def test_accept_commit_rejects():
         return lib.ts_accept_commit(*[args[n] for n in names])
 
     assert call(T=0) == ops.TS_ERR_INVALID_ARG
-    assert call(T=257) == ops.TS_ERR_INVALID_ARG
+    assert call(T=1025, stride=102400 + 1025) == ops.TS_ERR_INVALID_ARG
     assert call(D=96) == ops.TS_ERR_UNSUPPORTED
     assert call(stride=102400 + 119) == ops.TS_ERR_INVALID_ARG      # no room for T rows after L
     assert call(L=-1) == ops.TS_ERR_INVALID_ARG
@@ -222,7 +222,7 @@ def test_sample_rejects():
                                     min_p, u, tok, dtype, wsp, wsb, None)
     bad = ops.TS_ERR_INVALID_ARG
     assert call(R=120) == bad                                   # R != T + 1
-    assert call(T=257, R=258) == bad
+    assert call(T=1025, R=1026) == bad
     assert call(V=(1 << 20) + 1) == ops.TS_ERR_UNSUPPORTED
     assert call(V=0) == ops.TS_ERR_UNSUPPORTED
     assert call(logits=None) == bad

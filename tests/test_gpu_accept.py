@@ -120,6 +120,22 @@ def test_single_draft_and_full_chain():
     assert run_case(np.arange(-1, T - 1), draft, target, 99, L=0, extra=0, label="chain 256") == T
 
 
+@pytest.mark.parametrize("T", [257, 900, 1024])
+def test_large_forests(T):
+    """Past 256 drafts (the [1,9,9,9] tree with chains has 900): random forests
+    over a two-token vocabulary, and a chain of every draft."""
+    rng = np.random.default_rng(T)
+    parent = np.array([int(rng.integers(-1, t)) if t else -1 for t in range(T)], np.int32)
+    draft = rng.integers(0, 2, T).astype(np.int32)
+    target = rng.integers(0, 2, T + 1).astype(np.int32)
+    for rand in (0, int(rng.integers(0, 2**32))):
+        run_case(parent, draft, target, rand, D=128, seed=T, label=f"forest T={T} rand={rand}")
+    chain = np.arange(-1, T - 1, dtype=np.int32)
+    tok = (np.arange(T, dtype=np.int32) * 7) % 5000
+    assert run_case(chain, tok, np.concatenate([tok, [1]]).astype(np.int32), 5, L=3, extra=0,
+                    label=f"chain {T}") == T
+
+
 def test_full_size_cache():
     """LLaMA3.1-8B layer: 8 KV heads, 102,400 cached tokens, bf16; the commit
     writes only rows L..L+n-1 (the comparison covers the whole cache)."""

@@ -148,6 +148,15 @@ def test_deep_chain_window_from_the_path():
         min_p=0.05, u=c.u, label="chain 256, W=64")
 
 
+def test_901_rows_of_the_largest_tree():
+    """The [1,9,9,9] tree with 20 chains: 900 drafts, 901 rows to sample."""
+    parent = inputs.tree_plus_chains_parents(np.random.default_rng(2), shape=(1, 9, 9, 9))
+    c = inputs.make_sample(dtype="bf16", V=32000, parent=parent, seed=13)
+    assert c.R == 901
+    run(c.logits, "bf16", c.hist, c.parent, c.draft_tok, window=1024, penalty=1.2, temperature=1.0,
+        min_p=0.1, u=c.u, label="901 rows")
+
+
 def test_reused_workspace_with_garbage():
     ws = ops.alloc_workspace(int(ops.lib().ts_sample_workspace(257, 300000)), DEV)
     ws.fill_(0x7F)

@@ -101,3 +101,22 @@ def test_many_slices_and_reused_workspace():
         assert np.array_equal(parent.cpu().numpy(), rp) and np.array_equal(tok.cpu().numpy(), rt), f"V={V}"
         for d, k in enumerate(shape):
             assert cand[d, :k].cpu().tolist() == rc[d].tolist(), f"V={V} cand[{d}]"
+
+
+def test_largest_tree_feeds_verify():
+    """[1,9,9,9]: the 820-node tree built on the GPU drives the verify call past
+    256 drafts, against the oracle."""
+    from gpu_util import check_attn
+    from oracle import verify_attn_ref
+    rng = np.random.default_rng(19)
+    logits = rng.standard_normal((4, 3000)).astype(np.float32)
+    parent, _ = check(logits, [1, 9, 9, 9], "f32", "[1,9,9,9] for verify")
+    par = parent.cpu().numpy().astype(np.int32)
+    assert len(par) == 820
+    c = inputs.make_verify("tree1999", dtype="bf16", Hq=8, Hkv=2, D=128, L=600, seed=21, with_chains=False,
+                           parent=par)
+    out, lse = ops.tree_verify_attn(to_dev(c.q, "bf16"), to_dev(c.k_cache, "bf16"), to_dev(c.v_cache, "bf16"),
+                                    to_dev(c.k_draft, "bf16"), to_dev(c.v_draft, "bf16"), parent, scale=c.scale)
+    torch.cuda.synchronize()
+    ro, rl = verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, par, c.scale, "bf16")
+    check_attn(out, lse, ro, rl, "bf16", "verify on the built [1,9,9,9] tree")

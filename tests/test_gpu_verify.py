@@ -104,7 +104,7 @@ def test_head_shapes(shape):
     check_attn(out, lse, ro, rl, c.dtype, str(shape))
 
 
-@pytest.mark.parametrize("T", [1, 2, 64, 65, 256])
+@pytest.mark.parametrize("T", [1, 2, 64, 65, 256, 257, 900, 1024])
 def test_draft_counts(T):
     say(f"[T] T={T}")
     rng = np.random.default_rng(T)
@@ -123,6 +123,34 @@ def test_deep_chain_256():
     ro, rl = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, c.parent, c.scale, "bf16")
     out, lse = run_verify(c)
     check_attn(out, lse, ro, rl, "bf16", "chain256")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (2, 2)])
+def test_deep_chain_1024(Hq, Hkv):
+    """1024 drafts in one causal chain; with one query head per KV head a
+    256-row workgroup owns 256 drafts whose root walks run up to 1023 steps."""
+    say(f"[T] one causal chain of 1024 drafts, Hq={Hq} Hkv={Hkv}")
+    parent = np.arange(-1, 1023, dtype=np.int32)
+    c = inputs.make_verify("chain1k", dtype="bf16", Hq=Hq, Hkv=Hkv, D=128, L=333, seed=4, with_chains=False,
+                           parent=parent)
+    ro, rl = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, c.parent, c.scale, "bf16")
+    out, lse = run_verify(c)
+    check_attn(out, lse, ro, rl, "bf16", "chain1024")
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 8, 2, 128), ("bf16", 2, 2, 64), ("f32", 4, 1, 64)])
+def test_tree_1_9_9_9_plus_chains(dtype, Hq, Hkv, D):
+    """The summary page's largest tree shape, [1,9,9,9] (820 nodes), with the
+    20 four-token chains: 900 drafts under the ancestor mask."""
+    parent = inputs.tree_plus_chains_parents(np.random.default_rng(11), shape=(1, 9, 9, 9))
+    assert len(parent) == 900
+    say(f"[T] [1,9,9,9] + chains, {dtype} Hq={Hq} Hkv={Hkv} D={D}")
+    c = inputs.make_verify("t1999", dtype=dtype, Hq=Hq, Hkv=Hkv, D=D, L=1000, seed=12, with_chains=False,
+                           parent=parent)
+    ro, rl = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, c.parent, c.scale, dtype)
+    for ns in (0, 5):
+        out, lse = run_verify(c, num_splits=ns)
+        check_attn(out, lse, ro, rl, dtype, f"[1,9,9,9] splits={ns}")
 
 
 def test_out_of_range_parents_are_roots():
