@@ -99,6 +99,30 @@ def test_topk_ties_and_edges():
                                       err_msg=f"values n={n} k={k}")
 
 
+def test_topk_narrow_ranges_and_low_bit_keys():
+    """Scores that share sign, exponent and leading mantissa bits (as one head's
+    importance scores do), keys that differ only in their last mantissa bits, and
+    sizes around one wave, one 1024-thread round and the 4096-element limit of
+    the register-resident variant."""
+    say("[topk] narrow ranges, low-bit keys, variant boundaries")
+    rng = np.random.default_rng(5)
+    for n in (1, 63, 64, 65, 1023, 1024, 1025, 1600, 2047, 2048, 2049, 4095, 4096, 4097):
+        for kind in range(3):
+            if kind == 0:
+                s = 0.09 + 0.014 * rng.standard_normal((4, n))
+            elif kind == 1:
+                s = np.float32(0.3) + np.float32(3e-8) * rng.integers(0, 6, (4, n))
+            else:
+                s = np.float32(-1.5) - np.float32(1e-7) * rng.integers(0, 40, (4, n))
+            s = s.astype(np.float32)
+            for k in sorted({1, min(n, 64), min(n, 65), n}):
+                idx, val = ops.kv_topk_select(torch.from_numpy(s).cuda(), k)
+                torch.cuda.synchronize()
+                ref_idx, _ = oracle.topk_ref(s.astype(np.float64), k)
+                np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx, err_msg=f"n={n} k={k} kind={kind}")
+                np.testing.assert_array_equal(val.cpu().numpy(), np.take_along_axis(s, ref_idx, 1))
+
+
 def test_topk_negative_and_infinite_scores():
     s = np.array([[-1.0, -np.inf, 3.0, np.inf, -2.5, 3.0, -0.0, 0.0]], np.float32)
     idx, _ = ops.kv_topk_select(torch.from_numpy(s).cuda(), 4)
