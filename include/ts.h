@@ -88,7 +88,9 @@ int ts_abi_version(void);
  *            rounding). Must match the value given to the size query.
  *   workspace   >= ts_tree_verify_attn_workspace(...) bytes, 256-byte aligned;
  *            contents on entry are ignored.
- * Supported: T in [1, 1024], Hq % Hkv == 0, Hq/Hkv <= 16, D in {64, 128}, L >= 0.
+ * Supported: T in [1, 1024], Hq in [1, 4096], Hq % Hkv == 0, Hq/Hkv <= 16,
+ *            D in {64, 128}, 0 <= L <= 2^30, and one launch's worth of
+ *            (split, KV head, row group) units (TS_ERR_UNSUPPORTED beyond).
  * ---------------------------------------------------------------------- */
 size_t ts_tree_verify_attn_workspace(int T, int Hq, int Hkv, int D, int64_t L,
                                      ts_dtype dtype, int num_splits);

@@ -2,6 +2,7 @@
 // Nothing here allocates device memory or synchronises; every check runs on
 // the host before the first HIP call, so a rejected call has no side effect.
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -45,7 +46,7 @@ ts_status check_attn_shape(const char* fn, int T, int Hq, int Hkv, int D, int64_
   if (Hq < 1 || Hkv < 1) return fail(TS_ERR_INVALID_ARG, "%s: Hq=%d Hkv=%d must be >= 1", fn, Hq, Hkv);
   if (Hq % Hkv != 0) return fail(TS_ERR_INVALID_ARG, "%s: Hq=%d not a multiple of Hkv=%d", fn, Hq, Hkv);
   if (Hq / Hkv > 16) return fail(TS_ERR_UNSUPPORTED, "%s: group size Hq/Hkv=%d > 16", fn, Hq / Hkv);
-  if (Hkv > 65535) return fail(TS_ERR_UNSUPPORTED, "%s: Hkv=%d > 65535", fn, Hkv);
+  if (Hq > 4096) return fail(TS_ERR_UNSUPPORTED, "%s: Hq=%d > 4096", fn, Hq);
   if (D != 64 && D != 128) return fail(TS_ERR_UNSUPPORTED, "%s: D=%d (supported: 64, 128)", fn, D);
   if (L < 0) return fail(TS_ERR_INVALID_ARG, "%s: L=%lld < 0", fn, (long long)L);
   if (L > (int64_t)1 << 30) return fail(TS_ERR_UNSUPPORTED, "%s: L=%lld > 2^30", fn, (long long)L);
@@ -132,12 +133,18 @@ static ts_status attn_common(const char* fn, const void* q, const void* kc, cons
   if (cache_stride < L) return fail(TS_ERR_INVALID_ARG, "%s: cache_stride=%lld < L=%lld", fn, (long long)cache_stride, (long long)L);
   if (!std::isfinite(scale) || scale == 0.f) return fail(TS_ERR_INVALID_ARG, "%s: scale must be finite and non-zero", fn);
 
+  const AttnPlan plan = plan_attention(T, Hq, Hkv, D, L, dtype, num_splits);
+  // one workgroup per (split, KV head, row group), rounded up to a multiple of 8 per row group
+  if (((int64_t)plan.n_splits * Hkv + 7) / 8 * 8 * plan.n_rowgroups > INT32_MAX)
+    return fail(TS_ERR_UNSUPPORTED, "%s: %d splits x %d KV heads x %d row groups exceed one launch", fn,
+                plan.n_splits, Hkv, plan.n_rowgroups);
+
   AttnArgs a{};
   a.q = q; a.kc = kc; a.vc = vc; a.cache_stride = cache_stride; a.kd = kd; a.vd = vd;
   a.parent = parent; a.o_part = o_part; a.l_part = l_part;
   a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D; a.L = L;
   a.scale_log2 = scale * kLog2e;
-  a.plan = plan_attention(T, Hq, Hkv, D, L, dtype, num_splits);
+  a.plan = plan;
   hipError_t e = a.plan.path == kPathMfma    ? launch_attn_split_mfma(a, stream)
                  : a.plan.path == kPathSmall ? launch_attn_split_small(a, stream)
                                              : launch_attn_split_valu(a, dtype, stream);

@@ -63,6 +63,8 @@ def _err():
     (dict(Hq=30), ops.TS_ERR_INVALID_ARG, "multiple"),
     (dict(Hq=32 * 17, Hkv=1), ops.TS_ERR_UNSUPPORTED, "group size"),
     (dict(D=96), ops.TS_ERR_UNSUPPORTED, "D=96"),
+    (dict(Hq=8192, Hkv=1024), ops.TS_ERR_UNSUPPORTED, "Hq=8192"),
+    (dict(L=(1 << 30) + 1, stride=(1 << 30) + 1), ops.TS_ERR_UNSUPPORTED, "2^30"),
     (dict(L=-1), ops.TS_ERR_INVALID_ARG, "L=-1"),
     (dict(stride=100), ops.TS_ERR_INVALID_ARG, "cache_stride"),
     (dict(q=None), ops.TS_ERR_INVALID_ARG, "null"),
@@ -106,6 +108,11 @@ def test_partials_and_merge_reject():
     lib = ops.lib()
     st = lib.ts_tree_verify_attn_partials(P, P, P, 64, P, P, None, P, P, 4, 4, 1, 64, 64, 0.1, F, 0, None)
     assert st == ops.TS_ERR_INVALID_ARG and "parent" in _err()
+    # fp32 rows go 16 to a workgroup: 65535 splits x 256 KV heads x 1024 row groups is
+    # more workgroups than one launch holds
+    st = lib.ts_tree_verify_attn_partials(P, P, P, 1 << 30, P, P, P, P, P, 1024, 4096, 256, 128, 1 << 30,
+                                          0.1, F, 65535, None)
+    assert st == ops.TS_ERR_UNSUPPORTED and "one launch" in _err(), _err()
     assert lib.ts_attn_merge(P, P, 0, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
     assert lib.ts_attn_merge(P, P, 2, 10, 100, P, P, B, None) == ops.TS_ERR_UNSUPPORTED
     assert lib.ts_attn_merge(None, P, 2, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
