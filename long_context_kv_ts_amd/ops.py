@@ -5,10 +5,14 @@ current HIP stream; every step of the computation runs in the library's
 kernels. There is no fallback: if the library is missing or a call fails, an
 exception is raised.
 
-Entry points (same names as the C functions, without the ``ts_`` prefix where
-noted): ``tree_verify_attn``, ``tree_verify_attn_partials``, ``attn_merge``,
-``kv_importance_score``, ``kv_topk_select``, ``kv_gather``,
-``partial_draft_attn``.
+Entry points, named as the C functions without the ``ts_`` prefix:
+
+* verify and partial-cache step: ``tree_verify_attn``, ``tree_verify_attn_partials``,
+  ``attn_merge``, ``kv_importance_score``, ``kv_topk_select``, ``kv_gather``,
+  ``partial_draft_attn``;
+* decode step around them: ``build_draft_tree`` (with ``draft_tree_nodes``),
+  ``sample_tokens``, ``accept_commit``, and the ``NgramTable`` class over
+  ``ts_ngram_init`` / ``ts_ngram_update`` / ``ts_ngram_retrieve``.
 """
 from __future__ import annotations
 
