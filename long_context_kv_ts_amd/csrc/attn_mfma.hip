@@ -61,7 +61,6 @@ constexpr int kThreads = 512;
 constexpr int kWaves = 8;
 constexpr int kRowsPerGroup = kWaves * 32;
 constexpr int kKeys = 32;
-constexpr int kStages = 7;
 constexpr float kLazy = 8.0f;
 
 template <int D> struct Layout {
@@ -109,16 +108,22 @@ __device__ __forceinline__ float sum_xor32(float x) {
 
 template <bool B> using Flag = std::integral_constant<bool, B>;
 
-template <int D>
+// kStages-deep ring of K/V tiles; kMaxT drafts at most. Eight stages fit next to
+// the mask of up to 256 drafts, seven next to the mask of up to 1024.
+template <int D, int kStages, int kMaxT>
 __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a) {
   using Ly = Layout<D>;
+  // tiles issued ahead of the one being computed: the ring minus the tile being
+  // read and the one being published
+  constexpr int kAhead = kStages - 2;
   // K tiles of every stage, then V tiles: operand reads are a per-lane base
   // plus an immediate (stage * tile bytes + row offsets), all below 64 KB
+  static_assert((kStages - 1) * Layout<D>::tileElems * 2 + 24 * D * 2 < 65536, "ds_read offset");
   __shared__ __attribute__((aligned(1024))) bf16_t Ks[kStages][Ly::tileElems];
   __shared__ __attribute__((aligned(1024))) bf16_t Vs[kStages][Ly::tileElems];
   // ancestor rows of this row group's drafts (at most 256 of them) and the staged forest
-  __shared__ uint32_t anc[kRowsPerGroup * (TS_MAX_DRAFT / 32)];
-  __shared__ int32_t s_par[TS_MAX_DRAFT];
+  __shared__ uint32_t anc[kRowsPerGroup * (kMaxT / 32)];
+  __shared__ int32_t s_par[kMaxT];
 
   const AttnPlan& pl = a.plan;
   const int R = pl.n_rowgroups;
@@ -186,7 +191,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   // wait until tile j has landed; younger tiles may stay in flight
   auto wait_for = [&](int j) {
     const int after = issued - 1 - j;
-    if (after >= 4) __builtin_amdgcn_s_waitcnt(0x0F70 | (4 * Ly::loadsPerWave));
+    if (after >= 5) __builtin_amdgcn_s_waitcnt(0x0F70 | (5 * Ly::loadsPerWave));
+    else if (after == 4) __builtin_amdgcn_s_waitcnt(0x0F70 | (4 * Ly::loadsPerWave));
     else if (after == 3) __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * Ly::loadsPerWave));
     else if (after == 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * Ly::loadsPerWave));
     else if (after == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | Ly::loadsPerWave);
@@ -207,8 +213,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
 #pragma unroll
     for (int ks = 0; ks < Ly::KS; ++ks) asm volatile("" : : "v"(qf[ks]));
   }
-  // tiles 0..4 start streaming (Q has already landed)
-  for (int j = 0; j < 5; ++j) issue_upto(j);
+  // tiles 0..kAhead-1 start streaming (Q has already landed)
+  for (int j = 0; j < kAhead; ++j) issue_upto(j);
 
   const int words = (T + 31) >> 5;
   int t_lo, t_hi;
@@ -337,10 +343,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   // (if j+1 < nb_u), Vf = V(j-1) and P = P(j-1) (if j >= 1).
   auto iter = [&](auto prev, auto next, int j) {
     constexpr bool kPrev = decltype(prev)::value, kNext = decltype(next)::value;
-    // publish tile j+2, start tile j+5
+    // publish tile j+2, start tile j+kAhead
     wait_for(j + 2);
-    __syncthreads();                    // every wave is past iteration j-1: tile j-1 is free
-    issue_upto(j + 5);
+    __syncthreads();                    // every wave is past iteration j-1: tile j-2 is free
+    issue_upto(j + kAhead);
     f32x16_t Sn;
     if constexpr (kNext) qk(Sn);
     if constexpr (kPrev) pv(P);
@@ -362,18 +368,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
     if constexpr (kNext) S = Sn;
   };
 
-  // Steady-state iteration j (1 <= j, j + 5 < nb_u), stage U = j % kStages known
-  // at compile time: tiles j+2..j+4 are in flight, tile j+5 is a full cache
-  // tile. The barrier needs no LDS drain: the stage it recycles (tile j-2) was
-  // last read two iterations ago and those reads were consumed by products.
-  const bf16_t* cache_next = cache_base + (int64_t)(vt0 + 5) * kKeys * D;   // tile 5 onwards
+  // Steady-state iteration j (1 <= j, j + kAhead < nb_u), stage U = j % kStages
+  // known at compile time: tiles j+2..j+kAhead-1 are in flight, tile j+kAhead is
+  // a full cache tile. The barrier needs no LDS drain: the stage it recycles
+  // (tile j-2) was last read two iterations ago and those reads were consumed
+  // by products.
+  const bf16_t* cache_next = cache_base + (int64_t)(vt0 + kAhead) * kKeys * D;
   auto fast = [&](auto ust, int j) {
     constexpr int U = decltype(ust)::value;
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * Ly::loadsPerWave));        // tile j+2 landed
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ((kAhead - 3) * Ly::loadsPerWave));   // tile j+2 landed
     asm volatile("s_barrier" : : : "memory");
     {
-      const bf16_t* base = cache_next + (int64_t)j * kKeys * D;         // tile j+5
-      const uint32_t sb = my_lds + (uint32_t)(((U + 5) % kStages) * kTileBytes);
+      const bf16_t* base = cache_next + (int64_t)j * kKeys * D;         // tile j+kAhead
+      const uint32_t sb = my_lds + (uint32_t)(((U + kAhead) % kStages) * kTileBytes);
 #pragma unroll
       for (int n = 0; n < Ly::loadsPerWave; ++n) {
         const int q = wave * Ly::loadsPerWave + n;
@@ -419,15 +426,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
     else {
       iter(Flag<false>{}, Flag<true>{}, 0);
       int j = 1;
-      for (; j + kStages <= nb_u - 5; j += kStages) {       // j % kStages == 1
-        fast(std::integral_constant<int, 1>{}, j);
-        fast(std::integral_constant<int, 2>{}, j + 1);
-        fast(std::integral_constant<int, 3>{}, j + 2);
-        fast(std::integral_constant<int, 4>{}, j + 3);
-        fast(std::integral_constant<int, 5>{}, j + 4);
-        fast(std::integral_constant<int, 6>{}, j + 5);
-        fast(std::integral_constant<int, 0>{}, j + 6);
-        issued = j + kStages + 5;
+      for (; j + kStages <= nb_u - kAhead; j += kStages) {  // j % kStages == 1
+        fast(std::integral_constant<int, 1 % kStages>{}, j);
+        fast(std::integral_constant<int, 2 % kStages>{}, j + 1);
+        fast(std::integral_constant<int, 3 % kStages>{}, j + 2);
+        fast(std::integral_constant<int, 4 % kStages>{}, j + 3);
+        fast(std::integral_constant<int, 5 % kStages>{}, j + 4);
+        fast(std::integral_constant<int, 6 % kStages>{}, j + 5);
+        fast(std::integral_constant<int, 7 % kStages>{}, j + 6);
+        if constexpr (kStages == 8) fast(std::integral_constant<int, 0>{}, j + 7);
+        issued = j + kStages + kAhead;
       }
       for (; j < nb_u - 1; ++j) iter(Flag<true>{}, Flag<true>{}, j);
       iter(Flag<true>{}, Flag<false>{}, nb_u - 1);
@@ -438,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   for (int j = nb_u; j < nb; ++j) {
     wait_for(j);
     __syncthreads();                    // tile j visible; every wave is past tile j - 1
-    issue_upto(j + 4);
+    issue_upto(j + kAhead - 1);
     read_k(j);
     qk(S);
     float al;
@@ -476,8 +484,14 @@ hipError_t launch_attn_split_mfma(const AttnArgs& a, hipStream_t s) {
   const int R = a.plan.n_rowgroups;
   const int n_units = a.plan.n_splits * a.Hkv;
   const int blocks = ((n_units + 7) / 8) * 8 * R;
-  if (a.D == 128) attn_split_mfma_kernel<128><<<blocks, kThreads, 0, s>>>(a);
-  else attn_split_mfma_kernel<64><<<blocks, kThreads, 0, s>>>(a);
+  // up to 256 drafts: an 8-stage ring (tiles issued 6 ahead); more: 7 stages
+  if (a.T <= 256) {
+    if (a.D == 128) attn_split_mfma_kernel<128, 8, 256><<<blocks, kThreads, 0, s>>>(a);
+    else attn_split_mfma_kernel<64, 8, 256><<<blocks, kThreads, 0, s>>>(a);
+  } else {
+    if (a.D == 128) attn_split_mfma_kernel<128, 7, TS_MAX_DRAFT><<<blocks, kThreads, 0, s>>>(a);
+    else attn_split_mfma_kernel<64, 7, TS_MAX_DRAFT><<<blocks, kThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
