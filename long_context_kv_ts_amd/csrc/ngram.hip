@@ -6,10 +6,11 @@
 // only grows and "reached an empty slot" proves the key absent.
 //
 // Update (one 1024-thread workgroup, positions in chunks of 1024): thread q
-// takes the 4-gram ending at position c+q, finds in LDS whether an earlier
-// position of the chunk holds the same 4-gram (then it stays silent) and how
-// many do (its multiplicity, the last of them its last position). Keys
-// inserted concurrently are therefore distinct: a new entry is written and
+// takes the 4-gram ending at position c+q and claims it in an LDS hash table
+// of the chunk's 4-grams (2048 slots, linear probing, compare-and-swap): the
+// thread that claims a 4-gram owns it, and every thread holding it adds one to
+// the owner's multiplicity and raises its last position. Only owners insert,
+// so keys inserted concurrently are distinct: a new entry is written and
 // fenced before a compare-and-swap publishes its id in an empty slot, a lost
 // swap means another key took the slot, and probing continues. No thread ever
 // waits for another. Probing stops after `capacity` slots; an entry that
@@ -27,6 +28,7 @@ namespace ts {
 namespace {
 
 constexpr int kUpdThreads = 1024;
+constexpr int kUpdSlots = 2 * kUpdThreads;              // the chunk's LDS hash table, at most half full
 constexpr int kRetThreads = 256;
 constexpr int kRetPerThread = 16;
 constexpr int kRetPerWG = kRetThreads * kRetPerThread;          // 4096 entries a scan workgroup
@@ -107,6 +109,8 @@ __device__ void insert(NgramView t, int4 key, int m, int last) {
 __global__ __launch_bounds__(kUpdThreads) void ngram_update_kernel(void* table, const int32_t* __restrict__ tokens,
                                                                    int64_t from, int64_t to) {
   __shared__ int4 s_key[kUpdThreads];
+  __shared__ int s_slot[kUpdSlots];            // owner thread of the 4-gram hashed there, or -1
+  __shared__ int s_mult[kUpdThreads], s_last[kUpdThreads];
   const NgramView t = ngram_view(table, static_cast<const NgramHeader*>(table)->capacity_log2);
   const int q = threadIdx.x;
   for (int64_t c = from < 3 ? 3 : from; c < to; c += kUpdThreads) {
@@ -117,20 +121,34 @@ __global__ __launch_bounds__(kUpdThreads) void ngram_update_kernel(void* table, 
       key = make_int4(w[0], w[1], w[2], w[3]);
       s_key[q] = key;
     }
+    for (int i = q; i < kUpdSlots; i += kUpdThreads) s_slot[i] = -1;
+    s_mult[q] = 0;
+    s_last[q] = -1;
     __syncthreads();
+    int owner = -1;
     if (q < n) {
-      bool first = true;
-      int m = 0, last_q = q;
-      for (int i = 0; i < n; ++i) {
-        if (same(s_key[i], key)) {
-          first = first && i >= q;
-          ++m;
-          last_q = i;                           // positions grow with i
+      // claim the 4-gram or find the thread that did: n <= half the slots, so an
+      // empty slot is always reached
+      for (uint32_t h = ngram_hash(key) & (kUpdSlots - 1);; h = (h + 1) & (kUpdSlots - 1)) {
+        int cur = s_slot[h];
+        if (cur < 0) {
+          cur = atomicCAS(&s_slot[h], -1, q);
+          if (cur < 0) {
+            owner = q;
+            break;
+          }
+        }
+        if (same(s_key[cur], key)) {
+          owner = cur;
+          break;
         }
       }
-      if (first) insert(t, key, m, (int)(c + last_q));
+      atomicAdd(&s_mult[owner], 1);
+      atomicMax(&s_last[owner], q);
     }
-    __syncthreads();                            // the next chunk reuses s_key and sees these entries
+    __syncthreads();
+    if (q < n && owner == q) insert(t, key, s_mult[q], (int)(c + s_last[q]));
+    __syncthreads();                            // the next chunk reuses the LDS tables and sees these entries
   }
 }
 
