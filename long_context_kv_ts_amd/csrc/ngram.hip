@@ -10,9 +10,10 @@
 // of the chunk's 4-grams (2048 slots, linear probing, compare-and-swap): the
 // thread that claims a 4-gram owns it, and every thread holding it adds one to
 // the owner's multiplicity and raises its last position. Only owners insert,
-// so keys inserted concurrently are distinct: a new entry is written and
-// fenced before a compare-and-swap publishes its id in an empty slot, a lost
-// swap means another key took the slot, and probing continues. No thread ever
+// so keys inserted concurrently are distinct: an absent key's wave takes
+// consecutive entry ids with one atomic, the entry is written and fenced
+// before a compare-and-swap publishes its id in an empty slot, a lost swap
+// means another key took the slot, and probing continues. No thread ever
 // waits for another. Probing stops after `capacity` slots; an entry that
 // cannot be placed is counted in the header and left with count 0.
 //
@@ -57,8 +58,16 @@ __device__ __forceinline__ int load_acq(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ int load_relaxed(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The key of an entry whose id was read with load_acq: that acquire orders these
+// plain loads after the publisher's fence (entries are 8-byte aligned).
 __device__ __forceinline__ int4 entry_key(const NgramEntry* e) {
-  return make_int4(load_acq(&e->tok[0]), load_acq(&e->tok[1]), load_acq(&e->tok[2]), load_acq(&e->tok[3]));
+  const int2 a = *reinterpret_cast<const int2*>(&e->tok[0]);
+  const int2 b = *reinterpret_cast<const int2*>(&e->tok[2]);
+  return make_int4(a.x, a.y, b.x, b.y);
 }
 
 __global__ __launch_bounds__(256) void ngram_init_kernel(NgramView t, int capacity_log2, int max_entries) {
@@ -68,41 +77,62 @@ __global__ __launch_bounds__(256) void ngram_init_kernel(NgramView t, int capaci
   if (blockIdx.x == 0 && threadIdx.x == 0) *t.hdr = NgramHeader{capacity_log2, max_entries, 0, 0};
 }
 
-__device__ void insert(NgramView t, int4 key, int m, int last) {
+// Called by every thread of the update workgroup (`active` marks the owners of
+// distinct 4-grams), so the entry allocation is one atomic per wave:
+//   1. probe to the key (then add to its count and last position) or to the
+//      first empty slot, which proves the key absent (no other thread of the
+//      launch inserts the same key);
+//   2. the wave's absent keys take consecutive entry ids with one atomicAdd;
+//   3. each writes and fences its entry, then publishes its id with a
+//      compare-and-swap at that slot or, if another key took it meanwhile, at
+//      the next empty one.
+__device__ void insert(NgramView t, int4 key, int m, int last, bool active) {
   const uint32_t cap = 1u << t.hdr->capacity_log2, mask = cap - 1u;
   const int max_entries = t.hdr->max_entries;
-  int mine = -1;
-  uint32_t s = ngram_hash(key) & mask;
-  for (uint32_t probe = 0; probe < cap; ++probe, s = (s + 1u) & mask) {
-    const int cur = load_acq(&t.slots[s]);
-    if (cur >= 0) {
+  uint32_t s = ngram_hash(key) & mask, probe = 0;
+  bool absent = false;
+  if (active) {
+    for (; probe < cap; ++probe, s = (s + 1u) & mask) {
+      const int cur = load_acq(&t.slots[s]);
+      if (cur < 0) {
+        absent = true;
+        break;
+      }
       NgramEntry* e = t.entries + cur;
       if (same(entry_key(e), key)) {
         atomicAdd(&e->count, m);
         atomicMax(&e->last, last);
-        return;
+        break;
       }
-      continue;
     }
-    if (mine < 0) {                            // the key is absent: an entry of our own
-      mine = atomicAdd(&t.hdr->n_entries, 1);
-      if (mine >= max_entries) {
-        atomicAdd(&t.hdr->dropped, 1);
-        return;
-      }
-      NgramEntry* e = t.entries + mine;
-      e->tok[0] = key.x;
-      e->tok[1] = key.y;
-      e->tok[2] = key.z;
-      e->tok[3] = key.w;
-      e->count = m;
-      e->last = last;
-      __threadfence();
-    }
-    if (atomicCAS(&t.slots[s], -1, mine) == -1) return;
-    // another key took this slot in the same chunk: keep probing
+    if (probe == cap) atomicAdd(&t.hdr->dropped, 1);     // full table, key absent
   }
-  if (mine >= 0) t.entries[mine].count = 0;     // never published; retrieval skips it
+  const uint64_t want = __ballot(absent);
+  if (want == 0) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int leader = __ffsll((unsigned long long)want) - 1;
+  int base = 0;
+  if (lane == leader) base = atomicAdd(&t.hdr->n_entries, __popcll(want));
+  base = __shfl(base, leader, kWave);
+  if (!absent) return;
+  const int mine = base + __popcll(want & ((1ull << lane) - 1ull));
+  if (mine >= max_entries) {
+    atomicAdd(&t.hdr->dropped, 1);
+    return;
+  }
+  NgramEntry* e = t.entries + mine;
+  e->tok[0] = key.x;
+  e->tok[1] = key.y;
+  e->tok[2] = key.z;
+  e->tok[3] = key.w;
+  e->count = m;
+  e->last = last;
+  __threadfence();
+  for (; probe < cap; ++probe, s = (s + 1u) & mask) {
+    if (load_relaxed(&t.slots[s]) >= 0) continue;               // another key's slot
+    if (atomicCAS(&t.slots[s], -1, mine) == -1) return;
+  }
+  e->count = 0;                                                 // never published; retrieval skips it
   atomicAdd(&t.hdr->dropped, 1);
 }
 
@@ -147,7 +177,8 @@ __global__ __launch_bounds__(kUpdThreads) void ngram_update_kernel(void* table, 
       atomicMax(&s_last[owner], q);
     }
     __syncthreads();
-    if (q < n && owner == q) insert(t, key, s_mult[q], (int)(c + s_last[q]));
+    const bool own = q < n && owner == q;
+    insert(t, key, own ? s_mult[q] : 0, own ? (int)(c + s_last[q]) : 0, own);
     __syncthreads();                            // the next chunk reuses the LDS tables and sees these entries
   }
 }
