@@ -140,8 +140,8 @@ ts_status ts_attn_merge(const float* o_part, const float* l_part, int n_parts,
  *   q_recent [R][Hq][D]            the R most recent queries (R = gamma = 4)
  *   k_cache  [Hkv][cache_stride][D] rows [0, L) read; V is never read
  *   scores   [Hkv][L/chunk] fp32
- * Supported: L % chunk == 0, chunk in [1, 4096], R*(Hq/Hkv) <= 64, Hq/Hkv in
- * {1,2,4,8,16}, D in {64,128}.
+ * Supported: L % chunk == 0, chunk in [1, 4096], R*(Hq/Hkv) <= 64,
+ * Hq/Hkv <= 16, D in {64,128}.
  * ---------------------------------------------------------------------- */
 ts_status ts_kv_importance_score(const void* q_recent, const void* k_cache, int64_t cache_stride,
                                  float* scores, int R, int Hq, int Hkv, int D, int64_t L,

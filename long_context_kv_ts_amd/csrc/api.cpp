@@ -239,7 +239,7 @@ ts_status ts_kv_importance_score(const void* q_recent, const void* k_cache, int6
   if (R < 1 || Hq < 1 || Hkv < 1) return fail(TS_ERR_INVALID_ARG, "%s: R, Hq, Hkv must be >= 1", fn);
   if (Hq % Hkv) return fail(TS_ERR_INVALID_ARG, "%s: Hq=%d not a multiple of Hkv=%d", fn, Hq, Hkv);
   const int G = Hq / Hkv;
-  if (G > 16 || (G & (G - 1))) return fail(TS_ERR_UNSUPPORTED, "%s: group size %d not a power of two <= 16", fn, G);
+  if (G > 16) return fail(TS_ERR_UNSUPPORTED, "%s: group size %d > 16", fn, G);
   if (R * G > 64) return fail(TS_ERR_UNSUPPORTED, "%s: R*G=%d > 64", fn, R * G);
   if (Hkv > 65535) return fail(TS_ERR_UNSUPPORTED, "%s: Hkv=%d > 65535", fn, Hkv);
   if (D != 64 && D != 128) return fail(TS_ERR_UNSUPPORTED, "%s: D=%d (supported: 64, 128)", fn, D);

@@ -9,7 +9,11 @@
 // against all R*G query rows are one v_mfma_f32_16x16x32_bf16 chain per 16
 // rows, computed transposed (S^T = K Q^T) so that the K operand is loaded
 // straight from HBM into registers in the lane layout the instruction wants
-// and never passes through LDS. Each wave owns one chunk at a time.
+// and never passes through LDS. Each wave owns one chunk at a time. With G a
+// power of two a query's G heads are G aligned adjacent columns and their max
+// is a lane butterfly; other G (5, 6, 7 ... 15) pass the block's scores
+// through a per-wave LDS tile and each lane takes the max over its query's G
+// rows for one (query, key) pair.
 // fp32 (or other shapes): vector-ALU path with the query rows in LDS.
 #include "common.h"
 
@@ -57,6 +61,26 @@ __global__ __launch_bounds__(256) void importance_valu_kernel(
   if (lane == 0) scores[(int64_t)g * n_chunks + c] = tot / (float)(chunk * R);
 }
 
+// Rows x keys of one 16-key block, per wave (the padding column keeps the
+// transposed writes off a single bank).
+struct ScoreTile {
+  float v[64][17];
+};
+
+// Sum over the R queries and the block's valid keys of the max over each
+// query's G rows, from the tile (general G).
+__device__ __forceinline__ float tile_group_max_sum(const ScoreTile& t, int R, int G, int nkeys, int lane) {
+  float tot = 0.f;
+  for (int p = lane; p < R * 16; p += kWave) {
+    const int r = p >> 4, key = p & 15;
+    if (key >= nkeys) continue;
+    float v = -INFINITY;
+    for (int h = 0; h < G; ++h) v = fmaxf(v, t.v[r * G + h][key]);
+    tot += v;
+  }
+  return tot;
+}
+
 // ---------------------------------------------------------------------------
 // matrix-core path (bf16)
 //
@@ -67,11 +91,16 @@ __global__ __launch_bounds__(256) void importance_valu_kernel(
 // The reduction order over D is free, so reduction step ks of a lane takes
 // dims 32*ks + 8*(l/16) .. +7, i.e. 64 contiguous bytes per key per step.
 // ---------------------------------------------------------------------------
-template <int D, int NRB>
+template <int D, int NRB, bool kPow2>
 __global__ __launch_bounds__(256) void importance_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, int64_t stride,
     float* __restrict__ scores, int R, int Hq, int Hkv, int chunk, float scale, int n_chunks) {
   constexpr int KS = D / 32;                  // reduction steps per 16x16 block
+  ScoreTile* tiles = nullptr;                 // general G only: one tile per wave
+  if constexpr (!kPow2) {
+    __shared__ ScoreTile t[4];
+    tiles = t;
+  }
   const int g = blockIdx.y, G = Hq / Hkv, rows = R * G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, quad = lane >> 4;
@@ -116,17 +145,23 @@ __global__ __launch_bounds__(256) void importance_mfma_kernel(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[rb][ks], s, 0, 0, 0);
-        // s[i]: key kb + 4*quad + i, query row rb*16 + col. Max over the G heads
-        // of a recent query = max over G adjacent columns (lanes).
+        // s[i]: key kb + 4*quad + i, query row rb*16 + col
+        if constexpr (kPow2) {
+          // max over the G heads of a recent query = max over G adjacent columns (lanes)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[i] * scale;
-          for (int o = 1; o < G; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-          const int row = rb * 16 + col;
-          const bool head0 = (row % G) == 0 && row < rows && (kb + 4 * quad + i) < chunk;
-          tot += head0 ? v : 0.f;
+          for (int i = 0; i < 4; ++i) {
+            float v = s[i] * scale;
+            for (int o = 1; o < G; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+            const int row = rb * 16 + col;
+            const bool head0 = (row % G) == 0 && row < rows && (kb + 4 * quad + i) < chunk;
+            tot += head0 ? v : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tiles[wave].v[rb * 16 + col][4 * quad + i] = s[i] * scale;
         }
       }
+      if constexpr (!kPow2) tot += tile_group_max_sum(tiles[wave], R, G, min(16, chunk - kb), lane);
     }
     tot = wave_sum(tot);
     if (lane == 0) scores[(int64_t)g * n_chunks + c] = tot / (float)(chunk * R);
@@ -136,11 +171,16 @@ __global__ __launch_bounds__(256) void importance_mfma_kernel(
 // 64-token chunks: the whole chunk's K (16 KB) is requested before any
 // product, so each wave keeps 16 loads in flight instead of walking the chunk
 // one 16-key block at a time.
-template <int D, int NRB>
+template <int D, int NRB, bool kPow2>
 __global__ __launch_bounds__(256) void importance_mfma64_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, int64_t stride,
     float* __restrict__ scores, int R, int Hq, int Hkv, float scale, int n_chunks) {
   constexpr int KS = D / 32, CHUNK = 64, NKB = CHUNK / 16;
+  ScoreTile* tiles = nullptr;                 // general G only: one tile per wave
+  if constexpr (!kPow2) {
+    __shared__ ScoreTile t[4];
+    tiles = t;
+  }
   const int g = blockIdx.y, G = Hq / Hkv, rows = R * G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, quad = lane >> 4;
@@ -178,49 +218,61 @@ __global__ __launch_bounds__(256) void importance_mfma64_kernel(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][ks], qb[rb][ks], s, 0, 0, 0);
-        // s[i]: key 16*kb + 4*quad + i, query row rb*16 + col; max over the G
-        // heads of a recent query = max over G adjacent columns (lanes)
-        const int row = rb * 16 + col;
-        const bool head0 = (row % G) == 0 && row < rows;
+        // s[i]: key 16*kb + 4*quad + i, query row rb*16 + col
+        if constexpr (kPow2) {
+          // max over the G heads of a recent query = max over G adjacent columns (lanes)
+          const int row = rb * 16 + col;
+          const bool head0 = (row % G) == 0 && row < rows;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[i] * scale;
-          for (int o = 1; o < G; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-          tot += head0 ? v : 0.f;
+          for (int i = 0; i < 4; ++i) {
+            float v = s[i] * scale;
+            for (int o = 1; o < G; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+            tot += head0 ? v : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tiles[wave].v[rb * 16 + col][4 * quad + i] = s[i] * scale;
         }
       }
+      if constexpr (!kPow2) tot += tile_group_max_sum(tiles[wave], R, G, 16, lane);
     }
     tot = wave_sum(tot);
     if (lane == 0) scores[(int64_t)g * n_chunks + c] = tot * inv;
   }
 }
 
-template <int D>
-hipError_t launch_mfma(const bf16_t* q, const bf16_t* kc, int64_t stride, float* scores, int R,
-                       int Hq, int Hkv, int chunk, float scale, int n_chunks, hipStream_t s) {
+template <int D, bool kPow2>
+hipError_t launch_mfma_g(const bf16_t* q, const bf16_t* kc, int64_t stride, float* scores, int R,
+                         int Hq, int Hkv, int chunk, float scale, int n_chunks, hipStream_t s) {
   const int rows = R * (Hq / Hkv);
-  // enough waves to keep ~64 KB of K loads in flight per CU; each wave strides
-  // over chunks of its KV head
   // one chunk per wave (waves stride over chunks only past 65535 workgroups)
   int blocks_x = (n_chunks + 3) / 4;
   if (blocks_x > 65535) blocks_x = 65535;
   dim3 grid(blocks_x, Hkv);
   if (chunk == 64) {
     if (rows <= 16)
-      importance_mfma64_kernel<D, 1><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, scale, n_chunks);
+      importance_mfma64_kernel<D, 1, kPow2><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, scale, n_chunks);
     else if (rows <= 32)
-      importance_mfma64_kernel<D, 2><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, scale, n_chunks);
+      importance_mfma64_kernel<D, 2, kPow2><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, scale, n_chunks);
     else
-      importance_mfma64_kernel<D, 4><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, scale, n_chunks);
+      importance_mfma64_kernel<D, 4, kPow2><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, scale, n_chunks);
     return hipGetLastError();
   }
   if (rows <= 16)
-    importance_mfma_kernel<D, 1><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, chunk, scale, n_chunks);
+    importance_mfma_kernel<D, 1, kPow2><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, chunk, scale, n_chunks);
   else if (rows <= 32)
-    importance_mfma_kernel<D, 2><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, chunk, scale, n_chunks);
+    importance_mfma_kernel<D, 2, kPow2><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, chunk, scale, n_chunks);
   else
-    importance_mfma_kernel<D, 4><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, chunk, scale, n_chunks);
+    importance_mfma_kernel<D, 4, kPow2><<<grid, 256, 0, s>>>(q, kc, stride, scores, R, Hq, Hkv, chunk, scale, n_chunks);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mfma(const bf16_t* q, const bf16_t* kc, int64_t stride, float* scores, int R,
+                       int Hq, int Hkv, int chunk, float scale, int n_chunks, hipStream_t s) {
+  const int G = Hq / Hkv;
+  if ((G & (G - 1)) == 0) return launch_mfma_g<D, true>(q, kc, stride, scores, R, Hq, Hkv, chunk, scale, n_chunks, s);
+  return launch_mfma_g<D, false>(q, kc, stride, scores, R, Hq, Hkv, chunk, scale, n_chunks, s);
 }
 
 }  // namespace

@@ -131,7 +131,7 @@ def test_draft_attn_rejects():
     (dict(L=1000), ops.TS_ERR_UNSUPPORTED),          # not a multiple of chunk
     (dict(chunk=0), ops.TS_ERR_UNSUPPORTED),
     (dict(R=17), ops.TS_ERR_UNSUPPORTED),            # R*G > 64
-    (dict(Hq=24), ops.TS_ERR_UNSUPPORTED),           # G = 3 not a power of two
+    (dict(Hq=136), ops.TS_ERR_UNSUPPORTED),          # G = 17 > 16
     (dict(D=80), ops.TS_ERR_UNSUPPORTED),
     (dict(q=None), ops.TS_ERR_INVALID_ARG),
     (dict(k=MIS), ops.TS_ERR_INVALID_ARG),

@@ -48,7 +48,18 @@ def partial_case(L=None, seed=None):
 @pytest.mark.parametrize("L", [102400, 8192])
 def test_partial_step_full(L):
     say(f"[partial step] L={L}")
-    p = partial_case(L)
+    check_partial_step(partial_case(L))
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(28, 4), (12, 2), (40, 8)])
+def test_partial_step_qwen_group_sizes(Hq, Hkv):
+    """Qwen2.5-7B (28 query heads, 4 KV heads: G = 7), -1.5B (G = 6) and -14B (G = 5)
+    group sizes: the importance max then spans groups that are not a power of two."""
+    say(f"[partial step] Hq={Hq} Hkv={Hkv} G={Hq // Hkv}")
+    check_partial_step(inputs.make_partial(f"qwen_g{Hq // Hkv}", Hq=Hq, Hkv=Hkv, L=16384, seed=Hq))
+
+
+def check_partial_step(p):
     q, kc, vc = to_dev(p.q, "bf16"), to_dev(p.k_cache, "bf16"), to_dev(p.v_cache, "bf16")
     scores = ops.kv_importance_score(q, kc, p.chunk, scale=p.scale)
     idx, val = ops.kv_topk_select(scores, p.k)
@@ -138,7 +149,13 @@ def test_importance_shapes():
                                           (4, 32, 32, 128, 2048, 64, "bf16"),   # MHA
                                           (2, 16, 2, 64, 1920, 48, "bf16"),     # G=8, ragged 16-key block
                                           (3, 8, 2, 128, 1000, 40, "bf16"),
-                                          (4, 8, 2, 64, 1024, 64, "f32")):
+                                          (4, 28, 4, 128, 4096, 64, "bf16"),    # G=7 (Qwen2.5-7B)
+                                          (4, 12, 2, 128, 2048, 64, "bf16"),    # G=6
+                                          (4, 40, 8, 64, 1920, 40, "bf16"),     # G=5, chunk 40: ragged last 16-key block
+                                          (5, 36, 12, 128, 1000, 40, "bf16"),   # G=3, R=5
+                                          (5, 24, 2, 128, 2048, 64, "bf16"),    # G=12: 60 rows, 4 row blocks
+                                          (4, 15, 1, 64, 1024, 64, "bf16"),     # G=15
+                                          (4, 28, 4, 64, 1024, 64, "f32")):
         q = rng.standard_normal((R, Hq, D)).astype(np.float32)
         k = (rng.standard_normal((Hkv, L, D)) / np.sqrt(D)).astype(np.float32)
         if dt == "bf16":

@@ -93,6 +93,8 @@ def test_cache_prefix_view_never_reads_past_L():
 @pytest.mark.parametrize("shape", [
     dict(dtype="bf16", Hq=4, Hkv=4, D=128),     # MHA, one row per token
     dict(dtype="bf16", Hq=16, Hkv=2, D=64),     # G=8, D=64
+    dict(dtype="bf16", Hq=28, Hkv=4, D=128),    # G=7 (Qwen2.5-7B): 840 rows, 4 row groups
+    dict(dtype="bf16", Hq=40, Hkv=8, D=128),    # G=5 (Qwen2.5-14B)
     dict(dtype="f32", Hq=8, Hkv=2, D=128),
     dict(dtype="f32", Hq=16, Hkv=1, D=64),      # G=16
 ])
