@@ -68,7 +68,7 @@ AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype
   if (dtype == TS_BF16) p.path = p.rows_per_head > 16 ? kPathMfma : kPathSmall;
   else p.path = kPathValu;
   (void)D;
-  p.rows_per_group = p.path == kPathMfma ? mfma_rows_per_group() : p.path == kPathSmall ? 16 : kValuRows;
+  p.rows_per_group = p.path == kPathMfma ? mfma_rows_per_group(p.rows_per_head) : p.path == kPathSmall ? 16 : kValuRows;
   p.n_rowgroups = (p.rows_per_head + p.rows_per_group - 1) / p.rows_per_group;
   p.tile = p.path == kPathMfma ? mfma_tile_keys() : kTile;
   p.n_cache_tiles = (int)((L + p.tile - 1) / p.tile);

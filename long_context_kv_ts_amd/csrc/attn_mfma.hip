@@ -57,13 +57,14 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define TS_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int kThreads = 512;
-constexpr int kWaves = 8;
-constexpr int kRowsPerGroup = kWaves * 32;
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding (vmcnt is split over bits 3:0 and 15:14; lgkmcnt and expcnt left
+// at their maxima)
+constexpr int vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 constexpr int kKeys = 32;
 constexpr float kLazy = 8.0f;
 
-template <int D> struct Layout {
+template <int D, int kWaves> struct Layout {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int CH = D / 8;
@@ -73,10 +74,8 @@ template <int D> struct Layout {
   static constexpr int rowsPerLoad = 1024 / (D * 2);
 };
 
-template <int D> __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & (Layout<D>::CH - 1)); }
-template <int D> __device__ __forceinline__ int v_chunk(int r, int c) {
-  return c ^ ((4 * (r & 3)) & (Layout<D>::CH - 1));
-}
+template <int D> __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & (D / 8 - 1)); }
+template <int D> __device__ __forceinline__ int v_chunk(int r, int c) { return c ^ ((4 * (r & 3)) & (D / 8 - 1)); }
 
 __device__ __forceinline__ void lds_dma16(const bf16_t* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -85,9 +84,9 @@ __device__ __forceinline__ void lds_dma16(const bf16_t* base, uint32_t voff, uin
                : "memory", "m0");
 }
 
-template <int D>
+template <int D, int kWaves>
 __device__ __forceinline__ uint32_t dma_offset(int wave, int n, int lane, int nvalid) {
-  using Ly = Layout<D>;
+  using Ly = Layout<D, kWaves>;
   const int q = wave * Ly::loadsPerWave + n;
   const bool isv = q >= Ly::loadsPerTensor;
   const int mblk = isv ? q - Ly::loadsPerTensor : q;
@@ -109,16 +108,23 @@ __device__ __forceinline__ float sum_xor32(float x) {
 template <bool B> using Flag = std::integral_constant<bool, B>;
 
 // kStages-deep ring of K/V tiles; kMaxT drafts at most. Eight stages fit next to
-// the mask of up to 256 drafts, seven next to the mask of up to 1024.
-template <int D, int kStages, int kMaxT>
-__global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a) {
-  using Ly = Layout<D>;
+// the mask of up to 256 drafts, seven next to the mask of up to 1024. kWaves
+// waves of 32 rows each: 8 (two per SIMD), or 4 when a KV head has at most 128
+// rows (one query head per KV head), which would leave half of 8 waves idle.
+// Registers are budgeted for two waves per SIMD in both forms (8 / kWaves
+// workgroups a CU): one wave per SIMD may take 512 registers, and the compiler
+// then parks values in AGPRs and moves them back and forth in the loop.
+template <int D, int kStages, int kMaxT, int kWaves>
+__global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void attn_split_mfma_kernel(AttnArgs a) {
+  constexpr int kThreads = kWaves * 64;
+  constexpr int kRowsPerGroup = kWaves * 32;
+  using Ly = Layout<D, kWaves>;
   // tiles issued ahead of the one being computed: the ring minus the tile being
   // read and the one being published
   constexpr int kAhead = kStages - 2;
   // K tiles of every stage, then V tiles: operand reads are a per-lane base
   // plus an immediate (stage * tile bytes + row offsets), all below 64 KB
-  static_assert((kStages - 1) * Layout<D>::tileElems * 2 + 24 * D * 2 < 65536, "ds_read offset");
+  static_assert((kStages - 1) * Ly::tileElems * 2 + 24 * D * 2 < 65536, "ds_read offset");
   __shared__ __attribute__((aligned(1024))) bf16_t Ks[kStages][Ly::tileElems];
   __shared__ __attribute__((aligned(1024))) bf16_t Vs[kStages][Ly::tileElems];
   // ancestor rows of this row group's drafts (at most 256 of them) and the staged forest
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   const bf16_t* draft_base = static_cast<const bf16_t*>(wave_v ? a.vd : a.kd) + (int64_t)g * T * D;
   uint32_t off_full[Ly::loadsPerWave];
 #pragma unroll
-  for (int n = 0; n < Ly::loadsPerWave; ++n) off_full[n] = dma_offset<D>(wave, n, lane, kKeys);
+  for (int n = 0; n < Ly::loadsPerWave; ++n) off_full[n] = dma_offset<D, kWaves>(wave, n, lane, kKeys);
   const uint32_t k_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TS_LDS(void, &Ks[0][0])));
   const uint32_t v_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TS_LDS(void, &Vs[0][0])));
   constexpr uint32_t kTileBytes = Ly::tileElems * 2;
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
     } else {
 #pragma unroll
       for (int n = 0; n < Ly::loadsPerWave; ++n)
-        lds_dma16(base, dma_offset<D>(wave, n, lane, nvalid), lds_of(n));
+        lds_dma16(base, dma_offset<D, kWaves>(wave, n, lane, nvalid), lds_of(n));
     }
   };
   // tiles [0, issued) of this split have been issued (uniform)
@@ -191,12 +197,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   // wait until tile j has landed; younger tiles may stay in flight
   auto wait_for = [&](int j) {
     const int after = issued - 1 - j;
-    if (after >= 5) __builtin_amdgcn_s_waitcnt(0x0F70 | (5 * Ly::loadsPerWave));
-    else if (after == 4) __builtin_amdgcn_s_waitcnt(0x0F70 | (4 * Ly::loadsPerWave));
-    else if (after == 3) __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * Ly::loadsPerWave));
-    else if (after == 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * Ly::loadsPerWave));
-    else if (after == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | Ly::loadsPerWave);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (after >= 5) __builtin_amdgcn_s_waitcnt(vm_wait(5 * Ly::loadsPerWave));
+    else if (after == 4) __builtin_amdgcn_s_waitcnt(vm_wait(4 * Ly::loadsPerWave));
+    else if (after == 3) __builtin_amdgcn_s_waitcnt(vm_wait(3 * Ly::loadsPerWave));
+    else if (after == 2) __builtin_amdgcn_s_waitcnt(vm_wait(2 * Ly::loadsPerWave));
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(vm_wait(Ly::loadsPerWave));
+    else __builtin_amdgcn_s_waitcnt(vm_wait(0));
   };
 
   // ---- Q operand: lane holds row `col` of this wave's 32-row block -----------
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
   const bf16_t* cache_next = cache_base + (int64_t)(vt0 + kAhead) * kKeys * D;
   auto fast = [&](auto ust, int j) {
     constexpr int U = decltype(ust)::value;
-    __builtin_amdgcn_s_waitcnt(0x0F70 | ((kAhead - 3) * Ly::loadsPerWave));   // tile j+2 landed
+    __builtin_amdgcn_s_waitcnt(vm_wait((kAhead - 3) * Ly::loadsPerWave));    // tile j+2 landed
     asm volatile("s_barrier" : : : "memory");
     {
       const bf16_t* base = cache_next + (int64_t)j * kKeys * D;         // tile j+kAhead
@@ -476,23 +482,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_mfma_kernel(AttnArgs a
 
 }  // namespace
 
-int mfma_rows_per_group() { return kRowsPerGroup; }
+int mfma_rows_per_group(int rows_per_head) { return rows_per_head <= 128 ? 128 : 256; }
 int mfma_tile_keys() { return kKeys; }
 int mfma_groups_per_cu() { return 1; }
+
+template <int kWaves>
+hipError_t launch_waves(const AttnArgs& a, int blocks, hipStream_t s) {
+  constexpr int kThreads = kWaves * 64;
+  // up to 256 drafts: an 8-stage ring (tiles issued 6 ahead); more: 7 stages.
+  // The 4-wave form serves at most 128 rows per KV head, so at most 128 drafts.
+  if (kWaves == 4 && a.T > 128) return hipErrorInvalidValue;
+  if (kWaves == 4 || a.T <= 256) {
+    if (a.D == 128) attn_split_mfma_kernel<128, 8, 256, kWaves><<<blocks, kThreads, 0, s>>>(a);
+    else attn_split_mfma_kernel<64, 8, 256, kWaves><<<blocks, kThreads, 0, s>>>(a);
+  } else if constexpr (kWaves == 8) {
+    if (a.D == 128) attn_split_mfma_kernel<128, 7, TS_MAX_DRAFT, kWaves><<<blocks, kThreads, 0, s>>>(a);
+    else attn_split_mfma_kernel<64, 7, TS_MAX_DRAFT, kWaves><<<blocks, kThreads, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_split_mfma(const AttnArgs& a, hipStream_t s) {
   const int R = a.plan.n_rowgroups;
   const int n_units = a.plan.n_splits * a.Hkv;
   const int blocks = ((n_units + 7) / 8) * 8 * R;
-  // up to 256 drafts: an 8-stage ring (tiles issued 6 ahead); more: 7 stages
-  if (a.T <= 256) {
-    if (a.D == 128) attn_split_mfma_kernel<128, 8, 256><<<blocks, kThreads, 0, s>>>(a);
-    else attn_split_mfma_kernel<64, 8, 256><<<blocks, kThreads, 0, s>>>(a);
-  } else {
-    if (a.D == 128) attn_split_mfma_kernel<128, 7, TS_MAX_DRAFT><<<blocks, kThreads, 0, s>>>(a);
-    else attn_split_mfma_kernel<64, 7, TS_MAX_DRAFT><<<blocks, kThreads, 0, s>>>(a);
-  }
-  return hipGetLastError();
+  return a.plan.rows_per_group == 128 ? launch_waves<4>(a, blocks, s) : launch_waves<8>(a, blocks, s);
 }
 
 }  // namespace ts

@@ -143,7 +143,7 @@ struct AttnArgs {
 AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype, int num_splits);
 
 // Work decomposition of the matrix-core kernel (defined next to it).
-int mfma_rows_per_group();
+int mfma_rows_per_group(int rows_per_head);   // 256, or 128 when a KV head has at most 128 rows
 int mfma_groups_per_cu();
 int mfma_tile_keys();
 
