@@ -106,7 +106,7 @@ def test_head_shapes(shape):
     check_attn(out, lse, ro, rl, c.dtype, str(shape))
 
 
-@pytest.mark.parametrize("T", [1, 2, 64, 65, 256, 257, 900, 1024])
+@pytest.mark.parametrize("T", [1, 2, 5, 32, 33, 64, 65, 256, 257, 900, 1024])
 def test_draft_counts(T):
     say(f"[T] T={T}")
     rng = np.random.default_rng(T)
