@@ -26,7 +26,7 @@ SOURCES = ["api.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_small.hip", "attn_
 # consumes NaN (masked scores are -inf, every exp2 argument is finite or -inf),
 # so it is built without NaN semantics: maxima of matrix-core results then need
 # no quieting instruction and fuse into v_max3_f32.
-EXTRA_FLAGS = {"attn_mfma.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {"attn_mfma.hip": ["-fno-honor-nans"], "sample.hip": ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:

@@ -411,6 +411,7 @@ ts_status ts_sample_tokens(const void* logits, int R, int V, const int32_t* hist
   a.T = T;
   a.window = window;
   a.theta = penalty;
+  a.inv_theta = (float)(1.0 / (double)penalty);
   // greedy keeps s2 = 0; a tiny temperature saturates at a finite scale so that 0 * s2 stays 0
   a.s2 = temperature > 0.0f ? (float)std::fmin(1.4426950408889634 / (double)temperature, 1e30) : 0.0f;
   // greedy: the cut sits at the maximum, so the kept tokens are the maxima
@@ -422,6 +423,7 @@ ts_status ts_sample_tokens(const void* logits, int R, int V, const int32_t* hist
   a.nb = sample_subslices(V);
   a.sub = static_cast<SampleSub*>(workspace);
   a.cand = reinterpret_cast<SampleCand*>(a.sub + (size_t)R * a.nb);
+  a.wbits = reinterpret_cast<uint32_t*>(a.cand + (size_t)R * a.nb * kSampleList);
   return from_hip(launch_sample(a, dtype, stream), fn);
 }
 

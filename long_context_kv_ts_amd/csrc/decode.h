@@ -31,8 +31,8 @@ hipError_t launch_accept_commit(const int32_t* parent, const int32_t* draft_tok,
 
 // Target-token sampling: per row, the windowed repetition penalty, the
 // temperature, the min-p filter and an inverse-CDF draw from u[row].
-constexpr int kSampleSub = 4096;         // logits per sub-slice (the unit the draw is located in)
-constexpr int kSampleMaxSubs = 256;      // sub-slices per row at most (V <= 1048576)
+constexpr int kSampleSub = 1024;         // logits per sub-slice (the unit the draw is located in)
+constexpr int kSampleMaxSubs = 1024;     // sub-slices per row at most (V <= 1048576)
 constexpr int kSampleList = 32;          // kept candidates remembered per sub-slice
 struct SampleSub {                       // summary of one sub-slice
   float m;                               // largest penalised logit
@@ -55,12 +55,14 @@ struct SampleArgs {
   int T;
   int window;                 // penalty window W (tokens)
   float theta;                // penalty
+  float inv_theta;            // 1 / theta, rounded once
   float s2;                   // log2(e) / temperature (0: greedy)
   float cut;                  // temperature * ln(min_p) (<= 0; -inf keeps every token; greedy: 0)
   const float* u;             // [R] uniforms in [0, 1)
   int32_t* tok;               // [R]
   SampleSub* sub;             // [R][nb]
   SampleCand* cand;           // [R][nb][kSampleList]
+  uint32_t* wbits;            // [R][nb][kSampleSub / 32] window bit of each token
 };
 int sample_subslices(int V);
 size_t sample_workspace_bytes(int R, int V);

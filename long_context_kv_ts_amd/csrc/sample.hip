@@ -12,21 +12,26 @@
 //   3. the draw: the smallest token id whose cumulative weight exceeds
 //      u[r] * sum(w). tau = 0 is greedy: the first token with z_i == Z.
 //
-// Rows are cut into sub-slices of 4096 logits. Two launches, one read of the
-// logits:
-//   A. grid (sub-slices / kSubPerWG, rows): a workgroup issues the window's
-//      few loads, then the loads of all its sub-slices (16 logits a thread
-//      each, held raw in registers), marks the windowed tokens of its range in
-//      an LDS bitmap while they land, and for each sub-slice writes its
-//      maximum m, its kept weight relative to m with
-//      the sub-slice's own cut m + cut, and the kept tokens themselves while
-//      there are at most 32 (a deterministic compaction in thread order).
+// Rows are cut into sub-slices of 1024 logits. Two launches, one read of the
+// logits (a second only for sub-slices that keep many tokens under min-p):
+//   A. grid (workgroups per row, rows), kNT threads, kPW sub-slices a wave: a
+//      workgroup issues the window's few loads, then every logits load of its
+//      waves (16 logits a lane per sub-slice, held raw in registers), and
+//      marks the windowed tokens of its range in an LDS bitmap while they land
+//      (its only barriers); the bitmap is also stored, 32 words a sub-slice.
+//      Each wave then summarises its own sub-slices with DPP reductions and
+//      ballots: the maximum m, the kept weight relative to m at the
+//      sub-slice's own cut m + cut, and the kept tokens themselves while there
+//      are at most 32 (weights and list entries only for those).
 //   B. grid (rows): the row maximum Z gives the row's cut Z + cut >= m + cut,
 //      so a listed sub-slice's kept tokens are all in its list; with min-p off
-//      (cut = -inf) the sub-slice sum rescales exactly by 2^((m - Z) s2). Only
-//      a sub-slice with more than 32 kept tokens and min-p on is read again.
-//      A scan of the sub-slice weights finds the one the draw falls in; its
-//      list (sorted by id) or its logits give the token.
+//      (cut = -inf) the sub-slice sum rescales exactly by 2^((m - Z) s2). A
+//      sub-slice with more than 32 kept tokens and min-p on is read again, one
+//      a wave, with its stored window bits. A scan of the sub-slice weights (up
+//      to four a thread) finds the one the draw falls in; its list (sorted by
+//      id) or its logits give the token.
+#include <cfloat>
+
 #include "decode.h"
 
 namespace ts {
@@ -34,15 +39,20 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesS = kThreads / kWave;
-constexpr int kSubPerWG = 1;
-constexpr int kPT = kSampleSub / kThreads;              // logits per thread per sub-slice (16)
-constexpr int kBitWords = kSubPerWG * kSampleSub / 32;  // bitmap of one workgroup's range
+constexpr int kPL = kSampleSub / kWave;                 // logits a lane per sub-slice (scan)
+constexpr int kPT = kSampleSub / kThreads;              // logits a thread per sub-slice (pick)
+constexpr int kMaxScanSubs = 64;                        // sub-slices a scanning workgroup, at most
+constexpr int kPerT = kSampleMaxSubs / kThreads;        // sub-slices a picking thread, at most
 
+template <int kWords>
 struct Lds {
-  uint32_t bits[kBitWords];                 // windowed tokens of [i0, i1)
+  uint32_t bits[kWords];                    // windowed tokens of [i0, i1)
   int par[TS_MAX_DRAFT], dtok[TS_MAX_DRAFT];
   int path[TS_MAX_DRAFT];                   // draft tokens on the root path, leaf first
   int path_len;
+};
+
+struct BlockRed {
   float red[kWavesS];
   int ired[kWavesS];
 };
@@ -56,21 +66,25 @@ struct PickLds {
   SampleCand sorted[kSampleList];
 };
 
-// The window loads of one thread, issued ahead of the logits: the forest
-// entries tid + 256 k and up to 4 of the last min(n_hist, W) committed tokens.
-constexpr int kHistRegs = 4;
-constexpr int kDraftRegs = TS_MAX_DRAFT / kThreads;   // forest entries a thread stages
+// The window loads of one thread of a kNT-thread workgroup, issued ahead of
+// the logits: the forest entries tid + kNT k and the thread's share of the
+// last min(n_hist, W, 1024) committed tokens.
+template <int kNT>
 struct WindowRegs {
+  static constexpr int kDraftRegs = TS_MAX_DRAFT / kNT;
+  static constexpr int kHistRegs = kNT >= 1024 ? 1 : 1024 / kNT;
   int par[kDraftRegs], dtok[kDraftRegs];
   int hist[kHistRegs];
 };
 
-__device__ __forceinline__ void window_prefetch(const SampleArgs& a, int r, WindowRegs& w) {
+template <int kNT>
+__device__ __forceinline__ void window_prefetch(const SampleArgs& a, int r, WindowRegs<kNT>& w) {
+  constexpr int kDraftRegs = WindowRegs<kNT>::kDraftRegs, kHistRegs = WindowRegs<kNT>::kHistRegs;
   const int tid = threadIdx.x;
   const bool walk = r > 0 && a.window > 0;
 #pragma unroll
   for (int k = 0; k < kDraftRegs; ++k) {
-    const int t = tid + k * kThreads;
+    const int t = tid + k * kNT;
     w.par[k] = -1;
     w.dtok[k] = 0;
     if (walk && t < a.T) {
@@ -82,22 +96,24 @@ __device__ __forceinline__ void window_prefetch(const SampleArgs& a, int r, Wind
   const int h0 = a.n_hist - nh;
 #pragma unroll
   for (int k = 0; k < kHistRegs; ++k) {
-    const int e = tid + k * kThreads;
+    const int e = tid + k * kNT;
     w.hist[k] = e < nh ? a.hist[h0 + e] : -1;
   }
 }
 
-// Marks, in s.bits, the tokens of [i0, i1) that lie in row r's window: the
-// draft tokens on the root path of draft r-1 (at most W of them, leaf first)
-// and the last W - (path length) committed tokens.
-__device__ void mark_window(const SampleArgs& a, int r, int i0, int i1, Lds& s, const WindowRegs& w) {
+// Marks, in s.bits (nw words, all cleared first), the tokens of [i0, i1)
+// that lie in row r's window: the draft tokens on the root path of draft r-1
+// (at most W of them, leaf first) and the last W - (path length) committed
+// tokens.
+template <int kNT, typename L>
+__device__ void mark_window(const SampleArgs& a, int r, int i0, int i1, int nw, L& s, const WindowRegs<kNT>& w) {
+  constexpr int kDraftRegs = WindowRegs<kNT>::kDraftRegs, kHistRegs = WindowRegs<kNT>::kHistRegs;
   const int tid = threadIdx.x;
-  const int nw = (i1 - i0 + 31) >> 5;
-  for (int k = tid; k < nw; k += kThreads) s.bits[k] = 0u;
+  for (int k = tid; k < nw; k += kNT) s.bits[k] = 0u;
   const bool walk = r > 0 && a.window > 0;
 #pragma unroll
   for (int k = 0; k < kDraftRegs; ++k) {
-    const int t = tid + k * kThreads;
+    const int t = tid + k * kNT;
     if (walk && t < a.T) {
       s.par[t] = w.par[k];
       s.dtok[t] = w.dtok[k];
@@ -118,80 +134,165 @@ __device__ void mark_window(const SampleArgs& a, int r, int i0, int i1, Lds& s, 
   auto mark = [&](int tk) {
     if (tk >= i0 && tk < i1) atomicOr(&s.bits[(tk - i0) >> 5], 1u << ((tk - i0) & 31));
   };
-  for (int j = tid; j < len; j += kThreads) mark(s.path[j]);
+  for (int j = tid; j < len; j += kNT) mark(s.path[j]);
   // committed tokens: of the last nh, those with index >= nh - h belong to this row
   const int nh = min(a.n_hist, a.window);
   const int h = max(0, min(a.n_hist, a.window - len));
 #pragma unroll
   for (int k = 0; k < kHistRegs; ++k) {
-    const int e = tid + k * kThreads;
+    const int e = tid + k * kNT;
     if (e < nh && e >= nh - h) mark(w.hist[k]);
   }
-  for (int e = tid + kHistRegs * kThreads; e < nh; e += kThreads)   // windows above 1024 tokens
+  for (int e = tid + kHistRegs * kNT; e < nh; e += kNT)   // windows above 1024 tokens
     if (e >= nh - h) mark(a.hist[a.n_hist - nh + e]);
   __syncthreads();
 }
 
-__device__ __forceinline__ float penalised(float x, const Lds& s, int rel, float theta) {
-  if ((s.bits[rel >> 5] >> (rel & 31)) & 1u) return x > 0.0f ? x / theta : x * theta;
-  return x;
+// The penalty of a windowed token: x / theta above zero (as x times the
+// reciprocal 1 / theta rounded once, on the host), x * theta otherwise.
+__device__ __forceinline__ float penalty(float x, const SampleArgs& a) {
+  return x > 0.0f ? x * a.inv_theta : x * a.theta;
 }
 
-// Token of element e of this thread in the sub-slice starting at `base`:
-// groups of 16 bytes, consecutive threads on consecutive groups.
+__device__ __forceinline__ float penalised(float x, const uint32_t* bits, int rel, const SampleArgs& a) {
+  return ((bits[rel >> 5] >> (rel & 31)) & 1u) ? penalty(x, a) : x;
+}
+
+// Token of element e of a lane in the sub-slice starting at `base`: groups of
+// 16 bytes, consecutive lanes on consecutive groups.
 template <typename Tin>
-__device__ __forceinline__ int token_of(int base, int e) {
+__device__ __forceinline__ int token_of(int base, int e, int lane) {
   constexpr int kPer = 16 / sizeof(Tin);
-  return base + ((e / kPer) * kThreads + (int)threadIdx.x) * kPer + (e % kPer);
+  return base + ((e / kPer) * kWave + lane) * kPer + (e % kPer);
 }
 
-// The thread's 16 logits of a sub-slice at `base`, -inf past V. Rows that are
-// whole 16-byte groups from a 16-byte-aligned base (the host checks) take
-// 16-byte loads, all issued back to back with no branch around them (a group
-// past V is clamped onto the row's last group and masked afterwards); they
-// stay raw in registers until used. Other rows take element loads.
+// A lane's 16 logits of a sub-slice. Rows that are whole 16-byte groups from
+// a 16-byte-aligned base (the host checks) take 16-byte loads, issued back to
+// back with no branch around them (a group past V is clamped onto the row's
+// last group and masked afterwards); they stay raw in registers until used.
+// Other rows take element loads when the values are formed.
 template <typename Tin>
 struct SubRaw {
   static constexpr int kPer = 16 / sizeof(Tin);
-  static constexpr int kG = kPT / kPer;
+  static constexpr int kG = kPL / kPer;
   uint4 u[kG];
 };
 
 template <typename Tin, bool kVec>
-__device__ __forceinline__ void fetch_sub(const Tin* row, int base, int V, SubRaw<Tin>& w) {
+__device__ __forceinline__ void fetch_sub(const Tin* row, int base, int V, int lane, SubRaw<Tin>& w) {
   if constexpr (kVec) {
     constexpr int kPer = SubRaw<Tin>::kPer;
 #pragma unroll
     for (int g = 0; g < SubRaw<Tin>::kG; ++g) {
-      const int t0 = min(token_of<Tin>(base, g * kPer), V - kPer);
+      const int t0 = min(token_of<Tin>(base, g * kPer, lane), V - kPer);
       w.u[g] = *reinterpret_cast<const uint4*>(row + t0);
     }
   }
 }
 
-template <typename Tin, bool kVec>
-__device__ __forceinline__ void unpack_sub(const Tin* row, int base, int V, SubRaw<Tin>& w,
-                                           float (&x)[kPT]) {
+// The lane's penalised logits z of the sub-slice at `base` (-inf past V; a
+// sub-slice wholly inside the row skips that test), with window bit t - i0 of
+// `bits` (LDS or global) for token t. A group's kPer tokens start at a
+// multiple of kPer from the 1024-aligned i0, so one word holds all their bits.
+template <typename Tin, bool kVec, bool kFull>
+__device__ __forceinline__ void sub_values(const Tin* row, int base, int i0, const SampleArgs& a, int lane,
+                                           SubRaw<Tin>& w, const uint32_t* bitmap, float (&z)[kPL]) {
   constexpr int kPer = SubRaw<Tin>::kPer;
-  if constexpr (kVec) {
 #pragma unroll
-    for (int g = 0; g < SubRaw<Tin>::kG; ++g) {
+  for (int g = 0; g < SubRaw<Tin>::kG; ++g) {
+    const int t0 = token_of<Tin>(base, g * kPer, lane);
+    const uint32_t bits = bitmap[(t0 - i0) >> 5] >> ((t0 - i0) & 31);
+    Tin e[kPer];
+    if constexpr (kVec) {
       // the unpacking stays here: otherwise it is hoisted next to the loads,
       // whose wait would then precede the work meant to hide them
       asm volatile("" : "+v"(w.u[g].x), "+v"(w.u[g].y), "+v"(w.u[g].z), "+v"(w.u[g].w));
-      Tin e[kPer];
       __builtin_memcpy(e, &w.u[g], 16);
+    }
 #pragma unroll
-      for (int q = 0; q < kPer; ++q)
-        x[g * kPer + q] = token_of<Tin>(base, g * kPer + q) < V ? Elem<Tin>::load(&e[q]) : -INFINITY;
+    for (int q = 0; q < kPer; ++q) {
+      const bool in = kFull || t0 + q < a.V;
+      float x;
+      if constexpr (kVec) x = Elem<Tin>::load(&e[q]);
+      else x = in ? Elem<Tin>::load(row + t0 + q) : 0.0f;
+      // the factor by bit selects, no compares: the sign picks theta or
+      // 1 / theta (x = +-0 gives +-0 either way), the window bit picks it or 1
+      const uint32_t sgn = (uint32_t)(__float_as_int(x) >> 31);
+      const uint32_t f = (sgn & __float_as_uint(a.theta)) | (~sgn & __float_as_uint(a.inv_theta));
+      const uint32_t w_q = (uint32_t)((int)(bits << (31 - q)) >> 31);
+      x *= __uint_as_float((w_q & f) | (~w_q & 0x3f800000u));
+      z[g * kPer + q] = in ? x : -INFINITY;
+    }
+  }
+}
+
+// All-lane reductions of a wave without LDS traffic: DPP exchanges within
+// each row of 16 lanes (pairs, quads, half-row mirror, row mirror), then the
+// four row results read out of lanes 0, 16, 32 and 48.
+template <int kCtrl, typename T>
+__device__ __forceinline__ T dpp(T x) {
+  return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+template <typename T>
+__device__ __forceinline__ T readlane(T x, int l) {
+  return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_all(T v, Op op) {
+  v = op(v, dpp<0xB1>(v));                  // quad_perm [1,0,3,2]
+  v = op(v, dpp<0x4E>(v));                  // quad_perm [2,3,0,1]
+  v = op(v, dpp<0x141>(v));                 // row_half_mirror
+  v = op(v, dpp<0x140>(v));                 // row_mirror
+  return op(op(readlane(v, 0), readlane(v, 16)), op(readlane(v, 32), readlane(v, 48)));
+}
+__device__ __forceinline__ float wave_all_max(float v) { return wave_all(v, [](float x, float y) { return fmaxf(x, y); }); }
+__device__ __forceinline__ float wave_all_sum(float v) { return wave_all(v, [](float x, float y) { return x + y; }); }
+
+// Summary of sub-slice b (at `base`) by one wave: m, the kept weight relative
+// to m at the cut m + cut, the count n, and the kept tokens when n <= 32.
+template <typename Tin, bool kVec, bool kFull, typename L>
+__device__ __forceinline__ void summarise(const SampleArgs& a, const Tin* row, int r, int b, int i0, int lane,
+                                          SubRaw<Tin>& raw, const L& s) {
+  const int base = b * kSampleSub;
+  float z[kPL];
+  sub_values<Tin, kVec, kFull>(row, base, i0, a, lane, raw, s.bits, z);
+  float m = z[0];
+#pragma unroll
+  for (int e = 1; e < kPL; ++e) m = fmaxf(m, z[e]);
+  m = wave_all_max(m);
+  // kept: z >= m + cut, never -inf (the floor -FLT_MAX stands in for cut = -inf)
+  const float thr = fmaxf(m + a.cut, -FLT_MAX);
+  uint64_t kept[kPL];
+  int n = 0;
+#pragma unroll
+  for (int e = 0; e < kPL; ++e) {
+    kept[e] = __builtin_amdgcn_ballot_w64(z[e] >= thr);
+    n += __popcll(kept[e]);
+  }
+  float acc = 0.0f;
+  if (n <= kSampleList) {
+    // few kept: their weights, and the tokens in (element, lane) order, the
+    // slot being the ballot's count below this lane
+    SampleCand* list = a.cand + ((int64_t)r * a.nb + b) * kSampleList;
+    int off = 0;
+#pragma unroll
+    for (int e = 0; e < kPL; ++e) {
+      const uint64_t k_e = kept[e];
+      if (k_e == 0) continue;                   // a scalar test: no lane kept element e
+      if ((k_e >> lane) & 1u) {
+        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(k_e >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)k_e, 0u));
+        acc += __builtin_amdgcn_exp2f((z[e] - m) * a.s2);
+        list[off + pos] = SampleCand{z[e], token_of<Tin>(base, e, lane)};
+      }
+      off += __popcll(k_e);
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < kPT; ++e) {
-      const int t = token_of<Tin>(base, e);
-      x[e] = t < V ? Elem<Tin>::load(row + t) : -INFINITY;
-    }
+    for (int e = 0; e < kPL; ++e)
+      acc += z[e] >= thr ? __builtin_amdgcn_exp2f((z[e] - m) * a.s2) : 0.0f;
   }
+  acc = wave_all_sum(acc);
+  if (lane == 0) a.sub[r * a.nb + b] = SampleSub{m, acc, n, 0};
 }
 
 __device__ float block_max(float v, float* red) {
@@ -243,94 +344,84 @@ __device__ T block_excl_scan(T v, T* red, T& total) {
   return off + excl;
 }
 
-template <typename Tin, int kSPW, bool kVec>
-__global__ __launch_bounds__(kThreads) void sample_scan_kernel(SampleArgs a) {
-  __shared__ Lds s;
-  const int r = blockIdx.y, tid = threadIdx.x;
-  const int b0 = blockIdx.x * kSPW, b1 = min(a.nb, b0 + kSPW);
+template <typename Tin, int kNT, int kPW, bool kVec>
+__global__ __launch_bounds__(kNT) void sample_scan_kernel(SampleArgs a) {
+  constexpr int kW = kNT / kWave;
+  static_assert(kW * kPW <= kMaxScanSubs, "sub-slices a workgroup");
+  __shared__ Lds<kW * kPW * kSampleSub / 32> s;
+  const int r = blockIdx.y, lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int b0 = blockIdx.x * (kW * kPW), b1 = min(a.nb, b0 + kW * kPW);
   const int i0 = b0 * kSampleSub, i1 = min(a.V, b1 * kSampleSub);
   const Tin* row = static_cast<const Tin*>(a.logits) + (int64_t)r * a.V;
-  // the window's few loads first, then every logits load of the workgroup
-  // (sub-slices past the row's last one reload it); the bitmap is built
-  // while the logits are in flight
-  WindowRegs wr;
-  window_prefetch(a, r, wr);
-  SubRaw<Tin> raw[kSPW];
+  // wave w owns sub-slices b0 + w + kW k; the window's few loads go first,
+  // then every logits load of the wave (a sub-slice past the row's last one
+  // reloads it); the bitmap is built while the logits are in flight
+  WindowRegs<kNT> wr;
+  window_prefetch<kNT>(a, r, wr);
+  SubRaw<Tin> raw[kPW];
 #pragma unroll
-  for (int k = 0; k < kSPW; ++k) fetch_sub<Tin, kVec>(row, min(b0 + k, b1 - 1) * kSampleSub, a.V, raw[k]);
-  mark_window(a, r, i0, i1, s, wr);
+  for (int k = 0; k < kPW; ++k)
+    fetch_sub<Tin, kVec>(row, min(b0 + wave + kW * k, b1 - 1) * kSampleSub, a.V, lane, raw[k]);
+  const int nw = (b1 - b0) * (kSampleSub / 32);
+  mark_window<kNT>(a, r, i0, i1, nw, s, wr);
+  // the bitmap also goes to the workspace, for the picking kernel's rereads
+  for (int k = threadIdx.x; k < nw; k += kNT) a.wbits[((int64_t)r * a.nb + b0) * (kSampleSub / 32) + k] = s.bits[k];
 #pragma unroll
-  for (int k = 0; k < kSPW; ++k) {
-    const int b = b0 + k;
+  for (int k = 0; k < kPW; ++k) {
+    const int b = b0 + wave + kW * k;
     if (b >= b1) break;
-    const int base = b * kSampleSub;
-    float x[kPT];
-    unpack_sub<Tin, kVec>(row, base, a.V, raw[k], x);
-    float z[kPT];
-    float m = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < kPT; ++e) {
-      const int i = token_of<Tin>(base, e);
-      z[e] = i < a.V ? penalised(x[e], s, i - i0, a.theta) : -INFINITY;
-      m = fmaxf(m, z[e]);
-    }
-    m = block_max(m, s.red);
-    const float thr = m + a.cut;
-    float acc = 0.0f;
-    int cnt = 0;
-#pragma unroll
-    for (int e = 0; e < kPT; ++e) {
-      if (z[e] > -INFINITY && z[e] >= thr) {
-        acc += exp2f((z[e] - m) * a.s2);
-        ++cnt;
-      }
-    }
-    int n_all;
-    int slot = block_excl_scan<int>(cnt, s.ired, n_all);
-    if (n_all <= kSampleList) {
-      SampleCand* list = a.cand + ((int64_t)r * a.nb + b) * kSampleList;
-#pragma unroll
-      for (int e = 0; e < kPT; ++e) {
-        if (z[e] > -INFINITY && z[e] >= thr) list[slot++] = SampleCand{z[e], token_of<Tin>(base, e)};
-      }
-    }
-    acc = block_sum(acc, s.red);
-    if (tid == 0) a.sub[r * a.nb + b] = SampleSub{m, acc, n_all, 0};
+    if ((b + 1) * kSampleSub <= a.V)
+      summarise<Tin, kVec, true>(a, row, r, b, i0, lane, raw[k], s);
+    else
+      summarise<Tin, kVec, false>(a, row, r, b, i0, lane, raw[k], s);
   }
 }
 
-// Sum of the kept weights of sub-slice b at the row's cut, from its logits.
-template <typename Tin>
-__device__ float sub_weight(const SampleArgs& a, int r, int b, float Z, float thr, Lds& s) {
-  const int base = b * kSampleSub;
+// Sums of the kept weights of kU sub-slices b[u] at the row's cut thr
+// (relative to the row maximum Z), from their logits and stored window bits;
+// one wave, every load issued before the first sum.
+template <typename Tin, bool kVec, int kU>
+__device__ void reread_weights(const SampleArgs& a, int r, const int (&b)[kU], float Z, float thr, int lane,
+                               float (&w)[kU]) {
   const Tin* row = static_cast<const Tin*>(a.logits) + (int64_t)r * a.V;
-  WindowRegs wr;
-  window_prefetch(a, r, wr);
-  mark_window(a, r, base, min(a.V, base + kSampleSub), s, wr);
-  SubRaw<Tin> raw;
-  float x[kPT];
-  unpack_sub<Tin, false>(row, base, a.V, raw, x);
-  float acc = 0.0f;
+  SubRaw<Tin> raw[kU];
 #pragma unroll
-  for (int e = 0; e < kPT; ++e) {
-    const int i = token_of<Tin>(base, e);
-    if (i < a.V) {
-      const float z = penalised(x[e], s, i - base, a.theta);
-      if (z > -INFINITY && z >= thr) acc += exp2f((z - Z) * a.s2);
-    }
+  for (int u = 0; u < kU; ++u) fetch_sub<Tin, kVec>(row, b[u] * kSampleSub, a.V, lane, raw[u]);
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int base = b[u] * kSampleSub;
+    const uint32_t* bits = a.wbits + ((int64_t)r * a.nb + b[u]) * (kSampleSub / 32);
+    float z[kPL];
+    if (base + kSampleSub <= a.V)
+      sub_values<Tin, kVec, true>(row, base, base, a, lane, raw[u], bits, z);
+    else
+      sub_values<Tin, kVec, false>(row, base, base, a, lane, raw[u], bits, z);
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kPL; ++e)
+      if (z[e] > -INFINITY && z[e] >= thr) acc += exp2f((z[e] - Z) * a.s2);
+    w[u] = wave_all_sum(acc);
   }
-  return block_sum(acc, s.red);
 }
 
-template <typename Tin>
+template <typename Tin, bool kVec>
 __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
-  __shared__ Lds s;
+  __shared__ BlockRed s;
   __shared__ PickLds p;
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const bool greedy = a.s2 == 0.0f;
-  SampleSub sb{-INFINITY, 0.0f, 0, 0};
-  if (tid < a.nb) sb = a.sub[r * a.nb + tid];
-  const float Z = block_max(sb.m, s.red);
+  // thread tid owns sub-slices [q0, q0 + per), in row order
+  const int per = (a.nb + kThreads - 1) / kThreads;
+  const int q0 = tid * per;
+  SampleSub sb[kPerT];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kPerT; ++k) {
+    sb[k] = SampleSub{-INFINITY, 0.0f, 0, 0};
+    if (k < per && q0 + k < a.nb) sb[k] = a.sub[r * a.nb + q0 + k];
+    mloc = fmaxf(mloc, sb[k].m);
+  }
+  const float Z = block_max(mloc, s.red);
   const float thr = Z + a.cut;
   if (tid == 0) {
     p.bsel = a.nb;
@@ -343,50 +434,94 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
   float target = 0.0f;
   bool fallback = false;
   if (greedy) {
-    if (tid < a.nb && sb.m == Z) atomicMin(&p.bsel, tid);
+#pragma unroll
+    for (int k = 0; k < kPerT; ++k)
+      if (k < per && q0 + k < a.nb && sb[k].m == Z) {
+        atomicMin(&p.bsel, q0 + k);
+        break;
+      }
     __syncthreads();
   } else {
     // each sub-slice's weight at the row's cut (relative to Z)
-    float c = 0.0f;
-    if (tid < a.nb && sb.m > -INFINITY && sb.m >= thr) {
-      if (a.cut == -INFINITY) {
-        c = sb.s * exp2f((sb.m - Z) * a.s2);
-      } else if (sb.n <= kSampleList) {
-        const SampleCand* list = a.cand + ((int64_t)r * a.nb + tid) * kSampleList;
-        for (int j = 0; j < sb.n; ++j) {
-          const SampleCand e = list[j];
-          if (e.z >= thr) c += exp2f((e.z - Z) * a.s2);
+#pragma unroll
+    for (int k = 0; k < kPerT; ++k) {
+      if (k >= per) break;
+      const int q = q0 + k;
+      float c = 0.0f;
+      if (q < a.nb && sb[k].m > -INFINITY && sb[k].m >= thr) {
+        if (a.cut == -INFINITY) {
+          c = sb[k].s * exp2f((sb[k].m - Z) * a.s2);
+        } else if (sb[k].n <= kSampleList) {
+          const SampleCand* list = a.cand + ((int64_t)r * a.nb + q) * kSampleList;
+          for (int j = 0; j < sb[k].n; ++j) {
+            const SampleCand e = list[j];
+            if (e.z >= thr) c += exp2f((e.z - Z) * a.s2);
+          }
+        } else {
+          p.ovf[atomicAdd(&p.n_ovf, 1)] = q;
         }
-      } else {
-        p.ovf[atomicAdd(&p.n_ovf, 1)] = tid;
+      }
+      p.c[q] = c;                               // q < kSampleMaxSubs: per <= kPerT
+    }
+    __syncthreads();
+    // rare: sub-slices with more than 32 kept tokens are read again, one a
+    // wave, four at a time (past the end the last one is repeated, unused)
+    const int n_ovf = p.n_ovf;
+    constexpr int kU = 4;
+    for (int k = wave; k < n_ovf; k += kU * kWavesS) {
+      int bs[kU];
+      float w[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) bs[u] = p.ovf[min(k + u * kWavesS, n_ovf - 1)];
+      reread_weights<Tin, kVec, kU>(a, r, bs, Z, thr, lane, w);
+      if (lane == 0) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (k + u * kWavesS < n_ovf) p.c[bs[u]] = w[u];
       }
     }
-    p.c[tid] = c;                               // kThreads == kSampleMaxSubs
     __syncthreads();
-    const int n_ovf = p.n_ovf;
-    for (int k = 0; k < n_ovf; ++k) {           // rare: many kept tokens in one sub-slice
-      const int b = p.ovf[k];
-      const float w = sub_weight<Tin>(a, r, b, Z, thr, s);
-      if (tid == 0) p.c[b] = w;
-      __syncthreads();
+    float c[kPerT];
+    float mine = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kPerT; ++k) {
+      c[k] = k < per ? p.c[q0 + k] : 0.0f;
+      mine += c[k];
     }
-    c = p.c[tid];
     float total;
-    const float excl = block_excl_scan<float>(c, s.red, total);
+    const float excl = block_excl_scan<float>(mine, s.red, total);
     target = a.u[r] * total;
-    if (tid < a.nb && c > 0.0f && excl + c > target) atomicMin(&p.bsel, tid);
+    // the first sub-slice whose cumulative weight passes the target
+    float run = excl;
+#pragma unroll
+    for (int k = 0; k < kPerT; ++k) {
+      if (c[k] > 0.0f && run + c[k] > target) {
+        atomicMin(&p.bsel, q0 + k);
+        break;
+      }
+      run += c[k];
+    }
     __syncthreads();
-    if (p.bsel == a.nb) {                       // u * total at or past the end: the last kept token
+    const int bs = p.bsel;
+    if (bs == a.nb) {                           // u * total at or past the end: the last kept token
       fallback = true;
       __syncthreads();
-      if (tid < a.nb && c > 0.0f) atomicMax(&p.last, tid);
+#pragma unroll
+      for (int k = kPerT - 1; k >= 0; --k)
+        if (c[k] > 0.0f) {
+          atomicMax(&p.last, q0 + k);
+          break;
+        }
       __syncthreads();
       if (tid == 0) {
         p.bsel = p.last;
         p.last = -1;
       }
-    } else if (tid == p.bsel) {
-      p.base = excl;
+    } else if (bs >= q0 && bs < q0 + per) {
+      float pre = excl;
+#pragma unroll
+      for (int k = 0; k < kPerT; ++k) pre += k < bs - q0 ? c[k] : 0.0f;
+      p.base = pre;
     }
     __syncthreads();
   }
@@ -429,11 +564,7 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
   }
   // otherwise from the sub-slice's logits: thread tid owns tokens [c0, c1)
   const int base = b * kSampleSub, end = min(a.V, base + kSampleSub);
-  {
-    WindowRegs wr;
-    window_prefetch(a, r, wr);
-    mark_window(a, r, base, end, s, wr);
-  }
+  const uint32_t* bits = a.wbits + ((int64_t)r * a.nb + b) * (kSampleSub / 32);
   const Tin* row = static_cast<const Tin*>(a.logits) + (int64_t)r * a.V;
   const int c0 = min(end, base + tid * kPT), c1 = min(end, c0 + kPT);
   float w[kPT];
@@ -442,7 +573,7 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
   for (int j = 0; j < kPT; ++j) {
     w[j] = 0.0f;
     if (c0 + j < c1) {
-      const float z = penalised(Elem<Tin>::load(row + c0 + j), s, c0 + j - base, a.theta);
+      const float z = penalised(Elem<Tin>::load(row + c0 + j), bits, c0 + j - base, a);
       if (greedy) {
         if (z == Z) atomicMin(&p.win, c0 + j);
       } else if (z > -INFINITY && z >= thr) {
@@ -472,15 +603,22 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
 
 template <typename Tin>
 hipError_t launch_t(const SampleArgs& a, hipStream_t st) {
-  const dim3 grid((a.nb + kSubPerWG - 1) / kSubPerWG, a.R);
+  // 256 threads, one sub-slice a wave: of 256/512/1024 threads and 1/2/4
+  // sub-slices a wave, the fastest or within 2% of it for fp32 and bf16
+  constexpr int kNT = 256, kPW = 1;
+  constexpr int kSubs = kNT / kWave * kPW;
+  const dim3 grid((a.nb + kSubs - 1) / kSubs, a.R);
   constexpr int kPer = 16 / sizeof(Tin);
   // 16-byte loads when every row is whole 16-byte groups from an aligned base
   const bool vec = (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0 && a.V % kPer == 0;
   if (vec)
-    sample_scan_kernel<Tin, kSubPerWG, true><<<grid, kThreads, 0, st>>>(a);
+    sample_scan_kernel<Tin, kNT, kPW, true><<<grid, kNT, 0, st>>>(a);
   else
-    sample_scan_kernel<Tin, kSubPerWG, false><<<grid, kThreads, 0, st>>>(a);
-  sample_pick_kernel<Tin><<<a.R, kThreads, 0, st>>>(a);
+    sample_scan_kernel<Tin, kNT, kPW, false><<<grid, kNT, 0, st>>>(a);
+  if (vec)
+    sample_pick_kernel<Tin, true><<<a.R, kThreads, 0, st>>>(a);
+  else
+    sample_pick_kernel<Tin, false><<<a.R, kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -490,11 +628,11 @@ int sample_subslices(int V) { return V < 1 ? 1 : (V + kSampleSub - 1) / kSampleS
 
 size_t sample_workspace_bytes(int R, int V) {
   const size_t n = (size_t)R * sample_subslices(V);
-  return n * sizeof(SampleSub) + n * kSampleList * sizeof(SampleCand);
+  return n * sizeof(SampleSub) + n * kSampleList * sizeof(SampleCand) + n * (kSampleSub / 32) * sizeof(uint32_t);
 }
 
 hipError_t launch_sample(const SampleArgs& a, ts_dtype dtype, hipStream_t s) {
-  static_assert(kThreads == kSampleMaxSubs, "the picking workgroup holds one sub-slice per thread");
+  static_assert(kThreads * kPerT == kSampleMaxSubs, "a picking thread holds up to kPerT sub-slices");
   static_assert(kSampleList <= kThreads, "list entries are ranked one per thread");
   return dtype == TS_BF16 ? launch_t<bf16_t>(a, s) : launch_t<float>(a, s);
 }

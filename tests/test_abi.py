@@ -220,7 +220,7 @@ def test_sample_rejects():
     """Argument checks of ts_sample_tokens; none of these calls launches anything."""
     lib = ops.lib()
     ws = lib.ts_sample_workspace(121, 128256)
-    assert ws >= 121 * 32 * (16 + 32 * 8) and ws % 256 == 0
+    assert ws >= 121 * 126 * (16 + 32 * 8 + 128) and ws % 256 == 0    # 400 bytes a row and 1024 logits
     assert lib.ts_sample_workspace(0, 100) == 0 and lib.ts_sample_workspace(1, (1 << 20) + 1) == 0
 
     def call(logits=P, R=121, V=128256, hist=P, n_hist=4096, parent=P, draft=P, T=120, window=1024,

@@ -106,10 +106,11 @@ def test_knobs(window, penalty, temperature, min_p):
                                                           f"min_p={min_p}")
 
 
-@pytest.mark.parametrize("V", [1, 3, 7, 9, 4095, 4096, 4097, 8200, 128257])
+@pytest.mark.parametrize("V", [1, 3, 7, 9, 1023, 1024, 1025, 4095, 4096, 4097, 8200, 16385, 128257])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ragged_vocabularies_and_edges(V, dtype):
-    """Vocabularies around the 4096-logit slices, odd row lengths (misaligned
+    """Vocabularies around the 1024-logit sub-slices and the 4096-token ranges of
+    one scanning workgroup, odd row lengths (misaligned
     rows), window ids outside [0, V), -inf logits, u = 0 and u just below 1."""
     rng = np.random.default_rng(V)
     parent = np.array([-1, 0, 1, -1, 3], np.int32)
@@ -129,6 +130,31 @@ def test_ragged_vocabularies_and_edges(V, dtype):
     for tau, mp in ((1.0, 0.1), (0.7, 0.0), (0.0, 0.1)):
         run(x, dtype, hist, parent, draft, window=64, penalty=1.3, temperature=tau, min_p=mp, u=u,
             label=f"V={V} {dtype} tau={tau} min_p={mp}")
+
+
+@pytest.mark.parametrize("V", [128256, 100003])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_wide_kept_sets_reread_every_sub_slice(V, dtype):
+    """Flat logits with min-p on: every 1024-logit sub-slice keeps more tokens
+    than its 32-entry list, so each one is read again at the row's cut (one a
+    wave) and the token comes from the chosen sub-slice's logits, with the
+    window bits the scan stored. V = 100003 takes element loads."""
+    parent = np.array([-1, 0, 0, 1], np.int32)
+    c = inputs.make_sample(dtype=dtype, V=V, parent=parent, logit_std=0.3, hot_boost=0.5, seed=21)
+    for tau, mp in ((2.0, 0.05), (1.0, 0.3)):
+        run(c.logits, dtype, c.hist, c.parent, c.draft_tok, window=1024, penalty=1.2, temperature=tau,
+            min_p=mp, u=c.u, label=f"wide V={V} {dtype} tau={tau} min_p={mp}")
+
+
+@pytest.mark.parametrize("V", [1048576, 1048575])
+def test_largest_vocabulary(V):
+    """V = 2^20 (1024 sub-slices a row, four a picking thread) and one less."""
+    parent = np.array([-1, 0], np.int32)
+    for dtype in ("f32", "bf16"):
+        c = inputs.make_sample(dtype=dtype, V=V, parent=parent, n_hist=3000, seed=22)
+        for tau, mp in ((1.0, 0.1), (3.0, 0.02), (0.0, 0.1)):
+            run(c.logits, dtype, c.hist, c.parent, c.draft_tok, window=2048, penalty=1.2, temperature=tau,
+                min_p=mp, u=c.u, label=f"V={V} {dtype} tau={tau} min_p={mp}")
 
 
 def test_single_row_no_drafts_no_history():
