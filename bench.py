@@ -14,7 +14,7 @@ Inputs are seeded synthetic tensors resident in HBM before timing starts
 (verify inputs: seed 2; partial-KV inputs: seed 3, with 8 chunks per KV head
 carrying 3x keys). Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--cpu-heads H] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--cpu-heads H] [--cpu-seconds S] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -40,8 +40,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-heads", type=int, default=2,
+    ap.add_argument("--cpu-heads", type=int, default=8,
                     help="KV heads of the step the CPU oracle runs for the baseline (of 8)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="the CPU baseline repeats its sample until this much time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step instead of eager launches")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -228,7 +230,7 @@ def main():
     res["ngram_us"] = time_ngram(dev, args.steps)
 
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(vc, pc, args.cpu_heads)
+        res["cpu_baseline"] = cpu_baseline(vc, pc, args.cpu_heads, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
@@ -378,8 +380,9 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(vc, pc, heads):
-    """The oracle on `heads` of the 8 KV heads of one step, scaled to the step."""
+def cpu_baseline(vc, pc, heads, min_seconds):
+    """The oracle on `heads` of the 8 KV heads of one step, repeated until
+    `min_seconds` have passed (at least once); the mean is scaled to the step."""
     import oracle
     try:
         import threadpoolctl
@@ -389,20 +392,26 @@ def cpu_baseline(vc, pc, heads):
         threads = None
     cores = len(os.sched_getaffinity(0))
     hs = list(range(heads))
-    t0 = time.perf_counter()
-    oracle.verify_attn_ref(vc.q, vc.k_cache, vc.v_cache, vc.k_draft, vc.v_draft, vc.parent,
-                           vc.scale, "bf16", heads=hs)
-    s = oracle.importance_ref(pc.q, pc.k_cache, pc.scale, pc.chunk, "bf16", heads=hs)
-    idx, _ = oracle.topk_ref(s[hs], pc.k)
-    kp, vp = oracle.gather_ref(pc.k_cache[hs], pc.v_cache[hs], idx, pc.chunk)
     G = pc.Hq // pc.Hkv
-    oracle.draft_attn_ref(pc.q[:, :heads * G], kp, vp, pc.k_new[hs], pc.v_new[hs], pc.scale, "bf16")
-    dt = time.perf_counter() - t0
-    return {"value": round(dt * 1e6 * vc.Hkv / heads, 1), "unit": "us", "cores": threads or cores,
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.verify_attn_ref(vc.q, vc.k_cache, vc.v_cache, vc.k_draft, vc.v_draft, vc.parent,
+                               vc.scale, "bf16", heads=hs)
+        s = oracle.importance_ref(pc.q, pc.k_cache, pc.scale, pc.chunk, "bf16", heads=hs)
+        idx, _ = oracle.topk_ref(s[hs], pc.k)
+        kp, vp = oracle.gather_ref(pc.k_cache[hs], pc.v_cache[hs], idx, pc.chunk)
+        oracle.draft_attn_ref(pc.q[:, :heads * G], kp, vp, pc.k_new[hs], pc.v_new[hs], pc.scale, "bf16")
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    scale = vc.Hkv / heads
+    what = "the whole step" if heads == vc.Hkv else f"{heads} of {vc.Hkv} KV heads of one step"
+    return {"value": round(dt / reps * 1e6 * scale, 1), "unit": "us", "cores": threads or cores,
             "host_cores": cores, "kind": "oracle",
-            "sample": f"{heads} of {vc.Hkv} KV heads of one step (verify + importance + top-k + "
-                      f"gather + draft attention), float64 numpy, time x{vc.Hkv / heads:g}"}
-
+            "sample": f"{what} (verify + importance + top-k + gather + draft attention), float64 numpy, "
+                      f"mean of {reps} runs over {dt:.1f} s" + (f", time x{scale:g}" if heads != vc.Hkv else "")}
 
 if __name__ == "__main__":
     main()
