@@ -168,14 +168,16 @@ __global__ __launch_bounds__(256) void importance_mfma_kernel(
   }
 }
 
-// 64-token chunks: the whole chunk's K (16 KB) is requested before any
-// product, so each wave keeps 16 loads in flight instead of walking the chunk
-// one 16-key block at a time.
+// 64-token chunks, two waves a chunk: each wave requests its 32 keys' K (8 KB)
+// before any product; an 8 KB share a wave streams K faster than a 16 KB one.
+// The query fragments are read from global memory once per workgroup and
+// shared through LDS. The two halves' sums meet in LDS and are added in a
+// fixed order, so the score is deterministic.
 template <int D, int NRB, bool kPow2>
 __global__ __launch_bounds__(256) void importance_mfma64_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, int64_t stride,
     float* __restrict__ scores, int R, int Hq, int Hkv, float scale, int n_chunks) {
-  constexpr int KS = D / 32, CHUNK = 64, NKB = CHUNK / 16;
+  constexpr int KS = D / 32, CHUNK = 64, NKB = CHUNK / 32;   // a wave's 16-key blocks
   ScoreTile* tiles = nullptr;                 // general G only: one tile per wave
   if constexpr (!kPow2) {
     __shared__ ScoreTile t[4];
@@ -185,23 +187,34 @@ __global__ __launch_bounds__(256) void importance_mfma64_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, quad = lane >> 4;
 
-  bf16x8_t qb[NRB][KS];
+  __shared__ uint4 q_lds[NRB][KS][kWave];
+  if (wave == 0) {
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int row = rb * 16 + col;
-    const bool valid = row < rows;
-    const int r = valid ? row / G : 0, h = g * G + (valid ? row % G : 0);
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int row = rb * 16 + col;
+      const bool valid = row < rows;
+      const int r = valid ? row / G : 0, h = g * G + (valid ? row % G : 0);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 u = valid ? *reinterpret_cast<const uint4*>(q + ((int64_t)r * Hq + h) * D + ks * 32 + quad * 8)
-                            : make_uint4(0u, 0u, 0u, 0u);
-      qb[rb][ks] = __builtin_bit_cast(bf16x8_t, u);
+      for (int ks = 0; ks < KS; ++ks)
+        q_lds[rb][ks][lane] = valid ? *reinterpret_cast<const uint4*>(q + ((int64_t)r * Hq + h) * D + ks * 32 + quad * 8)
+                                    : make_uint4(0u, 0u, 0u, 0u);
     }
   }
+  __syncthreads();
+  bf16x8_t qb[NRB][KS];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[rb][ks] = __builtin_bit_cast(bf16x8_t, q_lds[rb][ks][lane]);
   const float inv = 1.f / (float)(CHUNK * R);
-  const int waves_total = gridDim.x * 4;
-  for (int c = blockIdx.x * 4 + wave; c < n_chunks; c += waves_total) {
-    const bf16_t* base = kc + ((int64_t)g * stride + (int64_t)c * CHUNK) * D;
+  __shared__ float half_sum[4];
+  // workgroup iteration p covers chunks 2p and 2p + 1; every wave runs every
+  // iteration (a wave past the last chunk only meets the barriers)
+  const int n_pairs = (n_chunks + 1) / 2, half = wave & 1;
+  for (int pr = blockIdx.x; pr < n_pairs; pr += gridDim.x) {
+    const int c = 2 * pr + (wave >> 1);
+    const bool live = c < n_chunks;
+    const bf16_t* base = kc + ((int64_t)g * stride + (int64_t)min(c, n_chunks - 1) * CHUNK + half * 32) * D;
     bf16x8_t ka[NKB][KS];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -237,7 +250,10 @@ __global__ __launch_bounds__(256) void importance_mfma64_kernel(
       if constexpr (!kPow2) tot += tile_group_max_sum(tiles[wave], R, G, 16, lane);
     }
     tot = wave_sum(tot);
-    if (lane == 0) scores[(int64_t)g * n_chunks + c] = tot * inv;
+    if (lane == 0 && half == 1) half_sum[wave] = tot;
+    __syncthreads();
+    if (lane == 0 && half == 0 && live) scores[(int64_t)g * n_chunks + c] = (tot + half_sum[wave + 1]) * inv;
+    __syncthreads();
   }
 }
 
@@ -245,8 +261,9 @@ template <int D, bool kPow2>
 hipError_t launch_mfma_g(const bf16_t* q, const bf16_t* kc, int64_t stride, float* scores, int R,
                          int Hq, int Hkv, int chunk, float scale, int n_chunks, hipStream_t s) {
   const int rows = R * (Hq / Hkv);
-  // one chunk per wave (waves stride over chunks only past 65535 workgroups)
-  int blocks_x = (n_chunks + 3) / 4;
+  // 64-token chunks: two chunks a workgroup; otherwise one chunk a wave
+  // (workgroups stride over chunks only past 65535 of them)
+  int blocks_x = chunk == 64 ? (n_chunks + 1) / 2 : (n_chunks + 3) / 4;
   if (blocks_x > 65535) blocks_x = 65535;
   dim3 grid(blocks_x, Hkv);
   if (chunk == 64) {
