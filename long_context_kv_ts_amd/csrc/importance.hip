@@ -9,7 +9,9 @@
 // against all R*G query rows are one v_mfma_f32_16x16x32_bf16 chain per 16
 // rows, computed transposed (S^T = K Q^T) so that the K operand is loaded
 // straight from HBM into registers in the lane layout the instruction wants
-// and never passes through LDS. Each wave owns one chunk at a time. With G a
+// and never passes through LDS. A wave owns one chunk at a time (64-token
+// chunks: half a chunk, 32 keys, with the query fragments shared through LDS
+// by the workgroup). With G a
 // power of two a query's G heads are G aligned adjacent columns and their max
 // is a lane butterfly; other G (5, 6, 7 ... 15) pass the block's scores
 // through a per-wave LDS tile and each lane takes the max over its query's G

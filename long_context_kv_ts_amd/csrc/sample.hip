@@ -54,7 +54,6 @@ struct Lds {
 
 struct BlockRed {
   float red[kWavesS];
-  int ired[kWavesS];
 };
 
 struct PickLds {
@@ -305,18 +304,6 @@ __device__ float block_max(float v, float* red) {
   for (int w = 1; w < kWavesS; ++w) m = fmaxf(m, red[w]);
   __syncthreads();
   return m;
-}
-
-__device__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float t = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kWavesS; ++w) t += red[w];
-  __syncthreads();
-  return t;
 }
 
 // Exclusive prefix over the threads in index order; total = the sum of all.
