@@ -14,7 +14,8 @@ Inputs are seeded synthetic tensors resident in HBM before timing starts
 (verify inputs: seed 2; partial-KV inputs: seed 3, with 8 chunks per KV head
 carrying 3x keys). Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--cpu-heads H] [--cpu-seconds S] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--unfused] [--graph] [--cpu-heads H] [--cpu-seconds S]
+                    [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -46,6 +47,9 @@ def parse():
                     help="the CPU baseline repeats its sample until this much time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step instead of eager launches")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the merge and the importance as two launches (default: one launch, "
+                         "ts_attn_merge_and_importance)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -131,8 +135,23 @@ def main():
                                workspace=dws)
         rec(6)
 
+    # The verify merge and the chunk importance depend on nothing of each other:
+    # the timed step runs them as one launch (bit-identical results); the
+    # per-kernel pass below keeps them apart so that each has its own time.
+    def step_fused():
+        ops.tree_verify_attn_partials(q, kc, vcache, kd, vd, parent, scale=vc.scale,
+                                      o_part=o_part, l_part=l_part)
+        ops.attn_merge_and_importance(o_part, l_part, pq, pk, pc.chunk, out=out, lse=lse, scale=pc.scale,
+                                      scores=scores)
+        ops.kv_topk_select(scores, pc.k, chunk_idx=idx, chunk_score=idx_s)
+        ops.kv_gather(pk, pv, idx, pc.chunk, k_part=kp, v_part=vp)
+        ops.partial_draft_attn(pq, kp, vp, pkn, pvn, scale=pc.scale, out=dout, lse=dlse,
+                               workspace=dws)
+
+    run_step = step if args.unfused else step_fused
     for _ in range(args.warmup):
         step()
+        run_step()
     torch.cuda.synchronize()
 
     # With --graph the step is replayed as one HIP graph (nothing in it
@@ -141,7 +160,7 @@ def main():
     if args.graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
+            run_step()
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
@@ -153,7 +172,7 @@ def main():
         if graph is not None:
             graph.replay()
         else:
-            step()
+            run_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
@@ -215,7 +234,8 @@ def main():
                                "64 of 1600 64-token chunks) + 4-query draft attention",
                    "T": T, "Hq": Hq, "Hkv": Hkv, "head_dim": D, "kv_len": L, "splits": S,
                    "chunk": pc.chunk, "topk": pc.k},
-        "timing": "graph replay of the step" if graph is not None else "eager launches",
+        "timing": ("graph replay of the step" if graph is not None else "eager launches") +
+                  ("" if args.unfused else "; verify merge and chunk importance as one launch"),
         "eager_ms_per_step": round(eager_ms, 4),
         "verify_us": round(avg["verify_split"] + avg["verify_merge"], 2),
         "verify_hbm_frac": round(kv_bytes / ((avg["verify_split"] + avg["verify_merge"]) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

@@ -148,6 +148,29 @@ ts_status ts_kv_importance_score(const void* q_recent, const void* k_cache, int6
                                  int chunk, float scale, ts_dtype dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * ts_attn_merge followed by ts_kv_importance_score, in one launch where the
+ * shapes allow. In a decode step the verify pass's merge and the partial-KV
+ * refresh's chunk importance depend on nothing of each other, so both can run
+ * as one grid: its first workgroups merge rows, the others score chunks, each
+ * with its own kernel's code. The results are bit-identical to the two calls.
+ * This is a launch-level variant of those two operations (model card CLI
+ * example and summary page "Approach": verification of the drafts and the
+ * dynamic partial cache), not an operation of its own.
+ *
+ * Arguments: those of ts_attn_merge (o_part .. out_dtype, with Dv its D and
+ * out_dtype its dtype), then those of ts_kv_importance_score, with the same
+ * meaning, layout, checks and errors. The two operations' buffers must not
+ * overlap. One launch when Dv = D = 128, n_parts <= 16, dtype is bf16,
+ * chunk = 64 and R*(Hq/Hkv) <= 64; otherwise the two launches of the separate
+ * calls, merge first, on the same stream.
+ * ---------------------------------------------------------------------- */
+ts_status ts_attn_merge_and_importance(const float* o_part, const float* l_part, int n_parts, int rows, int Dv,
+                                       void* out, float* lse, ts_dtype out_dtype, const void* q_recent,
+                                       const void* k_cache, int64_t cache_stride, float* scores, int R, int Hq,
+                                       int Hkv, int D, int64_t L, int chunk, float scale, ts_dtype dtype,
+                                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Top-k chunk selection (model card CLI: retrieval budget 4096 tokens =
  * k chunks of `chunk` tokens). Per KV head independently: the k chunks of
  * highest score, ties broken toward the lower chunk index, written in

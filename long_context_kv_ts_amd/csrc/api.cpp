@@ -162,15 +162,22 @@ ts_status ts_tree_verify_attn_partials(const void* q, const void* k_cache, const
                      num_splits, stream);
 }
 
-ts_status ts_attn_merge(const float* o_part, const float* l_part, int n_parts, int rows, int D,
-                        void* out, float* lse, ts_dtype dtype, hipStream_t stream) {
-  const char* fn = "ts_attn_merge";
+static ts_status check_merge(const char* fn, const float* o_part, const float* l_part, int n_parts, int rows,
+                             int D, const void* out, ts_dtype dtype) {
   if (dtype != TS_F32 && dtype != TS_BF16) return fail(TS_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
   if (!o_part || !l_part || !out) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (n_parts < 1 || rows < 1) return fail(TS_ERR_INVALID_ARG, "%s: n_parts=%d rows=%d must be >= 1", fn, n_parts, rows);
   if (D != 64 && D != 128) return fail(TS_ERR_UNSUPPORTED, "%s: D=%d (supported: 64, 128)", fn, D);
   if (!aligned16(o_part) || ((uintptr_t)out & 7u) != 0)
     return fail(TS_ERR_INVALID_ARG, "%s: o_part must be 16-byte and out 8-byte aligned", fn);
+  return TS_OK;
+}
+
+ts_status ts_attn_merge(const float* o_part, const float* l_part, int n_parts, int rows, int D,
+                        void* out, float* lse, ts_dtype dtype, hipStream_t stream) {
+  const char* fn = "ts_attn_merge";
+  const ts_status st = check_merge(fn, o_part, l_part, n_parts, rows, D, out, dtype);
+  if (st != TS_OK) return st;
   return from_hip(launch_attn_merge(o_part, l_part, n_parts, rows, D, out, lse, dtype, stream), fn);
 }
 
@@ -228,10 +235,9 @@ ts_status ts_partial_draft_attn(const void* q, const void* k_part, const void* v
                      workspace_bytes, stream);
 }
 
-ts_status ts_kv_importance_score(const void* q_recent, const void* k_cache, int64_t cache_stride,
-                                 float* scores, int R, int Hq, int Hkv, int D, int64_t L,
-                                 int chunk, float scale, ts_dtype dtype, hipStream_t stream) {
-  const char* fn = "ts_kv_importance_score";
+static ts_status check_importance(const char* fn, const void* q_recent, const void* k_cache,
+                                  int64_t cache_stride, const float* scores, int R, int Hq, int Hkv, int D,
+                                  int64_t L, int chunk, float scale, ts_dtype dtype) {
   if (dtype != TS_F32 && dtype != TS_BF16) return fail(TS_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
   if (!q_recent || !k_cache || !scores) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (!aligned16(q_recent) || !aligned16(k_cache) || ((uintptr_t)scores & 3u))
@@ -249,8 +255,37 @@ ts_status ts_kv_importance_score(const void* q_recent, const void* k_cache, int6
   if (L / chunk > (1 << 24)) return fail(TS_ERR_UNSUPPORTED, "%s: too many chunks", fn);
   if (cache_stride < L) return fail(TS_ERR_INVALID_ARG, "%s: cache_stride < L", fn);
   if (!std::isfinite(scale)) return fail(TS_ERR_INVALID_ARG, "%s: scale not finite", fn);
+  return TS_OK;
+}
+
+ts_status ts_kv_importance_score(const void* q_recent, const void* k_cache, int64_t cache_stride,
+                                 float* scores, int R, int Hq, int Hkv, int D, int64_t L,
+                                 int chunk, float scale, ts_dtype dtype, hipStream_t stream) {
+  const char* fn = "ts_kv_importance_score";
+  const ts_status st = check_importance(fn, q_recent, k_cache, cache_stride, scores, R, Hq, Hkv, D, L, chunk,
+                                        scale, dtype);
+  if (st != TS_OK) return st;
   return from_hip(launch_importance(q_recent, k_cache, cache_stride, scores, R, Hq, Hkv, D, L,
                                     chunk, scale, dtype, stream), fn);
+}
+
+ts_status ts_attn_merge_and_importance(const float* o_part, const float* l_part, int n_parts, int rows, int Dv,
+                                       void* out, float* lse, ts_dtype out_dtype, const void* q_recent,
+                                       const void* k_cache, int64_t cache_stride, float* scores, int R, int Hq,
+                                       int Hkv, int D, int64_t L, int chunk, float scale, ts_dtype dtype,
+                                       hipStream_t stream) {
+  const char* fn = "ts_attn_merge_and_importance";
+  ts_status st = check_merge(fn, o_part, l_part, n_parts, rows, Dv, out, out_dtype);
+  if (st != TS_OK) return st;
+  st = check_importance(fn, q_recent, k_cache, cache_stride, scores, R, Hq, Hkv, D, L, chunk, scale, dtype);
+  if (st != TS_OK) return st;
+  if (L > 0 && merge_importance_fusable(n_parts, Dv, D, R, Hq, Hkv, chunk, dtype))
+    return from_hip(launch_merge_importance(o_part, l_part, n_parts, rows, out, lse, out_dtype, q_recent, k_cache,
+                                            cache_stride, scores, R, Hq, Hkv, L, scale, stream), fn);
+  st = from_hip(launch_attn_merge(o_part, l_part, n_parts, rows, Dv, out, lse, out_dtype, stream), fn);
+  if (st != TS_OK) return st;
+  return from_hip(launch_importance(q_recent, k_cache, cache_stride, scores, R, Hq, Hkv, D, L, chunk, scale, dtype,
+                                    stream), fn);
 }
 
 ts_status ts_kv_topk_select(const float* scores, int Hkv, int n_chunks, int k,

@@ -156,6 +156,13 @@ hipError_t launch_attn_merge(const float* o_part, const float* l_part, int n_par
 hipError_t launch_importance(const void* q, const void* kc, int64_t stride, float* scores,
                              int R, int Hq, int Hkv, int D, int64_t L, int chunk, float scale,
                              ts_dtype dtype, hipStream_t s);
+// The merge and the 64-token chunk importance in one grid (fused.hip), for the
+// shapes merge_importance_fusable accepts.
+bool merge_importance_fusable(int n_parts, int Dm, int Di, int R, int Hq, int Hkv, int chunk, ts_dtype dtype);
+hipError_t launch_merge_importance(const float* o_part, const float* l_part, int n_parts, int rows, void* out,
+                                   float* lse, ts_dtype out_dtype, const void* q, const void* kc,
+                                   int64_t stride, float* scores, int R, int Hq, int Hkv, int64_t L,
+                                   float scale, hipStream_t s);
 hipError_t launch_topk(const float* scores, int Hkv, int n, int k, int32_t* idx, float* val,
                        hipStream_t s);
 hipError_t launch_gather(const void* kc, const void* vc, int64_t stride, const int32_t* idx,

@@ -8,7 +8,7 @@ exception is raised.
 Entry points, named as the C functions without the ``ts_`` prefix:
 
 * verify and partial-cache step: ``tree_verify_attn``, ``tree_verify_attn_partials``,
-  ``attn_merge``, ``kv_importance_score``, ``kv_topk_select``, ``kv_gather``,
+  ``attn_merge``, ``kv_importance_score``, ``attn_merge_and_importance``, ``kv_topk_select``, ``kv_gather``,
   ``partial_draft_attn``;
 * decode step around them: ``build_draft_tree`` (with ``draft_tree_nodes``),
   ``sample_tokens``, ``accept_commit``, and the ``NgramTable`` class over
@@ -49,6 +49,9 @@ SIGNATURES = {
                                _c_int, _c_void_p]),
     "ts_kv_importance_score": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int,
                                         _c_int, _c_int, _c_i64, _c_int, _c_f, _c_int, _c_void_p]),
+    "ts_attn_merge_and_importance": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                              _c_int, _c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int,
+                                              _c_int, _c_int, _c_i64, _c_int, _c_f, _c_int, _c_void_p]),
     "ts_kv_topk_select": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "ts_kv_gather": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int, _c_int, _c_int,
                               _c_i64, _c_void_p, _c_void_p, _c_int, _c_void_p]),
@@ -280,6 +283,37 @@ def kv_importance_score(q_recent, k_cache, chunk: int, *, scale=None, scores=Non
         chunk, float(1.0 / math.sqrt(D) if scale is None else scale), _dtype_code(q_recent),
         _stream(dev)))
     return scores
+
+
+def attn_merge_and_importance(o_part, l_part, q_recent, k_cache, chunk: int, *, out_dtype=torch.bfloat16,
+                              out=None, lse=None, scale=None, scores=None):
+    """ts_attn_merge_and_importance: attn_merge(o_part, l_part) and
+    kv_importance_score(q_recent, k_cache, chunk) in one launch where the
+    shapes allow -> (out, lse, scores), bit-identical to the two calls."""
+    _contig(o_part, "o_part")
+    _contig(l_part, "l_part")
+    S, Dv = o_part.shape[0], o_part.shape[-1]
+    rows = o_part[0].numel() // Dv
+    if l_part.numel() != S * rows:
+        raise ValueError("l_part does not match o_part")
+    _need(q_recent, "q_recent", 3)
+    dev = q_recent.device
+    _need(k_cache, "k_cache", 3, q_recent.dtype, dev)
+    _contig(q_recent, "q_recent")
+    R, Hq, D = q_recent.shape
+    Hkv, L, _ = k_cache.shape
+    stride = _cache_stride(k_cache, "k_cache")
+    if out is None:
+        out = torch.empty(o_part.shape[1:], dtype=out_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(l_part.shape[1:], dtype=torch.float32, device=dev)
+    if scores is None:
+        scores = torch.empty((Hkv, L // chunk), dtype=torch.float32, device=dev)
+    _check(lib().ts_attn_merge_and_importance(
+        o_part.data_ptr(), l_part.data_ptr(), S, rows, Dv, out.data_ptr(), lse.data_ptr(), _dtype_code(out),
+        q_recent.data_ptr(), k_cache.data_ptr(), stride, scores.data_ptr(), R, Hq, Hkv, D, L, chunk,
+        float(1.0 / math.sqrt(D) if scale is None else scale), _dtype_code(q_recent), _stream(dev)))
+    return out, lse, scores
 
 
 def kv_topk_select(scores, k: int, *, chunk_idx=None, chunk_score=None, want_scores=True):

@@ -119,6 +119,30 @@ def test_partials_and_merge_reject():
     assert lib.ts_attn_merge(MIS, P, 2, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
 
 
+def test_merge_and_importance_rejects():
+    """ts_attn_merge_and_importance runs both argument checks of the separate
+    calls (nothing is launched on these calls)."""
+    lib = ops.lib()
+
+    def call(**kw):
+        a = dict(o=P, l=P, S=16, rows=3840, Dv=128, out=P, lse=P, odt=B, q=P, k=P, stride=4096, scores=P,
+                 R=4, Hq=32, Hkv=8, D=128, L=4096, chunk=64, scale=0.1, dt=B)
+        a.update(kw)
+        return lib.ts_attn_merge_and_importance(a["o"], a["l"], a["S"], a["rows"], a["Dv"], a["out"], a["lse"],
+                                                a["odt"], a["q"], a["k"], a["stride"], a["scores"], a["R"],
+                                                a["Hq"], a["Hkv"], a["D"], a["L"], a["chunk"], a["scale"],
+                                                a["dt"], None)
+    assert call(S=0) == ops.TS_ERR_INVALID_ARG
+    assert call(Dv=100) == ops.TS_ERR_UNSUPPORTED
+    assert call(o=MIS) == ops.TS_ERR_INVALID_ARG
+    assert "ts_attn_merge_and_importance" in _err()
+    assert call(L=4000) == ops.TS_ERR_UNSUPPORTED          # L not a multiple of chunk
+    assert call(Hq=30) == ops.TS_ERR_INVALID_ARG           # Hq not a multiple of Hkv
+    assert call(R=8, Hq=128) == ops.TS_ERR_UNSUPPORTED     # R*G = 128 > 64
+    assert call(q=None) == ops.TS_ERR_INVALID_ARG
+    assert call(dt=7) == ops.TS_ERR_INVALID_ARG
+
+
 def test_draft_attn_rejects():
     lib = ops.lib()
     st = lib.ts_partial_draft_attn(P, P, P, P, P, P, P, 0, 32, 8, 128, 4096, 0.1, B, 0, P, 1 << 30, None)
