@@ -10,6 +10,11 @@ One step = one pass of the whole path for one LLaMA3.1-8B-shaped layer
      top-64 of 1600 chunks per KV head -> gather of the 4096-token partial cache;
   3. the 4-query draft attention over the partial cache.
 
+The verify merge and the chunk importance depend on nothing of each other and
+run as one launch (ts_attn_merge_and_importance; --unfused keeps two). The
+per-kernel times come from a second pass with the two apart and HIP events
+between kernels.
+
 Inputs are seeded synthetic tensors resident in HBM before timing starts
 (verify inputs: seed 2; partial-KV inputs: seed 3, with 8 chunks per KV head
 carrying 3x keys). Prints ONE JSON line.
