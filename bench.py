@@ -11,22 +11,36 @@ One step = one pass of the whole path for one LLaMA3.1-8B-shaped layer
   3. the 4-query draft attention over the partial cache.
 
 The verify merge and the chunk importance depend on nothing of each other and
-run as one launch (ts_attn_merge_and_importance; --unfused keeps two). The
-per-kernel times come from a second pass with the two apart and HIP events
-between kernels.
+run as one launch (ts_attn_merge_and_importance; --unfused keeps two).
+
+Timing (all on the stream every call launches on, torch's current stream):
+  * warm-up: at least W steps, then steps until at least --min-warm-s seconds
+    have passed and the last three 20-step batches agree within 2% (the chip
+    settles at its power limit a few milliseconds into sustained matrix-core
+    load), capped at --max-warm-s;
+  * the step (value): K steps back to back between two device syncs, wall
+    clock; HIP events between the steps give the per-step median/p10/p90;
+  * cold steps: each rep first writes a 1 GiB scratch buffer and reads it
+    back (outside the events), so that neither the 256 MB last-level cache
+    nor the L2 holds any input and no dirty line of the flush is left to be
+    written out during the timed call, then times one step;
+  * the fused and the unfused step alternated, each timed by events;
+  * per-kernel durations (HIP events between the kernels of the unfused step):
+    the roofline of the dominant kernel;
+  * one ts_tree_verify_attn call (split + merge), cold and warm, at 20,480 and
+    102,400 cached tokens (LLaMA3.1-8B) and at 102,400 (LLaMA2-7B MHA).
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts
 (verify inputs: seed 2; partial-KV inputs: seed 3, with 8 chunks per KV head
 carrying 3x keys). Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--unfused] [--graph] [--cpu-heads H] [--cpu-seconds S]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--no-verify-lines] [--no-probes] [--calibrate-copy]
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -39,6 +53,7 @@ sys.path.insert(0, ROOT)
 METRIC = "µs per tree-verify step @100K KV (LLaMA3.1-8B layer shape) + % HBM peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+FLUSH_BYTES = 1 << 30           # scratch written before each cold rep
 
 
 def parse():
@@ -46,11 +61,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--min-warm-s", type=float, default=1.0,
+                    help="warm up for at least this long (and until step times settle)")
+    ap.add_argument("--max-warm-s", type=float, default=8.0)
+    ap.add_argument("--cold-reps", type=int, default=30)
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="KV heads of the step the CPU oracle runs for the baseline (of 8)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="the CPU baseline repeats its sample until this much time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify-lines", action="store_true",
+                    help="skip the per-workload verify-call lines (20K, 100K, MHA 100K)")
+    ap.add_argument("--no-probes", action="store_true", help="skip the measured-ceiling probes")
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step instead of eager launches")
     ap.add_argument("--unfused", action="store_true",
                     help="time the merge and the importance as two launches (default: one launch, "
@@ -66,6 +88,84 @@ def to_dev(a, dtype, dev):
     if dtype == "bf16":
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
     return torch.from_numpy(a).to(dev)
+
+
+def stats(us):
+    xs = sorted(us)
+    q = lambda p: float(np.percentile(xs, p))
+    return {"median": round(q(50), 2), "p10": round(q(10), 2), "p90": round(q(90), 2),
+            "mean": round(float(np.mean(xs)), 2), "n": len(xs)}
+
+
+def log(msg):
+    print(f"# {msg}", file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Event timing on the current stream, plus the cold-cache flush."""
+
+    def __init__(self, dev):
+        import torch
+        self.torch = torch
+        self.dev = dev
+        self.flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+        self.sink = torch.empty(256, dtype=torch.int32, device=dev)
+        self.n_flush = 0
+
+    def events(self, n):
+        return [self.torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    def back_to_back(self, fn, reps):
+        """Per-call µs of `reps` back-to-back calls."""
+        ev = self.events(reps + 1)
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        self.torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]
+
+    def flush(self):
+        # A 1 GiB write evicts the 256 MB last-level cache and the L2; reading
+        # the buffer back then writes those dirty lines out before the timed
+        # call starts, so the call competes with no write-back of the flush.
+        from long_context_kv_ts_amd import probe
+        self.n_flush += 1
+        self.flush_buf.fill_(self.n_flush & 0x7FFFFFFF)
+        rc = probe.lib().ts_probe_stream_read(self.flush_buf.data_ptr(), FLUSH_BYTES, self.sink.data_ptr(),
+                                              self.torch.cuda.current_stream(self.dev).cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"flush read failed (hipError {rc})")
+
+    def cold(self, fn, reps):
+        """Per-call µs of `reps` calls, each after a 1 GiB scratch write and read-back (outside the events)."""
+        ev = self.events(2 * reps)
+        for i in range(reps):
+            self.flush()
+            ev[2 * i].record()
+            fn()
+            ev[2 * i + 1].record()
+        self.torch.cuda.synchronize()
+        return [ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(reps)]
+
+    def steady(self, fn, min_steps, min_s, max_s, batch=20, tol=0.02):
+        """Run `fn` at least `min_steps` times, then in batches until `min_s`
+        seconds have passed and the last three batch means agree within `tol`
+        (or `max_s` seconds have passed)."""
+        for _ in range(min_steps):
+            fn()
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        means, n = [], min_steps
+        while True:
+            means.append(float(np.mean(self.back_to_back(fn, batch))))
+            n += batch
+            el = time.perf_counter() - t0
+            last = means[-3:]
+            settled = len(last) == 3 and max(last) <= min(last) * (1.0 + tol)
+            if (el >= min_s and settled) or el >= max_s:
+                return {"steps": n, "seconds": round(el, 2), "settled": settled,
+                        "last_batch_means_us": [round(x, 2) for x in last]}
 
 
 def main():
@@ -93,7 +193,7 @@ def main():
     t0 = time.time()
     vc = inputs.workload("llama8b_100k")
     pc = inputs.workload("partial_100k")
-    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
 
     # ---- device-resident inputs and preallocated outputs -------------------
     q = to_dev(vc.q, "bf16", dev)
@@ -153,12 +253,10 @@ def main():
         ops.partial_draft_attn(pq, kp, vp, pkn, pvn, scale=pc.scale, out=dout, lse=dlse,
                                workspace=dws)
 
+    tm = Timer(dev)
     run_step = step if args.unfused else step_fused
-    for _ in range(args.warmup):
+    for _ in range(2):
         step()
-        run_step()
-    torch.cuda.synchronize()
-
     # With --graph the step is replayed as one HIP graph (nothing in it
     # allocates or clears memory); by default the launches are eager.
     graph = None
@@ -166,51 +264,51 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             run_step()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
+        timed_step = graph.replay
+    else:
+        timed_step = run_step
+    warm = tm.steady(timed_step, args.warmup, args.min_warm_s, args.max_warm_s)
+    log(f"warm-up: {warm}")
 
-    # timed region 1: K steps, wall clock between two syncs
+    # ---- the step: K steps back to back, wall clock between two syncs --------
+    ev = tm.events(args.steps + 1)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    ev[0].record()
     for i in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            run_step()
+        timed_step()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
+    step_warm = stats([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(args.steps)])
+    log(f"step: {ms_per_step * 1e3:.1f} us/step wall, events {step_warm}")
 
-    # timed region 2: the same K steps launched eagerly with HIP events between
-    # the kernels (on torch's current stream, which every call launches on):
-    # per-kernel durations for the roofline
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    # ---- cold steps ----------------------------------------------------------
+    step_cold = stats(tm.cold(timed_step, args.cold_reps))
+
+    # ---- the fused and the unfused step, alternated --------------------------
+    fu, un = [], []
+    for _ in range(max(args.steps // 2, 10)):
+        fu += tm.back_to_back(step_fused, 2)
+        un += tm.back_to_back(step, 2)
+    alternated = {"fused": stats(fu), "unfused": stats(un)}
+
+    # ---- per-kernel durations (unfused step, events between the kernels) ------
+    events = [tm.events(7) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t2 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t2) * 1e3 / args.steps
-
     per = {n: [] for n in names}
-    for ev in events:
+    for e in events:
         for j, n in enumerate(names):
-            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # us
+            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)   # us
     avg = {n: float(np.mean(v)) for n, v in per.items()}
     med = {n: float(np.median(v)) for n, v in per.items()}
 
     # ---- roofline of the dominant kernel (verify split-K) -------------------
-    vis = 0
-    par = vc.parent
-    for t in range(T):           # |A(t)| summed over draft rows (the ancestor walk of the mask)
-        a = t
-        while a >= 0:
-            vis += 1
-            a = int(par[a])
-    G = Hq // Hkv
-    pairs = Hq * (T * L + vis)                  # (query row, visible key) pairs
-    flops = 4.0 * D * pairs                     # QK^T and PV, 2 flops per MAC
+    flops = verify_flops(vc)
     kv_bytes = 2.0 * Hkv * L * D * 2            # K and V of the cache, read once
     t_split = avg["verify_split"] * 1e-6
     achieved = flops / t_split / 1e12
@@ -240,14 +338,24 @@ def main():
                    "T": T, "Hq": Hq, "Hkv": Hkv, "head_dim": D, "kv_len": L, "splits": S,
                    "chunk": pc.chunk, "topk": pc.k},
         "timing": ("graph replay of the step" if graph is not None else "eager launches") +
-                  ("" if args.unfused else "; verify merge and chunk importance as one launch"),
-        "eager_ms_per_step": round(eager_ms, 4),
-        "verify_us": round(avg["verify_split"] + avg["verify_merge"], 2),
-        "verify_hbm_frac": round(kv_bytes / ((avg["verify_split"] + avg["verify_merge"]) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                  ("" if args.unfused else "; verify merge and chunk importance as one launch") +
+                  "; value = wall clock of the back-to-back steps after a settled warm-up",
+        "warmup_settled": warm,
+        "step_us": {"warm": step_warm, "cold": step_cold},
+        "step_alternated_us": alternated,
         "kernel_us_avg": {n: round(v, 2) for n, v in avg.items()},
         "kernel_us_median": {n: round(v, 2) for n, v in med.items()},
         "roofline": roofline,
     }
+
+    # ---- one ts_tree_verify_attn call per workload ----------------------------
+    if not args.no_verify_lines:
+        res["verify_call_us"] = verify_lines(tm, dev, vc, (q, kc, vcache, kd, vd, parent), args)
+    peaks = None
+    if not args.no_probes:
+        peaks = measured_peaks(dev)
+        res["measured_peaks"] = peaks
+        roofline["frac_of_measured_mfma"] = round(achieved / peaks["mfma_bf16"]["sustained_tflops"], 4)
 
     res["accept_commit_us"] = time_accept_commit(vc, dev, args.steps)
     res["draft_tree_us"] = time_draft_tree(dev, args.steps)
@@ -257,6 +365,68 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(vc, pc, args.cpu_heads, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def verify_flops(c):
+    """Algorithmic flops of one verify call: 4*D per (query row, visible key)
+    pair, QK^T and PV at 2 flops per multiply-add."""
+    vis = 0
+    for t in range(c.T):           # |A(t)| summed over draft rows (the ancestor walk of the mask)
+        a = t
+        while a >= 0:
+            vis += 1
+            a = int(c.parent[a])
+    return 4.0 * c.D * c.Hq * (c.T * c.L + vis)
+
+
+def verify_lines(tm, dev, vc2, resident, args):
+    """One ts_tree_verify_attn call (split + merge, library-chosen splits) per
+    workload: median/p10/p90 cold (1 GiB scratch write and read-back before each call) and
+    warm (back to back), with %HBM of the cache's K+V and %MFMA of 2.5 PF."""
+    import torch
+    from long_context_kv_ts_amd import inputs, ops
+    lines = {}
+    for name in ("llama8b_100k", "llama8b_20k", "llama2_mha_100k"):
+        if name == "llama8b_100k":
+            c, (q, kc, vc, kd, vd, par) = vc2, resident
+        else:
+            t0 = time.time()
+            c = inputs.workload(name)
+            q, kc, vc = to_dev(c.q, "bf16", dev), to_dev(c.k_cache, "bf16", dev), to_dev(c.v_cache, "bf16", dev)
+            kd, vd, par = to_dev(c.k_draft, "bf16", dev), to_dev(c.v_draft, "bf16", dev), to_dev(c.parent, "i32", dev)
+            log(f"{name}: inputs in {time.time() - t0:.1f}s")
+        out = torch.empty_like(q)
+        lse = torch.empty((c.T, c.Hq), dtype=torch.float32, device=dev)
+        ws = ops.alloc_workspace(ops.verify_workspace_bytes(c.T, c.Hq, c.Hkv, c.D, c.L, torch.bfloat16), dev)
+        call = lambda: ops.tree_verify_attn(q, kc, vc, kd, vd, par, scale=c.scale, out=out, lse=lse, workspace=ws)
+        tm.steady(call, 3, 0.5, 4.0)
+        warm = stats(tm.back_to_back(call, args.steps))
+        cold = stats(tm.cold(call, args.cold_reps))
+        kv = 2.0 * c.Hkv * c.L * c.D * 2
+        fl = verify_flops(c)
+        t = cold["median"] * 1e-6
+        lines[name] = {"cold": cold, "warm": warm, "kv_bytes": kv, "flops": fl,
+                       "splits": ops.num_splits(c.T, c.Hq, c.Hkv, c.D, c.L, torch.bfloat16),
+                       "hbm_frac_cold": round(kv / t / 1e9 / HBM_PEAK_GBS, 4),
+                       "mfma_frac_cold": round(fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "hbm_frac_warm": round(kv / (warm["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"verify call {name}: cold {cold['median']} us, warm {warm['median']} us")
+        if name != "llama8b_100k":
+            del q, kc, vc, kd, vd, par
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return lines
+
+
+def measured_peaks(dev):
+    """What this GPU sustains, from the probe kernels (libts_probe.so)."""
+    from long_context_kv_ts_amd import probe
+    return {"mfma_bf16": probe.mfma_bf16_peak(dev),
+            "mfma_bf16_constant_operands": probe.mfma_bf16_peak(dev, toggle=False, seconds=0.2),
+            "mfma_bf16_1wave": probe.mfma_bf16_peak(dev, waves_per_simd=1, seconds=0.2),
+            "hbm_stream_read": probe.stream_read(dev),
+            "ns_per_wave_instr_per_simd": {"v_fma_f32": probe.valu_issue(dev, 0),
+                                           "v_exp_f32": probe.valu_issue(dev, 1)}}
 
 
 def time_accept_commit(vc, dev, reps):
@@ -437,6 +607,7 @@ def cpu_baseline(vc, pc, heads, min_seconds):
             "host_cores": cores, "kind": "oracle",
             "sample": f"{what} (verify + importance + top-k + gather + draft attention), float64 numpy, "
                       f"mean of {reps} runs over {dt:.1f} s" + (f", time x{scale:g}" if heads != vc.Hkv else "")}
+
 
 if __name__ == "__main__":
     main()

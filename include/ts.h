@@ -82,7 +82,8 @@ int ts_abi_version(void);
  *            outside [-1, t) are treated as -1 (never read out of bounds).
  *   out      [T][Hq][D]   written in `dtype`
  *   lse      [T][Hq] fp32, may be NULL
- *   scale    softmax scale (usually 1/sqrt(D))
+ *   scale    softmax scale (usually 1/sqrt(D)); finite and > 0, else
+ *            TS_ERR_INVALID_ARG
  *   num_splits  0 = library choice; otherwise the number of key ranges the
  *            work is split into (results agree across choices up to fp32
  *            rounding). Must match the value given to the size query.

@@ -19,6 +19,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libts.so")
+# measurement probes of the benchmark (matrix-core and vector-ALU rates, HBM
+# streaming read), kept out of the hot-path library
+PROBE_LIB = os.path.join(PKG, "libts_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 SOURCES = ["api.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_small.hip", "attn_merge.hip",
            "importance.hip", "topk.hip", "gather.hip", "accept.hip", "tree.hip", "sample.hip", "ngram.hip",
@@ -53,19 +57,25 @@ def _compile(src: str, hipcc: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    hipcc = _hipcc()
-    os.makedirs(OUT_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, hipcc), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, hipcc: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    hipcc = _hipcc()
+    os.makedirs(OUT_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, hipcc), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, hipcc)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, hipcc)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

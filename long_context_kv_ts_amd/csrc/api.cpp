@@ -131,7 +131,10 @@ static ts_status attn_common(const char* fn, const void* q, const void* kc, cons
     return fail(TS_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
   if (((uintptr_t)l_part & 3u) != 0) return fail(TS_ERR_INVALID_ARG, "%s: l_part misaligned", fn);
   if (cache_stride < L) return fail(TS_ERR_INVALID_ARG, "%s: cache_stride=%lld < L=%lld", fn, (long long)cache_stride, (long long)L);
-  if (!std::isfinite(scale) || scale == 0.f) return fail(TS_ERR_INVALID_ARG, "%s: scale must be finite and non-zero", fn);
+  // The kernels take each row's maximum of the raw products and scale it
+  // afterwards, which is the maximum of the scaled logits only for scale > 0.
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(TS_ERR_INVALID_ARG, "%s: scale must be finite and > 0 (got %g)", fn, (double)scale);
 
   const AttnPlan plan = plan_attention(T, Hq, Hkv, D, L, dtype, num_splits);
   // one workgroup per (split, KV head, row group), rounded up to a multiple of 8 per row group

@@ -153,6 +153,49 @@ def _contig(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _out(t: Optional[torch.Tensor], name: str, shape, dtype, device) -> Optional[torch.Tensor]:
+    """Check a caller-supplied output buffer: the C ABI sees only its address,
+    so a wrong size or type would become an out-of-bounds device write."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _workspace(t: Optional[torch.Tensor], name: str, need: int, device) -> Optional[torch.Tensor]:
+    """Check a caller-supplied workspace: a contiguous device buffer of at least `need` bytes."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, {need} required")
+    return t
+
+
+def _parts(o_part, l_part, device=None) -> None:
+    """Split partials: o_part [S][..][D] and l_part [S][..], fp32 on one GPU."""
+    if not isinstance(o_part, torch.Tensor) or o_part.dim() < 2:
+        raise ValueError("o_part must be a [S][..][D] tensor")
+    _need(o_part, "o_part", o_part.dim(), torch.float32, device)
+    _need(l_part, "l_part", o_part.dim() - 1, torch.float32, o_part.device)
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 # ---------------------------------------------------------------------------
 # workspace
 # ---------------------------------------------------------------------------
@@ -209,18 +252,21 @@ def tree_verify_attn(q, k_cache, v_cache, k_draft, v_draft, parent, *, scale=Non
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    _out(out, "out", (T, Hq, D), q.dtype, dev)
+    _out(lse, "lse", (T, Hq), torch.float32, dev)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
     need = verify_workspace_bytes(T, Hq, Hkv, D, L, q.dtype, num_splits)
+    _workspace(workspace, "workspace", need, dev)
     if workspace is None:
         workspace = alloc_workspace(need, dev)
     _check(lib().ts_tree_verify_attn(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stride, k_draft.data_ptr(),
         v_draft.data_ptr(), parent.data_ptr(), out.data_ptr(),
         lse.data_ptr() if lse is not None else None, T, Hq, Hkv, D, L, float(scale), code,
-        num_splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev)))
+        num_splits, workspace.data_ptr(), _nbytes(workspace), _stream(dev)))
     return out, lse
 
 
@@ -230,16 +276,30 @@ def tree_verify_attn_partials(q, k_cache, v_cache, k_draft, v_draft, parent, *, 
     _need(q, "q", 3)
     dev = q.device
     T, Hq, D = q.shape
-    Hkv, L, _ = k_cache.shape
-    _contig(q, "q")
+    _need(k_cache, "k_cache", 3, q.dtype, dev)
+    _need(v_cache, "v_cache", 3, q.dtype, dev)
+    _need(k_draft, "k_draft", 3, q.dtype, dev)
+    _need(v_draft, "v_draft", 3, q.dtype, dev)
+    _need(parent, "parent", 1, torch.int32, dev)
+    Hkv, L, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if tuple(k_draft.shape) != (Hkv, T, D) or tuple(v_draft.shape) != (Hkv, T, D):
+        raise ValueError(f"drafts must be [{Hkv}][{T}][{D}]")
+    if parent.shape[0] != T:
+        raise ValueError("parent must have T entries")
+    for n, t in (("q", q), ("k_draft", k_draft), ("v_draft", v_draft), ("parent", parent)):
+        _contig(t, n)
     stride = _cache_stride(k_cache, "k_cache")
+    if _cache_stride(v_cache, "v_cache") != stride:
+        raise ValueError("k_cache and v_cache must share the row stride")
     S = globals()["num_splits"](T, Hq, Hkv, D, L, q.dtype, num_splits)
+    _out(o_part, "o_part", (S, T, Hq, D), torch.float32, dev)
+    _out(l_part, "l_part", (S, T, Hq), torch.float32, dev)
     if o_part is None:
         o_part = torch.empty((S, T, Hq, D), dtype=torch.float32, device=dev)
     if l_part is None:
         l_part = torch.empty((S, T, Hq), dtype=torch.float32, device=dev)
-    if o_part.numel() < S * T * Hq * D or l_part.numel() < S * T * Hq:
-        raise ValueError("partial buffers too small")
     _check(lib().ts_tree_verify_attn_partials(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stride, k_draft.data_ptr(),
         v_draft.data_ptr(), parent.data_ptr(), o_part.data_ptr(), l_part.data_ptr(), T, Hq, Hkv,
@@ -250,14 +310,17 @@ def tree_verify_attn_partials(q, k_cache, v_cache, k_draft, v_draft, parent, *, 
 
 def attn_merge(o_part, l_part, *, out_dtype=torch.bfloat16, out=None, lse=None):
     """ts_attn_merge over the leading (parts) dim: o_part [S][..][D], l_part [S][..]."""
+    _parts(o_part, l_part)
+    dev = o_part.device
     _contig(o_part, "o_part")
     _contig(l_part, "l_part")
     S = o_part.shape[0]
     D = o_part.shape[-1]
     rows = o_part[0].numel() // D
-    if l_part.numel() != S * rows:
+    if tuple(l_part.shape) != tuple(o_part.shape[:-1]):
         raise ValueError("l_part does not match o_part")
-    dev = o_part.device
+    _out(out, "out", o_part.shape[1:], out.dtype if out is not None else out_dtype, dev)
+    _out(lse, "lse", l_part.shape[1:], torch.float32, dev)
     if out is None:
         out = torch.empty(o_part.shape[1:], dtype=out_dtype, device=dev)
     if lse is None:
@@ -276,6 +339,7 @@ def kv_importance_score(q_recent, k_cache, chunk: int, *, scale=None, scores=Non
     R, Hq, D = q_recent.shape
     Hkv, L, _ = k_cache.shape
     stride = _cache_stride(k_cache, "k_cache")
+    _out(scores, "scores", (Hkv, L // max(int(chunk), 1)), torch.float32, dev)
     if scores is None:
         scores = torch.empty((Hkv, L // chunk), dtype=torch.float32, device=dev)
     _check(lib().ts_kv_importance_score(
@@ -290,19 +354,23 @@ def attn_merge_and_importance(o_part, l_part, q_recent, k_cache, chunk: int, *, 
     """ts_attn_merge_and_importance: attn_merge(o_part, l_part) and
     kv_importance_score(q_recent, k_cache, chunk) in one launch where the
     shapes allow -> (out, lse, scores), bit-identical to the two calls."""
+    _need(q_recent, "q_recent", 3)
+    dev = q_recent.device
+    _parts(o_part, l_part, dev)
     _contig(o_part, "o_part")
     _contig(l_part, "l_part")
     S, Dv = o_part.shape[0], o_part.shape[-1]
     rows = o_part[0].numel() // Dv
-    if l_part.numel() != S * rows:
+    if tuple(l_part.shape) != tuple(o_part.shape[:-1]):
         raise ValueError("l_part does not match o_part")
-    _need(q_recent, "q_recent", 3)
-    dev = q_recent.device
     _need(k_cache, "k_cache", 3, q_recent.dtype, dev)
     _contig(q_recent, "q_recent")
     R, Hq, D = q_recent.shape
     Hkv, L, _ = k_cache.shape
     stride = _cache_stride(k_cache, "k_cache")
+    _out(out, "out", o_part.shape[1:], out.dtype if out is not None else out_dtype, dev)
+    _out(lse, "lse", l_part.shape[1:], torch.float32, dev)
+    _out(scores, "scores", (Hkv, L // max(int(chunk), 1)), torch.float32, dev)
     if out is None:
         out = torch.empty(o_part.shape[1:], dtype=out_dtype, device=dev)
     if lse is None:
@@ -322,6 +390,8 @@ def kv_topk_select(scores, k: int, *, chunk_idx=None, chunk_score=None, want_sco
     _contig(scores, "scores")
     Hkv, n = scores.shape
     dev = scores.device
+    _out(chunk_idx, "chunk_idx", (Hkv, k), torch.int32, dev)
+    _out(chunk_score, "chunk_score", (Hkv, k), torch.float32, dev)
     if chunk_idx is None:
         chunk_idx = torch.empty((Hkv, k), dtype=torch.int32, device=dev)
     if chunk_score is None and want_scores:
@@ -344,6 +414,10 @@ def kv_gather(k_cache, v_cache, chunk_idx, chunk: int, *, k_part=None, v_part=No
     stride = _cache_stride(k_cache, "k_cache")
     if _cache_stride(v_cache, "v_cache") != stride:
         raise ValueError("k_cache and v_cache must share the row stride")
+    if tuple(v_cache.shape) != (Hkv, L, D):
+        raise ValueError("v_cache must have the shape of k_cache")
+    _out(k_part, "k_part", (Hkv, k * chunk, D), k_cache.dtype, dev)
+    _out(v_part, "v_part", (Hkv, k * chunk, D), k_cache.dtype, dev)
     if k_part is None:
         k_part = torch.empty((Hkv, k * chunk, D), dtype=k_cache.dtype, device=dev)
     if v_part is None:
@@ -372,6 +446,11 @@ def build_draft_tree(logits, shape, *, parent=None, draft_tok=None, cand=None, w
     dev = logits.device
     P, V = logits.shape
     T = draft_tree_nodes(shape)
+    _out(parent, "parent", (T,), torch.int32, dev)
+    _out(draft_tok, "draft_tok", (T,), torch.int32, dev)
+    _out(cand, "cand", (len(shape), 16), torch.int32, dev)
+    need = int(lib().ts_build_draft_tree_workspace(V, len(shape)))
+    _workspace(workspace, "workspace", need, dev)
     if parent is None:
         parent = torch.empty(T, dtype=torch.int32, device=dev)
     if draft_tok is None:
@@ -379,11 +458,11 @@ def build_draft_tree(logits, shape, *, parent=None, draft_tok=None, cand=None, w
     if cand is None:
         cand = torch.empty((len(shape), 16), dtype=torch.int32, device=dev)
     if workspace is None:
-        workspace = alloc_workspace(int(lib().ts_build_draft_tree_workspace(V, len(shape))), dev)
+        workspace = alloc_workspace(need, dev)
     arr = (ctypes.c_int32 * len(shape))(*[int(k) for k in shape])
     _check(lib().ts_build_draft_tree(logits.data_ptr(), P, V, ctypes.cast(arr, ctypes.c_void_p), len(shape),
                                      parent.data_ptr(), draft_tok.data_ptr(), cand.data_ptr(),
-                                     _dtype_code(logits), workspace.data_ptr(), workspace.numel(),
+                                     _dtype_code(logits), workspace.data_ptr(), _nbytes(workspace),
                                      _stream(dev)))
     return parent, draft_tok, cand
 
@@ -415,6 +494,11 @@ def accept_commit(parent, draft_tok, target_tok, rand_u32: int, k_cache, v_cache
         raise ValueError("k_cache and v_cache must share the row stride")
     if cap < L + T:
         raise ValueError(f"cache capacity {cap} < L + T = {L + T}")
+    if tuple(v_cache.shape) != (Hkv, cap, D):
+        raise ValueError("v_cache must have the shape of k_cache")
+    _out(n_accepted, "n_accepted", (1,), torch.int32, dev)
+    _out(path, "path", (T,), torch.int32, dev)
+    _out(bonus, "bonus", (1,), torch.int32, dev)
     if n_accepted is None:
         n_accepted = torch.empty(1, dtype=torch.int32, device=dev)
     if path is None:
@@ -458,15 +542,18 @@ def sample_tokens(logits, *, hist=None, parent=None, draft_tok=None, window: int
         _contig(u, "u")
         if u.shape[0] != R:
             raise ValueError("u must have one uniform per row")
+    _out(tok, "tok", (R,), torch.int32, dev)
+    need = int(lib().ts_sample_workspace(R, V))
+    _workspace(workspace, "workspace", need, dev)
     if tok is None:
         tok = torch.empty(R, dtype=torch.int32, device=dev)
     if workspace is None:
-        workspace = alloc_workspace(int(lib().ts_sample_workspace(R, V)), dev)
+        workspace = alloc_workspace(need, dev)
     ptr = lambda t: t.data_ptr() if t is not None and t.numel() else None
     _check(lib().ts_sample_tokens(logits.data_ptr(), R, V, ptr(hist), n_hist, ptr(parent), ptr(draft_tok), T,
                                   int(window), float(penalty), float(temperature), float(min_p),
                                   ptr(u) if temperature > 0 else None, tok.data_ptr(), _dtype_code(logits),
-                                  workspace.data_ptr(), workspace.numel(), _stream(dev)))
+                                  workspace.data_ptr(), _nbytes(workspace), _stream(dev)))
     return tok
 
 
@@ -502,6 +589,11 @@ class NgramTable:
     def retrieve(self, first_tok, k: int = 20, *, out_tok=None, out_count=None, n_found=None, workspace=None):
         _need(first_tok, "first_tok", 1, torch.int32, self.device)
         dev = self.device
+        _out(out_tok, "out_tok", (k, 4), torch.int32, dev)
+        _out(out_count, "out_count", (k,), torch.int32, dev)
+        _out(n_found, "n_found", (1,), torch.int32, dev)
+        need = int(lib().ts_ngram_retrieve_workspace(self.max_entries, k))
+        _workspace(workspace, "workspace", need, dev)
         if out_tok is None:
             out_tok = torch.empty((k, 4), dtype=torch.int32, device=dev)
         if out_count is None:
@@ -509,10 +601,10 @@ class NgramTable:
         if n_found is None:
             n_found = torch.empty(1, dtype=torch.int32, device=dev)
         if workspace is None:
-            workspace = alloc_workspace(int(lib().ts_ngram_retrieve_workspace(self.max_entries, k)), dev)
+            workspace = alloc_workspace(need, dev)
         _check(lib().ts_ngram_retrieve(self.buf.data_ptr(), self.max_entries, first_tok.data_ptr(), int(k),
                                        out_tok.data_ptr(), out_count.data_ptr(), n_found.data_ptr(),
-                                       workspace.data_ptr(), workspace.numel(), _stream(dev)))
+                                       workspace.data_ptr(), _nbytes(workspace), _stream(dev)))
         return out_tok, out_count, n_found
 
     def header(self) -> dict:
@@ -532,8 +624,14 @@ def partial_draft_attn(q, k_part, v_part, k_new, v_new, *, scale=None, out=None,
         _need(t, n, 3, q.dtype, dev)
         _contig(t, n)
     _contig(q, "q")
-    Hkv, P, _ = k_part.shape
+    Hkv, P, Dk = k_part.shape
+    if Dk != D or tuple(v_part.shape) != (Hkv, P, D):
+        raise ValueError("partial cache shapes do not match q")
+    if tuple(k_new.shape) != (Hkv, Tq, D) or tuple(v_new.shape) != (Hkv, Tq, D):
+        raise ValueError(f"k_new / v_new must be [{Hkv}][{Tq}][{D}]")
     code = _dtype_code(q)
+    _out(out, "out", (Tq, Hq, D), q.dtype, dev)
+    _out(lse, "lse", (Tq, Hq), torch.float32, dev)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -541,11 +639,12 @@ def partial_draft_attn(q, k_part, v_part, k_new, v_new, *, scale=None, out=None,
     need = int(lib().ts_partial_draft_attn_workspace(Tq, Hq, Hkv, D, P, code, num_splits))
     if need == 0:
         raise TsError(TS_ERR_INVALID_ARG, lib().ts_last_error().decode())
+    _workspace(workspace, "workspace", need, dev)
     if workspace is None:
         workspace = alloc_workspace(need, dev)
     _check(lib().ts_partial_draft_attn(
         q.data_ptr(), k_part.data_ptr(), v_part.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
         out.data_ptr(), lse.data_ptr() if lse is not None else None, Tq, Hq, Hkv, D, P,
         float(1.0 / math.sqrt(D) if scale is None else scale), code, num_splits,
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(dev)))
+        workspace.data_ptr(), _nbytes(workspace), _stream(dev)))
     return out, lse

@@ -77,6 +77,9 @@ def _err():
     (dict(wsb=1024), ops.TS_ERR_WORKSPACE, "required"),
     (dict(dtype=7), ops.TS_ERR_INVALID_ARG, "dtype"),
     (dict(scale=float("nan")), ops.TS_ERR_INVALID_ARG, "scale"),
+    (dict(scale=0.0), ops.TS_ERR_INVALID_ARG, "scale"),
+    (dict(scale=-0.088), ops.TS_ERR_INVALID_ARG, "> 0"),
+    (dict(scale=float("inf")), ops.TS_ERR_INVALID_ARG, "scale"),
     (dict(ns=-2), ops.TS_ERR_INVALID_ARG, "num_splits"),
 ])
 def test_verify_rejects(kw, status, needle):
@@ -149,6 +152,12 @@ def test_draft_attn_rejects():
     assert st == ops.TS_ERR_UNSUPPORTED and "ts_partial_draft_attn" in _err()
     st = lib.ts_partial_draft_attn(P, P, P, P, P, P, P, 4, 32, 8, 128, 4096, 0.1, B, 0, P, 16, None)
     assert st == ops.TS_ERR_WORKSPACE
+    # a negative scale would turn each row's maximum into its minimum (and masked
+    # -inf logits into +inf): rejected before any launch
+    st = lib.ts_partial_draft_attn(P, P, P, P, P, P, P, 4, 32, 8, 128, 4096, -0.1, B, 0, P, 1 << 30, None)
+    assert st == ops.TS_ERR_INVALID_ARG and "> 0" in _err()
+    st = lib.ts_tree_verify_attn_partials(P, P, P, 64, P, P, P, P, P, 4, 4, 1, 64, 64, -0.1, F, 0, None)
+    assert st == ops.TS_ERR_INVALID_ARG and "> 0" in _err()
 
 
 @pytest.mark.parametrize("args,status", [

@@ -176,7 +176,7 @@ def test_out_of_range_parents_are_roots():
 # ---------------------------------------------------------------------------
 # structured full-size pins
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["llama8b_100k", "llama2_mha_100k"])
+@pytest.mark.parametrize("name", ["llama8b_20k", "llama8b_100k", "llama2_mha_100k"])
 def test_zero_keys_count_every_visible_key(name):
     """All keys zero: every logit is exactly 0, so lse[t,h] = ln(L + |A(t)|).
     At L = 102400 one key more or less moves lse by ~1e-5 (~10 fp32 ulp)."""
@@ -197,12 +197,14 @@ def test_zero_keys_count_every_visible_key(name):
     check_attn(out[:, :G], lse[:, :G], ro[:, :G], rl[:, :G], "bf16", "zero keys head 0")
 
 
-def test_dominant_drafts_show_the_exact_ancestor_pattern():
+@pytest.mark.parametrize("name", ["llama8b_20k", "llama8b_100k", "llama2_mha_100k"])
+def test_dominant_drafts_show_the_exact_ancestor_pattern(name):
     """Prefix keys 0; draft keys and queries along one axis with logit ~20; draft
     values one-hot per draft. The output is then ~ the mean of the one-hot
-    vectors of A(t), which exposes the mask row by row at full size."""
-    say("[dominant drafts] llama8b_100k")
-    c = inputs.workload("llama8b_100k")
+    vectors of A(t), which exposes the mask row by row at full size (GQA at
+    20,480 and 102,400 cached tokens, MHA at 102,400)."""
+    say(f"[dominant drafts] {name}")
+    c = inputs.workload(name)
     T, D = c.T, c.D
     c.k_cache[:] = 0
     one = inputs.f32_to_bf16_bits(np.float32(1.0))
