@@ -103,6 +103,25 @@ ts_status ts_tree_verify_attn(const void* q, const void* k_cache, const void* v_
                               ts_dtype dtype, int num_splits,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ts_tree_verify_attn without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Same arguments, results and checks as
+ * ts_tree_verify_attn, minus the workspace: the split partials go to a static
+ * device array of TS_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends. A call whose partials
+ * (ts_tree_verify_attn_workspace(...) bytes) exceed it returns
+ * TS_ERR_UNSUPPORTED before any HIP call. The stream must belong to the
+ * current device; the first call on a device looks its array up (no
+ * allocation). All calls on one GPU share the array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be ordered by the caller. */
+#define TS_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+ts_status ts_tree_verify_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      int64_t cache_stride, const void* k_draft, const void* v_draft,
+                                      const int32_t* parent, void* out, float* lse,
+                                      int T, int Hq, int Hkv, int D, int64_t L, float scale,
+                                      ts_dtype dtype, int num_splits, hipStream_t stream);
+
 /* The two phases of ts_tree_verify_attn, for callers that merge partial
  * results themselves (e.g. partials computed on several devices, each over
  * its own slice of the cache -- merging across devices is the same log-sum-

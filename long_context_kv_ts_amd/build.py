@@ -26,7 +26,7 @@ PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 SOURCES = ["api.cpp", "attn_valu.hip", "attn_mfma.hip", "attn_small.hip", "attn_merge.hip",
            "importance.hip", "topk.hip", "gather.hip", "accept.hip", "tree.hip", "sample.hip", "ngram.hip",
-           "fused.hip"]
+           "fused.hip", "noalloc.hip"]
 # Per-source extra flags. The matrix-core verify kernel never produces or
 # consumes NaN (masked scores are -inf, every exp2 argument is finite or -inf),
 # so it is built without NaN semantics: maxima of matrix-core results then need

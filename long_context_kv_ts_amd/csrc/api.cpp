@@ -184,6 +184,20 @@ ts_status ts_attn_merge(const float* o_part, const float* l_part, int n_parts, i
   return from_hip(launch_attn_merge(o_part, l_part, n_parts, rows, D, out, lse, dtype, stream), fn);
 }
 
+}  // extern "C"
+
+namespace ts {
+// The checks of the shape arguments of the attention calls (shared with the
+// no-allocation entry point).
+ts_status check_attn_args(const char* fn, int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype,
+                          int num_splits) {
+  return check_attn_shape(fn, T, Hq, Hkv, D, L, dtype, num_splits);
+}
+ts_status set_error(ts_status st, const char* msg) { return fail(st, "%s", msg); }
+}  // namespace ts
+
+extern "C" {
+
 static ts_status verify_like(const char* fn, const void* q, const void* kc, const void* vc,
                              int64_t cache_stride, const void* kd, const void* vd,
                              const int32_t* parent, bool need_parent, void* out, float* lse,
@@ -222,6 +236,21 @@ ts_status ts_tree_verify_attn(const void* q, const void* k_cache, const void* v_
                      parent, true, out, lse, T, Hq, Hkv, D, L, scale, dtype, num_splits,
                      workspace, workspace_bytes, stream);
 }
+
+}  // extern "C"
+
+namespace ts {
+ts_status tree_verify_into(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                           int64_t cache_stride, const void* k_draft, const void* v_draft, const int32_t* parent,
+                           void* out, float* lse, int T, int Hq, int Hkv, int D, int64_t L, float scale,
+                           ts_dtype dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return verify_like(fn, q, k_cache, v_cache, cache_stride, k_draft, v_draft, parent, true, out, lse, T, Hq,
+                     Hkv, D, L, scale, dtype, num_splits, workspace, workspace_bytes, stream);
+}
+}  // namespace ts
+
+extern "C" {
 
 size_t ts_partial_draft_attn_workspace(int Tq, int Hq, int Hkv, int D, int64_t P, ts_dtype dtype,
                                        int num_splits) {

@@ -142,6 +142,19 @@ struct AttnArgs {
 
 AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype, int num_splits);
 
+// Host-side pieces of the C ABI (api.cpp) that other entry points reuse: the
+// shape checks of the attention calls, recording an error message for
+// ts_last_error(), and ts_tree_verify_attn itself with a caller-chosen name
+// for its messages.
+ts_status check_attn_args(const char* fn, int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype,
+                          int num_splits);
+ts_status set_error(ts_status st, const char* msg);
+ts_status tree_verify_into(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                           int64_t cache_stride, const void* k_draft, const void* v_draft, const int32_t* parent,
+                           void* out, float* lse, int T, int Hq, int Hkv, int D, int64_t L, float scale,
+                           ts_dtype dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 // Work decomposition of the matrix-core kernel (defined next to it).
 int mfma_rows_per_group(int rows_per_head);   // 256, or 128 when a KV head has at most 128 rows
 int mfma_groups_per_cu();

@@ -7,7 +7,8 @@ exception is raised.
 
 Entry points, named as the C functions without the ``ts_`` prefix:
 
-* verify and partial-cache step: ``tree_verify_attn``, ``tree_verify_attn_partials``,
+* verify and partial-cache step: ``tree_verify_attn`` (and ``tree_verify_attn_noalloc``,
+  its variant without a workspace), ``tree_verify_attn_partials``,
   ``attn_merge``, ``kv_importance_score``, ``attn_merge_and_importance``, ``kv_topk_select``, ``kv_gather``,
   ``partial_draft_attn``;
 * decode step around them: ``build_draft_tree`` (with ``draft_tree_nodes``),
@@ -40,6 +41,9 @@ SIGNATURES = {
     "ts_tree_verify_attn": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_void_p, _c_void_p,
                                      _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
                                      _c_i64, _c_f, _c_int, _c_int, _c_void_p, _c_size, _c_void_p]),
+    "ts_tree_verify_attn_noalloc": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_void_p, _c_void_p,
+                                             _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                                             _c_i64, _c_f, _c_int, _c_int, _c_void_p]),
     "ts_tree_verify_attn_num_splits": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int]),
     "ts_tree_verify_attn_partials": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_void_p,
                                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
@@ -267,6 +271,47 @@ def tree_verify_attn(q, k_cache, v_cache, k_draft, v_draft, parent, *, scale=Non
         v_draft.data_ptr(), parent.data_ptr(), out.data_ptr(),
         lse.data_ptr() if lse is not None else None, T, Hq, Hkv, D, L, float(scale), code,
         num_splits, workspace.data_ptr(), _nbytes(workspace), _stream(dev)))
+    return out, lse
+
+
+def tree_verify_attn_noalloc(q, k_cache, v_cache, k_draft, v_draft, parent, *, scale=None, out=None,
+                             lse=None, want_lse=True, num_splits: int = 0):
+    """ts_tree_verify_attn_noalloc: ts_tree_verify_attn with the split partials
+    in the library's static device scratch instead of a workspace (the C call
+    allocates nothing; pass `out`/`lse` to keep this wrapper from allocating
+    them). Calls that overlap on one GPU race."""
+    _need(q, "q", 3)
+    dev = q.device
+    T, Hq, D = q.shape
+    _need(k_cache, "k_cache", 3, q.dtype, dev)
+    _need(v_cache, "v_cache", 3, q.dtype, dev)
+    _need(k_draft, "k_draft", 3, q.dtype, dev)
+    _need(v_draft, "v_draft", 3, q.dtype, dev)
+    _need(parent, "parent", 1, torch.int32, dev)
+    Hkv, L, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if tuple(k_draft.shape) != (Hkv, T, D) or tuple(v_draft.shape) != (Hkv, T, D):
+        raise ValueError(f"drafts must be [{Hkv}][{T}][{D}]")
+    if parent.shape[0] != T:
+        raise ValueError("parent must have T entries")
+    for n, t in (("q", q), ("k_draft", k_draft), ("v_draft", v_draft), ("parent", parent)):
+        _contig(t, n)
+    stride = _cache_stride(k_cache, "k_cache")
+    if _cache_stride(v_cache, "v_cache") != stride:
+        raise ValueError("k_cache and v_cache must share the row stride")
+    _out(out, "out", (T, Hq, D), q.dtype, dev)
+    _out(lse, "lse", (T, Hq), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().ts_tree_verify_attn_noalloc(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stride, k_draft.data_ptr(),
+            v_draft.data_ptr(), parent.data_ptr(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, T, Hq, Hkv, D, L,
+            float(1.0 / math.sqrt(D) if scale is None else scale), _dtype_code(q), num_splits, _stream(dev)))
     return out, lse
 
 

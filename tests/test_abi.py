@@ -308,3 +308,24 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         ops.lib()
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    """The no-allocation verify call checks its sizes on the host first: too
+    many partials for its static scratch, and the usual shape errors."""
+    lib = ops.lib()
+
+    def call(**kw):
+        a = dict(q=P, kc=P, vc=P, stride=102400, kd=P, vd=P, parent=P, out=P, lse=P, T=120, Hq=32, Hkv=8, D=128,
+                 L=102400, scale=0.088, dtype=B, ns=0)
+        a.update(kw)
+        return lib.ts_tree_verify_attn_noalloc(a["q"], a["kc"], a["vc"], a["stride"], a["kd"], a["vd"], a["parent"],
+                                               a["out"], a["lse"], a["T"], a["Hq"], a["Hkv"], a["D"], a["L"],
+                                               a["scale"], a["dtype"], a["ns"], None)
+    # 40 splits of 120 x 32 rows of 128 fp32 is 78.6 MB of partials: more than 64 MiB
+    assert lib.ts_tree_verify_attn_workspace(120, 32, 8, 128, 102400, B, 40) > 64 << 20
+    assert call(ns=40) == ops.TS_ERR_UNSUPPORTED
+    assert "static scratch" in _err() and "ts_tree_verify_attn_noalloc" in _err()
+    assert call(T=0) == ops.TS_ERR_UNSUPPORTED and "ts_tree_verify_attn_noalloc" in _err()
+    assert call(Hq=30) == ops.TS_ERR_INVALID_ARG
+    assert call(D=96) == ops.TS_ERR_UNSUPPORTED

@@ -1,0 +1,90 @@
+"""GPU: ts_tree_verify_attn_noalloc (the verify call whose split partials live
+in the library's static device scratch) against ts_tree_verify_attn with a
+caller workspace, through the C ABI. The two run the same kernels with the same
+split plan, so every output must be bit-identical; two calls in a row, the
+second with a smaller input (the scratch keeps the first call's contents), and
+the first also against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import check_attn, say, to_dev
+from long_context_kv_ts_amd import inputs, ops
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_case(c):
+    dt = c.dtype
+    return (to_dev(c.q, dt), to_dev(c.k_cache, dt), to_dev(c.v_cache, dt), to_dev(c.k_draft, dt),
+            to_dev(c.v_draft, dt), to_dev(c.parent, "i32"))
+
+
+def _both(args, scale, num_splits=0):
+    out_a, lse_a = ops.tree_verify_attn(*args, scale=scale, num_splits=num_splits)
+    q = args[0]
+    out_b = torch.full_like(q, 7.0)
+    lse_b = torch.full((q.shape[0], q.shape[1]), 7.0, dtype=torch.float32, device=q.device)
+    ops.tree_verify_attn_noalloc(*args, scale=scale, num_splits=num_splits, out=out_b, lse=lse_b)
+    torch.cuda.synchronize()
+    return out_a, lse_a, out_b, lse_b
+
+
+def _same(a, b, label):
+    ai = a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32)
+    bi = b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)
+    assert torch.equal(ai, bi), f"{label}: not bit-identical"
+
+
+def test_noalloc_matches_workspace_call_twice_in_a_row():
+    # 1: the LLaMA3.1-8B layer over 20,480 cached tokens (16 splits: 7.9 MB of partials)
+    say("[noalloc] llama8b_20k, then a smaller call")
+    c1 = inputs.workload("llama8b_20k")
+    a1 = _dev_case(c1)
+    out_a, lse_a, out_b, lse_b = _both(a1, c1.scale)
+    _same(out_a, out_b, "llama8b_20k out")
+    _same(lse_a, lse_b, "llama8b_20k lse")
+    ro, rl = oracle.verify_attn_ref(c1.q, c1.k_cache, c1.v_cache, c1.k_draft, c1.v_draft, c1.parent, c1.scale,
+                                    "bf16")
+    check_attn(out_b, lse_b, ro, rl, "bf16", "noalloc llama8b_20k vs oracle")
+    # 2: a smaller call right after: fewer drafts, heads and cached tokens, a ragged tail
+    c2 = inputs.make_verify("noalloc2", dtype="bf16", Hq=8, Hkv=2, D=128, L=1000, seed=21, with_chains=True)
+    a2 = _dev_case(c2)
+    out_a, lse_a, out_b, lse_b = _both(a2, c2.scale)
+    _same(out_a, out_b, "small out")
+    _same(lse_a, lse_b, "small lse")
+    ro, rl = oracle.verify_attn_ref(c2.q, c2.k_cache, c2.v_cache, c2.k_draft, c2.v_draft, c2.parent, c2.scale,
+                                    "bf16")
+    check_attn(out_b, lse_b, ro, rl, "bf16", "noalloc small vs oracle")
+
+
+def test_noalloc_full_size_then_fp32():
+    """The 102,400-token layer (16 splits, 31.7 MB of partials, within the
+    64 MiB scratch), then an fp32 call on the vector-ALU path."""
+    say("[noalloc] llama8b_100k, then tiny fp32")
+    c1 = inputs.workload("llama8b_100k")
+    need = ops.verify_workspace_bytes(c1.T, c1.Hq, c1.Hkv, c1.D, c1.L, torch.bfloat16)
+    assert need <= 64 << 20
+    out_a, lse_a, out_b, lse_b = _both(_dev_case(c1), c1.scale)
+    _same(out_a, out_b, "llama8b_100k out")
+    _same(lse_a, lse_b, "llama8b_100k lse")
+    c2 = inputs.workload("tiny")
+    out_a, lse_a, out_b, lse_b = _both(_dev_case(c2), c2.scale, num_splits=3)
+    _same(out_a, out_b, "tiny out")
+    _same(lse_a, lse_b, "tiny lse")
+    ro, rl = oracle.verify_attn_ref(c2.q, c2.k_cache, c2.v_cache, c2.k_draft, c2.v_draft, c2.parent, c2.scale,
+                                    "f32")
+    check_attn(out_b, lse_b, ro, rl, "f32", "noalloc tiny vs oracle")
+
+
+def test_noalloc_rejects_too_large_a_split_plan():
+    """40 splits of the 120-draft, 32-head rows over 102,400 tokens need 78.6 MB
+    of partials, more than the scratch holds: an error, nothing launched."""
+    dev = torch.device("cuda:0")
+    q = torch.zeros((120, 32, 128), dtype=torch.bfloat16, device=dev)
+    kc = torch.zeros((8, 102400, 128), dtype=torch.bfloat16, device=dev)
+    kd = torch.zeros((8, 120, 128), dtype=torch.bfloat16, device=dev)
+    par = torch.full((120,), -1, dtype=torch.int32, device=dev)
+    with pytest.raises(ops.TsError, match="static scratch"):
+        ops.tree_verify_attn_noalloc(q, kc, kc, kd, kd, par, num_splits=40)
