@@ -129,3 +129,110 @@ def test_rows_follow_the_forest():
     x = np.tile(np.array([1.0, 0.95]), (5, 1))
     g, _ = sample_ref(x, [], parent, draft, window=4, penalty=1.2, temperature=0.0, min_p=0.1, u=[0.5] * 5)
     assert g.tolist() == [0, 1, 1, 1, 1]
+
+
+# ---------------------------------------------------------------------------
+# top-p (nucleus) filter
+# ---------------------------------------------------------------------------
+TOPP_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "top_p_example.json")
+
+
+def test_top_p_hand_worked_example():
+    """Kept sets, renormalised probabilities and draws worked by hand (tests/golden/top_p_example.json)."""
+    ex = json.load(open(TOPP_GOLDEN))
+    x = np.array(ex["logits"])
+    for c in ex["cases"]:
+        q, keep, _ = kept_probs(x, c["temperature"], c["min_p"], c["top_p"])
+        assert np.nonzero(keep)[0].tolist() == c["kept"], c
+        np.testing.assert_allclose(q, c["probs"], rtol=0, atol=1e-12)
+        for u, tok in c["draws"]:
+            t, _ = sample_row(x, [], 1.2, c["temperature"], c["min_p"], u, c["top_p"])
+            assert t == tok, (c, u)
+
+
+def _brute_keep(p, top_p):
+    """Token i is kept iff the exact sum of the strictly larger probabilities is below top_p."""
+    import math
+    return np.array([math.fsum(pj for pj in p if pj > pi) < top_p for pi in p])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_top_p_brute_force_with_ties(seed):
+    """Against an O(V^2) exact sum over strictly more probable tokens, on
+    logits with many exact ties."""
+    rng = np.random.default_rng(seed)
+    V = int(rng.integers(2, 60))
+    x = np.round(rng.standard_normal(V) * 2, 1)          # one decimal: ties are common
+    tau = float(rng.choice([0.4, 0.8, 1.0, 1.2]))
+    for top_p in (0.05, 0.3, 0.5, 0.77, 0.9, 0.99):
+        _, keep, y = kept_probs(x, tau, 0.0, top_p)
+        p = softmax(y)
+        above = np.array([sum(pj for pj in p if pj > pi) for pi in p])
+        clear = np.abs(above - top_p) > 1e-9
+        assert np.array_equal(keep[clear], _brute_keep(p, top_p)[clear]), (seed, top_p)
+        # ties are kept or dropped together
+        for v in np.unique(p):
+            assert len(set(keep[p == v])) == 1
+
+
+def test_top_p_is_the_sorted_cumulative_rule_on_distinct_values():
+    """With distinct probabilities the rule is the textbook one: sort
+    descending and keep while the cumulative mass before a token is below
+    top_p (the smallest prefix whose mass reaches top_p)."""
+    rng = np.random.default_rng(9)
+    for _ in range(30):
+        x = rng.standard_normal(300) * 2.5
+        top_p = float(rng.uniform(0.05, 0.99))
+        _, keep, y = kept_probs(x, 1.0, 0.0, top_p)
+        p = softmax(y)
+        order = np.argsort(-p)
+        before = np.cumsum(p[order]) - p[order]
+        ref = np.zeros(len(p), bool)
+        ref[order[before < top_p]] = True
+        assert np.array_equal(keep, ref)
+        assert p[keep].sum() >= top_p - 1e-12 and p[keep].sum() - p[keep].min() < top_p
+
+
+def test_top_p_limits_and_monotone():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal(500)
+    x[[3, 77]] = x.max() + 1.0                          # two tokens tie at the maximum
+    x[5] = -np.inf
+    _, keep1, _ = kept_probs(x, 1.0, 0.0, 1.0)
+    assert keep1.sum() == 499 and not keep1[5]          # top_p = 1: every token of non-zero probability
+    _, keep0, _ = kept_probs(x, 1.0, 0.0, 1e-9)
+    assert np.nonzero(keep0)[0].tolist() == [3, 77]     # tiny top_p: the tied maxima only
+    prev = keep0
+    for top_p in np.linspace(0.01, 0.999, 40):
+        _, k, _ = kept_probs(x, 1.0, 0.0, float(top_p))
+        assert (k | prev).sum() == k.sum()              # growing top_p only adds tokens
+        prev = k
+
+
+def test_top_p_and_min_p_intersect_like_the_sequential_filters():
+    """Kept = passes min-p and passes top-p on the same distribution; the same
+    as top-p first, then min-p on the renormalised remainder."""
+    rng = np.random.default_rng(11)
+    for _ in range(30):
+        x = rng.standard_normal(200) * 2
+        tau, min_p, top_p = float(rng.uniform(0.4, 1.5)), float(rng.uniform(0.01, 0.5)), float(rng.uniform(0.1, 0.99))
+        _, keep, y = kept_probs(x, tau, min_p, top_p)
+        p = softmax(y)
+        k1 = _brute_keep(p, top_p)
+        r = np.where(k1, p, 0.0)
+        r = r / r.sum()
+        seq = k1 & (r >= min_p * r.max())
+        both = k1 & (p >= min_p * p.max())
+        assert np.array_equal(seq, both)
+        clear = (np.abs(p - min_p * p.max()) > 1e-12)
+        assert np.array_equal(keep[clear], both[clear])
+
+
+def test_top_p_diagnostics_flag_the_nearest_boundary():
+    """The near-boundary set flips exactly the value whose mass-above is nearest top_p."""
+    ex = json.load(open(TOPP_GOLDEN))
+    x = np.array(ex["logits"])
+    _, d = sample_row(x, [], 1.2, 1.0, 0.0, 0.5, 0.66)
+    assert abs(d["topp_margin"] - 0.01) < 1e-12                 # id 2 has 0.65 above it
+    assert np.nonzero(d["keep"])[0].tolist() == [1, 2, 4]
+    assert np.nonzero(d["keep_alt"])[0].tolist() == [1, 4]
