@@ -360,6 +360,8 @@ def main():
     res["accept_commit_us"] = time_accept_commit(vc, dev, args.steps)
     res["draft_tree_us"] = time_draft_tree(dev, args.steps)
     res["sample_us"] = time_sample(dev, args.steps)
+    # the summary page's temperature ablation samples with top-p: temperature 0.8, top-p 0.9, no min-p
+    res["sample_top_p_us"] = time_sample(dev, args.steps, temperature=0.8, min_p=0.0, top_p=0.9)
     res["ngram_us"] = time_ngram(dev, args.steps)
 
     if not args.no_cpu_baseline:
@@ -491,10 +493,10 @@ def time_draft_tree(dev, reps):
     return round(e0.elapsed_time(e1) * 1e3 / reps, 2)
 
 
-def time_sample(dev, reps):
+def time_sample(dev, reps, temperature=None, min_p=None, top_p=1.0):
     """Target tokens for the 121 verify rows over the LLaMA3.1 vocabulary:
     fp32 logits [121][128256], penalty 1.2 over 1024 tokens, temperature 1,
-    min-p 0.1 (its own figure, not part of value)."""
+    min-p 0.1 by default (its own figure, not part of value)."""
     import torch
     from long_context_kv_ts_amd import inputs, ops
     c = inputs.make_sample(dtype="f32")
@@ -504,7 +506,8 @@ def time_sample(dev, reps):
     ws = ops.alloc_workspace(int(ops.lib().ts_sample_workspace(c.R, c.V)), dev)
     tok = torch.empty(c.R, dtype=torch.int32, device=dev)
     kw = dict(hist=hist, parent=parent, draft_tok=dtok, window=inputs.PENALTY_WINDOW, penalty=inputs.PENALTY,
-              temperature=inputs.TEMPERATURE, min_p=inputs.MIN_P, u=u, tok=tok, workspace=ws)
+              temperature=inputs.TEMPERATURE if temperature is None else temperature,
+              min_p=inputs.MIN_P if min_p is None else min_p, top_p=top_p, u=u, tok=tok, workspace=ws)
     for _ in range(3):
         ops.sample_tokens(logits, **kw)
     torch.cuda.synchronize()

@@ -58,7 +58,7 @@ const char* ts_last_error(void);
 /* ABI version of this header (bumped on any signature change). */
 int ts_abi_version(void);
 
-#define TS_ABI_VERSION 1
+#define TS_ABI_VERSION 2
 #define TS_MAX_DRAFT 1024 /* max draft tokens T of one verify call */
 
 /* ------------------------------------------------------------------------
@@ -320,20 +320,26 @@ ts_status ts_accept_commit(const int32_t* parent, const int32_t* draft_tok, cons
  *              penalised logit
  *   min_p      in [0, 1]: token i is kept when p_i >= min_p * max p, where
  *              p = softmax(penalised / tau); 0 keeps every token
+ *   top_p      in (0, 1]: token i is also required to have less than top_p
+ *              of the probability p on tokens strictly more probable than
+ *              itself (the nucleus; tokens of equal probability are kept or
+ *              dropped together); 1 keeps every token. Both filters use the
+ *              same p, so the kept set is their intersection (the summary
+ *              page's temperature ablation samples with top-p)
  *   u          fp32 [R] on the device, uniforms in [0, 1) drawn by the caller
  *              (may be NULL when tau = 0)
  *   tok        int32 [R] out: the smallest kept id whose cumulative kept
  *              probability (id order) exceeds u[r]; when rounding leaves
  *              u[r] at or past the end, the last kept id
  * Supported: V in [1, 1048576], T in [0, 1024]. Workspace: at least
- * ts_sample_workspace(R, V) bytes (400 bytes per row and 1024 logits),
- * 256-byte aligned, contents ignored on entry.
+ * ts_sample_workspace(R, V) bytes (400 bytes per row and 1024 logits, plus
+ * 4 per row), 256-byte aligned, contents ignored on entry.
  * ---------------------------------------------------------------------- */
 size_t ts_sample_workspace(int R, int V);   /* 0 on bad sizes */
 
 ts_status ts_sample_tokens(const void* logits, int R, int V, const int32_t* hist, int n_hist,
                            const int32_t* parent, const int32_t* draft_tok, int T, int window,
-                           float penalty, float temperature, float min_p, const float* u,
+                           float penalty, float temperature, float min_p, float top_p, const float* u,
                            int32_t* tok, ts_dtype dtype, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 

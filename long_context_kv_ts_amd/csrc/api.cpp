@@ -444,7 +444,7 @@ size_t ts_sample_workspace(int R, int V) {
 
 ts_status ts_sample_tokens(const void* logits, int R, int V, const int32_t* hist, int n_hist,
                            const int32_t* parent, const int32_t* draft_tok, int T, int window,
-                           float penalty, float temperature, float min_p, const float* u,
+                           float penalty, float temperature, float min_p, float top_p, const float* u,
                            int32_t* tok, ts_dtype dtype, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {
   const char* fn = "ts_sample_tokens";
@@ -464,6 +464,7 @@ ts_status ts_sample_tokens(const void* logits, int R, int V, const int32_t* hist
   if (!(temperature >= 0.0f) || !std::isfinite(temperature))
     return fail(TS_ERR_INVALID_ARG, "%s: temperature=%g", fn, temperature);
   if (!(min_p >= 0.0f && min_p <= 1.0f)) return fail(TS_ERR_INVALID_ARG, "%s: min_p=%g outside [0, 1]", fn, min_p);
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(TS_ERR_INVALID_ARG, "%s: top_p=%g outside (0, 1]", fn, top_p);
   if (!workspace || ((uintptr_t)workspace & 255u)) return fail(TS_ERR_INVALID_ARG, "%s: workspace null or not 256-byte aligned", fn);
   const size_t need = ts_sample_workspace(R, V);
   if (workspace_bytes < need) return fail(TS_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
@@ -491,6 +492,12 @@ ts_status ts_sample_tokens(const void* logits, int R, int V, const int32_t* hist
   a.sub = static_cast<SampleSub*>(workspace);
   a.cand = reinterpret_cast<SampleCand*>(a.sub + (size_t)R * a.nb);
   a.wbits = reinterpret_cast<uint32_t*>(a.cand + (size_t)R * a.nb * kSampleList);
+  // top-p is off at 1 (every token of non-zero weight has less than the whole
+  // weight above it) and under greedy decoding (the maximum always survives)
+  a.top_p = top_p;
+  a.topp_cut = top_p < 1.0f && temperature > 0.0f
+                   ? reinterpret_cast<float*>(a.wbits + (size_t)R * a.nb * (kSampleSub / 32))
+                   : nullptr;
   return from_hip(launch_sample(a, dtype, stream), fn);
 }
 

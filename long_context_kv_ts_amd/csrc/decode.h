@@ -38,7 +38,7 @@ struct SampleSub {                       // summary of one sub-slice
   float m;                               // largest penalised logit
   float s;                               // sum of 2^((z - m) * s2) over z >= m + cut
   int n;                                 // how many z >= m + cut (listed: the first kSampleList)
-  int pad;
+  float wall;                            // sum of 2^((z - m) * s2) over every finite z (top-p only)
 };
 struct SampleCand {
   float z;                               // penalised logit
@@ -59,6 +59,8 @@ struct SampleArgs {
   float s2;                   // log2(e) / temperature (0: greedy)
   float cut;                  // temperature * ln(min_p) (<= 0; -inf keeps every token; greedy: 0)
   const float* u;             // [R] uniforms in [0, 1)
+  float top_p;                // nucleus mass (1: off)
+  float* topp_cut;            // [R] each row's top-p cut on z (nullptr: top-p off)
   int32_t* tok;               // [R]
   SampleSub* sub;             // [R][nb]
   SampleCand* cand;           // [R][nb][kSampleList]

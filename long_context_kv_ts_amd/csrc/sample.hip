@@ -9,7 +9,11 @@
 //   2. temperature tau and the min-p filter: with Z the row's largest
 //      penalised logit z, token i is kept when z_i >= Z + tau * ln(min_p),
 //      i.e. p_i >= min_p * max p, with weight w_i = 2^((z_i - Z) * log2(e)/tau);
-//   3. the draw: the smallest token id whose cumulative weight exceeds
+//   3. top-p (when top_p < 1): with W the row's total weight, token i is also
+//      required to have the weight of the tokens with a larger z below
+//      top_p * W, i.e. z_i >= z*, the value at which the weight at or above
+//      it first reaches top_p * W (tokens of equal z share the decision);
+//   4. the draw: the smallest token id whose cumulative weight exceeds
 //      u[r] * sum(w). tau = 0 is greedy: the first token with z_i == Z.
 //
 // Rows are cut into sub-slices of 1024 logits. Two launches, one read of the
@@ -23,7 +27,10 @@
 //      ballots: the maximum m, the kept weight relative to m at the
 //      sub-slice's own cut m + cut, and the kept tokens themselves while there
 //      are at most 32 (weights and list entries only for those).
-//   B. grid (rows): the row maximum Z gives the row's cut Z + cut >= m + cut,
+//   T. (top-p only) grid (rows): each row's z* by a weighted radix select over
+//      the row's logits, written to the workspace;
+//   B. grid (rows): the row maximum Z gives the row's cut Z + cut >= m + cut
+//      (raised to z* under top-p),
 //      so a listed sub-slice's kept tokens are all in its list; with min-p off
 //      (cut = -inf) the sub-slice sum rescales exactly by 2^((m - Z) s2). A
 //      sub-slice with more than 32 kept tokens and min-p on is read again, one
@@ -291,7 +298,16 @@ __device__ __forceinline__ void summarise(const SampleArgs& a, const Tin* row, i
       acc += z[e] >= thr ? __builtin_amdgcn_exp2f((z[e] - m) * a.s2) : 0.0f;
   }
   acc = wave_all_sum(acc);
-  if (lane == 0) a.sub[r * a.nb + b] = SampleSub{m, acc, n, 0};
+  // top-p needs the weight of every finite token; without min-p that is acc
+  float wall = acc;
+  if (a.topp_cut != nullptr && a.cut > -INFINITY) {
+    wall = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kPL; ++e)
+      wall += z[e] > -INFINITY ? __builtin_amdgcn_exp2f((z[e] - m) * a.s2) : 0.0f;
+    wall = wave_all_sum(wall);
+  }
+  if (lane == 0) a.sub[r * a.nb + b] = SampleSub{m, acc, n, wall};
 }
 
 __device__ float block_max(float v, float* red) {
@@ -404,12 +420,13 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
   float mloc = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kPerT; ++k) {
-    sb[k] = SampleSub{-INFINITY, 0.0f, 0, 0};
+    sb[k] = SampleSub{-INFINITY, 0.0f, 0, 0.0f};
     if (k < per && q0 + k < a.nb) sb[k] = a.sub[r * a.nb + q0 + k];
     mloc = fmaxf(mloc, sb[k].m);
   }
   const float Z = block_max(mloc, s.red);
-  const float thr = Z + a.cut;
+  // the row's cut: min-p, raised to the row's top-p cut z* when top-p is on
+  const float thr = fmaxf(Z + a.cut, a.topp_cut != nullptr && !greedy ? a.topp_cut[r] : -INFINITY);
   if (tid == 0) {
     p.bsel = a.nb;
     p.win = INT32_MAX;
@@ -436,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
       const int q = q0 + k;
       float c = 0.0f;
       if (q < a.nb && sb[k].m > -INFINITY && sb[k].m >= thr) {
-        if (a.cut == -INFINITY) {
+        if (thr == -INFINITY) {
           c = sb[k].s * exp2f((sb[k].m - Z) * a.s2);
         } else if (sb[k].n <= kSampleList) {
           const SampleCand* list = a.cand + ((int64_t)r * a.nb + q) * kSampleList;
@@ -518,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
     return;
   }
   const SampleSub chosen = a.sub[r * a.nb + b];
-  const bool listed = chosen.n <= kSampleList && (greedy || a.cut > -INFINITY);
+  const bool listed = chosen.n <= kSampleList && (greedy || thr > -INFINITY);
   if (listed) {
     // the sub-slice's kept tokens, in token order (greedy: its maxima)
     const SampleCand* list = a.cand + ((int64_t)r * a.nb + b) * kSampleList;
@@ -588,6 +605,175 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
   if (tid == 0) a.tok[r] = p.win != INT32_MAX ? p.win : p.last;
 }
 
+// ---------------------------------------------------------------------------
+// Top-p cut of each row: a weighted radix select over the row's penalised
+// logits z, from the largest down, for the value z* at which the weight at or
+// above it first reaches top_p * W (W: the row's total weight, from the
+// scan's summaries). Pass 0 bins z by its weight, 1/8 of a power of two per
+// bin below the row maximum (bin 255 takes everything further down), which
+// spreads a row's tokens over the bins; passes 1..4 take the 8-bit digits of
+// the order-preserving key of z inside the chosen bin, high to low. Each pass
+// sums per bin the weight, the count and the smallest and largest key, and
+// the search ends as soon as the chosen bin holds a single key. The weights
+// are summed in fp32 in an unspecified order, so a z* whose cumulative weight
+// is within rounding of top_p * W may come out one value either side.
+constexpr int kToppThreads = 1024;
+
+__device__ __forceinline__ uint32_t topp_key(float f) {
+  if (f == 0.0f) f = 0.0f;               // -0 and +0: one key
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float topp_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <typename Tin>
+__global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a) {
+  constexpr int kW = kToppThreads / kWave;
+  __shared__ float hw[256];
+  __shared__ uint32_t hc[256], kmin[256], kmax[256];
+  __shared__ float red[kW];
+  __shared__ float s_m;                  // weight above the chosen bin
+  __shared__ int s_sel;                  // chosen bin of the pass
+  __shared__ uint32_t s_key;             // z*'s key once known
+  __shared__ int s_done;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const Tin* row = static_cast<const Tin*>(a.logits) + (int64_t)r * a.V;
+  const uint32_t* bits = a.wbits + (int64_t)r * a.nb * (kSampleSub / 32);
+
+  // the row maximum and total weight from the sub-slice summaries (nb <= 1024)
+  SampleSub sb = SampleSub{-INFINITY, 0.0f, 0, 0.0f};
+  if (tid < a.nb) sb = a.sub[(int64_t)r * a.nb + tid];
+  float v = wave_max(sb.m);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float Z = red[0];
+#pragma unroll
+  for (int w = 1; w < kW; ++w) Z = fmaxf(Z, red[w]);
+  __syncthreads();
+  v = wave_sum(sb.m > -INFINITY ? sb.wall * exp2f((sb.m - Z) * a.s2) : 0.0f);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float W = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) W += red[w];
+  const float target = a.top_p * W;
+  if (tid == 0) {
+    s_m = 0.0f;
+    s_done = 0;
+    s_key = 0u;
+  }
+
+  // pass 0: weight bins; passes 1..4: key digits inside bin b0
+  int b0 = -1;
+  uint32_t prefix = 0u, mask = 0u;
+  for (int pass = 0; pass < 5; ++pass) {
+    const int shift = 32 - 8 * pass;       // pass >= 1: digit (key >> shift) & 255
+    if (tid < 256) {
+      hw[tid] = 0.0f;
+      hc[tid] = 0u;
+      kmin[tid] = 0xFFFFFFFFu;
+      kmax[tid] = 0u;
+    }
+    __syncthreads();
+    for (int t = tid; t < a.V; t += kToppThreads) {
+      float z = Elem<Tin>::load(row + t);
+      if ((bits[t >> 5] >> (t & 31)) & 1u) z = penalty(z, a);
+      if (!(z > -INFINITY)) continue;
+      const int bin = (int)fminf((Z - z) * a.s2 * 8.0f, 255.0f);
+      const uint32_t key = topp_key(z);
+      int d;
+      if (pass == 0) d = bin;
+      else if (bin == b0 && (key & mask) == prefix) d = (int)((key >> shift) & 255u);
+      else continue;
+      atomicAdd(&hw[d], exp2f((z - Z) * a.s2));
+      atomicAdd(&hc[d], 1u);
+      atomicMin(&kmin[d], key);
+      atomicMax(&kmax[d], key);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // bins in order of decreasing z: pass 0 ascending, key digits descending
+      float c[4], tot = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = pass == 0 ? 4 * lane + j : 255 - 4 * lane - j;
+        c[j] = hw[d];
+        tot += c[j];
+      }
+      float incl = tot;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const float y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
+      }
+      float run = s_m + incl - tot;      // weight above this lane's first bin
+      int sel = -1;
+      float above = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = pass == 0 ? 4 * lane + j : 255 - 4 * lane - j;
+        if (sel < 0 && hc[d] > 0u && run + c[j] >= target) {
+          sel = d;
+          above = run;
+        }
+        run += c[j];
+      }
+      // the first bin (in z order) that reaches the target; rounding can leave
+      // the target past the total, and then the last non-empty bin is taken
+      const uint64_t hit = __ballot(sel >= 0);
+      int last = -1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = pass == 0 ? 4 * lane + j : 255 - 4 * lane - j;
+        if (hc[d] > 0u) last = d;
+      }
+      const uint64_t any = __ballot(last >= 0);
+      if (hit != 0ull) {
+        const int src = __ffsll((unsigned long long)hit) - 1;
+        if (lane == src) {
+          s_sel = sel;
+          s_m = above;
+        }
+      } else if (any != 0ull) {
+        const int src = 63 - __clzll((unsigned long long)any);
+        if (lane == src) {
+          // everything up to this bin lies above it
+          float up = s_m + incl - tot;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int d = pass == 0 ? 4 * lane + j : 255 - 4 * lane - j;
+            if (d == last) break;
+            up += c[j];
+          }
+          s_sel = last;
+          s_m = up;
+        }
+      } else if (lane == 0) {
+        s_sel = -1;                      // no finite token (outside the contract)
+      }
+    }
+    __syncthreads();
+    const int sel = s_sel;
+    if (sel < 0) {
+      if (tid == 0) a.topp_cut[r] = -INFINITY;
+      return;
+    }
+    if (kmin[sel] == kmax[sel] || pass == 4) {
+      if (tid == 0) a.topp_cut[r] = topp_value(kmax[sel]);
+      return;
+    }
+    if (pass == 0) {
+      b0 = sel;
+    } else {
+      prefix |= (uint32_t)sel << shift;
+      mask |= 255u << shift;
+    }
+    __syncthreads();                       // every thread has read this pass's bins
+  }
+}
+
 template <typename Tin>
 hipError_t launch_t(const SampleArgs& a, hipStream_t st) {
   // 256 threads, one sub-slice a wave: of 256/512/1024 threads and 1/2/4
@@ -602,6 +788,7 @@ hipError_t launch_t(const SampleArgs& a, hipStream_t st) {
     sample_scan_kernel<Tin, kNT, kPW, true><<<grid, kNT, 0, st>>>(a);
   else
     sample_scan_kernel<Tin, kNT, kPW, false><<<grid, kNT, 0, st>>>(a);
+  if (a.topp_cut != nullptr) sample_topp_kernel<Tin><<<a.R, kToppThreads, 0, st>>>(a);
   if (vec)
     sample_pick_kernel<Tin, true><<<a.R, kThreads, 0, st>>>(a);
   else
@@ -615,7 +802,8 @@ int sample_subslices(int V) { return V < 1 ? 1 : (V + kSampleSub - 1) / kSampleS
 
 size_t sample_workspace_bytes(int R, int V) {
   const size_t n = (size_t)R * sample_subslices(V);
-  return n * sizeof(SampleSub) + n * kSampleList * sizeof(SampleCand) + n * (kSampleSub / 32) * sizeof(uint32_t);
+  return n * sizeof(SampleSub) + n * kSampleList * sizeof(SampleCand) + n * (kSampleSub / 32) * sizeof(uint32_t) +
+         (size_t)R * sizeof(float);
 }
 
 hipError_t launch_sample(const SampleArgs& a, ts_dtype dtype, hipStream_t s) {

@@ -68,7 +68,7 @@ SIGNATURES = {
                                   _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "ts_sample_workspace": (_c_size, [_c_int, _c_int]),
     "ts_sample_tokens": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_int,
-                                  _c_int, ctypes.c_float, ctypes.c_float, ctypes.c_float, _c_void_p,
+                                  _c_int, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, _c_void_p,
                                   _c_void_p, _c_int, _c_void_p, _c_size, _c_void_p]),
     "ts_ngram_table_bytes": (_c_size, [_c_int, _c_int]),
     "ts_ngram_init": (_c_int, [_c_void_p, _c_size, _c_int, _c_int, _c_void_p]),
@@ -559,12 +559,12 @@ def accept_commit(parent, draft_tok, target_tok, rand_u32: int, k_cache, v_cache
 
 
 def sample_tokens(logits, *, hist=None, parent=None, draft_tok=None, window: int = 1024,
-                  penalty: float = 1.2, temperature: float = 1.0, min_p: float = 0.1, u=None,
-                  tok=None, workspace=None):
+                  penalty: float = 1.2, temperature: float = 1.0, min_p: float = 0.1, top_p: float = 1.0,
+                  u=None, tok=None, workspace=None):
     """ts_sample_tokens -> tok [R] int32: the target's token for each of the
     R = T + 1 verified positions of logits [R][V] (row 0 after the committed
     context, row t+1 after draft t), with the windowed repetition penalty,
-    temperature, min-p and the caller's uniforms u [R] (fp32, device)."""
+    temperature, min-p, top-p and the caller's uniforms u [R] (fp32, device)."""
     _need(logits, "logits", 2)
     _contig(logits, "logits")
     dev = logits.device
@@ -596,7 +596,7 @@ def sample_tokens(logits, *, hist=None, parent=None, draft_tok=None, window: int
         workspace = alloc_workspace(need, dev)
     ptr = lambda t: t.data_ptr() if t is not None and t.numel() else None
     _check(lib().ts_sample_tokens(logits.data_ptr(), R, V, ptr(hist), n_hist, ptr(parent), ptr(draft_tok), T,
-                                  int(window), float(penalty), float(temperature), float(min_p),
+                                  int(window), float(penalty), float(temperature), float(min_p), float(top_p),
                                   ptr(u) if temperature > 0 else None, tok.data_ptr(), _dtype_code(logits),
                                   workspace.data_ptr(), _nbytes(workspace), _stream(dev)))
     return tok

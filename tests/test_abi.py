@@ -40,7 +40,7 @@ def test_every_declared_function_is_exported_and_bound():
         assert name in ops.SIGNATURES, f"{name} not bound in ops.py"
         assert len(ops.SIGNATURES[name][1]) == nargs, f"{name}: binding has wrong arg count"
     assert set(ops.SIGNATURES) == set(protos)
-    assert lib.ts_abi_version() == 1
+    assert lib.ts_abi_version() == 2
 
 
 def _verify(**kw):
@@ -257,9 +257,9 @@ def test_sample_rejects():
     assert lib.ts_sample_workspace(0, 100) == 0 and lib.ts_sample_workspace(1, (1 << 20) + 1) == 0
 
     def call(logits=P, R=121, V=128256, hist=P, n_hist=4096, parent=P, draft=P, T=120, window=1024,
-             penalty=1.2, temp=1.0, min_p=0.1, u=P, tok=P, dtype=F, wsp=P, wsb=1 << 20):
+             penalty=1.2, temp=1.0, min_p=0.1, top_p=1.0, u=P, tok=P, dtype=F, wsp=P, wsb=1 << 20):
         return lib.ts_sample_tokens(logits, R, V, hist, n_hist, parent, draft, T, window, penalty, temp,
-                                    min_p, u, tok, dtype, wsp, wsb, None)
+                                    min_p, top_p, u, tok, dtype, wsp, wsb, None)
     bad = ops.TS_ERR_INVALID_ARG
     assert call(R=120) == bad                                   # R != T + 1
     assert call(T=1025, R=1026) == bad
@@ -274,6 +274,8 @@ def test_sample_rejects():
     assert call(penalty=0.0) == bad and call(penalty=float("inf")) == bad
     assert call(temp=-1.0) == bad and call(temp=float("nan")) == bad
     assert call(min_p=1.5) == bad and call(min_p=-0.1) == bad
+    assert call(top_p=0.0) == bad and call(top_p=1.01) == bad and call(top_p=float("nan")) == bad
+    assert "top_p" in _err()
     assert call(dtype=7) == bad
     assert call(wsp=P + 16) == bad
     assert call(wsb=ws - 4) == ops.TS_ERR_WORKSPACE

@@ -31,18 +31,25 @@ def _i32(a):
     return to_dev(a, "i32") if a.size else None
 
 
+def _is_draw(g, u, q, cdf, keep, border):
+    """Token g is the inverse-CDF draw at u of the kept distribution q (within VALID_TOL)."""
+    lo, hi = cdf[g] - q[g], cdf[g]
+    return (q[g] > 0 or border) and lo - VALID_TOL <= u < hi + VALID_TOL
+
+
 def run(logits, dtype, hist, parent, draft, *, window, penalty, temperature, min_p, u, label,
-        workspace=None):
+        workspace=None, top_p=1.0):
     R = logits.shape[0]
     u = np.asarray(u, np.float32)
     tok = ops.sample_tokens(to_dev(logits, dtype), hist=_i32(hist), parent=_i32(parent) if len(parent) else None,
                             draft_tok=_i32(draft) if len(draft) else None, window=window, penalty=penalty,
-                            temperature=temperature, min_p=min_p, u=to_dev(u, "f32"), workspace=workspace)
+                            temperature=temperature, min_p=min_p, top_p=top_p, u=to_dev(u, "f32"),
+                            workspace=workspace)
     torch.cuda.synchronize()
     got = tok.cpu().numpy()
     ref, diags = sample_ref(widen(logits, dtype), hist, parent if len(parent) else None, draft,
                             window=window, penalty=penalty, temperature=temperature, min_p=min_p,
-                            u=u.astype(np.float64))
+                            u=u.astype(np.float64), top_p=top_p)
     near = 0
     for r in range(R):
         g, e, d = int(got[r]), int(ref[r]), diags[r]
@@ -52,17 +59,21 @@ def run(logits, dtype, hist, parent, draft, *, window, penalty, temperature, min
                 assert 0 <= g < len(z) and z[g] >= z.max() - 1e-6 * abs(z.max()), f"{label} row {r}: {g} != {e}"
                 near += 1
             continue
-        if d["u_margin"] > EXACT_MARGIN and d["keep_margin"] > EXACT_MARGIN:
+        if d["u_margin"] > EXACT_MARGIN and d["keep_margin"] > EXACT_MARGIN and d["topp_margin"] > EXACT_MARGIN:
             assert g == e, f"{label} row {r}: token {g} != oracle {e} (u={u[r]})"
             continue
         near += 1
         assert 0 <= g < len(d["q"]), f"{label} row {r}: token {g} out of range"
-        q, cdf = d["q"], d["cdf"]
-        lo, hi = cdf[g] - q[g], cdf[g]
         y = d["z"] / temperature
         border = abs((y[g] - y.max()) - np.log(min_p)) < VALID_TOL if min_p > 0 else False
-        assert (q[g] > 0 or border) and lo - VALID_TOL <= u[r] < hi + VALID_TOL, \
-            f"{label} row {r}: token {g} (oracle {e}) is not a draw at u={u[r]} (cdf {lo}..{hi})"
+        ok = _is_draw(g, u[r], d["q"], d["cdf"], d["keep"], border)
+        if not ok and d["topp_margin"] <= EXACT_MARGIN:
+            # top-p within rounding of a cumulative boundary: the nearest
+            # probability value may be kept or dropped
+            w = np.where(d["keep_alt"], np.exp(y - y.max()), 0.0)
+            q2 = w / w.sum()
+            ok = _is_draw(g, u[r], q2, np.cumsum(q2), d["keep_alt"], border)
+        assert ok, f"{label} row {r}: token {g} (oracle {e}) is not a draw at u={u[r]}"
     say(f"  {label}: {R} rows, {near} near a boundary, tokens {got[:6].tolist()}...")
     return got
 
@@ -190,3 +201,72 @@ def test_reused_workspace_with_garbage():
         c = inputs.make_sample(dtype=dtype, V=V, seed=seed)
         run(c.logits, dtype, c.hist, c.parent, c.draft_tok, window=1024, penalty=1.2, temperature=1.0,
             min_p=0.1, u=c.u, label=f"shared workspace V={V}", workspace=ws)
+
+
+# ---------------------------------------------------------------------------
+# top-p (nucleus)
+# ---------------------------------------------------------------------------
+TOPP_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "top_p_example.json")
+
+
+def test_top_p_hand_worked_example():
+    ex = json.load(open(TOPP_GOLDEN))
+    x = np.array([ex["logits"]], np.float32)
+    for c in ex["cases"]:
+        for u, tok in c["draws"]:
+            g = run(x, "f32", [], [], [], window=0, penalty=1.2, temperature=c["temperature"], min_p=c["min_p"],
+                    top_p=c["top_p"], u=[u], label=f"golden top_p={c['top_p']} u={u}")
+            assert g.tolist() == [tok]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("temperature,min_p,top_p", [
+    (1.0, 0.1, 0.9),              # the CLI's min-p with a nucleus on top
+    (0.4, 0.0, 0.9),              # the temperature ablation's range, top-p alone
+    (0.8, 0.0, 0.95),
+    (1.2, 0.0, 0.9),
+    (1.0, 0.0, 0.5),
+])
+def test_top_p_verify_rows_full_vocabulary(dtype, temperature, min_p, top_p):
+    """121 rows over the 128,256-token vocabulary with the pages' penalty."""
+    c = inputs.make_sample(dtype=dtype)
+    run(c.logits, dtype, c.hist, c.parent, c.draft_tok, window=inputs.PENALTY_WINDOW, penalty=inputs.PENALTY,
+        temperature=temperature, min_p=min_p, top_p=top_p, u=c.u,
+        label=f"top-p 121x128256 {dtype} tau={temperature} min_p={min_p} top_p={top_p}")
+
+
+@pytest.mark.parametrize("top_p", [1e-6, 0.3, 0.999])
+def test_top_p_flat_and_tied_logits(top_p):
+    """Logits that take few distinct values: whole groups of equal
+    probability are kept or dropped together (all tied: every token kept)."""
+    rng = np.random.default_rng(31)
+    V = 40000
+    x = np.zeros((4, V), np.float32)                     # row 0: all equal
+    x[1] = rng.integers(0, 4, V).astype(np.float32)      # four values
+    x[2] = np.round(rng.standard_normal(V) * 2, 1)       # many ties
+    x[3] = rng.standard_normal(V).astype(np.float32) * 0.01
+    u = rng.random(4, dtype=np.float32)
+    for tau in (1.0, 0.5):
+        parent = np.array([-1, 0, 1], np.int32)
+        run(x, "f32", [], parent, np.array([5, 6, 7], np.int32), window=4, penalty=1.2, temperature=tau,
+            min_p=0.0, top_p=top_p, u=u, label=f"tied tau={tau} top_p={top_p}")
+
+
+@pytest.mark.parametrize("V", [7, 1025, 4097, 128257])
+def test_top_p_ragged_vocabularies(V):
+    rng = np.random.default_rng(V + 1)
+    parent = np.array([-1, 0, 1], np.int32)
+    draft = rng.integers(0, V, 3).astype(np.int32)
+    hist = rng.integers(0, V, 200).astype(np.int32)
+    x = (rng.standard_normal((4, V)) * 2).astype(np.float32)
+    x[1, ::5] = -np.inf
+    u = rng.random(4, dtype=np.float32)
+    for dtype in ("f32", "bf16"):
+        xx = x
+        if dtype == "bf16":
+            fin = np.isfinite(x)
+            xx = inputs.f32_to_bf16_bits(np.where(fin, x, 0))
+            xx[~fin] = 0xFF80
+        for tau, mp, tp in ((1.0, 0.0, 0.8), (0.6, 0.05, 0.7)):
+            run(xx, dtype, hist, parent, draft, window=64, penalty=1.3, temperature=tau, min_p=mp, top_p=tp,
+                u=u, label=f"top-p V={V} {dtype} tau={tau} min_p={mp} top_p={tp}")
