@@ -2,16 +2,18 @@
 """Benchmark of the TokenSwift-style hot path on one MI355X.
 
 One step = one pass of the whole path for one LLaMA3.1-8B-shaped layer
-(32 query heads, 8 KV heads, head_dim 128, bf16) over a 102,400-token cache:
+(32 query heads, 8 KV heads, head_dim 128, bf16) over one 102,400-token cache:
 
   1. tree-verify attention of 120 draft queries ([1,3,3,3] tree + 20 four-token
      chains) over the full cache: split-K kernel, then log-sum-exp merge;
-  2. partial-KV refresh: chunk importance from the 4 latest queries ->
-     top-64 of 1600 chunks per KV head -> gather of the 4096-token partial cache;
+  2. partial-KV refresh of the same cache: chunk importance from the 4 latest
+     queries -> top-64 of 1600 chunks per KV head -> gather of the 4096-token
+     partial cache;
   3. the 4-query draft attention over the partial cache.
 
-The verify merge and the chunk importance depend on nothing of each other and
-run as one launch (ts_attn_merge_and_importance; --unfused keeps two).
+The verify split kernel scores the chunks on the same reads of K
+(ts_tree_verify_attn_partials_and_importance); --unfused times the separate
+launches (split, merge, importance, top-k, gather, draft attention).
 
 Timing (all on the stream every call launches on, torch's current stream):
   * warm-up: at least W steps, then steps until at least --min-warm-s seconds
@@ -30,9 +32,11 @@ Timing (all on the stream every call launches on, torch's current stream):
   * one ts_tree_verify_attn call (split + merge), cold and warm, at 20,480 and
     102,400 cached tokens (LLaMA3.1-8B) and at 102,400 (LLaMA2-7B MHA).
 
-Inputs are seeded synthetic tensors resident in HBM before timing starts
-(verify inputs: seed 2; partial-KV inputs: seed 3, with 8 chunks per KV head
-carrying 3x keys). Prints ONE JSON line.
+Inputs are seeded synthetic tensors resident in HBM before timing starts:
+the cache and the 4 recent queries of the partial-KV workload (seed 3, 8
+chunks per KV head carrying 3x keys) and the drafts of the verify workload
+(seed 2: queries, draft K/V, the tree + chains forest). The verify-call lines
+run the verify workload with its own cache. Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--unfused] [--graph] [--cpu-heads H] [--cpu-seconds S]
                     [--no-cpu-baseline] [--no-verify-lines] [--no-probes] [--calibrate-copy]
@@ -196,8 +200,8 @@ def main():
     log(f"inputs generated in {time.time() - t0:.1f}s")
 
     # ---- device-resident inputs and preallocated outputs -------------------
+    # one cache for the whole step: the partial-KV workload's
     q = to_dev(vc.q, "bf16", dev)
-    kc, vcache = to_dev(vc.k_cache, "bf16", dev), to_dev(vc.v_cache, "bf16", dev)
     kd, vd = to_dev(vc.k_draft, "bf16", dev), to_dev(vc.v_draft, "bf16", dev)
     parent = to_dev(vc.parent, "i32", dev)
     T, Hq, Hkv, D, L = vc.T, vc.Hq, vc.Hkv, vc.D, vc.L
@@ -209,6 +213,7 @@ def main():
 
     pq = to_dev(pc.q, "bf16", dev)
     pk, pv = to_dev(pc.k_cache, "bf16", dev), to_dev(pc.v_cache, "bf16", dev)
+    kc, vcache = pk, pv
     pkn, pvn = to_dev(pc.k_new, "bf16", dev), to_dev(pc.v_new, "bf16", dev)
     scores = torch.empty((pc.Hkv, pc.n_chunks), dtype=torch.float32, device=dev)
     idx = torch.empty((pc.Hkv, pc.k), dtype=torch.int32, device=dev)
@@ -240,14 +245,14 @@ def main():
                                workspace=dws)
         rec(6)
 
-    # The verify merge and the chunk importance depend on nothing of each other:
-    # the timed step runs them as one launch (bit-identical results); the
-    # per-kernel pass below keeps them apart so that each has its own time.
+    # The timed step: the verify split kernel also scores the cache's chunks on
+    # the same reads of K; the per-kernel pass below runs the separate launches
+    # so that each has its own time.
     def step_fused():
-        ops.tree_verify_attn_partials(q, kc, vcache, kd, vd, parent, scale=vc.scale,
-                                      o_part=o_part, l_part=l_part)
-        ops.attn_merge_and_importance(o_part, l_part, pq, pk, pc.chunk, out=out, lse=lse, scale=pc.scale,
-                                      scores=scores)
+        ops.tree_verify_attn_partials_and_importance(q, kc, vcache, kd, vd, parent, pq, pc.chunk, scale=vc.scale,
+                                                     imp_scale=pc.scale, o_part=o_part, l_part=l_part,
+                                                     scores=scores)
+        ops.attn_merge(o_part, l_part, out=out, lse=lse)
         ops.kv_topk_select(scores, pc.k, chunk_idx=idx, chunk_score=idx_s)
         ops.kv_gather(pk, pv, idx, pc.chunk, k_part=kp, v_part=vp)
         ops.partial_draft_attn(pq, kp, vp, pkn, pvn, scale=pc.scale, out=dout, lse=dlse,
@@ -294,30 +299,61 @@ def main():
         un += tm.back_to_back(step, 2)
     alternated = {"fused": stats(fu), "unfused": stats(un)}
 
-    # ---- per-kernel durations (unfused step, events between the kernels) ------
-    events = [tm.events(7) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    per = {n: [] for n in names}
-    for e in events:
-        for j, n in enumerate(names):
-            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)   # us
-    avg = {n: float(np.mean(v)) for n, v in per.items()}
-    med = {n: float(np.median(v)) for n, v in per.items()}
+    # ---- per-kernel durations (events between the kernels) ------------------
+    def per_kernel(fn, n_ev, labels):
+        events = [tm.events(n_ev) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            fn(events[i])
+        torch.cuda.synchronize()
+        per = {n: [] for n in labels}
+        for e in events:
+            for j, n in enumerate(labels):
+                per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)   # us
+        return ({n: float(np.mean(v)) for n, v in per.items()}, {n: float(np.median(v)) for n, v in per.items()})
 
-    # ---- roofline of the dominant kernel (verify split-K) -------------------
+    def step_fused_ev(ev):
+        ev[0].record()
+        ops.tree_verify_attn_partials_and_importance(q, kc, vcache, kd, vd, parent, pq, pc.chunk, scale=vc.scale,
+                                                     imp_scale=pc.scale, o_part=o_part, l_part=l_part,
+                                                     scores=scores)
+        ev[1].record()
+        ops.attn_merge(o_part, l_part, out=out, lse=lse)
+        ev[2].record()
+        ops.kv_topk_select(scores, pc.k, chunk_idx=idx, chunk_score=idx_s)
+        ev[3].record()
+        ops.kv_gather(pk, pv, idx, pc.chunk, k_part=kp, v_part=vp)
+        ev[4].record()
+        ops.partial_draft_attn(pq, kp, vp, pkn, pvn, scale=pc.scale, out=dout, lse=dlse, workspace=dws)
+        ev[5].record()
+
+    fused_names = ["verify_split_importance", "verify_merge", "topk", "gather", "draft_attn"]
+    avg, med = per_kernel(step, 7, names)
+    favg, fmed = per_kernel(step_fused_ev, 6, fused_names)
+
+    # ---- roofline of the dominant kernel of the timed step ---------------------
+    # the split kernel that also scores the chunks: the verify's QK^T and PV
+    # flops plus the importance's QK^T flops (4 queries x 4 heads per KV head)
     flops = verify_flops(vc)
+    imp_flops = 2.0 * pc.R * pc.Hq * pc.L * pc.D
     kv_bytes = 2.0 * Hkv * L * D * 2            # K and V of the cache, read once
+    dom = "verify_split" if args.unfused else "verify_split_importance"
+    t_dom = (avg if args.unfused else favg)[dom] * 1e-6
+    dom_flops = flops if args.unfused else flops + imp_flops
+    achieved = dom_flops / t_dom / 1e12
     t_split = avg["verify_split"] * 1e-6
-    achieved = flops / t_split / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(), "kernel": "verify split-K (attn_split_mfma_kernel)",
-                "algorithmic_flops": flops, "algorithmic_bytes": kv_bytes,
-                "hbm_GBs": round(kv_bytes / t_split / 1e9, 1),
-                "hbm_frac": round(kv_bytes / t_split / 1e9 / HBM_PEAK_GBS, 4)}
+                "traffic": measured_traffic(),
+                "kernel": ("verify split-K (attn_split_mfma_kernel)" if args.unfused else
+                           "verify split-K with chunk importance (attn_split_mfma_kernel, importance wave)"),
+                "kernel_us": round(t_dom * 1e6, 2),
+                "algorithmic_flops": dom_flops, "algorithmic_bytes": kv_bytes,
+                "hbm_GBs": round(kv_bytes / t_dom / 1e9, 1),
+                "hbm_frac": round(kv_bytes / t_dom / 1e9 / HBM_PEAK_GBS, 4),
+                "verify_split_alone": {"us": round(t_split * 1e6, 2),
+                                       "TFLOPs": round(flops / t_split / 1e12, 2),
+                                       "frac": round(flops / t_split / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
     res = {
         "metric": METRIC,
@@ -332,25 +368,27 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "llama3.1-8b layer, 102400-token bf16 KV cache: tree-verify of 120 drafts "
-                               "([1,3,3,3] tree + 20 4-gram chains) + partial-KV refresh (4 queries, "
-                               "64 of 1600 64-token chunks) + 4-query draft attention",
+        "config": {"workload": "llama3.1-8b layer, one 102400-token bf16 KV cache: tree-verify of 120 drafts "
+                               "([1,3,3,3] tree + 20 4-gram chains) + partial-KV refresh of the same cache "
+                               "(4 queries, 64 of 1600 64-token chunks) + 4-query draft attention",
                    "T": T, "Hq": Hq, "Hkv": Hkv, "head_dim": D, "kv_len": L, "splits": S,
                    "chunk": pc.chunk, "topk": pc.k},
         "timing": ("graph replay of the step" if graph is not None else "eager launches") +
-                  ("" if args.unfused else "; verify merge and chunk importance as one launch") +
+                  ("" if args.unfused else "; chunk importance scored by the verify split kernel") +
                   "; value = wall clock of the back-to-back steps after a settled warm-up",
         "warmup_settled": warm,
         "step_us": {"warm": step_warm, "cold": step_cold},
         "step_alternated_us": alternated,
         "kernel_us_avg": {n: round(v, 2) for n, v in avg.items()},
         "kernel_us_median": {n: round(v, 2) for n, v in med.items()},
+        "step_kernel_us_avg": {n: round(v, 2) for n, v in favg.items()},
+        "step_kernel_us_median": {n: round(v, 2) for n, v in fmed.items()},
         "roofline": roofline,
     }
 
     # ---- one ts_tree_verify_attn call per workload ----------------------------
     if not args.no_verify_lines:
-        res["verify_call_us"] = verify_lines(tm, dev, vc, (q, kc, vcache, kd, vd, parent), args)
+        res["verify_call_us"] = verify_lines(tm, dev, vc, args)
     peaks = None
     if not args.no_probes:
         peaks = measured_peaks(dev)
@@ -381,7 +419,7 @@ def verify_flops(c):
     return 4.0 * c.D * c.Hq * (c.T * c.L + vis)
 
 
-def verify_lines(tm, dev, vc2, resident, args):
+def verify_lines(tm, dev, vc2, args):
     """One ts_tree_verify_attn call (split + merge, library-chosen splits) per
     workload: median/p10/p90 cold (1 GiB scratch write and read-back before each call) and
     warm (back to back), with %HBM of the cache's K+V and %MFMA of 2.5 PF."""
@@ -389,14 +427,11 @@ def verify_lines(tm, dev, vc2, resident, args):
     from long_context_kv_ts_amd import inputs, ops
     lines = {}
     for name in ("llama8b_100k", "llama8b_20k", "llama2_mha_100k"):
-        if name == "llama8b_100k":
-            c, (q, kc, vc, kd, vd, par) = vc2, resident
-        else:
-            t0 = time.time()
-            c = inputs.workload(name)
-            q, kc, vc = to_dev(c.q, "bf16", dev), to_dev(c.k_cache, "bf16", dev), to_dev(c.v_cache, "bf16", dev)
-            kd, vd, par = to_dev(c.k_draft, "bf16", dev), to_dev(c.v_draft, "bf16", dev), to_dev(c.parent, "i32", dev)
-            log(f"{name}: inputs in {time.time() - t0:.1f}s")
+        t0 = time.time()
+        c = vc2 if name == "llama8b_100k" else inputs.workload(name)
+        q, kc, vc = to_dev(c.q, "bf16", dev), to_dev(c.k_cache, "bf16", dev), to_dev(c.v_cache, "bf16", dev)
+        kd, vd, par = to_dev(c.k_draft, "bf16", dev), to_dev(c.v_draft, "bf16", dev), to_dev(c.parent, "i32", dev)
+        log(f"{name}: inputs in {time.time() - t0:.1f}s")
         out = torch.empty_like(q)
         lse = torch.empty((c.T, c.Hq), dtype=torch.float32, device=dev)
         ws = ops.alloc_workspace(ops.verify_workspace_bytes(c.T, c.Hq, c.Hkv, c.D, c.L, torch.bfloat16), dev)
@@ -413,8 +448,7 @@ def verify_lines(tm, dev, vc2, resident, args):
                        "mfma_frac_cold": round(fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                        "hbm_frac_warm": round(kv / (warm["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"verify call {name}: cold {cold['median']} us, warm {warm['median']} us")
-        if name != "llama8b_100k":
-            del q, kc, vc, kd, vd, par
+        del q, kc, vc, kd, vd, par
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     return lines
@@ -594,7 +628,7 @@ def cpu_baseline(vc, pc, heads, min_seconds):
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.verify_attn_ref(vc.q, vc.k_cache, vc.v_cache, vc.k_draft, vc.v_draft, vc.parent,
+        oracle.verify_attn_ref(vc.q, pc.k_cache, pc.v_cache, vc.k_draft, vc.v_draft, vc.parent,
                                vc.scale, "bf16", heads=hs)
         s = oracle.importance_ref(pc.q, pc.k_cache, pc.scale, pc.chunk, "bf16", heads=hs)
         idx, _ = oracle.topk_ref(s[hs], pc.k)

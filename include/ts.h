@@ -148,6 +148,26 @@ ts_status ts_attn_merge(const float* o_part, const float* l_part, int n_parts,
                         int rows, int D, void* out, float* lse, ts_dtype dtype,
                         hipStream_t stream);
 
+/* ts_tree_verify_attn_partials followed by ts_kv_importance_score over the
+ * same cache, in one launch where the shapes allow. In a decode step the
+ * verification pass reads the whole cache of a layer and the partial-cache
+ * refresh scores that same cache's chunks against the latest queries (tool
+ * listing, "How it works"; summary page, "Approach"): one pass over K can
+ * serve both. The arguments are those of ts_tree_verify_attn_partials, then
+ * those of ts_kv_importance_score that differ (q_recent [R][Hq][D], R, chunk,
+ * imp_scale, scores [Hkv][L/chunk]), with the same meaning, layout, checks and
+ * errors; the importance is taken over k_cache rows [0, L). Results are those
+ * of the two calls (o_part, l_part bit-identical; scores equal up to fp32
+ * summation order). One launch when dtype is bf16, D = 128, chunk = 64,
+ * L % 64 == 0, T <= 256, Hq/Hkv is 1, 2 or 4 with R*(Hq/Hkv) <= 32, and the
+ * verify rows of a KV head (T*Hq/Hkv, above 128) leave the last 32 of their
+ * last 256-row group empty (e.g. 480 rows); otherwise the two launches. */
+ts_status ts_tree_verify_attn_partials_and_importance(
+    const void* q, const void* k_cache, const void* v_cache, int64_t cache_stride, const void* k_draft,
+    const void* v_draft, const int32_t* parent, float* o_part, float* l_part, int T, int Hq, int Hkv, int D,
+    int64_t L, float scale, ts_dtype dtype, int num_splits, const void* q_recent, int R, int chunk,
+    float imp_scale, float* scores, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Chunk importance (summary page, "Approach": the reduced cache is chosen by
  * how strongly queries attend to its keys). For KV head g and chunk

@@ -85,6 +85,9 @@ AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype
   }
   if (s > p.n_virtual) s = p.n_virtual;
   p.tiles_per_split = (p.n_virtual + s - 1) / s;
+  // matrix-core splits start on even 32-key tiles, i.e. on 64-token chunk
+  // boundaries (the split kernel can score chunks on the same reads)
+  if (p.path == kPathMfma) p.tiles_per_split += p.tiles_per_split & 1;
   p.n_splits = (p.n_virtual + p.tiles_per_split - 1) / p.tiles_per_split;
   return p;
 }
@@ -116,11 +119,20 @@ size_t ts_tree_verify_attn_workspace(int T, int Hq, int Hkv, int D, int64_t L, t
          align_up((size_t)p.n_splits * rows * sizeof(float));
 }
 
+// chunk importance scored by the split kernel on the same reads of K
+struct ImpFusion {
+  const void* q_recent;
+  float* scores;
+  int R;
+  float scale;
+};
+
 static ts_status attn_common(const char* fn, const void* q, const void* kc, const void* vc,
                              int64_t cache_stride, const void* kd, const void* vd,
                              const int32_t* parent, bool need_parent, float* o_part, float* l_part,
                              int T, int Hq, int Hkv, int D, int64_t L, float scale,
-                             ts_dtype dtype, int num_splits, hipStream_t stream) {
+                             ts_dtype dtype, int num_splits, hipStream_t stream,
+                             const ImpFusion* imp = nullptr) {
   ts_status st = check_attn_shape(fn, T, Hq, Hkv, D, L, dtype, num_splits);
   if (st != TS_OK) return st;
   if (!q || !kd || !vd || !o_part || !l_part) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
@@ -148,6 +160,12 @@ static ts_status attn_common(const char* fn, const void* q, const void* kc, cons
   a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D; a.L = L;
   a.scale_log2 = scale * kLog2e;
   a.plan = plan;
+  if (imp != nullptr) {
+    a.q_imp = imp->q_recent;
+    a.scores = imp->scores;
+    a.imp_R = imp->R;
+    a.imp_scale = imp->scale;
+  }
   hipError_t e = a.plan.path == kPathMfma    ? launch_attn_split_mfma(a, stream)
                  : a.plan.path == kPathSmall ? launch_attn_split_small(a, stream)
                                              : launch_attn_split_valu(a, dtype, stream);
@@ -163,6 +181,37 @@ ts_status ts_tree_verify_attn_partials(const void* q, const void* k_cache, const
   return attn_common("ts_tree_verify_attn_partials", q, k_cache, v_cache, cache_stride, k_draft,
                      v_draft, parent, true, o_part, l_part, T, Hq, Hkv, D, L, scale, dtype,
                      num_splits, stream);
+}
+
+static ts_status check_importance(const char* fn, const void* q_recent, const void* k_cache,
+                                  int64_t cache_stride, const float* scores, int R, int Hq, int Hkv, int D,
+                                  int64_t L, int chunk, float scale, ts_dtype dtype);
+
+ts_status ts_tree_verify_attn_partials_and_importance(
+    const void* q, const void* k_cache, const void* v_cache, int64_t cache_stride, const void* k_draft,
+    const void* v_draft, const int32_t* parent, float* o_part, float* l_part, int T, int Hq, int Hkv, int D,
+    int64_t L, float scale, ts_dtype dtype, int num_splits, const void* q_recent, int R, int chunk,
+    float imp_scale, float* scores, hipStream_t stream) {
+  const char* fn = "ts_tree_verify_attn_partials_and_importance";
+  ts_status st = check_importance(fn, q_recent, k_cache, cache_stride, scores, R, Hq, Hkv, D, L, chunk,
+                                  imp_scale, dtype);
+  if (st != TS_OK) return st;
+  st = check_attn_shape(fn, T, Hq, Hkv, D, L, dtype, num_splits);
+  if (st != TS_OK) return st;
+  const AttnPlan plan = plan_attention(T, Hq, Hkv, D, L, dtype, num_splits);
+  const bool fused = dtype == TS_BF16 && chunk == 64 &&
+                     attn_mfma_importance_fusable(plan, T, Hq / Hkv, D, L, R);
+  if (!fused) {
+    // two launches: the split kernel, then the importance kernel
+    st = attn_common(fn, q, k_cache, v_cache, cache_stride, k_draft, v_draft, parent, true, o_part, l_part, T, Hq,
+                     Hkv, D, L, scale, dtype, num_splits, stream);
+    if (st != TS_OK) return st;
+    return from_hip(launch_importance(q_recent, k_cache, cache_stride, scores, R, Hq, Hkv, D, L, chunk, imp_scale,
+                                      dtype, stream), fn);
+  }
+  ImpFusion f{q_recent, scores, R, imp_scale};
+  return attn_common(fn, q, k_cache, v_cache, cache_stride, k_draft, v_draft, parent, true, o_part, l_part, T, Hq,
+                     Hkv, D, L, scale, dtype, num_splits, stream, &f);
 }
 
 static ts_status check_merge(const char* fn, const float* o_part, const float* l_part, int n_parts, int rows,

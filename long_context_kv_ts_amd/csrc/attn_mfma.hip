@@ -40,12 +40,28 @@
 // the split; they run unpipelined after it.
 //
 // Softmax in base 2 on fp32 scores (exact bf16 products, fp32 sums); scale is
-// applied in fp32 after the product. The running max is only raised when a new
-// score exceeds it by more than 2^8 ("lazy rescale"), which keeps every
-// probability <= 256 and makes rescaling of the accumulators rare. The
-// probabilities are rounded to bf16 for the PV product; the row sum uses the
-// unrounded values. Draft tiles are masked by the ancestor-or-self bitmask
-// built in LDS from parent[] (a 32-key tile is one word of a row's mask).
+// applied in fp32 after the product. The running max m is only raised when a
+// new score exceeds it by more than 2^8 ("lazy rescale"), which makes
+// rescaling of the accumulators rare. In the steady state the probabilities
+// are formed against the current m without a row maximum at all: a lane whose
+// 16 probabilities of a tile sum to more than 2^12 (one of them is then above
+// 2^8, or m is still -inf) flags the wave, which redoes that tile with the row
+// maximum before its probabilities are used; otherwise every probability stays
+// below 2^12. The probabilities are rounded to bf16 for the PV product; the
+// row sum uses the unrounded values. Draft tiles are masked by the
+// ancestor-or-self bitmask built in LDS from parent[] (a 32-key tile is one
+// word of a row's mask).
+//
+// Chunk importance on the same reads (kImp). When the last row group of a KV
+// head ends in a wave that holds no query row (480 rows = 256 + 224 for the
+// LLaMA3.1-8B layer), that wave scores 64-token chunks of the cache for the R
+// recent queries instead: its Q operand holds the R*G recent query rows and it
+// runs S = Q . K^T (untransposed: the same register operands in the other
+// order) on the K tiles already in LDS, skipping PV. A lane then holds one key
+// and 16 query rows, a recent query's G heads being G consecutive registers,
+// so the maximum over the heads and the sum over the queries are in-lane;
+// every second tile completes a chunk, whose mean the wave reduces with DPP
+// and writes. Splits then start on even tiles (64-token chunks).
 #include "common.h"
 #include <type_traits>
 
@@ -77,10 +93,17 @@ template <int D, int kWaves> struct Layout {
 template <int D> __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & (D / 8 - 1)); }
 template <int D> __device__ __forceinline__ int v_chunk(int r, int c) { return c ^ ((4 * (r & 3)) & (D / 8 - 1)); }
 
+// The base address and the LDS destination are wave-uniform; they are passed
+// through readfirstlane so that they stay scalar operands even where the
+// compiler cannot prove it (free when they already live in scalar registers).
 __device__ __forceinline__ void lds_dma16(const bf16_t* base, uint32_t voff, uint32_t lds) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t bs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(base), "s"(lds)
+               : "v"(voff), "s"(reinterpret_cast<const bf16_t*>(bs)), "s"(ls)
                : "memory", "m0");
 }
 
@@ -107,6 +130,12 @@ __device__ __forceinline__ float sum_xor32(float x) {
 
 template <bool B> using Flag = std::integral_constant<bool, B>;
 
+// Lane exchange within quads of lanes (DPP quad_perm).
+template <int kCtrl>
+__device__ __forceinline__ float quad_dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
 // kStages-deep ring of K/V tiles; kMaxT drafts at most. Eight stages fit next to
 // the mask of up to 256 drafts, seven next to the mask of up to 1024. kWaves
 // waves of 32 rows each: 8 (two per SIMD), or 4 when a KV head has at most 128
@@ -114,7 +143,7 @@ template <bool B> using Flag = std::integral_constant<bool, B>;
 // Registers are budgeted for two waves per SIMD in both forms (8 / kWaves
 // workgroups a CU): one wave per SIMD may take 512 registers, and the compiler
 // then parks values in AGPRs and moves them back and forth in the loop.
-template <int D, int kStages, int kMaxT, int kWaves>
+template <int D, int kStages, int kMaxT, int kWaves, bool kImp>
 __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void attn_split_mfma_kernel(AttnArgs a) {
   constexpr int kThreads = kWaves * 64;
   constexpr int kRowsPerGroup = kWaves * 32;
@@ -211,14 +240,25 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void attn_split_mfma_kerne
   const bool row_ok = row < pl.rows_per_head;
   const int row_t = row_ok ? row / G : 0;
   const int row_h = g * G + (row_ok ? row % G : 0);
-  {
+  // the importance wave: the last wave of the last row group, holding no query row
+  bool imp = false;
+  if constexpr (kImp) imp = rg == R - 1 && wave == kWaves - 1 && rg * kRowsPerGroup + wave * 32 >= pl.rows_per_head;
+  if (imp) {
+    // row col = (recent query col / G, head g*G + col % G); rows past R*G are zero
+    const bool ok = col < a.imp_R * G;
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q_imp) + ((int64_t)(ok ? col / G : 0) * Hq + g * G + col % G) * D;
+#pragma unroll
+    for (int ks = 0; ks < Ly::KS; ++ks)
+      qf[ks] = ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + ks * 16 + half * 8))
+                  : __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+  } else {
     const bf16_t* qp = static_cast<const bf16_t*>(a.q) + ((int64_t)row_t * Hq + row_h) * D;
 #pragma unroll
     for (int ks = 0; ks < Ly::KS; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + ks * 16 + half * 8));
-#pragma unroll
-    for (int ks = 0; ks < Ly::KS; ++ks) asm volatile("" : : "v"(qf[ks]));
   }
+#pragma unroll
+  for (int ks = 0; ks < Ly::KS; ++ks) asm volatile("" : : "v"(qf[ks]));
   // tiles 0..kAhead-1 start streaming (Q has already landed)
   for (int j = 0; j < kAhead; ++j) issue_upto(j);
 
@@ -247,22 +287,167 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void attn_split_mfma_kerne
     for (int db = 0; db < Ly::DB; ++db) asm volatile("" : "+v"(voff[db]));
   }
 
+  f32x16_t S;
+  bf16x8_t Kf[Ly::KS];
+  auto read_k_at = [&](uint32_t so) {          // so: stage offset in bytes
+#pragma unroll
+    for (int ks = 0; ks < Ly::KS; ++ks)
+      Kf[ks] = *reinterpret_cast<__attribute__((address_space(3))) bf16x8_t*>(koff[ks] + so);
+  };
+  auto read_k = [&](int j) { read_k_at((uint32_t)(j % kStages) * kTileBytes); };
+  auto qk = [&](f32x16_t& Sx) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Sx[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < Ly::KS; ++ks) Sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Kf[ks], qf[ks], Sx, 0, 0, 0);
+  };
+  // Chunk importance of tile j from S = Q . K^T (importance wave only): lane
+  // holds key lane % 32 and query rows 8*(e/4) + 4*half + e%4 in register e, so
+  // recent query r's G heads (rows r*G .. r*G + G-1) are G consecutive
+  // registers. Per key, the maximum over the heads of each query, summed over
+  // the queries; an odd tile completes a 64-token chunk.
+  float imp_acc = 0.f;
+  const int imp_rows = a.imp_R * G;
+  const float imp_scale = a.imp_scale;
+  auto imp_sum = [&](const f32x16_t& Sx, auto gc) {
+    constexpr int GG = decltype(gc)::value;
+    float sum = 0.f;
+#pragma unroll
+    for (int e0 = 0; e0 < 16; e0 += 4) {
+      // registers e0..e0+3 are rows rb..rb+3
+      const int rb = 8 * (e0 >> 2) + 4 * half;
+#pragma unroll
+      for (int q0 = 0; q0 < 4; q0 += GG) {
+        // the query of rows rb+q0 .. rb+q0+GG-1
+        float v = Sx[e0 + q0] * imp_scale;
+#pragma unroll
+        for (int h = 1; h < GG; ++h) v = fmaxf(v, Sx[e0 + q0 + h] * imp_scale);
+        sum += rb + q0 < imp_rows ? v : 0.f;
+      }
+    }
+    return sum;
+  };
+  auto imp_tile = [&](const f32x16_t& Sx, int j) {
+    imp_acc += G == 4   ? imp_sum(Sx, std::integral_constant<int, 4>{})
+               : G == 2 ? imp_sum(Sx, std::integral_constant<int, 2>{})
+                        : imp_sum(Sx, std::integral_constant<int, 1>{});
+    const int vt = vt0 + j;
+    if (vt & 1) {
+      // sum over the 64 lanes: DPP within rows of 16, then the four rows
+      float x = imp_acc;
+      x += quad_dpp<0xB1>(x);                        // quad_perm [1,0,3,2]
+      x += quad_dpp<0x4E>(x);                        // quad_perm [2,3,0,1]
+      x += quad_dpp<0x141>(x);                       // row_half_mirror
+      x += quad_dpp<0x140>(x);                       // row_mirror
+      const float tot = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16))) +
+                        (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)) +
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
+      if (lane == 0) a.scores[(int64_t)g * (a.L >> 6) + (vt >> 1)] = tot * (1.f / (64.f * (float)a.imp_R));
+      imp_acc = 0.f;
+    }
+  };
+  // the importance wave's product: S = Q . K^T (operands of qk in the other order)
+  auto qk_imp = [&](f32x16_t& Sx) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Sx[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < Ly::KS; ++ks) Sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], Kf[ks], Sx, 0, 0, 0);
+  };
+
+  // Tiles past the last full cache tile (ragged cache tail, drafts) are masked;
+  // they form a suffix of the split and run after the pipelined prefix.
+  const int full_tiles = (int)(a.L / kKeys);
+  const int nb_u = max(0, min(nb, full_tiles - vt0));
+
+  const bf16_t* cache_next = cache_base + (int64_t)(vt0 + kAhead) * kKeys * D;
+  // the importance wave's steady-state iteration: the same barrier and loads, QK^T
+  // and its chunk scores, no V
+  auto fast_imp = [&](auto ust, int j) {
+    constexpr int U = decltype(ust)::value;
+    __builtin_amdgcn_s_waitcnt(vm_wait((kAhead - 3) * Ly::loadsPerWave));    // tile j+2 landed
+    asm volatile("s_barrier" : : : "memory");
+    {
+      const bf16_t* base = cache_next + (int64_t)j * kKeys * D;         // tile j+kAhead
+      const uint32_t sb = my_lds + (uint32_t)(((U + kAhead) % kStages) * kTileBytes);
+#pragma unroll
+      for (int n = 0; n < Ly::loadsPerWave; ++n) {
+        const int q = wave * Ly::loadsPerWave + n;
+        const int mblk = q >= Ly::loadsPerTensor ? q - Ly::loadsPerTensor : q;
+        lds_dma16(base, off_full[n], sb + (uint32_t)(mblk * 1024));
+      }
+    }
+    f32x16_t Sn;
+    qk_imp(Sn);
+    read_k_at((uint32_t)(((U + 2) % kStages) * kTileBytes));
+    imp_tile(S, j);
+    S = Sn;
+  };
+  auto steady = [&](auto&& body, int& j) {
+    for (; j + kStages <= nb_u - kAhead; j += kStages) {  // j % kStages == 1
+      body(std::integral_constant<int, 1 % kStages>{}, j);
+      body(std::integral_constant<int, 2 % kStages>{}, j + 1);
+      body(std::integral_constant<int, 3 % kStages>{}, j + 2);
+      body(std::integral_constant<int, 4 % kStages>{}, j + 3);
+      body(std::integral_constant<int, 5 % kStages>{}, j + 4);
+      body(std::integral_constant<int, 6 % kStages>{}, j + 5);
+      body(std::integral_constant<int, 7 % kStages>{}, j + 6);
+      if constexpr (kStages == 8) body(std::integral_constant<int, 0>{}, j + 7);
+      issued = j + kStages + kAhead;
+    }
+  };
+
+
+  // ---- the importance wave: its own loop, with the same barriers and loads ----
+  if constexpr (kImp) {
+    if (imp) {
+      // iteration j: publish tile j+2, start tile j+kAhead, QK^T(j+1), score tile j
+      auto iter_imp = [&](auto next, int j) {
+        constexpr bool kNext = decltype(next)::value;
+        wait_for(j + 2);
+        __syncthreads();
+        issue_upto(j + kAhead);
+        f32x16_t Sn;
+        if constexpr (kNext) qk_imp(Sn);
+        read_k(j + 2);
+        imp_tile(S, j);
+        if constexpr (kNext) S = Sn;
+      };
+      if (nb_u > 0) {
+        wait_for(1);
+        __syncthreads();
+        read_k(0);
+        qk_imp(S);
+        if (nb_u > 1) read_k(1);
+        if (nb_u == 1) {
+          iter_imp(Flag<false>{}, 0);
+        } else {
+          iter_imp(Flag<true>{}, 0);
+          int j = 1;
+          steady(fast_imp, j);
+          for (; j < nb_u - 1; ++j) iter_imp(Flag<true>{}, j);
+          iter_imp(Flag<false>{}, nb_u - 1);
+        }
+      }
+      // the masked suffix holds only draft tiles here: barriers and loads only
+      for (int j = nb_u; j < nb; ++j) {
+        wait_for(j);
+        __syncthreads();
+        issue_upto(j + kAhead - 1);
+      }
+      return;
+    }
+  }
+
   f32x16_t O[Ly::DB];
 #pragma unroll
   for (int db = 0; db < Ly::DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
   float m = -INFINITY, lsum = 0.f;
-  f32x16_t S;
   bf16x8_t P[2];
-  bf16x8_t Kf[Ly::KS];
   bf16x8_t Vf[2][Ly::DB];
 
-  auto read_k_at = [&](uint32_t so) {          // so: stage offset in bytes
-#pragma unroll
-    for (int ks = 0; ks < Ly::KS; ++ks)
-      Kf[ks] = *reinterpret_cast<__attribute__((address_space(3))) bf16x8_t*>(koff[ks] + so);
-  };
   auto read_v_at = [&](uint32_t so) {
 #pragma unroll
     for (int db = 0; db < Ly::DB; ++db) {
@@ -278,14 +463,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void attn_split_mfma_kerne
       }
     }
   };
-  auto read_k = [&](int j) { read_k_at((uint32_t)(j % kStages) * kTileBytes); };
   auto read_v = [&](int j) { read_v_at((uint32_t)(j % kStages) * kTileBytes); };
-  auto qk = [&](f32x16_t& Sx) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) Sx[e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < Ly::KS; ++ks) Sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Kf[ks], qf[ks], Sx, 0, 0, 0);
-  };
   auto pv = [&](const bf16x8_t* Px) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
@@ -333,17 +511,59 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void attn_split_mfma_kerne
     lsum = lsum * *alpha + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
     return __builtin_amdgcn_ballot_w64(need) != 0;
   };
+  // Unmasked tiles: the probabilities against the current m, with no row
+  // maximum. A lane whose 16 probabilities sum to more than 2^12 (so one
+  // exceeds 2^8, or m is still -inf) flags the wave, which then redoes the
+  // tile with the row maximum (softmax_fix) before the probabilities are used.
+  auto softmax_fast = [&](f32x16_t Sx, bf16x8_t* Px, float& st) -> bool {
+    const float nmb = -m;
+    float pe[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(Sx[e], c, nmb));
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Px[hh][e] = static_cast<__bf16>(pe[8 * hh + e]);
+    float s4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s4[i] = (pe[4 * i] + pe[4 * i + 1]) + (pe[4 * i + 2] + pe[4 * i + 3]);
+    st = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    return st > 4096.0f;
+  };
+  auto softmax_fix = [&](f32x16_t Sx, bf16x8_t* Px, float* alpha) -> bool {
+    float t2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float t = fmaxf(fmaxf(Sx[8 * i], Sx[8 * i + 1]), Sx[8 * i + 2]);
+      t = fmaxf(fmaxf(t, Sx[8 * i + 3]), Sx[8 * i + 4]);
+      t = fmaxf(fmaxf(t, Sx[8 * i + 5]), Sx[8 * i + 6]);
+      t2[i] = fmaxf(t, Sx[8 * i + 7]);
+    }
+    float mx = fmaxf(t2[0], t2[1]);
+    mx = max_xor32(mx) * c;
+    const bool need = mx > m + kLazy;
+    *alpha = need ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
+    m = need ? mx : m;
+    const float nmb = -fmaxf(m, -3.0e38f);
+    float pe[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(Sx[e], c, nmb));
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Px[hh][e] = static_cast<__bf16>(pe[8 * hh + e]);
+    float s4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s4[i] = (pe[4 * i] + pe[4 * i + 1]) + (pe[4 * i + 2] + pe[4 * i + 3]);
+    lsum = lsum * *alpha + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
+    return __builtin_amdgcn_ballot_w64(need) != 0;
+  };
   auto rescale = [&](float alpha) {
 #pragma unroll
     for (int db = 0; db < Ly::DB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) O[db][e] *= alpha;
   };
-
-  // Tiles past the last full cache tile (ragged cache tail, drafts) are masked;
-  // they form a suffix of the split and run after the pipelined prefix.
-  const int full_tiles = (int)(a.L / kKeys);
-  const int nb_u = max(0, min(nb, full_tiles - vt0));
 
   // Pipelined iteration j over unmasked tiles. On entry: S = S(j), Kf = K(j+1)
   // (if j+1 < nb_u), Vf = V(j-1) and P = P(j-1) (if j >= 1).
@@ -379,7 +599,6 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void attn_split_mfma_kerne
   // a full cache tile. The barrier needs no LDS drain: the stage it recycles
   // (tile j-2) was last read two iterations ago and those reads were consumed
   // by products.
-  const bf16_t* cache_next = cache_base + (int64_t)(vt0 + kAhead) * kKeys * D;
   auto fast = [&](auto ust, int j) {
     constexpr int U = decltype(ust)::value;
     __builtin_amdgcn_s_waitcnt(vm_wait((kAhead - 3) * Ly::loadsPerWave));    // tile j+2 landed
@@ -399,24 +618,30 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void attn_split_mfma_kerne
     pv(P);
     read_k_at((uint32_t)(((U + 2) % kStages) * kTileBytes));
     read_v_at((uint32_t)(U * kTileBytes));
-    float al;
     bf16x8_t Pn[2];
-    const bool rs = softmax(Flag<false>{}, S, Pn, &al, j);
+    float st;
+    const bool bad = softmax_fast(S, Pn, st);
+    const float lsum_fast = lsum + st;
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
     for (int i = 0; i < 7; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-    asm volatile("" : : "v"(Pn[0]), "v"(Pn[1]), "v"(lsum), "v"(m));
-    if (rs) rescale(al);
+    asm volatile("" : : "v"(Pn[0]), "v"(Pn[1]), "v"(lsum_fast));
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+      float al;
+      if (softmax_fix(S, Pn, &al)) rescale(al);
+    } else {
+      lsum = lsum_fast;
+    }
     P[0] = Pn[0]; P[1] = Pn[1];
     S = Sn;
   };
@@ -432,17 +657,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void attn_split_mfma_kerne
     else {
       iter(Flag<false>{}, Flag<true>{}, 0);
       int j = 1;
-      for (; j + kStages <= nb_u - kAhead; j += kStages) {  // j % kStages == 1
-        fast(std::integral_constant<int, 1 % kStages>{}, j);
-        fast(std::integral_constant<int, 2 % kStages>{}, j + 1);
-        fast(std::integral_constant<int, 3 % kStages>{}, j + 2);
-        fast(std::integral_constant<int, 4 % kStages>{}, j + 3);
-        fast(std::integral_constant<int, 5 % kStages>{}, j + 4);
-        fast(std::integral_constant<int, 6 % kStages>{}, j + 5);
-        fast(std::integral_constant<int, 7 % kStages>{}, j + 6);
-        if constexpr (kStages == 8) fast(std::integral_constant<int, 0>{}, j + 7);
-        issued = j + kStages + kAhead;
-      }
+      steady(fast, j);
       for (; j < nb_u - 1; ++j) iter(Flag<true>{}, Flag<true>{}, j);
       iter(Flag<true>{}, Flag<false>{}, nb_u - 1);
     }
@@ -483,6 +698,17 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void attn_split_mfma_kerne
 }  // namespace
 
 int mfma_rows_per_group(int rows_per_head) { return rows_per_head <= 128 ? 128 : 256; }
+
+bool attn_mfma_importance_fusable(const AttnPlan& p, int T, int G, int D, int64_t L, int R) {
+  // the 8-wave, 8-stage D = 128 kernel whose last row group ends in a wave with
+  // no query row; R*G recent query rows fit that wave's 32 and a query's G heads
+  // sit in one lane quad; the cache is whole 64-token chunks and the splits
+  // start on even tiles
+  const int last = p.rows_per_head - (p.n_rowgroups - 1) * p.rows_per_group;
+  return p.path == kPathMfma && p.rows_per_group == 256 && D == 128 && T <= 256 && last <= 224 &&
+         (G == 1 || G == 2 || G == 4) && R >= 1 && R * G <= 32 && L > 0 && L % 64 == 0 &&
+         p.tiles_per_split % 2 == 0;
+}
 int mfma_tile_keys() { return kKeys; }
 int mfma_groups_per_cu() { return 1; }
 
@@ -492,12 +718,21 @@ hipError_t launch_waves(const AttnArgs& a, int blocks, hipStream_t s) {
   // up to 256 drafts: an 8-stage ring (tiles issued 6 ahead); more: 7 stages.
   // The 4-wave form serves at most 128 rows per KV head, so at most 128 drafts.
   if (kWaves == 4 && a.T > 128) return hipErrorInvalidValue;
+  if (a.q_imp != nullptr) {
+    // chunk importance in the all-padding wave (the caller checked the shape)
+    if constexpr (kWaves == 8) {
+      if (a.D != 128 || a.T > 256) return hipErrorInvalidValue;
+      attn_split_mfma_kernel<128, 8, 256, 8, true><<<blocks, kThreads, 0, s>>>(a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (kWaves == 4 || a.T <= 256) {
-    if (a.D == 128) attn_split_mfma_kernel<128, 8, 256, kWaves><<<blocks, kThreads, 0, s>>>(a);
-    else attn_split_mfma_kernel<64, 8, 256, kWaves><<<blocks, kThreads, 0, s>>>(a);
+    if (a.D == 128) attn_split_mfma_kernel<128, 8, 256, kWaves, false><<<blocks, kThreads, 0, s>>>(a);
+    else attn_split_mfma_kernel<64, 8, 256, kWaves, false><<<blocks, kThreads, 0, s>>>(a);
   } else if constexpr (kWaves == 8) {
-    if (a.D == 128) attn_split_mfma_kernel<128, 7, TS_MAX_DRAFT, kWaves><<<blocks, kThreads, 0, s>>>(a);
-    else attn_split_mfma_kernel<64, 7, TS_MAX_DRAFT, kWaves><<<blocks, kThreads, 0, s>>>(a);
+    if (a.D == 128) attn_split_mfma_kernel<128, 7, TS_MAX_DRAFT, kWaves, false><<<blocks, kThreads, 0, s>>>(a);
+    else attn_split_mfma_kernel<64, 7, TS_MAX_DRAFT, kWaves, false><<<blocks, kThreads, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -138,6 +138,12 @@ struct AttnArgs {
   int64_t L;
   float scale_log2;         // scale * log2(e)
   AttnPlan plan;
+  // chunk importance over the same cache, computed by the split kernel's
+  // all-padding wave (q_imp == nullptr: off; see attn_mfma_importance_fusable)
+  const void* q_imp;        // [imp_R][Hq][D] the recent queries
+  float* scores;            // [Hkv][L / 64]
+  int imp_R;
+  float imp_scale;
 };
 
 AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype, int num_splits);
@@ -157,6 +163,9 @@ ts_status tree_verify_into(const char* fn, const void* q, const void* k_cache, c
 
 // Work decomposition of the matrix-core kernel (defined next to it).
 int mfma_rows_per_group(int rows_per_head);   // 256, or 128 when a KV head has at most 128 rows
+// Whether the matrix-core split kernel can score 64-token chunks of the cache
+// for R recent queries of group size G in its last row group's all-padding wave.
+bool attn_mfma_importance_fusable(const AttnPlan& p, int T, int G, int D, int64_t L, int R);
 int mfma_groups_per_cu();
 int mfma_tile_keys();
 

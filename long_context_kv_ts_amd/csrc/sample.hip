@@ -425,8 +425,7 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
     mloc = fmaxf(mloc, sb[k].m);
   }
   const float Z = block_max(mloc, s.red);
-  // the row's cut: min-p, raised to the row's top-p cut z* when top-p is on
-  const float thr = fmaxf(Z + a.cut, a.topp_cut != nullptr && !greedy ? a.topp_cut[r] : -INFINITY);
+  const float thr = Z + a.cut;
   if (tid == 0) {
     p.bsel = a.nb;
     p.win = INT32_MAX;
@@ -453,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
       const int q = q0 + k;
       float c = 0.0f;
       if (q < a.nb && sb[k].m > -INFINITY && sb[k].m >= thr) {
-        if (thr == -INFINITY) {
+        if (a.cut == -INFINITY) {
           c = sb[k].s * exp2f((sb[k].m - Z) * a.s2);
         } else if (sb[k].n <= kSampleList) {
           const SampleCand* list = a.cand + ((int64_t)r * a.nb + q) * kSampleList;
@@ -535,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
     return;
   }
   const SampleSub chosen = a.sub[r * a.nb + b];
-  const bool listed = chosen.n <= kSampleList && (greedy || thr > -INFINITY);
+  const bool listed = chosen.n <= kSampleList && (greedy || a.cut > -INFINITY);
   if (listed) {
     // the sub-slice's kept tokens, in token order (greedy: its maxima)
     const SampleCand* list = a.cand + ((int64_t)r * a.nb + b) * kSampleList;
@@ -606,18 +605,35 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-p cut of each row: a weighted radix select over the row's penalised
-// logits z, from the largest down, for the value z* at which the weight at or
-// above it first reaches top_p * W (W: the row's total weight, from the
-// scan's summaries). Pass 0 bins z by its weight, 1/8 of a power of two per
-// bin below the row maximum (bin 255 takes everything further down), which
-// spreads a row's tokens over the bins; passes 1..4 take the 8-bit digits of
-// the order-preserving key of z inside the chosen bin, high to low. Each pass
-// sums per bin the weight, the count and the smallest and largest key, and
-// the search ends as soon as the chosen bin holds a single key. The weights
-// are summed in fp32 in an unspecified order, so a z* whose cumulative weight
-// is within rounding of top_p * W may come out one value either side.
+// Top-p rows (top_p < 1, tau > 0): one 1024-thread workgroup per row finds the
+// row's cut and draws the token itself, in place of the pick kernel.
+//   * Z and the total weight W = sum 2^((z - Z) s2) come from the scan's
+//     sub-slice summaries.
+//   * The cut z* -- the value at which the weight at or above it first
+//     reaches top_p * W -- by a weighted select from the largest z down.
+//     Pass 0 sums the weight of every token into one of 32 bins, a power of
+//     two of weight each below the maximum (the last bin takes everything
+//     further down); every thread keeps its own row of bins in LDS, so the
+//     pass needs no atomics. The bin where the cumulative weight crosses
+//     top_p * W is usually narrow: a second pass copies its tokens' keys
+//     into LDS (ballot-compacted, one slot reservation per wave), and key
+//     passes over them cut their key range into 2048 sub-ranges until one
+//     key is left. A bin with more tokens than LDS holds (nearly flat
+//     logits) runs the key passes over the row instead.
+//   * The row's cut is the larger of z* and the min-p cut. A last pass sums
+//     the kept weight of every 1024-logit sub-slice (four waves a sub-slice,
+//     added in a fixed order); a scan finds the sub-slice the draw
+//     u * (kept weight) falls in, and a scan over its 1024 tokens the token.
+// Every pass over the row loads a thread's next eight 4-token groups before
+// using any (a group past the row reloads the last one and is masked). The
+// weights are summed in fp32 in an unspecified order, so a cut within
+// rounding of a cumulative boundary may come out one value either side.
 constexpr int kToppThreads = 1024;
+constexpr int kToppWaves = kToppThreads / kWave;
+constexpr int kToppBins = 2048;           // key-pass bins
+constexpr int kToppCoarse = 32;           // pass-0 bins: powers of two of weight
+constexpr int kToppCand = 16384;          // keys of the crossing bin held in LDS
+constexpr int kToppBatch = 8;             // 4-token groups a thread loads at once
 
 __device__ __forceinline__ uint32_t topp_key(float f) {
   if (f == 0.0f) f = 0.0f;               // -0 and +0: one key
@@ -628,150 +644,374 @@ __device__ __forceinline__ float topp_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-template <typename Tin>
+// Exclusive prefix over the workgroup's threads in index order; total = the sum.
+__device__ float topp_scan(float v, float* red, float& total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  float incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const float y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  float excl = __shfl_up(incl, 1, kWave);
+  if (lane == 0) excl = 0.0f;
+  if (lane == kWave - 1) red[wave] = incl;
+  __syncthreads();
+  float off = 0.0f, tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kToppWaves; ++w) {
+    off += w < wave ? red[w] : 0.0f;
+    tot += red[w];
+  }
+  __syncthreads();
+  total = tot;
+  return off + excl;
+}
+
+// Raw loads of a 4-token group from token t0 (a multiple of 4, t0 < V): one
+// 16-byte (fp32) or 8-byte (bf16) load when the rows allow it, else four
+// element loads clamped into the row; plus the group's window-bit word.
+template <typename Tin, bool kVec>
+struct ToppRaw {
+  uint4 u;                               // fp32 bits, or bf16 pairs in x and y
+  uint32_t w;
+};
+template <typename Tin, bool kVec>
+__device__ __forceinline__ void topp_fetch(int V, const Tin* row, const uint32_t* bits, int t0, ToppRaw<Tin, kVec>& r) {
+  if constexpr (kVec) {
+    if constexpr (sizeof(Tin) == 4) {
+      r.u = *reinterpret_cast<const uint4*>(row + t0);
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(row + t0);
+      r.u = make_uint4(v.x, v.y, 0u, 0u);
+    }
+  } else {
+    uint32_t e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const Tin x = row[min(t0 + i, V - 1)];
+      if constexpr (sizeof(Tin) == 4) e[i] = __builtin_bit_cast(uint32_t, x);
+      else e[i] = (uint32_t)x << 16;
+    }
+    r.u = make_uint4(e[0], e[1], e[2], e[3]);
+  }
+  r.w = bits[t0 >> 5] >> (t0 & 31);
+}
+// The group's penalised logits (selects from the two factors held in
+// registers, no branch); -inf past V or when `valid` is false.
+template <typename Tin, bool kVec>
+__device__ __forceinline__ void topp_values(int V, float theta, float inv_theta, int t0, bool valid,
+                                            const ToppRaw<Tin, kVec>& r, float (&z)[4]) {
+  float x[4];
+  if constexpr (kVec && sizeof(Tin) == 2) {
+    x[0] = __uint_as_float(r.u.x << 16); x[1] = __uint_as_float(r.u.x & 0xffff0000u);
+    x[2] = __uint_as_float(r.u.y << 16); x[3] = __uint_as_float(r.u.y & 0xffff0000u);
+  } else {
+    x[0] = __uint_as_float(r.u.x); x[1] = __uint_as_float(r.u.y);
+    x[2] = __uint_as_float(r.u.z); x[3] = __uint_as_float(r.u.w);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = x[i] * (x[i] > 0.0f ? inv_theta : theta);
+    const float v = ((r.w >> i) & 1u) ? p : x[i];
+    z[i] = valid && t0 + i < V ? v : -INFINITY;
+  }
+}
+
+// f(k, z) for every 4-token group g = threadIdx.x + k * kToppThreads of the row
+// (z = -inf past the row); the loop is uniform across the workgroup. Every
+// load of a batch is issued before the first is used (a group past the row
+// reloads the last one).
+template <typename Tin, bool kVec, typename F>
+__device__ __forceinline__ void topp_visit(int V, float theta, float inv_theta, const Tin* row, const uint32_t* bits,
+                                           int ngroups, F&& f) {
+  for (int k0 = 0; k0 * kToppThreads < ngroups; k0 += kToppBatch) {
+    ToppRaw<Tin, kVec> raw[kToppBatch];
+#pragma unroll
+    for (int j = 0; j < kToppBatch; ++j) {
+      const int g = threadIdx.x + (k0 + j) * kToppThreads;
+      topp_fetch<Tin, kVec>(V, row, bits, 4 * min(g, ngroups - 1), raw[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kToppBatch; ++j) {
+      const int g = threadIdx.x + (k0 + j) * kToppThreads;
+      float z[4];
+      topp_values<Tin, kVec>(V, theta, inv_theta, 4 * g, g < ngroups, raw[j], z);
+      f(k0 + j, z);
+    }
+  }
+}
+
+struct ToppLds {
+  union {
+    float ph[kToppThreads][kToppCoarse + 1];   // pass 0: each thread's bins (padded row)
+    struct {
+      float hw[kToppBins];                   // key passes: weight per bin
+      uint32_t kmn[kToppBins], kmx[kToppBins];   // smallest and largest key per bin (none: ~0 and 0)
+      uint32_t cand[kToppCand];              // keys of the crossing bin
+    } k;
+    float part[4 * kSampleMaxSubs];        // kept weight of each sub-slice, per wave quarter
+  } u;
+  float coarse[kToppWaves][kToppCoarse];
+  float red[kToppWaves];
+  float above;                           // weight above the current range
+  uint32_t lo, hi;                       // the current key range
+  int sel, last, ncand;
+  int win, lastk;
+};
+
+// Among the 2048 key bins (in order of decreasing z), the first whose
+// cumulative weight (after s.above) reaches `target`, else the last non-empty
+// one; sets s.above to the weight before it and returns it.
+__device__ int topp_select(ToppLds& s, float target) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s.sel = INT32_MAX;
+    s.last = -1;
+  }
+  const float above0 = s.above;
+  const int b0 = 2 * tid, b1 = 2 * tid + 1;
+  const float c0 = s.u.k.hw[b0], c1 = s.u.k.hw[b1];
+  // a bin holds tokens iff its smallest key is set (every token of the
+  // crossing coarse bin has a positive weight: they are within a factor 2)
+  const bool n0 = s.u.k.kmn[b0] != 0xFFFFFFFFu, n1 = s.u.k.kmn[b1] != 0xFFFFFFFFu;
+  float tot;
+  const float run = above0 + topp_scan(c0 + c1, s.red, tot);   // its barriers order the init above
+  float my_above = 0.0f;
+  int my_sel = INT32_MAX;
+  if (n0 && run + c0 >= target) {
+    my_sel = b0;
+    my_above = run;
+  } else if (n1 && run + c0 + c1 >= target) {
+    my_sel = b1;
+    my_above = run + c0;
+  }
+  if (my_sel != INT32_MAX) atomicMin(&s.sel, my_sel);
+  const int my_last = n1 ? b1 : n0 ? b0 : -1;
+  if (my_last >= 0) atomicMax(&s.last, my_last);
+  __syncthreads();
+  const bool hit = s.sel != INT32_MAX;
+  const int sel = hit ? s.sel : s.last;
+  __syncthreads();
+  if (sel >= 0 && (sel == b0 || sel == b1)) s.above = hit ? my_above : (sel == b0 ? run : run + c0);
+  __syncthreads();
+  return sel;
+}
+
+__device__ __forceinline__ void topp_clear_keys(ToppLds& s) {
+  for (int b = threadIdx.x; b < kToppBins; b += kToppThreads) {
+    s.u.k.hw[b] = 0.0f;
+    s.u.k.kmn[b] = 0xFFFFFFFFu;
+    s.u.k.kmx[b] = 0u;
+  }
+}
+
+// One key pass: the tokens with keys in [lo, hi] into bins of (key - lo) >> shift,
+// in order of decreasing key.
+__device__ __forceinline__ void topp_key_bin(ToppLds& s, uint32_t key, float Z, float s2, uint32_t lo, uint32_t hi,
+                                             int shift) {
+  if (key < lo || key > hi) return;
+  const int b = kToppBins - 1 - (int)((key - lo) >> shift);
+  atomicAdd(&s.u.k.hw[b], __builtin_amdgcn_exp2f((topp_value(key) - Z) * s2));
+  atomicMin(&s.u.k.kmn[b], key);
+  atomicMax(&s.u.k.kmx[b], key);
+}
+
+template <typename Tin, bool kVec>
 __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a) {
-  constexpr int kW = kToppThreads / kWave;
-  __shared__ float hw[256];
-  __shared__ uint32_t hc[256], kmin[256], kmax[256];
-  __shared__ float red[kW];
-  __shared__ float s_m;                  // weight above the chosen bin
-  __shared__ int s_sel;                  // chosen bin of the pass
-  __shared__ uint32_t s_key;             // z*'s key once known
-  __shared__ int s_done;
+  __shared__ ToppLds s;
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const Tin* row = static_cast<const Tin*>(a.logits) + (int64_t)r * a.V;
   const uint32_t* bits = a.wbits + (int64_t)r * a.nb * (kSampleSub / 32);
+  const int V = a.V;
+  const int ngroups = (V + 3) / 4;
+  const float th = a.theta, ith = a.inv_theta;
 
   // the row maximum and total weight from the sub-slice summaries (nb <= 1024)
   SampleSub sb = SampleSub{-INFINITY, 0.0f, 0, 0.0f};
   if (tid < a.nb) sb = a.sub[(int64_t)r * a.nb + tid];
-  float v = wave_max(sb.m);
-  if (lane == 0) red[wave] = v;
+  const float vmax = wave_max(sb.m);
+  if (lane == 0) s.red[wave] = vmax;
   __syncthreads();
-  float Z = red[0];
+  float Z = s.red[0];
 #pragma unroll
-  for (int w = 1; w < kW; ++w) Z = fmaxf(Z, red[w]);
+  for (int w = 1; w < kToppWaves; ++w) Z = fmaxf(Z, s.red[w]);
   __syncthreads();
-  v = wave_sum(sb.m > -INFINITY ? sb.wall * exp2f((sb.m - Z) * a.s2) : 0.0f);
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float W = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kW; ++w) W += red[w];
+  float W;
+  topp_scan(sb.m > -INFINITY ? sb.wall * __builtin_amdgcn_exp2f((sb.m - Z) * a.s2) : 0.0f, s.red, W);
+  if (!(Z > -INFINITY)) {                // no finite logit in the row (outside the contract)
+    if (tid == 0) a.tok[r] = -1;
+    return;
+  }
   const float target = a.top_p * W;
+  auto coarse_of = [&](float z) -> int {   // pass-0 bin: whole powers of two below the maximum
+    const float d = (Z - z) * a.s2;
+    return d < (float)(kToppCoarse - 1) ? (int)d : kToppCoarse - 1;
+  };
+
+  // ---- pass 0: each thread's own coarse bins ---------------------------------
+#pragma unroll
+  for (int b = 0; b < kToppCoarse; ++b) s.u.ph[tid][b] = 0.0f;
   if (tid == 0) {
-    s_m = 0.0f;
-    s_done = 0;
-    s_key = 0u;
+    s.above = 0.0f;
+    s.ncand = 0;
+  }
+  topp_visit<Tin, kVec>(V, th, ith, row, bits, ngroups, [&](int, const float (&z)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (z[i] > -INFINITY) s.u.ph[tid][coarse_of(z[i])] += __builtin_amdgcn_exp2f((z[i] - Z) * a.s2);
+  });
+  __syncthreads();
+  // bin totals: lane b < 32 of each wave adds its wave's 64 rows, then wave 0 the 16 waves
+  if (lane < kToppCoarse) {
+    float t = 0.0f;
+    for (int j = 0; j < kWave; ++j) t += s.u.ph[wave * kWave + j][lane];
+    s.coarse[wave][lane] = t;
+  }
+  __syncthreads();
+  int bc = -1;                           // the crossing coarse bin
+  if (wave == 0) {
+    float c = 0.0f;
+    if (lane < kToppCoarse)
+      for (int w = 0; w < kToppWaves; ++w) c += s.coarse[w][lane];
+    float incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float y = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += y;
+    }
+    const float excl = incl - c;
+    const uint64_t hit = __ballot(lane < kToppCoarse && c > 0.0f && incl >= target);
+    const uint64_t any = __ballot(lane < kToppCoarse && c > 0.0f);
+    const int src = hit ? __ffsll((unsigned long long)hit) - 1 : (any ? 63 - __clzll((unsigned long long)any) : -1);
+    if (lane == 0) s.sel = src;
+    if (src >= 0 && lane == src) s.above = excl;
+  }
+  __syncthreads();
+  bc = s.sel;
+  __syncthreads();
+  if (bc < 0) {                          // nothing finite (cannot happen past the check above)
+    if (tid == 0) a.tok[r] = -1;
+    return;
   }
 
-  // pass 0: weight bins; passes 1..4: key digits inside bin b0
-  int b0 = -1;
-  uint32_t prefix = 0u, mask = 0u;
-  for (int pass = 0; pass < 5; ++pass) {
-    const int shift = 32 - 8 * pass;       // pass >= 1: digit (key >> shift) & 255
-    if (tid < 256) {
-      hw[tid] = 0.0f;
-      hc[tid] = 0u;
-      kmin[tid] = 0xFFFFFFFFu;
-      kmax[tid] = 0u;
-    }
-    __syncthreads();
-    for (int t = tid; t < a.V; t += kToppThreads) {
-      float z = Elem<Tin>::load(row + t);
-      if ((bits[t >> 5] >> (t & 31)) & 1u) z = penalty(z, a);
-      if (!(z > -INFINITY)) continue;
-      const int bin = (int)fminf((Z - z) * a.s2 * 8.0f, 255.0f);
-      const uint32_t key = topp_key(z);
-      int d;
-      if (pass == 0) d = bin;
-      else if (bin == b0 && (key & mask) == prefix) d = (int)((key >> shift) & 255u);
-      else continue;
-      atomicAdd(&hw[d], exp2f((z - Z) * a.s2));
-      atomicAdd(&hc[d], 1u);
-      atomicMin(&kmin[d], key);
-      atomicMax(&kmax[d], key);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // bins in order of decreasing z: pass 0 ascending, key digits descending
-      float c[4], tot = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = pass == 0 ? 4 * lane + j : 255 - 4 * lane - j;
-        c[j] = hw[d];
-        tot += c[j];
-      }
-      float incl = tot;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const float y = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += y;
-      }
-      float run = s_m + incl - tot;      // weight above this lane's first bin
-      int sel = -1;
-      float above = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = pass == 0 ? 4 * lane + j : 255 - 4 * lane - j;
-        if (sel < 0 && hc[d] > 0u && run + c[j] >= target) {
-          sel = d;
-          above = run;
-        }
-        run += c[j];
-      }
-      // the first bin (in z order) that reaches the target; rounding can leave
-      // the target past the total, and then the last non-empty bin is taken
-      const uint64_t hit = __ballot(sel >= 0);
-      int last = -1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = pass == 0 ? 4 * lane + j : 255 - 4 * lane - j;
-        if (hc[d] > 0u) last = d;
-      }
-      const uint64_t any = __ballot(last >= 0);
-      if (hit != 0ull) {
-        const int src = __ffsll((unsigned long long)hit) - 1;
-        if (lane == src) {
-          s_sel = sel;
-          s_m = above;
-        }
-      } else if (any != 0ull) {
-        const int src = 63 - __clzll((unsigned long long)any);
-        if (lane == src) {
-          // everything up to this bin lies above it
-          float up = s_m + incl - tot;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int d = pass == 0 ? 4 * lane + j : 255 - 4 * lane - j;
-            if (d == last) break;
-            up += c[j];
-          }
-          s_sel = last;
-          s_m = up;
-        }
-      } else if (lane == 0) {
-        s_sel = -1;                      // no finite token (outside the contract)
-      }
-    }
-    __syncthreads();
-    const int sel = s_sel;
-    if (sel < 0) {
-      if (tid == 0) a.topp_cut[r] = -INFINITY;
-      return;
-    }
-    if (kmin[sel] == kmax[sel] || pass == 4) {
-      if (tid == 0) a.topp_cut[r] = topp_value(kmax[sel]);
-      return;
-    }
-    if (pass == 0) {
-      b0 = sel;
-    } else {
-      prefix |= (uint32_t)sel << shift;
-      mask |= 255u << shift;
-    }
-    __syncthreads();                       // every thread has read this pass's bins
+  // ---- the crossing bin's keys into LDS, ballot-compacted --------------------
+  if (tid == 0) {
+    s.lo = 0xFFFFFFFFu;
+    s.hi = 0u;
   }
+  __syncthreads();
+  uint32_t kmin_own = 0xFFFFFFFFu, kmax_own = 0u;
+  topp_visit<Tin, kVec>(V, th, ith, row, bits, ngroups, [&](int, const float (&z)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool in = z[i] > -INFINITY && coarse_of(z[i]) == bc;
+      const uint64_t m = __ballot(in);
+      if (m == 0ull) continue;
+      int base = 0;
+      if (lane == __ffsll((unsigned long long)m) - 1) base = atomicAdd(&s.ncand, __popcll(m));
+      base = __shfl(base, __ffsll((unsigned long long)m) - 1, kWave);
+      const int slot = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t key = topp_key(z[i]);
+      if (in) {
+        if (slot < kToppCand) s.u.k.cand[slot] = key;
+        kmin_own = min(kmin_own, key);
+        kmax_own = max(kmax_own, key);
+      }
+    }
+  });
+  // the crossing bin's key range: the key passes start from it
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin_own = min(kmin_own, (uint32_t)__shfl_xor((int)kmin_own, o, kWave));
+    kmax_own = max(kmax_own, (uint32_t)__shfl_xor((int)kmax_own, o, kWave));
+  }
+  if (lane == 0) {
+    atomicMin(&s.lo, kmin_own);
+    atomicMax(&s.hi, kmax_own);
+  }
+  __syncthreads();
+  const int n = s.ncand;
+  uint32_t lo = s.lo, hi = s.hi;
+  bool done = lo == hi;
+  for (int pass = 0; pass < 3 && !done; ++pass) {
+    const int nbits = 32 - __clz((int)(hi - lo));
+    const int shift = nbits > 11 ? nbits - 11 : 0;
+    topp_clear_keys(s);
+    __syncthreads();
+    if (n <= kToppCand) {
+      for (int i = tid; i < n; i += kToppThreads) topp_key_bin(s, s.u.k.cand[i], Z, a.s2, lo, hi, shift);
+    } else {
+      // a crowded bin (nearly flat logits): the key passes read the row
+      topp_visit<Tin, kVec>(V, th, ith, row, bits, ngroups, [&](int, const float (&z)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (z[i] > -INFINITY && coarse_of(z[i]) == bc) topp_key_bin(s, topp_key(z[i]), Z, a.s2, lo, hi, shift);
+      });
+    }
+    __syncthreads();
+    const int d = topp_select(s, target);
+    lo = s.u.k.kmn[d];
+    hi = s.u.k.kmx[d];
+    done = lo == hi;
+    __syncthreads();
+  }
+  const float zstar = topp_value(lo);
+  const float thr = fmaxf(Z + a.cut, zstar);
+  if (tid == 0) a.topp_cut[r] = zstar;
+
+  // ---- the kept weight of every sub-slice at the row's cut ------------------
+  for (int q = tid; q < 4 * a.nb; q += kToppThreads) s.u.part[q] = 0.0f;
+  if (tid == 0) {
+    s.win = INT32_MAX;
+    s.lastk = -1;
+    s.sel = INT32_MAX;
+    s.last = -1;
+  }
+  __syncthreads();
+  topp_visit<Tin, kVec>(V, th, ith, row, bits, ngroups, [&](int k, const float (&z)[4]) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (z[i] > -INFINITY && z[i] >= thr) acc += __builtin_amdgcn_exp2f((z[i] - Z) * a.s2);
+    acc = wave_sum(acc);
+    // a wave's 64 groups are 256 tokens of sub-slice 4k + wave/4
+    const int q = 4 * k + (wave >> 2);
+    if (lane == 0 && q < a.nb) s.u.part[4 * q + (wave & 3)] = acc;
+  });
+  __syncthreads();
+  float c = 0.0f;
+  if (tid < a.nb) c = (s.u.part[4 * tid] + s.u.part[4 * tid + 1]) + (s.u.part[4 * tid + 2] + s.u.part[4 * tid + 3]);
+  float total;
+  const float excl = topp_scan(c, s.red, total);
+  const float target2 = a.u[r] * total;
+  if (c > 0.0f && excl + c > target2) atomicMin(&s.sel, tid);
+  if (c > 0.0f) atomicMax(&s.last, tid);
+  __syncthreads();
+  const bool fallback = s.sel == INT32_MAX;   // u * total at or past the end: the last kept token
+  const int q = fallback ? s.last : s.sel;
+  if (q < 0) {                           // nothing kept (cannot happen: the maximum always is)
+    if (tid == 0) a.tok[r] = -1;
+    return;
+  }
+  if (tid == q) s.above = excl;
+  __syncthreads();
+  const float base = s.above;
+  const int t = q * kSampleSub + tid;
+  float w = 0.0f;
+  if (t < V) {
+    const float x = Elem<Tin>::load(row + t);
+    const float z = ((bits[t >> 5] >> (t & 31)) & 1u) ? x * (x > 0.0f ? ith : th) : x;
+    if (z > -INFINITY && z >= thr) w = __builtin_amdgcn_exp2f((z - Z) * a.s2);
+  }
+  float tot_q;
+  const float run = base + topp_scan(w, s.red, tot_q) + w;
+  if (w > 0.0f) {
+    if (!fallback && run > target2) atomicMin(&s.win, t);
+    atomicMax(&s.lastk, t);
+  }
+  __syncthreads();
+  if (tid == 0) a.tok[r] = s.win != INT32_MAX ? s.win : s.lastk;
 }
 
 template <typename Tin>
@@ -788,11 +1028,17 @@ hipError_t launch_t(const SampleArgs& a, hipStream_t st) {
     sample_scan_kernel<Tin, kNT, kPW, true><<<grid, kNT, 0, st>>>(a);
   else
     sample_scan_kernel<Tin, kNT, kPW, false><<<grid, kNT, 0, st>>>(a);
-  if (a.topp_cut != nullptr) sample_topp_kernel<Tin><<<a.R, kToppThreads, 0, st>>>(a);
-  if (vec)
+  if (a.topp_cut != nullptr) {
+    // top-p rows: the cut and the draw in one kernel
+    if (vec)
+      sample_topp_kernel<Tin, true><<<a.R, kToppThreads, 0, st>>>(a);
+    else
+      sample_topp_kernel<Tin, false><<<a.R, kToppThreads, 0, st>>>(a);
+  } else if (vec) {
     sample_pick_kernel<Tin, true><<<a.R, kThreads, 0, st>>>(a);
-  else
+  } else {
     sample_pick_kernel<Tin, false><<<a.R, kThreads, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

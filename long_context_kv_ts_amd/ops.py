@@ -9,6 +9,7 @@ Entry points, named as the C functions without the ``ts_`` prefix:
 
 * verify and partial-cache step: ``tree_verify_attn`` (and ``tree_verify_attn_noalloc``,
   its variant without a workspace), ``tree_verify_attn_partials``,
+  ``tree_verify_attn_partials_and_importance``,
   ``attn_merge``, ``kv_importance_score``, ``attn_merge_and_importance``, ``kv_topk_select``, ``kv_gather``,
   ``partial_draft_attn``;
 * decode step around them: ``build_draft_tree`` (with ``draft_tree_nodes``),
@@ -49,6 +50,10 @@ SIGNATURES = {
                                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
                                               _c_int, _c_int, _c_int, _c_i64, _c_f, _c_int, _c_int,
                                               _c_void_p]),
+    "ts_tree_verify_attn_partials_and_importance": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_void_p,
+                                                             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                                             _c_int, _c_int, _c_int, _c_i64, _c_f, _c_int, _c_int,
+                                                             _c_void_p, _c_int, _c_int, _c_f, _c_void_p, _c_void_p]),
     "ts_attn_merge": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                _c_int, _c_void_p]),
     "ts_kv_importance_score": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int,
@@ -351,6 +356,53 @@ def tree_verify_attn_partials(q, k_cache, v_cache, k_draft, v_draft, parent, *, 
         D, L, float(1.0 / math.sqrt(D) if scale is None else scale), _dtype_code(q), num_splits,
         _stream(dev)))
     return o_part, l_part
+
+
+def tree_verify_attn_partials_and_importance(q, k_cache, v_cache, k_draft, v_draft, parent, q_recent, chunk: int,
+                                             *, scale=None, imp_scale=None, o_part=None, l_part=None, scores=None,
+                                             num_splits: int = 0):
+    """ts_tree_verify_attn_partials_and_importance: the verify split partials
+    and the chunk importance of the same cache for the recent queries q_recent
+    [R][Hq][D], in one launch where the shapes allow -> (o_part, l_part, scores)."""
+    _need(q, "q", 3)
+    dev = q.device
+    T, Hq, D = q.shape
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_draft", k_draft), ("v_draft", v_draft),
+                 ("q_recent", q_recent)):
+        _need(t, n, 3, q.dtype, dev)
+    _need(parent, "parent", 1, torch.int32, dev)
+    Hkv, L, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if tuple(k_draft.shape) != (Hkv, T, D) or tuple(v_draft.shape) != (Hkv, T, D):
+        raise ValueError(f"drafts must be [{Hkv}][{T}][{D}]")
+    if parent.shape[0] != T:
+        raise ValueError("parent must have T entries")
+    R = q_recent.shape[0]
+    if tuple(q_recent.shape[1:]) != (Hq, D):
+        raise ValueError(f"q_recent must be [R][{Hq}][{D}]")
+    for n, t in (("q", q), ("k_draft", k_draft), ("v_draft", v_draft), ("parent", parent), ("q_recent", q_recent)):
+        _contig(t, n)
+    stride = _cache_stride(k_cache, "k_cache")
+    if _cache_stride(v_cache, "v_cache") != stride:
+        raise ValueError("k_cache and v_cache must share the row stride")
+    S = globals()["num_splits"](T, Hq, Hkv, D, L, q.dtype, num_splits)
+    _out(o_part, "o_part", (S, T, Hq, D), torch.float32, dev)
+    _out(l_part, "l_part", (S, T, Hq), torch.float32, dev)
+    _out(scores, "scores", (Hkv, L // max(int(chunk), 1)), torch.float32, dev)
+    if o_part is None:
+        o_part = torch.empty((S, T, Hq, D), dtype=torch.float32, device=dev)
+    if l_part is None:
+        l_part = torch.empty((S, T, Hq), dtype=torch.float32, device=dev)
+    if scores is None:
+        scores = torch.empty((Hkv, L // chunk), dtype=torch.float32, device=dev)
+    sc = float(1.0 / math.sqrt(D) if scale is None else scale)
+    isc = float(1.0 / math.sqrt(D) if imp_scale is None else imp_scale)
+    _check(lib().ts_tree_verify_attn_partials_and_importance(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stride, k_draft.data_ptr(), v_draft.data_ptr(),
+        parent.data_ptr(), o_part.data_ptr(), l_part.data_ptr(), T, Hq, Hkv, D, L, sc, _dtype_code(q), num_splits,
+        q_recent.data_ptr(), R, int(chunk), isc, scores.data_ptr(), _stream(dev)))
+    return o_part, l_part, scores
 
 
 def attn_merge(o_part, l_part, *, out_dtype=torch.bfloat16, out=None, lse=None):

@@ -331,3 +331,25 @@ def test_noalloc_rejects_before_any_hip_call():
     assert call(T=0) == ops.TS_ERR_UNSUPPORTED and "ts_tree_verify_attn_noalloc" in _err()
     assert call(Hq=30) == ops.TS_ERR_INVALID_ARG
     assert call(D=96) == ops.TS_ERR_UNSUPPORTED
+
+
+def test_partials_and_importance_rejects():
+    """ts_tree_verify_attn_partials_and_importance runs the checks of both calls before any launch."""
+    lib = ops.lib()
+
+    def call(**kw):
+        a = dict(q=P, kc=P, vc=P, stride=4096, kd=P, vd=P, parent=P, o=P, l=P, T=120, Hq=32, Hkv=8, D=128, L=4096,
+                 scale=0.088, dt=B, ns=0, qr=P, R=4, chunk=64, isc=0.088, scores=P)
+        a.update(kw)
+        return lib.ts_tree_verify_attn_partials_and_importance(
+            a["q"], a["kc"], a["vc"], a["stride"], a["kd"], a["vd"], a["parent"], a["o"], a["l"], a["T"], a["Hq"],
+            a["Hkv"], a["D"], a["L"], a["scale"], a["dt"], a["ns"], a["qr"], a["R"], a["chunk"], a["isc"],
+            a["scores"], None)
+    name = "ts_tree_verify_attn_partials_and_importance"
+    assert call(qr=None) == ops.TS_ERR_INVALID_ARG and name in _err()
+    assert call(L=4000) == ops.TS_ERR_UNSUPPORTED and name in _err()          # not whole chunks
+    assert call(R=17) == ops.TS_ERR_UNSUPPORTED                              # R*G > 64
+    assert call(T=0) == ops.TS_ERR_UNSUPPORTED
+    assert call(parent=None) == ops.TS_ERR_INVALID_ARG
+    assert call(scale=-1.0) == ops.TS_ERR_INVALID_ARG and "> 0" in _err()
+    assert call(o=MIS) == ops.TS_ERR_INVALID_ARG
