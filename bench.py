@@ -252,8 +252,7 @@ def main():
         ops.tree_verify_attn_partials_and_importance(q, kc, vcache, kd, vd, parent, pq, pc.chunk, scale=vc.scale,
                                                      imp_scale=pc.scale, o_part=o_part, l_part=l_part,
                                                      scores=scores)
-        ops.attn_merge(o_part, l_part, out=out, lse=lse)
-        ops.kv_topk_select(scores, pc.k, chunk_idx=idx, chunk_score=idx_s)
+        ops.attn_merge_and_topk(o_part, l_part, scores, pc.k, out=out, lse=lse, chunk_idx=idx, chunk_score=idx_s)
         ops.kv_gather(pk, pv, idx, pc.chunk, k_part=kp, v_part=vp)
         ops.partial_draft_attn(pq, kp, vp, pkn, pvn, scale=pc.scale, out=dout, lse=dlse,
                                workspace=dws)
@@ -318,18 +317,16 @@ def main():
                                                      imp_scale=pc.scale, o_part=o_part, l_part=l_part,
                                                      scores=scores)
         ev[1].record()
-        ops.attn_merge(o_part, l_part, out=out, lse=lse)
+        ops.attn_merge_and_topk(o_part, l_part, scores, pc.k, out=out, lse=lse, chunk_idx=idx, chunk_score=idx_s)
         ev[2].record()
-        ops.kv_topk_select(scores, pc.k, chunk_idx=idx, chunk_score=idx_s)
-        ev[3].record()
         ops.kv_gather(pk, pv, idx, pc.chunk, k_part=kp, v_part=vp)
-        ev[4].record()
+        ev[3].record()
         ops.partial_draft_attn(pq, kp, vp, pkn, pvn, scale=pc.scale, out=dout, lse=dlse, workspace=dws)
-        ev[5].record()
+        ev[4].record()
 
-    fused_names = ["verify_split_importance", "verify_merge", "topk", "gather", "draft_attn"]
+    fused_names = ["verify_split_importance", "merge_topk", "gather", "draft_attn"]
     avg, med = per_kernel(step, 7, names)
-    favg, fmed = per_kernel(step_fused_ev, 6, fused_names)
+    favg, fmed = per_kernel(step_fused_ev, 5, fused_names)
 
     # ---- roofline of the dominant kernel of the timed step ---------------------
     # the split kernel that also scores the chunks: the verify's QK^T and PV

@@ -223,6 +223,20 @@ ts_status ts_attn_merge_and_importance(const float* o_part, const float* l_part,
 ts_status ts_kv_topk_select(const float* scores, int Hkv, int n_chunks, int k,
                             int32_t* chunk_idx, float* chunk_score, hipStream_t stream);
 
+/* ts_attn_merge followed by ts_kv_topk_select, in one launch where the merge
+ * allows: in a decode step both depend only on the verify pass (its split
+ * partials and, through ts_tree_verify_attn_partials_and_importance, the chunk
+ * scores), and run as one grid whose first Hkv workgroups select chunks. The
+ * arguments are those of ts_attn_merge (Dv its D), then those of
+ * ts_kv_topk_select, with the same meaning, checks and errors; the two
+ * operations' buffers must not overlap. Results are bit-identical to the two
+ * calls. One launch when Dv = 128 and n_parts <= 16; otherwise the two
+ * launches, merge first. */
+ts_status ts_attn_merge_and_topk(const float* o_part, const float* l_part, int n_parts, int rows, int Dv,
+                                 void* out, float* lse, ts_dtype out_dtype, const float* scores, int Hkv,
+                                 int n_chunks, int k, int32_t* chunk_idx, float* chunk_score,
+                                 hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Gather of the chosen chunks into a partial cache (summary page, "Approach").
  *   k_part[g][i*chunk + u][:] = k_cache[g][chunk_idx[g][i]*chunk + u][:]

@@ -369,15 +369,38 @@ ts_status ts_attn_merge_and_importance(const float* o_part, const float* l_part,
                                     stream), fn);
 }
 
-ts_status ts_kv_topk_select(const float* scores, int Hkv, int n_chunks, int k,
-                            int32_t* chunk_idx, float* chunk_score, hipStream_t stream) {
-  const char* fn = "ts_kv_topk_select";
+static ts_status check_topk(const char* fn, const float* scores, int Hkv, int n_chunks, int k,
+                            const int32_t* chunk_idx, const float* chunk_score) {
   if (!scores || !chunk_idx) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (((uintptr_t)scores & 3u) || ((uintptr_t)chunk_idx & 3u) || ((uintptr_t)chunk_score & 3u))
     return fail(TS_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   if (Hkv < 1 || Hkv > 65535) return fail(TS_ERR_INVALID_ARG, "%s: Hkv=%d", fn, Hkv);
   if (n_chunks < 1 || n_chunks > 65536) return fail(TS_ERR_UNSUPPORTED, "%s: n_chunks=%d outside [1, 65536]", fn, n_chunks);
   if (k < 1 || k > n_chunks) return fail(TS_ERR_INVALID_ARG, "%s: k=%d outside [1, n_chunks=%d]", fn, k, n_chunks);
+  return TS_OK;
+}
+
+ts_status ts_kv_topk_select(const float* scores, int Hkv, int n_chunks, int k,
+                            int32_t* chunk_idx, float* chunk_score, hipStream_t stream) {
+  const char* fn = "ts_kv_topk_select";
+  const ts_status st = check_topk(fn, scores, Hkv, n_chunks, k, chunk_idx, chunk_score);
+  if (st != TS_OK) return st;
+  return from_hip(launch_topk(scores, Hkv, n_chunks, k, chunk_idx, chunk_score, stream), fn);
+}
+
+ts_status ts_attn_merge_and_topk(const float* o_part, const float* l_part, int n_parts, int rows, int Dv, void* out,
+                                 float* lse, ts_dtype out_dtype, const float* scores, int Hkv, int n_chunks, int k,
+                                 int32_t* chunk_idx, float* chunk_score, hipStream_t stream) {
+  const char* fn = "ts_attn_merge_and_topk";
+  ts_status st = check_merge(fn, o_part, l_part, n_parts, rows, Dv, out, out_dtype);
+  if (st != TS_OK) return st;
+  st = check_topk(fn, scores, Hkv, n_chunks, k, chunk_idx, chunk_score);
+  if (st != TS_OK) return st;
+  if (merge_topk_fusable(n_parts, Dv))
+    return from_hip(launch_merge_topk(o_part, l_part, n_parts, rows, out, lse, out_dtype, scores, Hkv, n_chunks, k,
+                                      chunk_idx, chunk_score, stream), fn);
+  st = from_hip(launch_attn_merge(o_part, l_part, n_parts, rows, Dv, out, lse, out_dtype, stream), fn);
+  if (st != TS_OK) return st;
   return from_hip(launch_topk(scores, Hkv, n_chunks, k, chunk_idx, chunk_score, stream), fn);
 }
 

@@ -187,6 +187,12 @@ hipError_t launch_merge_importance(const float* o_part, const float* l_part, int
                                    float scale, hipStream_t s);
 hipError_t launch_topk(const float* scores, int Hkv, int n, int k, int32_t* idx, float* val,
                        hipStream_t s);
+// The merge and the top-k selection in one grid (fused.hip), for the merges
+// merge_topk_fusable accepts.
+bool merge_topk_fusable(int n_parts, int Dm);
+hipError_t launch_merge_topk(const float* o_part, const float* l_part, int n_parts, int rows, void* out, float* lse,
+                             ts_dtype out_dtype, const float* scores, int Hkv, int n, int k, int32_t* idx, float* val,
+                             hipStream_t s);
 hipError_t launch_gather(const void* kc, const void* vc, int64_t stride, const int32_t* idx,
                          int Hkv, int k, int chunk, int D, int64_t L, void* kp, void* vp,
                          int elem_bytes, hipStream_t s);

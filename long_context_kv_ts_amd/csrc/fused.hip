@@ -12,6 +12,7 @@
 // query rows. Anything else takes the two separate launches.
 #include "importance_block.h"
 #include "merge_block.h"
+#include "topk_block.h"
 
 namespace ts {
 namespace {
@@ -59,7 +60,51 @@ hipError_t launch_rows(const MergePart& m, const ImportancePart& p, int imp_bx, 
   return hipGetLastError();
 }
 
+// The verify merge and the top-k chunk selection in one launch: the first Hkv
+// workgroups select one KV head's chunks each (256 threads, eight scores a
+// thread per round), the rest merge rows, each with its own kernel's code.
+struct TopkPart {
+  const float* scores;
+  int n, k;
+  int32_t* idx;
+  float* val;
+};
+
+template <typename Tout, bool kResident>
+__global__ __launch_bounds__(256) void merge_topk_kernel(MergePart m, TopkPart t, int Hkv) {
+  const int b = blockIdx.x;
+  if (b < Hkv) {
+    topk_block<256, 8, kResident>(t.scores, t.n, t.k, t.idx, t.val, b);
+    return;
+  }
+  merge_block<Tout, 128, 1>(m.o_part, m.l_part, m.S, m.rows, static_cast<Tout*>(m.out), m.lse, b - Hkv);
+}
+
 }  // namespace
+
+bool merge_topk_fusable(int n_parts, int Dm) {
+  const int need = ((n_parts + kMergeBatch - 1) / kMergeBatch) * (128 / 4);   // lanes a merged row needs
+  return Dm == 128 && need <= kWave;
+}
+
+hipError_t launch_merge_topk(const float* o_part, const float* l_part, int n_parts, int rows, void* out, float* lse,
+                             ts_dtype out_dtype, const float* scores, int Hkv, int n, int k, int32_t* idx, float* val,
+                             hipStream_t s) {
+  const int merge_blocks = (rows + MergeShape<1>::rows - 1) / MergeShape<1>::rows;
+  const int64_t blocks = (int64_t)merge_blocks + Hkv;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  const MergePart m{o_part, l_part, n_parts, rows, out, lse};
+  const TopkPart t{scores, n, k, idx, val};
+  const bool resident = n <= 256 * 8;
+  if (out_dtype == TS_BF16) {
+    if (resident) merge_topk_kernel<bf16_t, true><<<(int)blocks, 256, 0, s>>>(m, t, Hkv);
+    else merge_topk_kernel<bf16_t, false><<<(int)blocks, 256, 0, s>>>(m, t, Hkv);
+  } else {
+    if (resident) merge_topk_kernel<float, true><<<(int)blocks, 256, 0, s>>>(m, t, Hkv);
+    else merge_topk_kernel<float, false><<<(int)blocks, 256, 0, s>>>(m, t, Hkv);
+  }
+  return hipGetLastError();
+}
 
 bool merge_importance_fusable(int n_parts, int Dm, int Di, int R, int Hq, int Hkv, int chunk, ts_dtype dtype) {
   const int need = ((n_parts + kMergeBatch - 1) / kMergeBatch) * (128 / 4);   // lanes a merged row needs

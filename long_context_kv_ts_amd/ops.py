@@ -61,6 +61,8 @@ SIGNATURES = {
     "ts_attn_merge_and_importance": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                               _c_int, _c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int,
                                               _c_int, _c_int, _c_i64, _c_int, _c_f, _c_int, _c_void_p]),
+    "ts_attn_merge_and_topk": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_int,
+                                        _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "ts_kv_topk_select": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "ts_kv_gather": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int, _c_int, _c_int,
                               _c_i64, _c_void_p, _c_void_p, _c_int, _c_void_p]),
@@ -479,6 +481,41 @@ def attn_merge_and_importance(o_part, l_part, q_recent, k_cache, chunk: int, *, 
         q_recent.data_ptr(), k_cache.data_ptr(), stride, scores.data_ptr(), R, Hq, Hkv, D, L, chunk,
         float(1.0 / math.sqrt(D) if scale is None else scale), _dtype_code(q_recent), _stream(dev)))
     return out, lse, scores
+
+
+def attn_merge_and_topk(o_part, l_part, scores, k: int, *, out_dtype=torch.bfloat16, out=None, lse=None,
+                        chunk_idx=None, chunk_score=None, want_scores=True):
+    """ts_attn_merge_and_topk: attn_merge(o_part, l_part) and kv_topk_select(scores, k)
+    in one launch where the merge allows -> (out, lse, chunk_idx, chunk_score),
+    bit-identical to the two calls."""
+    _parts(o_part, l_part)
+    dev = o_part.device
+    _contig(o_part, "o_part")
+    _contig(l_part, "l_part")
+    S, Dv = o_part.shape[0], o_part.shape[-1]
+    rows = o_part[0].numel() // Dv
+    if tuple(l_part.shape) != tuple(o_part.shape[:-1]):
+        raise ValueError("l_part does not match o_part")
+    _need(scores, "scores", 2, torch.float32, dev)
+    _contig(scores, "scores")
+    Hkv, n = scores.shape
+    _out(out, "out", o_part.shape[1:], out.dtype if out is not None else out_dtype, dev)
+    _out(lse, "lse", l_part.shape[1:], torch.float32, dev)
+    _out(chunk_idx, "chunk_idx", (Hkv, k), torch.int32, dev)
+    _out(chunk_score, "chunk_score", (Hkv, k), torch.float32, dev)
+    if out is None:
+        out = torch.empty(o_part.shape[1:], dtype=out_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(l_part.shape[1:], dtype=torch.float32, device=dev)
+    if chunk_idx is None:
+        chunk_idx = torch.empty((Hkv, k), dtype=torch.int32, device=dev)
+    if chunk_score is None and want_scores:
+        chunk_score = torch.empty((Hkv, k), dtype=torch.float32, device=dev)
+    _check(lib().ts_attn_merge_and_topk(o_part.data_ptr(), l_part.data_ptr(), S, rows, Dv, out.data_ptr(),
+                                        lse.data_ptr(), _dtype_code(out), scores.data_ptr(), Hkv, n, k,
+                                        chunk_idx.data_ptr(),
+                                        chunk_score.data_ptr() if chunk_score is not None else None, _stream(dev)))
+    return out, lse, chunk_idx, chunk_score
 
 
 def kv_topk_select(scores, k: int, *, chunk_idx=None, chunk_score=None, want_scores=True):

@@ -146,6 +146,31 @@ def test_merge_and_importance_rejects():
     assert call(dt=7) == ops.TS_ERR_INVALID_ARG
 
 
+def test_merge_and_topk_rejects():
+    """ts_attn_merge_and_topk runs the argument checks of ts_attn_merge and of
+    ts_kv_topk_select (nothing is launched on these calls)."""
+    lib = ops.lib()
+
+    def call(**kw):
+        a = dict(o=P, l=P, S=16, rows=3840, Dv=128, out=P, lse=P, odt=B, scores=P, Hkv=8, n=1600, k=64,
+                 idx=P, val=P)
+        a.update(kw)
+        return lib.ts_attn_merge_and_topk(a["o"], a["l"], a["S"], a["rows"], a["Dv"], a["out"], a["lse"],
+                                          a["odt"], a["scores"], a["Hkv"], a["n"], a["k"], a["idx"], a["val"],
+                                          None)
+    assert call(S=0) == ops.TS_ERR_INVALID_ARG
+    assert call(Dv=100) == ops.TS_ERR_UNSUPPORTED
+    assert call(o=MIS) == ops.TS_ERR_INVALID_ARG
+    assert "ts_attn_merge_and_topk" in _err()
+    assert call(scores=None) == ops.TS_ERR_INVALID_ARG
+    assert call(idx=P + 2) == ops.TS_ERR_INVALID_ARG
+    assert call(k=0) == ops.TS_ERR_INVALID_ARG
+    assert call(k=1601) == ops.TS_ERR_INVALID_ARG
+    assert call(n=65537, k=4) == ops.TS_ERR_UNSUPPORTED
+    assert call(Hkv=0) == ops.TS_ERR_INVALID_ARG
+    assert call(odt=7) == ops.TS_ERR_INVALID_ARG
+
+
 def test_draft_attn_rejects():
     lib = ops.lib()
     st = lib.ts_partial_draft_attn(P, P, P, P, P, P, P, 0, 32, 8, 128, 4096, 0.1, B, 0, P, 1 << 30, None)

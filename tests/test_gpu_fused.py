@@ -1,14 +1,19 @@
-"""GPU: ts_attn_merge_and_importance against ts_attn_merge and
-ts_kv_importance_score called separately (each pinned to the oracle in
-tests/test_gpu_verify.py and tests/test_gpu_partial.py). The one-launch path
-runs the same per-workgroup code as the two kernels, so every output must be
-bit-identical; shapes outside it take the two launches and must be too."""
+"""GPU: the calls that share one launch between two operations --
+ts_attn_merge_and_importance, ts_attn_merge_and_topk and
+ts_tree_verify_attn_partials_and_importance -- against the separate calls
+(each pinned to the oracle in tests/test_gpu_verify.py and
+tests/test_gpu_partial.py) and against the oracle at full size. The one-launch
+paths run the same per-workgroup code as the separate kernels, so every output
+must be bit-identical (the verify-with-importance kernel: to a stated
+tolerance on the scores); shapes outside them take the separate launches and
+must be too."""
 import numpy as np
 import pytest
 import torch
 
 from gpu_util import DEV, say
 from long_context_kv_ts_amd import ops
+from oracle import partial_kv
 
 pytestmark = pytest.mark.gpu
 
@@ -191,3 +196,59 @@ def test_partials_and_importance_split_counts(ns):
     say(f"[verify+importance] splits={ns}")
     fused, sep = _partials_and_scores(c, q_rec, 64, 0.0884, num_splits=ns)
     _check_same(fused, sep, f"splits={ns}")
+
+
+# ---------------------------------------------------------------------------
+# ts_attn_merge_and_topk: the merge and the chunk top-k in one grid.
+
+def _scores(seed, Hkv, n, ties=False):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    s = torch.randn((Hkv, n), generator=g)
+    if ties:
+        s = torch.round(s * 4) / 4                        # many equal scores
+        s[:, : n // 4] = 0.5
+    return s.to(DEV)
+
+
+@pytest.mark.parametrize("case", [
+    # S, T, Hq_v, Dv, Hkv, n_chunks, k, out dtype
+    dict(S=16, T=120, Hq_v=32, Dv=128, Hkv=8, n=1600, k=64, odt=torch.bfloat16),
+    dict(S=16, T=120, Hq_v=32, Dv=128, Hkv=8, n=2048, k=2048, odt=torch.bfloat16),
+    dict(S=9, T=5, Hq_v=64, Dv=128, Hkv=4, n=3000, k=100, odt=torch.float32),
+    dict(S=1, T=3, Hq_v=8, Dv=128, Hkv=2, n=1, k=1, odt=torch.bfloat16),
+    dict(S=16, T=120, Hq_v=32, Dv=128, Hkv=8, n=20000, k=313, odt=torch.bfloat16),
+    dict(S=20, T=120, Hq_v=32, Dv=128, Hkv=8, n=1600, k=64, odt=torch.bfloat16),
+    dict(S=16, T=120, Hq_v=32, Dv=64, Hkv=8, n=1600, k=64, odt=torch.bfloat16),
+], ids=["bench-shape", "k-equals-n", "streamed-f32", "tiny", "n20000", "S20-two-launches", "D64-two-launches"])
+@pytest.mark.parametrize("ties", [False, True], ids=["distinct", "ties"])
+def test_merge_topk_bit_identical_to_separate_calls(case, ties):
+    c = dict(case)
+    say(f"fused merge+topk {case} ties={ties}")
+    o_part, l_part, _, _ = _inputs(7, c["S"], c["T"], c["Hq_v"], c["Dv"], 1, 1, 1, 64, 64, empty_splits=True)
+    scores = _scores(8, c["Hkv"], c["n"], ties)
+    out_a, lse_a = ops.attn_merge(o_part, l_part, out_dtype=c["odt"])
+    idx_a, val_a = ops.kv_topk_select(scores, c["k"])
+    out_b, lse_b, idx_b, val_b = ops.attn_merge_and_topk(o_part, l_part, scores, c["k"], out_dtype=c["odt"])
+    torch.cuda.synchronize()
+    iv = torch.int16 if c["odt"] == torch.bfloat16 else torch.int32
+    assert torch.equal(out_a.view(iv), out_b.view(iv))
+    assert torch.equal(lse_a.view(torch.int32), lse_b.view(torch.int32))
+    assert torch.equal(idx_a, idx_b)
+    assert torch.equal(val_a.view(torch.int32), val_b.view(torch.int32))
+    # the top-k half against the oracle on its own too
+    ref_idx, _ = partial_kv.topk_ref(scores.cpu().numpy().astype(np.float64), c["k"])
+    np.testing.assert_array_equal(idx_b.cpu().numpy(), ref_idx)
+
+
+def test_merge_topk_without_scores_and_reused_outputs():
+    o_part, l_part, _, _ = _inputs(9, 16, 120, 32, 128, 1, 1, 1, 64, 64)
+    scores = _scores(10, 8, 1600)
+    out, lse, idx, val = ops.attn_merge_and_topk(o_part, l_part, scores, 64)
+    ref = (out.clone(), lse.clone(), idx.clone(), val.clone())
+    out.fill_(7.0)
+    lse.fill_(7.0)
+    idx.fill_(-1)
+    ops.attn_merge_and_topk(o_part, l_part, scores, 64, out=out, lse=lse, chunk_idx=idx, want_scores=False)
+    torch.cuda.synchronize()
+    for a, b in zip(ref[:3], (out, lse, idx)):
+        assert torch.equal(a, b)
