@@ -28,13 +28,20 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave, in DPP lane moves:
+// shifts by 1, 2, 4 and 8 within each row of 16 lanes, then each row's total
+// broadcast into the rows above it.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_add(uint32_t x) {
+  return x + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, kRowMask, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int) {
+  x = dpp_add<0x111, 0xF>(x);    // row_shr:1
+  x = dpp_add<0x112, 0xF>(x);    // row_shr:2
+  x = dpp_add<0x114, 0xF>(x);    // row_shr:4
+  x = dpp_add<0x118, 0xF>(x);    // row_shr:8
+  x = dpp_add<0x142, 0xA>(x);    // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xC>(x);    // row_bcast:31 into rows 2 and 3
   return x;
 }
 
@@ -59,11 +66,13 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ scores, int
   const int n_rounds = (n + kRound - 1) / kRound;
 
   uint32_t rk[kPer];
+  float rv[kPer];
   if constexpr (kResident) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int i = j * kThreads + tid;
-      rk[j] = i < n ? order_key(s[i]) : 0u;
+      rv[j] = i < n ? s[i] : 0.f;
+      rk[j] = order_key(rv[j]);
     }
   }
   auto key_at = [&](int r, int j) -> uint32_t {
@@ -161,7 +170,10 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ scores, int
       const uint32_t pos = gb + min(eb, need);
       if (keep && pos < (uint32_t)k) {
         idx_out[(int64_t)g * k + pos] = i;
-        if (val_out) val_out[(int64_t)g * k + pos] = s[i];
+        if (val_out) {
+          if constexpr (kResident) val_out[(int64_t)g * k + pos] = rv[j];
+          else val_out[(int64_t)g * k + pos] = s[i];
+        }
       }
     }
     if (r + 1 < n_rounds) __syncthreads();      // cnt_* is rewritten next round
