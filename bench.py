@@ -245,17 +245,18 @@ def main():
                                workspace=dws)
         rec(6)
 
-    # The timed step: the verify split kernel also scores the cache's chunks on
-    # the same reads of K; the per-kernel pass below runs the separate launches
-    # so that each has its own time.
+    # The timed step, four kernels: the verify split kernel also scores the
+    # cache's chunks on the same reads of K; the merge shares its grid with the
+    # top-k; the draft pass gathers the chosen chunks as it reads them, then
+    # merges its splits. The per-kernel pass below also runs the separate
+    # launches so that each has its own time.
     def step_fused():
         ops.tree_verify_attn_partials_and_importance(q, kc, vcache, kd, vd, parent, pq, pc.chunk, scale=vc.scale,
                                                      imp_scale=pc.scale, o_part=o_part, l_part=l_part,
                                                      scores=scores)
         ops.attn_merge_and_topk(o_part, l_part, scores, pc.k, out=out, lse=lse, chunk_idx=idx, chunk_score=idx_s)
-        ops.kv_gather(pk, pv, idx, pc.chunk, k_part=kp, v_part=vp)
-        ops.partial_draft_attn(pq, kp, vp, pkn, pvn, scale=pc.scale, out=dout, lse=dlse,
-                               workspace=dws)
+        ops.kv_gather_and_draft_attn(pk, pv, idx, pc.chunk, pq, pkn, pvn, scale=pc.scale, k_part=kp, v_part=vp,
+                                     out=dout, lse=dlse, workspace=dws)
 
     tm = Timer(dev)
     run_step = step if args.unfused else step_fused
@@ -319,14 +320,13 @@ def main():
         ev[1].record()
         ops.attn_merge_and_topk(o_part, l_part, scores, pc.k, out=out, lse=lse, chunk_idx=idx, chunk_score=idx_s)
         ev[2].record()
-        ops.kv_gather(pk, pv, idx, pc.chunk, k_part=kp, v_part=vp)
+        ops.kv_gather_and_draft_attn(pk, pv, idx, pc.chunk, pq, pkn, pvn, scale=pc.scale, k_part=kp, v_part=vp,
+                                     out=dout, lse=dlse, workspace=dws)
         ev[3].record()
-        ops.partial_draft_attn(pq, kp, vp, pkn, pvn, scale=pc.scale, out=dout, lse=dlse, workspace=dws)
-        ev[4].record()
 
-    fused_names = ["verify_split_importance", "merge_topk", "gather", "draft_attn"]
+    fused_names = ["verify_split_importance", "merge_topk", "gather_draft_attn"]
     avg, med = per_kernel(step, 7, names)
-    favg, fmed = per_kernel(step_fused_ev, 5, fused_names)
+    favg, fmed = per_kernel(step_fused_ev, 4, fused_names)
 
     # ---- roofline of the dominant kernel of the timed step ---------------------
     # the split kernel that also scores the chunks: the verify's QK^T and PV

@@ -249,6 +249,27 @@ ts_status ts_kv_gather(const void* k_cache, const void* v_cache, int64_t cache_s
                        const int32_t* chunk_idx, int Hkv, int k, int chunk, int D, int64_t L,
                        void* k_part, void* v_part, ts_dtype dtype, hipStream_t stream);
 
+/* ts_kv_gather followed by ts_partial_draft_attn over the gathered cache, in
+ * one pass where possible: the draft step refreshes the partial cache from the
+ * chosen chunks (summary page, "Approach": dynamic partial-cache update) and
+ * attends over it (tool listing, "How it works"); with bf16 and 64-token
+ * chunks the attention reads each chosen chunk from the full cache once and
+ * writes the copy on the way, instead of a separate copy pass and a second
+ * read. Arguments are those of ts_kv_gather (k_cache .. v_part, with
+ * Hkv, D and dtype given once below) and of ts_partial_draft_attn with
+ * P = k*chunk; the same checks and errors, all made before anything runs.
+ * k_part and v_part hold the gathered chunks and out / lse the draft
+ * attention afterwards, bit-identical to the two calls with the same
+ * num_splits (an index outside [0, L/chunk) is a zero chunk in both). The
+ * partial cache must not overlap the full cache. Otherwise (fp32, other chunk
+ * sizes, more than 16 query rows per KV head) the two calls are made. */
+ts_status ts_kv_gather_and_draft_attn(const void* k_cache, const void* v_cache, int64_t cache_stride,
+                                      const int32_t* chunk_idx, int k, int chunk, int64_t L,
+                                      void* k_part, void* v_part, const void* q, const void* k_new,
+                                      const void* v_new, void* out, float* lse, int Tq, int Hq, int Hkv,
+                                      int D, float scale, ts_dtype dtype, int num_splits, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Draft attention over the partial cache (tool listing, "How it works":
  * drafting runs the target model itself over the reduced cache, proposing

@@ -127,12 +127,21 @@ struct ImpFusion {
   float scale;
 };
 
+// The gather of the chosen chunks done by the pass over the partial cache
+// (small path): the source cache and where the copies go.
+struct GatherFusion {
+  const int32_t* chunk_idx;
+  int64_t n_chunks;          // chunks in the source cache
+  void* k_part;
+  void* v_part;
+};
+
 static ts_status attn_common(const char* fn, const void* q, const void* kc, const void* vc,
                              int64_t cache_stride, const void* kd, const void* vd,
                              const int32_t* parent, bool need_parent, float* o_part, float* l_part,
                              int T, int Hq, int Hkv, int D, int64_t L, float scale,
                              ts_dtype dtype, int num_splits, hipStream_t stream,
-                             const ImpFusion* imp = nullptr) {
+                             const ImpFusion* imp = nullptr, const GatherFusion* gf = nullptr) {
   ts_status st = check_attn_shape(fn, T, Hq, Hkv, D, L, dtype, num_splits);
   if (st != TS_OK) return st;
   if (!q || !kd || !vd || !o_part || !l_part) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
@@ -142,7 +151,8 @@ static ts_status attn_common(const char* fn, const void* q, const void* kc, cons
       (L > 0 && (!aligned16(kc) || !aligned16(vc))))
     return fail(TS_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
   if (((uintptr_t)l_part & 3u) != 0) return fail(TS_ERR_INVALID_ARG, "%s: l_part misaligned", fn);
-  if (cache_stride < L) return fail(TS_ERR_INVALID_ARG, "%s: cache_stride=%lld < L=%lld", fn, (long long)cache_stride, (long long)L);
+  if (!gf && cache_stride < L)
+    return fail(TS_ERR_INVALID_ARG, "%s: cache_stride=%lld < L=%lld", fn, (long long)cache_stride, (long long)L);
   // The kernels take each row's maximum of the raw products and scale it
   // afterwards, which is the maximum of the scaled logits only for scale > 0.
   if (!std::isfinite(scale) || !(scale > 0.f))
@@ -165,6 +175,12 @@ static ts_status attn_common(const char* fn, const void* q, const void* kc, cons
     a.scores = imp->scores;
     a.imp_R = imp->R;
     a.imp_scale = imp->scale;
+  }
+  if (gf != nullptr) {
+    a.gidx = gf->chunk_idx;
+    a.g_chunks = gf->n_chunks;
+    a.kp = gf->k_part;
+    a.vp = gf->v_part;
   }
   hipError_t e = a.plan.path == kPathMfma    ? launch_attn_split_mfma(a, stream)
                  : a.plan.path == kPathSmall ? launch_attn_split_small(a, stream)
@@ -252,7 +268,7 @@ static ts_status verify_like(const char* fn, const void* q, const void* kc, cons
                              const int32_t* parent, bool need_parent, void* out, float* lse,
                              int T, int Hq, int Hkv, int D, int64_t L, float scale,
                              ts_dtype dtype, int num_splits, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+                             size_t workspace_bytes, hipStream_t stream, const GatherFusion* gf = nullptr) {
   ts_status st = check_attn_shape(fn, T, Hq, Hkv, D, L, dtype, num_splits);
   if (st != TS_OK) return st;
   if (!out) return fail(TS_ERR_INVALID_ARG, "%s: out is null", fn);
@@ -270,7 +286,7 @@ static ts_status verify_like(const char* fn, const void* q, const void* kc, cons
   float* l_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                            align_up((size_t)p.n_splits * rows * D * sizeof(float)));
   st = attn_common(fn, q, kc, vc, cache_stride, kd, vd, parent, need_parent, o_part, l_part, T,
-                   Hq, Hkv, D, L, scale, dtype, num_splits, stream);
+                   Hq, Hkv, D, L, scale, dtype, num_splits, stream, nullptr, gf);
   if (st != TS_OK) return st;
   return from_hip(launch_attn_merge(o_part, l_part, p.n_splits, (int)rows, D, out, lse, dtype, stream), fn);
 }
@@ -404,10 +420,9 @@ ts_status ts_attn_merge_and_topk(const float* o_part, const float* l_part, int n
   return from_hip(launch_topk(scores, Hkv, n_chunks, k, chunk_idx, chunk_score, stream), fn);
 }
 
-ts_status ts_kv_gather(const void* k_cache, const void* v_cache, int64_t cache_stride,
-                       const int32_t* chunk_idx, int Hkv, int k, int chunk, int D, int64_t L,
-                       void* k_part, void* v_part, ts_dtype dtype, hipStream_t stream) {
-  const char* fn = "ts_kv_gather";
+static ts_status check_gather(const char* fn, const void* k_cache, const void* v_cache, int64_t cache_stride,
+                              const int32_t* chunk_idx, int Hkv, int k, int chunk, int D, int64_t L,
+                              const void* k_part, const void* v_part, ts_dtype dtype) {
   if (dtype != TS_F32 && dtype != TS_BF16) return fail(TS_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
   if (!k_cache || !v_cache || !chunk_idx || !k_part || !v_part)
     return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
@@ -420,8 +435,58 @@ ts_status ts_kv_gather(const void* k_cache, const void* v_cache, int64_t cache_s
   if (((int64_t)chunk * D * elem_size(dtype)) % 16) return fail(TS_ERR_UNSUPPORTED, "%s: chunk*D*elem not a multiple of 16 bytes", fn);
   if (((int64_t)cache_stride * D * elem_size(dtype)) % 16) return fail(TS_ERR_UNSUPPORTED, "%s: cache head stride not a multiple of 16 bytes", fn);
   if (L / chunk > 2147483647LL) return fail(TS_ERR_UNSUPPORTED, "%s: too many chunks", fn);
+  return TS_OK;
+}
+
+ts_status ts_kv_gather(const void* k_cache, const void* v_cache, int64_t cache_stride,
+                       const int32_t* chunk_idx, int Hkv, int k, int chunk, int D, int64_t L,
+                       void* k_part, void* v_part, ts_dtype dtype, hipStream_t stream) {
+  const char* fn = "ts_kv_gather";
+  const ts_status st = check_gather(fn, k_cache, v_cache, cache_stride, chunk_idx, Hkv, k, chunk, D, L, k_part,
+                                    v_part, dtype);
+  if (st != TS_OK) return st;
   return from_hip(launch_gather(k_cache, v_cache, cache_stride, chunk_idx, Hkv, k, chunk, D, L,
                                 k_part, v_part, elem_size(dtype), stream), fn);
+}
+
+ts_status ts_kv_gather_and_draft_attn(const void* k_cache, const void* v_cache, int64_t cache_stride,
+                                      const int32_t* chunk_idx, int k, int chunk, int64_t L, void* k_part,
+                                      void* v_part, const void* q, const void* k_new, const void* v_new,
+                                      void* out, float* lse, int Tq, int Hq, int Hkv, int D, float scale,
+                                      ts_dtype dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  const char* fn = "ts_kv_gather_and_draft_attn";
+  ts_status st = check_gather(fn, k_cache, v_cache, cache_stride, chunk_idx, Hkv, k, chunk, D, L, k_part, v_part,
+                              dtype);
+  if (st != TS_OK) return st;
+  if ((int64_t)k * chunk > (int64_t)INT32_MAX) return fail(TS_ERR_UNSUPPORTED, "%s: k*chunk too large", fn);
+  const int64_t P = (int64_t)k * chunk;
+  st = check_attn_shape(fn, Tq, Hq, Hkv, D, P, dtype, num_splits);
+  if (st != TS_OK) return st;
+  // every argument of the draft pass is checked before anything runs
+  if (!q || !k_new || !v_new || !out || !workspace) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) || ((uintptr_t)lse & 3u))
+    return fail(TS_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return fail(TS_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  const size_t need = ts_tree_verify_attn_workspace(Tq, Hq, Hkv, D, P, dtype, num_splits);
+  if (workspace_bytes < need)
+    return fail(TS_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(TS_ERR_INVALID_ARG, "%s: scale must be finite and > 0 (got %g)", fn, (double)scale);
+  const AttnPlan p = plan_attention(Tq, Hq, Hkv, D, P, dtype, num_splits);
+  if (((int64_t)p.n_splits * Hkv + 7) / 8 * 8 * p.n_rowgroups > INT32_MAX)
+    return fail(TS_ERR_UNSUPPORTED, "%s: %d splits x %d KV heads exceed one launch", fn, p.n_splits, Hkv);
+  if (dtype == TS_BF16 && chunk == kTile && p.path == kPathSmall) {
+    const GatherFusion gf{chunk_idx, L / chunk, k_part, v_part};
+    return verify_like(fn, q, k_cache, v_cache, cache_stride, k_new, v_new, nullptr, false, out, lse, Tq, Hq, Hkv,
+                       D, P, scale, dtype, num_splits, workspace, workspace_bytes, stream, &gf);
+  }
+  st = from_hip(launch_gather(k_cache, v_cache, cache_stride, chunk_idx, Hkv, k, chunk, D, L, k_part, v_part,
+                              elem_size(dtype), stream), fn);
+  if (st != TS_OK) return st;
+  return verify_like(fn, q, k_part, v_part, P, k_new, v_new, nullptr, false, out, lse, Tq, Hq, Hkv, D, P, scale,
+                     dtype, num_splits, workspace, workspace_bytes, stream);
 }
 
 // Node count of a tree shape, or -1 (with ts_last_error) if the shape is not supported.

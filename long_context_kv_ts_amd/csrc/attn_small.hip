@@ -18,6 +18,11 @@
 //     lane's 8 values of two blocks (k-slot 8*g + e is key 16*(e/4)+4*g+e%4).
 // Softmax in base 2 with lazy rescaling (probabilities <= 2^8), scale applied
 // in fp32 after the product, P rounded to bf16 for PV, row sums unrounded.
+//
+// With kGather the partial cache is gathered on the way: cache tile i of a KV
+// head is the chosen 64-token chunk of the full cache, read from there, and the
+// wave also writes it to the partial cache -- K from the operand registers, V
+// read back from its LDS slice -- so the chunk crosses HBM once on each side.
 #include "common.h"
 
 namespace ts {
@@ -26,6 +31,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 #define TS_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 constexpr int kThreads = 256;      // 4 independent waves
@@ -53,7 +59,7 @@ __device__ __forceinline__ void lds_dma16(const bf16_t* base, uint32_t voff, uin
                : "memory", "m0");
 }
 
-template <int D>
+template <int D, bool kGather>
 __global__ __launch_bounds__(kThreads) void attn_split_small_kernel(AttnArgs a) {
   using Ly = SLayout<D>;
   __shared__ __attribute__((aligned(1024))) bf16_t Vs[4][Ly::tileElems];
@@ -105,17 +111,35 @@ __global__ __launch_bounds__(kThreads) void attn_split_small_kernel(AttnArgs a) 
     const bool draft = vt >= pl.n_cache_tiles;
     const int key0 = draft ? (vt - pl.n_cache_tiles) * kTile : vt * kTile;
     const int nvalid = draft ? min(kTile, T - key0) : (int)min((int64_t)kTile, a.L - key0);
+    // source rows of the tile: with kGather a cache tile is the chosen chunk of
+    // the full cache (a whole tile: the partial cache is whole chunks)
+    int64_t src0 = (int64_t)g * a.cache_stride + key0;
+    bool zero_tile = false;                     // an out-of-range chunk index (wave-uniform)
+    if constexpr (kGather) {
+      if (!draft) {
+        const int ci = a.gidx[(int64_t)g * pl.n_cache_tiles + vt];
+        zero_tile = ci < 0 || (int64_t)ci >= a.g_chunks;
+        src0 = (int64_t)g * a.cache_stride + (zero_tile ? 0 : (int64_t)ci * kTile);
+      }
+    }
     const bf16_t* kb = draft ? static_cast<const bf16_t*>(a.kd) + ((int64_t)g * T + key0) * D
-                             : static_cast<const bf16_t*>(a.kc) + ((int64_t)g * a.cache_stride + key0) * D;
+                             : static_cast<const bf16_t*>(a.kc) + src0 * D;
     const bf16_t* vb = draft ? static_cast<const bf16_t*>(a.vd) + ((int64_t)g * T + key0) * D
-                             : static_cast<const bf16_t*>(a.vc) + ((int64_t)g * a.cache_stride + key0) * D;
+                             : static_cast<const bf16_t*>(a.vc) + src0 * D;
 
     // V tile -> this wave's LDS slice (rows past nvalid re-read row nvalid-1)
+    if (!zero_tile) {
 #pragma unroll
-    for (int n = 0; n < Ly::loads; ++n) {
-      const int r = n * Ly::rowsPerLoad + lane / Ly::CH;
-      const int cc = vs_chunk<D>(r, lane % Ly::CH);
-      lds_dma16(vb, (uint32_t)((min(r, nvalid - 1) * D + cc * 8) * 2), vlds + n * 1024);
+      for (int n = 0; n < Ly::loads; ++n) {
+        const int r = n * Ly::rowsPerLoad + lane / Ly::CH;
+        const int cc = vs_chunk<D>(r, lane % Ly::CH);
+        lds_dma16(vb, (uint32_t)((min(r, nvalid - 1) * D + cc * 8) * 2), vlds + n * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < Ly::loads; ++n)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(vlds + n * 1024 + lane * 16) =
+            u32x4_t{0u, 0u, 0u, 0u};
     }
     // K operands straight from HBM: block j, step ks -> key 16*j + l%16
     bf16x8_t kf[4][Ly::KS];
@@ -124,8 +148,21 @@ __global__ __launch_bounds__(kThreads) void attn_split_small_kernel(AttnArgs a) 
       const int key = min(16 * j + col, nvalid - 1);
 #pragma unroll
       for (int ks = 0; ks < Ly::KS; ++ks)
-        kf[j][ks] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(kb + (int64_t)key * D + ks * 32 + grp * 8));
+        kf[j][ks] = zero_tile ? __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u))
+                              : __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                                                                 kb + (int64_t)key * D + ks * 32 + grp * 8));
+    }
+    // the gathered K chunk -> the partial cache (every key of a cache tile is valid)
+    if constexpr (kGather) {
+      if (!draft) {
+        bf16_t* kp = static_cast<bf16_t*>(a.kp) + ((int64_t)g * a.L + key0) * D;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int ks = 0; ks < Ly::KS; ++ks)
+            *reinterpret_cast<uint4*>(kp + (int64_t)(16 * j + col) * D + ks * 32 + grp * 8) =
+                __builtin_bit_cast(uint4, kf[j][ks]);
+      }
     }
     f32x4_t S[4];
 #pragma unroll
@@ -179,6 +216,20 @@ __global__ __launch_bounds__(kThreads) void attn_split_small_kernel(AttnArgs a) 
 
     // the wave's own V loads have landed
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    // the gathered V chunk -> the partial cache: each lane stores the 16-byte
+    // pieces it brought into LDS, at the offsets it read them from
+    if constexpr (kGather) {
+      if (!draft) {
+        uint8_t* vp = static_cast<uint8_t*>(a.vp) + ((int64_t)g * a.L + key0) * D * 2;
+#pragma unroll
+        for (int n = 0; n < Ly::loads; ++n) {
+          const int r = n * Ly::rowsPerLoad + lane / Ly::CH;
+          const int cc = vs_chunk<D>(r, lane % Ly::CH);
+          const u32x4_t v = *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(vlds + n * 1024 + lane * 16);
+          *reinterpret_cast<u32x4_t*>(vp + (r * D + cc * 8) * 2) = v;
+        }
+      }
+    }
     // O^T += V^T P^T: for chunk h (keys 32h..32h+31) lane l needs dim 16*db + l%16
     // of keys 32h + 16*(e/4) + 4*(l/16) + e%4: two transposing reads of 4 keys
 #pragma unroll
@@ -224,8 +275,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_small_kernel(AttnArgs a) 
 hipError_t launch_attn_split_small(const AttnArgs& a, hipStream_t s) {
   if (a.T > kSmallMaxDrafts || a.plan.rows_per_head > 16) return hipErrorInvalidValue;   // the plan never sends these
   dim3 grid((a.plan.n_splits + 3) / 4, a.Hkv);
-  if (a.D == 128) attn_split_small_kernel<128><<<grid, kThreads, 0, s>>>(a);
-  else attn_split_small_kernel<64><<<grid, kThreads, 0, s>>>(a);
+  if (a.gidx != nullptr) {
+    // the gathered cache is whole 64-token chunks, one tile each
+    if (a.L % kTile != 0 || a.plan.n_cache_tiles * (int64_t)kTile != a.L) return hipErrorInvalidValue;
+    if (a.D == 128) attn_split_small_kernel<128, true><<<grid, kThreads, 0, s>>>(a);
+    else attn_split_small_kernel<64, true><<<grid, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  if (a.D == 128) attn_split_small_kernel<128, false><<<grid, kThreads, 0, s>>>(a);
+  else attn_split_small_kernel<64, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -144,6 +144,14 @@ struct AttnArgs {
   float* scores;            // [Hkv][L / 64]
   int imp_R;
   float imp_scale;
+  // gather fused into the pass over a partial cache (small path only; gidx ==
+  // nullptr: off): cache tile i of KV head g is chunk gidx[g][i] of the cache
+  // kc/vc (cache_stride, g_chunks chunks of kTile tokens), and is also copied
+  // to kp/vp [Hkv][L][D]; an index outside [0, g_chunks) is a zero tile
+  const int32_t* gidx;      // [Hkv][L / kTile]
+  int64_t g_chunks;
+  void* kp;
+  void* vp;
 };
 
 AttnPlan plan_attention(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype, int num_splits);

@@ -66,6 +66,10 @@ SIGNATURES = {
     "ts_kv_topk_select": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "ts_kv_gather": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int, _c_int, _c_int,
                               _c_i64, _c_void_p, _c_void_p, _c_int, _c_void_p]),
+    "ts_kv_gather_and_draft_attn": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int, _c_i64,
+                                             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                             _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_int,
+                                             _c_void_p, _c_size, _c_void_p]),
     "ts_draft_tree_nodes": (_c_int, [_c_void_p, _c_int]),
     "ts_build_draft_tree_workspace": (_c_size, [_c_int, _c_int]),
     "ts_build_draft_tree": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p,
@@ -560,6 +564,65 @@ def kv_gather(k_cache, v_cache, chunk_idx, chunk: int, *, k_part=None, v_part=No
                               Hkv, k, chunk, D, L, k_part.data_ptr(), v_part.data_ptr(),
                               _dtype_code(k_cache), _stream(dev)))
     return k_part, v_part
+
+
+def kv_gather_and_draft_attn(k_cache, v_cache, chunk_idx, chunk: int, q, k_new, v_new, *, scale=None,
+                             k_part=None, v_part=None, out=None, lse=None, want_lse=True, num_splits: int = 0,
+                             workspace=None):
+    """ts_kv_gather_and_draft_attn: kv_gather(k_cache, v_cache, chunk_idx, chunk)
+    then partial_draft_attn(q, k_part, v_part, k_new, v_new) in one pass where
+    possible -> (k_part, v_part, out, lse), bit-identical to the two calls."""
+    _need(k_cache, "k_cache", 3)
+    dev = k_cache.device
+    _need(v_cache, "v_cache", 3, k_cache.dtype, dev)
+    _need(chunk_idx, "chunk_idx", 2, torch.int32, dev)
+    _contig(chunk_idx, "chunk_idx")
+    Hkv, L, D = k_cache.shape
+    k = chunk_idx.shape[1]
+    if chunk_idx.shape[0] != Hkv:
+        raise ValueError(f"chunk_idx must be [{Hkv}][k]")
+    stride = _cache_stride(k_cache, "k_cache")
+    if _cache_stride(v_cache, "v_cache") != stride:
+        raise ValueError("k_cache and v_cache must share the row stride")
+    if tuple(v_cache.shape) != (Hkv, L, D):
+        raise ValueError("v_cache must have the shape of k_cache")
+    _need(q, "q", 3, k_cache.dtype, dev)
+    _contig(q, "q")
+    Tq, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q and the cache differ in head dim")
+    for n, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t, n, 3, q.dtype, dev)
+        _contig(t, n)
+        if tuple(t.shape) != (Hkv, Tq, D):
+            raise ValueError(f"{n} must be [{Hkv}][{Tq}][{D}]")
+    P = k * chunk
+    code = _dtype_code(q)
+    _out(k_part, "k_part", (Hkv, P, D), q.dtype, dev)
+    _out(v_part, "v_part", (Hkv, P, D), q.dtype, dev)
+    _out(out, "out", (Tq, Hq, D), q.dtype, dev)
+    _out(lse, "lse", (Tq, Hq), torch.float32, dev)
+    if k_part is None:
+        k_part = torch.empty((Hkv, P, D), dtype=q.dtype, device=dev)
+    if v_part is None:
+        v_part = torch.empty((Hkv, P, D), dtype=q.dtype, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=dev)
+    need = int(lib().ts_partial_draft_attn_workspace(Tq, Hq, Hkv, D, P, code, num_splits))
+    if need == 0:
+        raise TsError(TS_ERR_INVALID_ARG, lib().ts_last_error().decode())
+    _workspace(workspace, "workspace", need, dev)
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    _check(lib().ts_kv_gather_and_draft_attn(
+        k_cache.data_ptr(), v_cache.data_ptr(), stride, chunk_idx.data_ptr(), k, chunk, L, k_part.data_ptr(),
+        v_part.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, Tq, Hq, Hkv, D,
+        float(1.0 / math.sqrt(D) if scale is None else scale), code, num_splits, workspace.data_ptr(),
+        _nbytes(workspace), _stream(dev)))
+    return k_part, v_part, out, lse
 
 
 def draft_tree_nodes(shape) -> int:

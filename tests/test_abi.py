@@ -171,6 +171,35 @@ def test_merge_and_topk_rejects():
     assert call(odt=7) == ops.TS_ERR_INVALID_ARG
 
 
+def test_gather_and_draft_attn_rejects():
+    """ts_kv_gather_and_draft_attn checks the gather's and the draft pass's
+    arguments before anything runs."""
+    lib = ops.lib()
+
+    def call(**kw):
+        a = dict(kc=P, vc=P, stride=102400, idx=P, k=64, chunk=64, L=102400, kp=P, vp=P, q=P, kn=P, vn=P,
+                 out=P, lse=P, Tq=4, Hq=32, Hkv=8, D=128, scale=0.1, dt=B, ns=0, ws=P, wsb=1 << 30)
+        a.update(kw)
+        return lib.ts_kv_gather_and_draft_attn(a["kc"], a["vc"], a["stride"], a["idx"], a["k"], a["chunk"], a["L"],
+                                               a["kp"], a["vp"], a["q"], a["kn"], a["vn"], a["out"], a["lse"],
+                                               a["Tq"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["dt"], a["ns"],
+                                               a["ws"], a["wsb"], None)
+    assert call(kc=None) == ops.TS_ERR_INVALID_ARG
+    assert "ts_kv_gather_and_draft_attn" in _err()
+    assert call(L=102400 - 32) == ops.TS_ERR_UNSUPPORTED      # L not a multiple of chunk
+    assert call(stride=4096) == ops.TS_ERR_INVALID_ARG        # stride < L
+    assert call(q=None) == ops.TS_ERR_INVALID_ARG
+    assert call(q=MIS) == ops.TS_ERR_INVALID_ARG
+    assert call(ws=P + 64) == ops.TS_ERR_INVALID_ARG          # workspace not 256-byte aligned
+    assert call(wsb=16) == ops.TS_ERR_WORKSPACE
+    assert call(scale=-0.1) == ops.TS_ERR_INVALID_ARG
+    assert call(scale=0.0, chunk=32, L=102400) == ops.TS_ERR_INVALID_ARG   # the two-call path checks first too
+    assert call(wsb=16, chunk=32) == ops.TS_ERR_WORKSPACE
+    assert call(Tq=2000) == ops.TS_ERR_UNSUPPORTED
+    assert call(D=96) == ops.TS_ERR_UNSUPPORTED
+    assert call(dt=7) == ops.TS_ERR_INVALID_ARG
+
+
 def test_draft_attn_rejects():
     lib = ops.lib()
     st = lib.ts_partial_draft_attn(P, P, P, P, P, P, P, 0, 32, 8, 128, 4096, 0.1, B, 0, P, 1 << 30, None)

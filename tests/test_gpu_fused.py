@@ -252,3 +252,74 @@ def test_merge_topk_without_scores_and_reused_outputs():
     torch.cuda.synchronize()
     for a, b in zip(ref[:3], (out, lse, idx)):
         assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# ts_kv_gather_and_draft_attn: the gather done by the draft pass.
+
+def _gather_draft_inputs(seed, Hkv, L, D, Tq, Hq, k, chunk, dtype=torch.bfloat16, bad_idx=False):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    kc = torch.randn((Hkv, L, D), generator=g).to(dtype).to(DEV)
+    vc = torch.randn((Hkv, L, D), generator=g).to(dtype).to(DEV)
+    idx = torch.stack([torch.randperm(L // chunk, generator=g)[:k].sort().values for _ in range(Hkv)])
+    if bad_idx:
+        idx[0, 1] = -1                    # out of range: a zero chunk in both paths
+        idx[-1, -1] = L // chunk
+    q = torch.randn((Tq, Hq, D), generator=g).to(dtype).to(DEV)
+    kn = torch.randn((Hkv, Tq, D), generator=g).to(dtype).to(DEV)
+    vn = torch.randn((Hkv, Tq, D), generator=g).to(dtype).to(DEV)
+    return kc, vc, idx.to(torch.int32).to(DEV), q, kn, vn
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("case", [
+    # Hkv, L, D, Tq, Hq, k, chunk, splits, dtype
+    dict(Hkv=8, L=102400, D=128, Tq=4, Hq=32, k=64, chunk=64, ns=0, dt=torch.bfloat16),
+    dict(Hkv=8, L=8192, D=128, Tq=4, Hq=32, k=64, chunk=64, ns=7, dt=torch.bfloat16),
+    dict(Hkv=4, L=16384, D=128, Tq=1, Hq=28, k=40, chunk=64, ns=0, dt=torch.bfloat16),
+    dict(Hkv=8, L=8192, D=64, Tq=2, Hq=32, k=33, chunk=64, ns=0, dt=torch.bfloat16),
+    dict(Hkv=8, L=8192, D=128, Tq=4, Hq=32, k=64, chunk=32, ns=0, dt=torch.bfloat16),
+    dict(Hkv=8, L=8192, D=128, Tq=4, Hq=32, k=16, chunk=64, ns=0, dt=torch.float32),
+    dict(Hkv=2, L=4096, D=128, Tq=16, Hq=16, k=8, chunk=64, ns=0, dt=torch.bfloat16),
+], ids=["bench-shape", "splits7", "G7-Tq1", "D64", "chunk32-two-calls", "f32-two-calls", "mfma-path-two-calls"])
+def test_gather_draft_bit_identical_to_separate_calls(case):
+    c = dict(case)
+    say(f"gather+draft {case}")
+    kc, vc, idx, q, kn, vn = _gather_draft_inputs(11, c["Hkv"], c["L"], c["D"], c["Tq"], c["Hq"], c["k"],
+                                                  c["chunk"], c["dt"], bad_idx=True)
+    kp_a, vp_a = ops.kv_gather(kc, vc, idx, c["chunk"])
+    out_a, lse_a = ops.partial_draft_attn(q, kp_a, vp_a, kn, vn, scale=0.088, num_splits=c["ns"])
+    kp_b, vp_b, out_b, lse_b = ops.kv_gather_and_draft_attn(kc, vc, idx, c["chunk"], q, kn, vn, scale=0.088,
+                                                            num_splits=c["ns"])
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(kp_a), _bits(kp_b))
+    assert torch.equal(_bits(vp_a), _bits(vp_b))
+    assert torch.equal(_bits(out_a), _bits(out_b))
+    assert torch.equal(lse_a.view(torch.int32), lse_b.view(torch.int32))
+    assert torch.isfinite(out_b.float()).all()
+
+
+def test_gather_draft_full_size_against_the_oracle():
+    """The launch the decode step times, at its real size: 64 chunks of 64
+    tokens per KV head chosen from a 102,400-token LLaMA3.1-8B cache, gathered
+    and attended by 4 draft tokens, against the oracle's gather (bit-exact)
+    and draft attention (element by element)."""
+    from long_context_kv_ts_amd import inputs
+    from gpu_util import check_attn, to_dev
+    import oracle
+    p = inputs.make_partial(L=102400, seed=3)
+    rng = np.random.default_rng(5)
+    gidx = np.stack([np.sort(rng.choice(p.L // p.chunk, p.k, replace=False)) for _ in range(p.Hkv)]).astype(np.int32)
+    say("gather+draft full size vs oracle")
+    kp, vp, out, lse = ops.kv_gather_and_draft_attn(
+        to_dev(p.k_cache, "bf16"), to_dev(p.v_cache, "bf16"), torch.from_numpy(gidx).to(DEV), p.chunk,
+        to_dev(p.q, "bf16"), to_dev(p.k_new, "bf16"), to_dev(p.v_new, "bf16"), scale=p.scale)
+    torch.cuda.synchronize()
+    rkp, rvp = oracle.gather_ref(p.k_cache, p.v_cache, gidx, p.chunk)
+    np.testing.assert_array_equal(kp.view(torch.int16).cpu().numpy().view(np.uint16), rkp)
+    np.testing.assert_array_equal(vp.view(torch.int16).cpu().numpy().view(np.uint16), rvp)
+    ro, rl = oracle.draft_attn_ref(p.q, rkp, rvp, p.k_new, p.v_new, p.scale, "bf16")
+    check_attn(out, lse, ro, rl, "bf16", "gathered draft attention")
