@@ -50,7 +50,10 @@ typedef enum ts_status {
   TS_ERR_HIP = 4          /* a HIP launch failed; message from the runtime  */
 } ts_status;
 
-typedef enum ts_dtype { TS_F32 = 0, TS_BF16 = 1 } ts_dtype;
+/* Element type of the tensors of a call. A call given any other value returns
+ * TS_ERR_INVALID_ARG; the last enumerator only widens the type to the range of
+ * an int, so that such a value is a valid ts_dtype in C++ as in C. */
+typedef enum ts_dtype { TS_F32 = 0, TS_BF16 = 1, TS_DTYPE_INT_RANGE_ = 0x7fffffff } ts_dtype;
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ts_last_error(void);

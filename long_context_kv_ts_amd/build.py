@@ -66,6 +66,39 @@ def _link(objs, lib: str, hipcc: str) -> None:
     os.replace(tmp, lib)
 
 
+# Host-sanitized variant of the library for the CPU tests of the C ABI: api.cpp
+# (argument checks, work planning, workspace carving) built with AddressSanitizer
+# and UndefinedBehaviorSanitizer on its host code only, linked with the same
+# kernel objects. Loading it needs the sanitizer runtime preloaded
+# (tests/test_abi_sanitized.py does that in a child process).
+SAN_DIR = os.path.join(PKG, "_build_san")
+SAN_LIB = os.path.join(SAN_DIR, "libts_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(hipcc: str | None = None, verbose: bool = True) -> str:
+    """Build SAN_LIB from api.cpp (sanitized) and the kernel objects of build()."""
+    hipcc = hipcc or _hipcc()
+    os.makedirs(SAN_DIR, exist_ok=True)
+    obj = os.path.join(SAN_DIR, "api_san.o")
+    cmd = [hipcc, "-O1", "-g", *[f for f in _flags() if f != "-O3"], *SAN_FLAGS, "-c",
+           os.path.join(CSRC, "api.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    objs = [obj] + [os.path.join(OUT_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "api.cpp"]
+    tmp = SAN_LIB + ".tmp"
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS[:4], "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 def build(verbose: bool = True) -> str:
     hipcc = _hipcc()
     os.makedirs(OUT_DIR, exist_ok=True)
@@ -76,6 +109,7 @@ def build(verbose: bool = True) -> str:
     _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, hipcc)
     if verbose:
         print(f"built {LIB} and {PROBE_LIB}")
+    build_host_sanitized(hipcc, verbose)
     return LIB
 
 

@@ -34,7 +34,9 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 #define TS_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int kThreads = 256;      // 4 independent waves
+constexpr int kBlockWaves = 1;     // independent waves (splits) per workgroup: one spreads the
+                                   // splits over the most compute units
+constexpr int kThreads = kBlockWaves * 64;
 constexpr int kSmallMaxDrafts = 16;  // this path serves heads of at most 16 query rows
 constexpr float kLazy = 8.0f;
 
@@ -62,7 +64,7 @@ __device__ __forceinline__ void lds_dma16(const bf16_t* base, uint32_t voff, uin
 template <int D, bool kGather>
 __global__ __launch_bounds__(kThreads) void attn_split_small_kernel(AttnArgs a) {
   using Ly = SLayout<D>;
-  __shared__ __attribute__((aligned(1024))) bf16_t Vs[4][Ly::tileElems];
+  __shared__ __attribute__((aligned(1024))) bf16_t Vs[kBlockWaves][Ly::tileElems];
   // at most 16 query rows per head reach this kernel, so at most 16 drafts: one mask word each
   __shared__ uint32_t anc[kSmallMaxDrafts];
   __shared__ int32_t s_par[kSmallMaxDrafts];
@@ -71,12 +73,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_small_kernel(AttnArgs a) 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = blockIdx.y;
-  const int split = blockIdx.x * 4 + wave;
+  const int split = blockIdx.x * kBlockWaves + wave;
   const int G = a.G, T = a.T, Hq = a.Hq;
   const float c = a.scale_log2;
 
   // the mask is needed by the wave(s) whose range reaches the drafts
-  const int last_split = min(blockIdx.x * 4 + 3, pl.n_splits - 1);
+  const int last_split = min(blockIdx.x * kBlockWaves + kBlockWaves - 1, pl.n_splits - 1);
   const bool block_has_draft = (last_split + 1) * pl.tiles_per_split > pl.n_cache_tiles;
   const int words = (T + 31) >> 5;                 // 1
   if (block_has_draft) build_ancestor_rows(a.parent, words, 0, T, anc, s_par, tid, kThreads);
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_small_kernel(AttnArgs a) 
 
 hipError_t launch_attn_split_small(const AttnArgs& a, hipStream_t s) {
   if (a.T > kSmallMaxDrafts || a.plan.rows_per_head > 16) return hipErrorInvalidValue;   // the plan never sends these
-  dim3 grid((a.plan.n_splits + 3) / 4, a.Hkv);
+  dim3 grid((a.plan.n_splits + kBlockWaves - 1) / kBlockWaves, a.Hkv);
   if (a.gidx != nullptr) {
     // the gathered cache is whole 64-token chunks, one tile each
     if (a.L % kTile != 0 || a.plan.n_cache_tiles * (int64_t)kTile != a.L) return hipErrorInvalidValue;

@@ -25,7 +25,7 @@ from typing import Optional, Tuple
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libts.so")
+_LIB_PATH = os.environ.get("TS_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libts.so")
 _lib = None
 
 TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_WORKSPACE, TS_ERR_HIP = range(5)
