@@ -11,9 +11,12 @@ One step = one pass of the whole path for one LLaMA3.1-8B-shaped layer
      partial cache;
   3. the 4-query draft attention over the partial cache.
 
-The verify split kernel scores the chunks on the same reads of K
-(ts_tree_verify_attn_partials_and_importance); --unfused times the separate
-launches (split, merge, importance, top-k, gather, draft attention).
+The timed step is four kernels: the verify split kernel, which also scores
+the chunks on the same reads of K (ts_tree_verify_attn_partials_and_importance);
+the merge sharing its grid with the top-k (ts_attn_merge_and_topk); the draft
+pass that gathers the chosen chunks as it reads them (ts_kv_gather_and_draft_attn:
+split kernel, then its merge). --unfused times the separate launches (split,
+merge, importance, top-k, gather, draft split + merge).
 
 Timing (all on the stream every call launches on, torch's current stream):
   * warm-up: at least W steps, then steps until at least --min-warm-s seconds
@@ -27,8 +30,8 @@ Timing (all on the stream every call launches on, torch's current stream):
     nor the L2 holds any input and no dirty line of the flush is left to be
     written out during the timed call, then times one step;
   * the fused and the unfused step alternated, each timed by events;
-  * per-kernel durations (HIP events between the kernels of the unfused step):
-    the roofline of the dominant kernel;
+  * per-kernel durations (HIP events between the calls of the fused and of the
+    unfused step, each settled again first): the roofline of the dominant kernel;
   * one ts_tree_verify_attn call (split + merge), cold and warm, at 20,480 and
     102,400 cached tokens (LLaMA3.1-8B) and at 102,400 (LLaMA2-7B MHA).
 
@@ -79,8 +82,8 @@ def parse():
     ap.add_argument("--no-probes", action="store_true", help="skip the measured-ceiling probes")
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step instead of eager launches")
     ap.add_argument("--unfused", action="store_true",
-                    help="time the merge and the importance as two launches (default: one launch, "
-                         "ts_attn_merge_and_importance)")
+                    help="time the step as its separate launches (split, merge, importance, top-k, gather, "
+                         "draft split + merge) instead of the four fused kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -301,6 +304,11 @@ def main():
 
     # ---- per-kernel durations (events between the kernels) ------------------
     def per_kernel(fn, n_ev, labels):
+        # the clock sags for a few dozen launches after the GPU has idled (as
+        # between the regions of this script): settle the instrumented step
+        # again before recording, so that the kernels run as in the timed region
+        warm_ev = tm.events(n_ev)
+        tm.steady(lambda: fn(warm_ev), 1, 0.5, args.max_warm_s)
         events = [tm.events(n_ev) for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
@@ -341,7 +349,8 @@ def main():
     t_split = avg["verify_split"] * 1e-6
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(),
+                "traffic": measured_traffic("attn_split_mfma_kernel<128, 8, 256, 8, false>" if args.unfused
+                                            else TRAFFIC_KERNEL),
                 "kernel": ("verify split-K (attn_split_mfma_kernel)" if args.unfused else
                            "verify split-K with chunk importance (attn_split_mfma_kernel, importance wave)"),
                 "kernel_us": round(t_dom * 1e6, 2),
@@ -454,12 +463,7 @@ def verify_lines(tm, dev, vc2, args):
 def measured_peaks(dev):
     """What this GPU sustains, from the probe kernels (libts_probe.so)."""
     from long_context_kv_ts_amd import probe
-    return {"mfma_bf16": probe.mfma_bf16_peak(dev),
-            "mfma_bf16_constant_operands": probe.mfma_bf16_peak(dev, toggle=False, seconds=0.2),
-            "mfma_bf16_1wave": probe.mfma_bf16_peak(dev, waves_per_simd=1, seconds=0.2),
-            "hbm_stream_read": probe.stream_read(dev),
-            "ns_per_wave_instr_per_simd": {"v_fma_f32": probe.valu_issue(dev, 0),
-                                           "v_exp_f32": probe.valu_issue(dev, 1)}}
+    return probe.measure_all(dev)
 
 
 def time_accept_commit(vc, dev, reps):
@@ -582,7 +586,8 @@ def time_ngram(dev, reps):
     return round(e0.elapsed_time(e1) * 1e3 / reps, 2)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_split_102400_hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_split_importance_102400_hbm_traffic.txt")
+TRAFFIC_KERNEL = "attn_split_mfma_kernel<128, 8, 256, 8, true>"
 KERNEL_SOURCES = [os.path.join(ROOT, "long_context_kv_ts_amd", "csrc", f) for f in ("attn_mfma.hip", "common.h")]
 
 
@@ -594,14 +599,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the verify split kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by what the same counters read
-    for a plain copy of known size; None if the kernel source has changed since."""
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs, scaled by what the same counters read for a plain copy of
+    known size; None if the counters are of another kernel or its source has
+    changed since."""
     try:
         kv = dict(line.split("=", 1) for line in open(TRAFFIC_FILE) if "=" in line and not line.startswith("#"))
         kv = {k.strip(): v.strip() for k, v in kv.items()}
-        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        if kv.get("kernel") != kernel or kv.get("kernel_source_sha256_16") != kernel_source_hash():
             return None
         return round(float(kv["fetch_kib"]) * float(kv["fetch_scale"]) * 1024
                      + float(kv["write_kib"]) * float(kv["write_scale"]) * 1024)

@@ -2,8 +2,8 @@
  * ts_probe.h -- measurement probes of libts_probe.so (MI355X, gfx950).
  *
  * Not part of the hot path: these kernels measure what this GPU sustains
- * (matrix-core bf16 rate, vector-ALU issue rates, plain streaming reads from
- * HBM), so that the kernels' roofline fractions can also be stated against
+ * (matrix-core bf16 rate, vector-ALU issue rates, LDS read bandwidth, plain
+ * streaming reads from HBM), so that the kernels' roofline fractions can also be stated against
  * measured ceilings next to the published peaks. The benchmark calls them.
  *
  * Every call enqueues one launch on `stream` and returns 0, or a hipError_t
@@ -36,6 +36,14 @@ double ts_probe_mfma_bf16_flops(int waves_per_simd, int iters);
  * (op 0) or v_exp_f32 (op 1). Wave instructions per SIMD of one launch:
  * 2 * 16 * iters. */
 int ts_probe_valu(int op, int iters, float* sink, hipStream_t stream);
+
+/* LDS read bandwidth: one 512-thread workgroup per CU, every wave issuing
+ * `iters` rounds of 16 reads of its own slices of a 96 KB LDS array, as
+ * ds_read_b128 (transposed = 0, 1 KB a wave read) or ds_read_b64_tr_b16
+ * (transposed != 0, 512 B a wave read). Bytes of one launch:
+ * ts_probe_lds_read_bytes(transposed, iters). */
+int ts_probe_lds_read(int transposed, int iters, uint32_t* sink, hipStream_t stream);
+double ts_probe_lds_read_bytes(int transposed, int iters);
 
 /* A plain streaming read of `bytes` (a multiple of 16, 16-byte aligned) with
  * 16-byte loads, consecutive lanes on consecutive 16 bytes and eight loads in

@@ -1,5 +1,6 @@
 // Measurement probes (libts_probe.so): the matrix-core bf16 rate, vector-ALU
-// issue rates and a plain HBM streaming read, as this GPU sustains them. The
+// issue rates, LDS read bandwidth and a plain HBM streaming read, as this GPU
+// sustains them. The
 // benchmark states the hot-path kernels' fractions against these next to the
 // published peaks. Nothing here is part of the hot path.
 #include <hip/hip_runtime.h>
@@ -87,9 +88,65 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const uint4* 
   if (acc == 0x9e3779b9u) sink[threadIdx.x] = acc;    // keeps the loads; practically never taken
 }
 
+// LDS read bandwidth: one 512-thread workgroup per CU over a 96 KB LDS array,
+// every wave reading its own 1 KB (kTr: 512 B) slices, 16 reads a round, as
+// ds_read_b128 (kTr false) or the transposing ds_read_b64_tr_b16 that feeds
+// the V^T operand of the verify kernel's PV product (kTr true). The XOR of
+// the results keeps the reads; the vector ALU work per read is below the LDS
+// time.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kLdsVec = 6144;                    // 16-byte elements: 96 KB
+
+template <bool kTr>
+__global__ __launch_bounds__(512) void lds_read_probe_kernel(int iters, uint32_t* sink) {
+  __shared__ u32x4_t buf[kLdsVec];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kLdsVec; i += 512) buf[i] = u32x4_t{(uint32_t)i, (uint32_t)i + 1u, 7u, 9u};
+  __syncthreads();
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(&buf[0]);
+  uint32_t acc = 0u;
+  if constexpr (kTr) {
+    s16x4_t x = {0, 0, 0, 0};
+    const uint32_t base = (uint32_t)(wave * 512 + lane * 8);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t off = (base + (uint32_t)r * 4096u + (uint32_t)it * 512u) % (uint32_t)(kLdsVec * 16);
+        x ^= __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(lds0 + off));
+      }
+    }
+    // all 32 bits of acc depend on the reads (a 16-bit result could never equal
+    // the test value below, and the reads would be dropped)
+    acc = (((uint32_t)(uint16_t)x[0] << 16) | (uint16_t)x[1]) ^ (((uint32_t)(uint16_t)x[2] << 16) | (uint16_t)x[3]);
+  } else {
+    u32x4_t x = {0u, 0u, 0u, 0u};
+    const int base = lane + wave * 64;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x ^= buf[(base + r * 512 + it * 64) % kLdsVec];
+    }
+    acc = x[0] ^ x[1] ^ x[2] ^ x[3];
+  }
+  if (acc == 0x9e3779b9u) sink[tid & 255] = acc;    // keeps the reads; practically never taken
+}
+
 }  // namespace
 
 extern "C" {
+
+int ts_probe_lds_read(int transposed, int iters, uint32_t* sink, hipStream_t stream) {
+  if (!sink || iters < 1) return (int)hipErrorInvalidValue;
+  if (transposed) lds_read_probe_kernel<true><<<kCUs, 512, 0, stream>>>(iters, sink);
+  else lds_read_probe_kernel<false><<<kCUs, 512, 0, stream>>>(iters, sink);
+  return (int)hipGetLastError();
+}
+
+double ts_probe_lds_read_bytes(int transposed, int iters) {
+  // 256 workgroups x 8 waves x 16 reads a round; 1 KB (b128) or 512 B (tr_b64) a wave read
+  return (double)kCUs * 8 * 16 * (double)iters * (transposed ? 512.0 : 1024.0);
+}
 
 int ts_probe_mfma_bf16(int waves_per_simd, int toggle, int iters, float* sink, hipStream_t stream) {
   if (!sink || iters < 1 || (waves_per_simd != 1 && waves_per_simd != 2)) return (int)hipErrorInvalidValue;

@@ -1,6 +1,6 @@
 """ctypes binding of ``libts_probe.so`` (``include/ts_probe.h``): measurement
 probes of what this GPU sustains -- the bf16 matrix-core rate, vector-ALU issue
-rates and a plain HBM streaming read. The benchmark reports the hot-path
+rates, LDS read bandwidth and a plain HBM streaming read. The benchmark reports the hot-path
 kernels against these next to the published peaks. Not part of the hot path.
 """
 from __future__ import annotations
@@ -29,6 +29,10 @@ def lib() -> ctypes.CDLL:
         l.ts_probe_valu.restype = ctypes.c_int
         l.ts_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
         l.ts_probe_stream_read.restype = ctypes.c_int
+        l.ts_probe_lds_read.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        l.ts_probe_lds_read.restype = ctypes.c_int
+        l.ts_probe_lds_read_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+        l.ts_probe_lds_read_bytes.restype = ctypes.c_double
         _lib = l
     return _lib
 
@@ -100,3 +104,33 @@ def stream_read(dev, nbytes: int = 209_715_200, copies: int = 4, reps: int = 40)
     del bufs
     return {"GBs": round(nbytes / (med * 1e-6) / 1e9, 1), "bytes": nbytes, "launch_us": round(med, 2),
             "buffers": copies}
+
+
+def lds_read(dev, transposed: bool, iters: int = 4000, reps: int = 10):
+    """LDS read bandwidth over all CUs (TB/s) with ds_read_b128 or, transposed,
+    ds_read_b64_tr_b16; median over `reps` launches."""
+    sink = torch.empty(256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    launch = lambda: _ok(lib().ts_probe_lds_read(int(transposed), iters, sink.data_ptr(), stream), "lds probe")
+    _timed(launch, 2)
+    us = statistics.median(_timed(launch, reps))
+    nbytes = lib().ts_probe_lds_read_bytes(int(transposed), iters)
+    return {"TBs": round(nbytes / (us * 1e-6) / 1e12, 2), "per_cu_GBs": round(nbytes / (us * 1e-6) / 1e9 / 256, 1),
+            "launch_us": round(us, 2), "instruction": "ds_read_b64_tr_b16" if transposed else "ds_read_b128"}
+
+
+def measure_all(dev) -> dict:
+    """Every probe once: what the benchmark reports as the measured ceilings."""
+    return {"mfma_bf16": mfma_bf16_peak(dev),
+            "mfma_bf16_constant_operands": mfma_bf16_peak(dev, toggle=False, seconds=0.2),
+            "mfma_bf16_1wave": mfma_bf16_peak(dev, waves_per_simd=1, seconds=0.2),
+            "hbm_stream_read": stream_read(dev),
+            "lds_read_b128": lds_read(dev, False),
+            "lds_read_tr_b64": lds_read(dev, True),
+            "ns_per_wave_instr_per_simd": {"v_fma_f32": valu_issue(dev, 0), "v_exp_f32": valu_issue(dev, 1)}}
+
+
+if __name__ == "__main__":
+    import json
+
+    print(json.dumps(measure_all(torch.device("cuda:0")), indent=1))

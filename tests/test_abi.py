@@ -43,6 +43,18 @@ def test_every_declared_function_is_exported_and_bound():
     assert lib.ts_abi_version() == 2
 
 
+def test_every_probe_function_is_exported_and_bound():
+    """include/ts_probe.h: the measurement probes in libts_probe.so."""
+    from long_context_kv_ts_amd import probe
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "ts_probe.h")).read(), flags=re.S)
+    names = re.findall(r"\b(ts_probe_\w+)\s*\(", text)
+    assert len(names) >= 6
+    lib = probe.lib()
+    for name in names:
+        fn = getattr(lib, name)
+        assert fn.argtypes is not None, f"{name} not bound in probe.py"
+
+
 def _verify(**kw):
     a = dict(q=P, kc=P, vc=P, stride=1024, kd=P, vd=P, parent=P, out=P, lse=P, T=120, Hq=32,
              Hkv=8, D=128, L=1024, scale=0.088, dtype=B, ns=0, ws=P, wsb=1 << 40, stream=None)
