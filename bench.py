@@ -24,14 +24,18 @@ Timing (all on the stream every call launches on, torch's current stream):
     settles at its power limit a few milliseconds into sustained matrix-core
     load), capped at --max-warm-s;
   * the step (value): K steps back to back between two device syncs, wall
-    clock; HIP events between the steps give the per-step median/p10/p90;
+    clock, with no event between the steps (an event recorded between two
+    launches idles the GPU for several µs); batches of 5 steps with events
+    around each give the median/p10/p90;
   * cold steps: each rep first writes a 1 GiB scratch buffer and reads it
     back (outside the events), so that neither the 256 MB last-level cache
     nor the L2 holds any input and no dirty line of the flush is left to be
     written out during the timed call, then times one step;
   * the fused and the unfused step alternated, each timed by events;
-  * per-kernel durations (HIP events between the calls of the fused and of the
-    unfused step, each settled again first): the roofline of the dominant kernel;
+  * per-kernel durations: HIP events between the calls of the fused and of
+    the unfused step, each settled again first (every event idles the GPU for
+    a few µs before the next launch: that gap is inside each call's figure):
+    the roofline of the dominant kernel;
   * one ts_tree_verify_attn call (split + merge), cold and warm, at 20,480 and
     102,400 cached tokens (LLaMA3.1-8B) and at 102,400 (LLaMA2-7B MHA).
 
@@ -122,6 +126,20 @@ class Timer:
     def events(self, n):
         return [self.torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
+    def batches(self, fn, n_batches, per_batch):
+        """Per-call µs of `n_batches` batches of `per_batch` back-to-back calls,
+        with events only around each batch: an event recorded between two
+        launches leaves the GPU idle for several µs before the next one, so
+        per-call events would time that idle gap too."""
+        ev = self.events(2 * n_batches)
+        for b in range(n_batches):
+            ev[2 * b].record()
+            for _ in range(per_batch):
+                fn()
+            ev[2 * b + 1].record()
+        self.torch.cuda.synchronize()
+        return [ev[2 * b].elapsed_time(ev[2 * b + 1]) * 1e3 / per_batch for b in range(n_batches)]
+
     def back_to_back(self, fn, reps):
         """Per-call µs of `reps` back-to-back calls."""
         ev = self.events(reps + 1)
@@ -179,7 +197,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the sharded multi-GPU path is design only, not implemented "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
@@ -228,25 +246,15 @@ def main():
     dws = ops.alloc_workspace(ops.lib().ts_partial_draft_attn_workspace(
         pc.R, pc.Hq, pc.Hkv, pc.D, pc.k * pc.chunk, ops.TS_BF16, 0), dev)
 
-    names = ["verify_split", "verify_merge", "importance", "topk", "gather", "draft_attn"]
-
-    def step(ev=None):
-        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
-        rec(0)
+    def step():
         ops.tree_verify_attn_partials(q, kc, vcache, kd, vd, parent, scale=vc.scale,
                                       o_part=o_part, l_part=l_part)
-        rec(1)
         ops.attn_merge(o_part, l_part, out=out, lse=lse)
-        rec(2)
         ops.kv_importance_score(pq, pk, pc.chunk, scale=pc.scale, scores=scores)
-        rec(3)
         ops.kv_topk_select(scores, pc.k, chunk_idx=idx, chunk_score=idx_s)
-        rec(4)
         ops.kv_gather(pk, pv, idx, pc.chunk, k_part=kp, v_part=vp)
-        rec(5)
         ops.partial_draft_attn(pq, kp, vp, pkn, pvn, scale=pc.scale, out=dout, lse=dlse,
                                workspace=dws)
-        rec(6)
 
     # The timed step, four kernels: the verify split kernel also scores the
     # cache's chunks on the same reads of K; the merge shares its grid with the
@@ -279,62 +287,80 @@ def main():
     log(f"warm-up: {warm}")
 
     # ---- the step: K steps back to back, wall clock between two syncs --------
-    ev = tm.events(args.steps + 1)
+    # (no event between the steps: each would leave the GPU idle for a few µs)
+    ev = tm.events(2)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     ev[0].record()
     for i in range(args.steps):
         timed_step()
-        ev[i + 1].record()
+    ev[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
-    step_warm = stats([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(args.steps)])
-    log(f"step: {ms_per_step * 1e3:.1f} us/step wall, events {step_warm}")
+    gpu_us_per_step = ev[0].elapsed_time(ev[1]) * 1e3 / args.steps
+    # the spread: batches of 5 steps with events around each batch
+    step_warm = stats(tm.batches(timed_step, max(args.steps // 5, 4), 5))
+    log(f"step: {ms_per_step * 1e3:.1f} us/step wall, {gpu_us_per_step:.1f} us/step between events; "
+        f"5-step batches {step_warm}")
 
     # ---- cold steps ----------------------------------------------------------
     step_cold = stats(tm.cold(timed_step, args.cold_reps))
 
     # ---- the fused and the unfused step, alternated --------------------------
     fu, un = [], []
-    for _ in range(max(args.steps // 2, 10)):
-        fu += tm.back_to_back(step_fused, 2)
-        un += tm.back_to_back(step, 2)
+    for _ in range(max(args.steps // 5, 10)):
+        fu += tm.batches(step_fused, 1, 5)
+        un += tm.batches(step, 1, 5)
     alternated = {"fused": stats(fu), "unfused": stats(un)}
 
-    # ---- per-kernel durations (events between the kernels) ------------------
-    def per_kernel(fn, n_ev, labels):
-        # the clock sags for a few dozen launches after the GPU has idled (as
-        # between the regions of this script): settle the instrumented step
-        # again before recording, so that the kernels run as in the timed region
-        warm_ev = tm.events(n_ev)
-        tm.steady(lambda: fn(warm_ev), 1, 0.5, args.max_warm_s)
-        events = [tm.events(n_ev) for _ in range(args.steps)]
+    # ---- per-kernel durations ------------------------------------------------
+    # Events between the calls of the step, after settling the instrumented
+    # step again (the clock sags for a few dozen launches after the GPU has
+    # idled, as between this script's regions). Each recorded event idles the
+    # GPU for a few µs before the next launch, and that gap is inside the
+    # duration of the call after it; timing each call alone in a loop instead
+    # changes the power state (a loop of verify calls alone runs hotter and
+    # slower than the step) or times the host's call overhead (the short calls).
+    fused_calls = [
+        ("verify_split_importance", lambda: ops.tree_verify_attn_partials_and_importance(
+            q, kc, vcache, kd, vd, parent, pq, pc.chunk, scale=vc.scale, imp_scale=pc.scale, o_part=o_part,
+            l_part=l_part, scores=scores)),
+        ("merge_topk", lambda: ops.attn_merge_and_topk(o_part, l_part, scores, pc.k, out=out, lse=lse, chunk_idx=idx,
+                                                       chunk_score=idx_s)),
+        ("gather_draft_attn", lambda: ops.kv_gather_and_draft_attn(pk, pv, idx, pc.chunk, pq, pkn, pvn, scale=pc.scale,
+                                                                   k_part=kp, v_part=vp, out=dout, lse=dlse,
+                                                                   workspace=dws)),
+    ]
+    unfused_calls = [
+        ("verify_split", lambda: ops.tree_verify_attn_partials(q, kc, vcache, kd, vd, parent, scale=vc.scale,
+                                                               o_part=o_part, l_part=l_part)),
+        ("verify_merge", lambda: ops.attn_merge(o_part, l_part, out=out, lse=lse)),
+        ("importance", lambda: ops.kv_importance_score(pq, pk, pc.chunk, scale=pc.scale, scores=scores)),
+        ("topk", lambda: ops.kv_topk_select(scores, pc.k, chunk_idx=idx, chunk_score=idx_s)),
+        ("gather", lambda: ops.kv_gather(pk, pv, idx, pc.chunk, k_part=kp, v_part=vp)),
+        ("draft_attn", lambda: ops.partial_draft_attn(pq, kp, vp, pkn, pvn, scale=pc.scale, out=dout, lse=dlse,
+                                                      workspace=dws)),
+    ]
+
+    def per_call(calls):
+        def run(ev):
+            for i, (_, fn) in enumerate(calls):
+                ev[i].record()
+                fn()
+            ev[len(calls)].record()
+        warm_ev = tm.events(len(calls) + 1)
+        tm.steady(lambda: run(warm_ev), 1, 0.5, args.max_warm_s)
+        events = [tm.events(len(calls) + 1) for _ in range(args.steps)]
         torch.cuda.synchronize()
-        for i in range(args.steps):
-            fn(events[i])
-        torch.cuda.synchronize()
-        per = {n: [] for n in labels}
         for e in events:
-            for j, n in enumerate(labels):
-                per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)   # us
+            run(e)
+        torch.cuda.synchronize()
+        per = {n: [e[j].elapsed_time(e[j + 1]) * 1e3 for e in events] for j, (n, _) in enumerate(calls)}
         return ({n: float(np.mean(v)) for n, v in per.items()}, {n: float(np.median(v)) for n, v in per.items()})
 
-    def step_fused_ev(ev):
-        ev[0].record()
-        ops.tree_verify_attn_partials_and_importance(q, kc, vcache, kd, vd, parent, pq, pc.chunk, scale=vc.scale,
-                                                     imp_scale=pc.scale, o_part=o_part, l_part=l_part,
-                                                     scores=scores)
-        ev[1].record()
-        ops.attn_merge_and_topk(o_part, l_part, scores, pc.k, out=out, lse=lse, chunk_idx=idx, chunk_score=idx_s)
-        ev[2].record()
-        ops.kv_gather_and_draft_attn(pk, pv, idx, pc.chunk, pq, pkn, pvn, scale=pc.scale, k_part=kp, v_part=vp,
-                                     out=dout, lse=dlse, workspace=dws)
-        ev[3].record()
-
-    fused_names = ["verify_split_importance", "merge_topk", "gather_draft_attn"]
-    avg, med = per_kernel(step, 7, names)
-    favg, fmed = per_kernel(step_fused_ev, 4, fused_names)
+    favg, fmed = per_call(fused_calls)
+    avg, med = per_call(unfused_calls)
 
     # ---- roofline of the dominant kernel of the timed step ---------------------
     # the split kernel that also scores the chunks: the verify's QK^T and PV
@@ -380,9 +406,13 @@ def main():
                    "T": T, "Hq": Hq, "Hkv": Hkv, "head_dim": D, "kv_len": L, "splits": S,
                    "chunk": pc.chunk, "topk": pc.k},
         "timing": ("graph replay of the step" if graph is not None else "eager launches") +
-                  ("" if args.unfused else "; chunk importance scored by the verify split kernel") +
-                  "; value = wall clock of the back-to-back steps after a settled warm-up",
+                  ("" if args.unfused else "; four kernels: verify split with chunk importance, merge with "
+                   "top-k, draft split with gather, draft merge") +
+                  "; value = wall clock of the back-to-back steps after a settled warm-up, no event between "
+                  "steps; step_us.warm = means of 5-step batches; step_us.cold = one step after a 1 GiB "
+                  "flush, events around it (one event's idle gap included)",
         "warmup_settled": warm,
+        "gpu_us_per_step": round(gpu_us_per_step, 2),
         "step_us": {"warm": step_warm, "cold": step_cold},
         "step_alternated_us": alternated,
         "kernel_us_avg": {n: round(v, 2) for n, v in avg.items()},
@@ -427,8 +457,9 @@ def verify_flops(c):
 
 def verify_lines(tm, dev, vc2, args):
     """One ts_tree_verify_attn call (split + merge, library-chosen splits) per
-    workload: median/p10/p90 cold (1 GiB scratch write and read-back before each call) and
-    warm (back to back), with %HBM of the cache's K+V and %MFMA of 2.5 PF."""
+    workload: median/p10/p90 cold (1 GiB scratch write and read-back before each call,
+    events around the call) and warm (means of 5-call back-to-back batches), with %HBM of
+    the cache's K+V and %MFMA of 2.5 PF."""
     import torch
     from long_context_kv_ts_amd import inputs, ops
     lines = {}
@@ -443,7 +474,7 @@ def verify_lines(tm, dev, vc2, args):
         ws = ops.alloc_workspace(ops.verify_workspace_bytes(c.T, c.Hq, c.Hkv, c.D, c.L, torch.bfloat16), dev)
         call = lambda: ops.tree_verify_attn(q, kc, vc, kd, vd, par, scale=c.scale, out=out, lse=lse, workspace=ws)
         tm.steady(call, 3, 0.5, 4.0)
-        warm = stats(tm.back_to_back(call, args.steps))
+        warm = stats(tm.batches(call, max(args.steps // 5, 4), 5))
         cold = stats(tm.cold(call, args.cold_reps))
         kv = 2.0 * c.Hkv * c.L * c.D * 2
         fl = verify_flops(c)
