@@ -323,3 +323,44 @@ def test_gather_draft_full_size_against_the_oracle():
     np.testing.assert_array_equal(vp.view(torch.int16).cpu().numpy().view(np.uint16), rvp)
     ro, rl = oracle.draft_attn_ref(p.q, rkp, rvp, p.k_new, p.v_new, p.scale, "bf16")
     check_attn(out, lse, ro, rl, "bf16", "gathered draft attention")
+
+
+def test_bench_step_at_full_size_against_the_oracle():
+    """The decode step exactly as the benchmark times it -- four kernels through
+    the three combined calls, on the 102,400-token LLaMA3.1-8B cache with its 4
+    recent queries and the 120-draft forest -- against the oracle: verify output
+    and lse element by element, chunk scores within 1e-5, the top-64 bit-exact on
+    the GPU's own scores and within the near-tie rule on the oracle's, the partial
+    cache bit-exact, the draft attention element by element."""
+    from long_context_kv_ts_amd import inputs
+    from gpu_util import check_attn, to_dev
+    import oracle
+    from test_gpu_partial import topk_matches_with_near_tie_rule
+    pc = inputs.workload("partial_100k")
+    vc = inputs.workload("llama8b_100k", L=64)          # the same drafts and forest, without its own cache
+    say("bench step at full size vs oracle")
+    kc, v_c = to_dev(pc.k_cache, "bf16"), to_dev(pc.v_cache, "bf16")
+    q, kd, vd = to_dev(vc.q, "bf16"), to_dev(vc.k_draft, "bf16"), to_dev(vc.v_draft, "bf16")
+    parent = torch.from_numpy(vc.parent).to(DEV)
+    pq = to_dev(pc.q, "bf16")
+    o_part, l_part, scores = ops.tree_verify_attn_partials_and_importance(
+        q, kc, v_c, kd, vd, parent, pq, pc.chunk, scale=vc.scale, imp_scale=pc.scale)
+    out, lse, idx, _ = ops.attn_merge_and_topk(o_part, l_part, scores, pc.k)
+    kp, vp, dout, dlse = ops.kv_gather_and_draft_attn(kc, v_c, idx, pc.chunk, pq, to_dev(pc.k_new, "bf16"),
+                                                      to_dev(pc.v_new, "bf16"), scale=pc.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.verify_attn_ref(vc.q, pc.k_cache, pc.v_cache, vc.k_draft, vc.v_draft, vc.parent, vc.scale,
+                                    "bf16")
+    check_attn(out, lse, ro, rl, "bf16", "step verify")
+    ref_s = oracle.importance_ref(pc.q, pc.k_cache, pc.scale, pc.chunk, "bf16")
+    gs = scores.cpu().numpy().astype(np.float64)
+    assert np.abs(gs - ref_s).max() <= 1e-5 * np.abs(ref_s).max()
+    gidx = idx.cpu().numpy()
+    same_prec, _ = oracle.topk_ref(gs, pc.k)
+    np.testing.assert_array_equal(gidx, same_prec)
+    topk_matches_with_near_tie_rule(gidx, ref_s, pc.k)
+    rkp, rvp = oracle.gather_ref(pc.k_cache, pc.v_cache, gidx, pc.chunk)
+    np.testing.assert_array_equal(kp.view(torch.int16).cpu().numpy().view(np.uint16), rkp)
+    np.testing.assert_array_equal(vp.view(torch.int16).cpu().numpy().view(np.uint16), rvp)
+    rd, rdl = oracle.draft_attn_ref(pc.q, rkp, rvp, pc.k_new, pc.v_new, pc.scale, "bf16")
+    check_attn(dout, dlse, rd, rdl, "bf16", "step draft attention")
