@@ -53,15 +53,62 @@ __device__ __forceinline__ void load8(const float* p, float* o) {
   o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
 }
 
+// Reductions over the 64 lanes of a wave, the result in every lane, in lane
+// moves that need no LDS: DPP within rows of 16 lanes (quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror, row_mirror), then the row pairs and
+// halves exchanged by v_permlane16_swap and v_permlane32_swap.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dpp_f32<0xB1>(v));
+  v = op(v, dpp_f32<0x4E>(v));
+  v = op(v, dpp_f32<0x141>(v));
+  v = op(v, dpp_f32<0x140>(v));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+// Inclusive prefix sum over the 64 lanes of a wave in DPP lane moves: shifts
+// by 1, 2, 4 and 8 within each row of 16 lanes, then each row's total
+// broadcast into the rows above it (row_bcast:15 into rows 1 and 3,
+// row_bcast:31 into rows 2 and 3). Lanes a move has no source for add zero.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_add_u32(uint32_t x) {
+  return x + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, kRowMask, 0xF, false);
+}
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add_f32(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x = dpp_add_u32<0x111, 0xF>(x);
+  x = dpp_add_u32<0x112, 0xF>(x);
+  x = dpp_add_u32<0x114, 0xF>(x);
+  x = dpp_add_u32<0x118, 0xF>(x);
+  x = dpp_add_u32<0x142, 0xA>(x);
+  x = dpp_add_u32<0x143, 0xC>(x);
+  return x;
+}
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  x = dpp_add_f32<0x111, 0xF>(x);
+  x = dpp_add_f32<0x112, 0xF>(x);
+  x = dpp_add_f32<0x114, 0xF>(x);
+  x = dpp_add_f32<0x118, 0xF>(x);
+  x = dpp_add_f32<0x142, 0xA>(x);
+  x = dpp_add_f32<0x143, 0xC>(x);
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan(int x) { return (int)wave_incl_scan((uint32_t)x); }
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 
 // Ancestor-or-self bitmask rows of the drafts t in [t_lo, t_hi), built in LDS:

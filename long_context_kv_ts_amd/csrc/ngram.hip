@@ -192,14 +192,8 @@ struct Cand {
 // Exclusive prefix of v over the workgroup's threads (index order); total = the sum.
 __device__ int block_excl_scan(int v, int* red, int& total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
-  int excl = __shfl_up(incl, 1, kWave);
-  if (lane == 0) excl = 0;
+  const int incl = wave_incl_scan(v);
+  const int excl = incl - v;
   if (lane == kWave - 1) red[wave] = incl;
   __syncthreads();
   int off = 0;

@@ -326,14 +326,8 @@ __device__ float block_max(float v, float* red) {
 template <typename T>
 __device__ T block_excl_scan(T v, T* red, T& total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  T incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const T y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
-  T excl = __shfl_up(incl, 1, kWave);
-  if (lane == 0) excl = T(0);
+  const T incl = wave_incl_scan(v);
+  const T excl = incl - v;
   if (lane == kWave - 1) red[wave] = incl;
   __syncthreads();
   T off = T(0);
@@ -647,14 +641,8 @@ __device__ __forceinline__ float topp_value(uint32_t k) {
 // Exclusive prefix over the workgroup's threads in index order; total = the sum.
 __device__ float topp_scan(float v, float* red, float& total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  float incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const float y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
-  float excl = __shfl_up(incl, 1, kWave);
-  if (lane == 0) excl = 0.0f;
+  const float incl = wave_incl_scan(v);
+  const float excl = incl - v;
   if (lane == kWave - 1) red[wave] = incl;
   __syncthreads();
   float off = 0.0f, tot = 0.0f;
@@ -874,12 +862,7 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
     float c = 0.0f;
     if (lane < kToppCoarse)
       for (int w = 0; w < kToppWaves; ++w) c += s.coarse[w][lane];
-    float incl = c;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const float y = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += y;
-    }
+    const float incl = wave_incl_scan(c);
     const float excl = incl - c;
     const uint64_t hit = __ballot(lane < kToppCoarse && c > 0.0f && incl >= target);
     const uint64_t any = __ballot(lane < kToppCoarse && c > 0.0f);
@@ -908,9 +891,10 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
       const bool in = z[i] > -INFINITY && coarse_of(z[i]) == bc;
       const uint64_t m = __ballot(in);
       if (m == 0ull) continue;
+      const int l0 = __ffsll((unsigned long long)m) - 1;
       int base = 0;
-      if (lane == __ffsll((unsigned long long)m) - 1) base = atomicAdd(&s.ncand, __popcll(m));
-      base = __shfl(base, __ffsll((unsigned long long)m) - 1, kWave);
+      if (lane == l0) base = atomicAdd(&s.ncand, __popcll(m));
+      base = __builtin_amdgcn_readlane(base, l0);
       const int slot = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
       const uint32_t key = topp_key(z[i]);
       if (in) {

@@ -28,23 +28,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave, in DPP lane moves:
-// shifts by 1, 2, 4 and 8 within each row of 16 lanes, then each row's total
-// broadcast into the rows above it.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ uint32_t dpp_add(uint32_t x) {
-  return x + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, kRowMask, 0xF, false);
-}
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int) {
-  x = dpp_add<0x111, 0xF>(x);    // row_shr:1
-  x = dpp_add<0x112, 0xF>(x);    // row_shr:2
-  x = dpp_add<0x114, 0xF>(x);    // row_shr:4
-  x = dpp_add<0x118, 0xF>(x);    // row_shr:8
-  x = dpp_add<0x142, 0xA>(x);    // row_bcast:15 into rows 1 and 3
-  x = dpp_add<0x143, 0xC>(x);    // row_bcast:31 into rows 2 and 3
-  return x;
-}
-
 __device__ __forceinline__ uint32_t popc_below(uint64_t ballot, int lane) {
   return (uint32_t)__popcll(ballot & ((1ull << lane) - 1ull));
 }
@@ -106,7 +89,7 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ scores, int
         c[j] = h[255 - 4 * lane - j];
         tot += c[j];
       }
-      uint32_t above = wave_incl_scan(tot, lane) - tot;   // elements with larger digits
+      uint32_t above = wave_incl_scan(tot) - tot;   // elements with larger digits
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (above < need && above + c[j] >= need) {
@@ -152,7 +135,7 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ scores, int
       // entry e = j*16 + w covers elements (r*4 + j)*1024 + w*64 + [0, 64): index order
       const uint32_t a = lane < kPer * kWaves ? cnt_gt[lane] : 0u;
       const uint32_t b = lane < kPer * kWaves ? cnt_eq[lane] : 0u;
-      const uint32_t ia = wave_incl_scan(a, lane), ib = wave_incl_scan(b, lane);
+      const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
       if (lane < kPer * kWaves) {
         cnt_gt[lane] = base_gt + ia - a;
         cnt_eq[lane] = base_eq + ib - b;
