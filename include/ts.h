@@ -390,8 +390,9 @@ ts_status ts_accept_commit(const int32_t* parent, const int32_t* draft_tok, cons
  *              probability (id order) exceeds u[r]; when rounding leaves
  *              u[r] at or past the end, the last kept id
  * Supported: V in [1, 1048576], T in [0, 1024]. Workspace: at least
- * ts_sample_workspace(R, V) bytes (400 bytes per row and 1024 logits, plus
- * 4 per row), 256-byte aligned, contents ignored on entry.
+ * ts_sample_workspace(R, V) bytes (532 bytes per row and 1024 logits, plus
+ * 65,668 per row: the top-p lists), 256-byte aligned, contents ignored on
+ * entry. Calls that share a workspace must not overlap.
  * ---------------------------------------------------------------------- */
 size_t ts_sample_workspace(int R, int V);   /* 0 on bad sizes */
 

@@ -626,15 +626,22 @@ ts_status ts_sample_tokens(const void* logits, int R, int V, const int32_t* hist
   a.u = u;
   a.tok = tok;
   a.nb = sample_subslices(V);
-  a.sub = static_cast<SampleSub*>(workspace);
+  // the top-p row records first: each on a 128-byte line of its own
+  a.topp_row = static_cast<ToppRow*>(workspace);
+  a.sub = reinterpret_cast<SampleSub*>(a.topp_row + R);
   a.cand = reinterpret_cast<SampleCand*>(a.sub + (size_t)R * a.nb);
   a.wbits = reinterpret_cast<uint32_t*>(a.cand + (size_t)R * a.nb * kSampleList);
   // top-p is off at 1 (every token of non-zero weight has less than the whole
   // weight above it) and under greedy decoding (the maximum always survives)
   a.top_p = top_p;
-  a.topp_cut = top_p < 1.0f && temperature > 0.0f
-                   ? reinterpret_cast<float*>(a.wbits + (size_t)R * a.nb * (kSampleSub / 32))
-                   : nullptr;
+  // (the per-sub-slice bins first: 16-byte aligned for their vector reads)
+  const bool topp = top_p < 1.0f && temperature > 0.0f;
+  a.topp_hist = topp ? reinterpret_cast<float*>(a.wbits + (size_t)R * a.nb * (kSampleSub / 32)) : nullptr;
+  a.topp_above = topp ? a.topp_hist + (size_t)R * a.nb * kToppCoarseBins : nullptr;
+  a.topp_key = topp ? reinterpret_cast<uint32_t*>(a.topp_above + (size_t)R * a.nb) : nullptr;
+  a.topp_id = topp ? reinterpret_cast<int32_t*>(a.topp_key + (size_t)R * kToppCandMax) : nullptr;
+  a.topp_cut = topp ? reinterpret_cast<float*>(a.topp_id + (size_t)R * kToppCandMax) : nullptr;
+  if (!topp) a.topp_row = nullptr;
   return from_hip(launch_sample(a, dtype, stream), fn);
 }
 

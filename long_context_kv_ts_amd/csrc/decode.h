@@ -32,6 +32,8 @@ hipError_t launch_accept_commit(const int32_t* parent, const int32_t* draft_tok,
 // Target-token sampling: per row, the windowed repetition penalty, the
 // temperature, the min-p filter and an inverse-CDF draw from u[row].
 constexpr int kSampleSub = 1024;         // logits per sub-slice (the unit the draw is located in)
+constexpr int kToppCoarseBins = 32;      // top-p coarse bins per sub-slice: powers of two of weight
+constexpr int kToppCandMax = 8192;       // top-p: tokens of a row's crossing coarse bin held in a list
 constexpr int kSampleMaxSubs = 1024;     // sub-slices per row at most (V <= 1048576)
 constexpr int kSampleList = 32;          // kept candidates remembered per sub-slice
 struct SampleSub {                       // summary of one sub-slice
@@ -44,6 +46,15 @@ struct SampleCand {
   float z;                               // penalised logit
   int idx;                               // token id
 };
+struct ToppRow {                         // one top-p row's coarse result, a cache line of its own
+  float Z;                               // largest penalised logit
+  float target;                          // top_p times the row's total weight
+  float above;                           // weight of the coarse bins above the crossing one
+  int bc;                                // the crossing coarse bin (-1: no finite logit)
+  int n;                                 // tokens in the crossing bin (counted by atomics)
+  int pad[27];
+};
+static_assert(sizeof(ToppRow) == 128, "a row record fills one cache line");
 struct SampleArgs {
   const void* logits;         // [R][V]
   int R, V;
@@ -61,6 +72,11 @@ struct SampleArgs {
   const float* u;             // [R] uniforms in [0, 1)
   float top_p;                // nucleus mass (1: off)
   float* topp_cut;            // [R] each row's top-p cut on z (nullptr: top-p off)
+  float* topp_hist;           // [R][nb][32] top-p: each sub-slice's weight per coarse bin
+  float* topp_above;          // [R][nb] top-p: each sub-slice's weight above the crossing bin
+  uint32_t* topp_key;         // [R][kToppCandMax] top-p: keys of the crossing bin's tokens
+  int32_t* topp_id;           // [R][kToppCandMax] and their token ids
+  ToppRow* topp_row;          // [R]
   int32_t* tok;               // [R]
   SampleSub* sub;             // [R][nb]
   SampleCand* cand;           // [R][nb][kSampleList]

@@ -16,8 +16,9 @@
 //   4. the draw: the smallest token id whose cumulative weight exceeds
 //      u[r] * sum(w). tau = 0 is greedy: the first token with z_i == Z.
 //
-// Rows are cut into sub-slices of 1024 logits. Two launches, one read of the
-// logits (a second only for sub-slices that keep many tokens under min-p):
+// Rows are cut into sub-slices of 1024 logits. Without top-p, two launches
+// and one read of the logits (a second only for sub-slices that keep many
+// tokens under min-p):
 //   A. grid (workgroups per row, rows), kNT threads, kPW sub-slices a wave: a
 //      workgroup issues the window's few loads, then every logits load of its
 //      waves (16 logits a lane per sub-slice, held raw in registers), and
@@ -27,10 +28,18 @@
 //      ballots: the maximum m, the kept weight relative to m at the
 //      sub-slice's own cut m + cut, and the kept tokens themselves while there
 //      are at most 32 (weights and list entries only for those).
-//   T. (top-p only) grid (rows): each row's z* by a weighted radix select over
-//      the row's logits, written to the workspace;
-//   B. grid (rows): the row maximum Z gives the row's cut Z + cut >= m + cut
-//      (raised to z* under top-p),
+//   H. (top-p only) grid (workgroups per row, rows), one sub-slice a wave: the
+//      weight of the sub-slice's tokens in each of 32 coarse bins below the
+//      row maximum (powers of two of weight);
+//   C. (top-p only) grid (rows): the bin totals in a fixed order, the bin where
+//      the cumulative weight crosses top_p * W, and each sub-slice's weight
+//      above it;
+//   E. (top-p only) grid (workgroups per row, rows): the crossing bin's tokens
+//      into a per-row list (sub-slices whose maximum lies below it are not
+//      read);
+//   T. (top-p only) grid (rows): z* by key passes over that list, the kept
+//      weight of every sub-slice and the draw, in place of B;
+//   B. grid (rows): the row maximum Z gives the row's cut Z + cut >= m + cut,
 //      so a listed sub-slice's kept tokens are all in its list; with min-p off
 //      (cut = -inf) the sub-slice sum rescales exactly by 2^((m - Z) s2). A
 //      sub-slice with more than 32 kept tokens and min-p on is read again, one
@@ -599,34 +608,37 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-p rows (top_p < 1, tau > 0): one 1024-thread workgroup per row finds the
-// row's cut and draws the token itself, in place of the pick kernel.
+// Top-p rows (top_p < 1, tau > 0): four launches after the scan find each
+// row's cut and draw the token, in place of the pick kernel.
 //   * Z and the total weight W = sum 2^((z - Z) s2) come from the scan's
 //     sub-slice summaries.
 //   * The cut z* -- the value at which the weight at or above it first
 //     reaches top_p * W -- by a weighted select from the largest z down.
-//     Pass 0 sums the weight of every token into one of 32 bins, a power of
-//     two of weight each below the maximum (the last bin takes everything
-//     further down); every thread keeps its own row of bins in LDS, so the
-//     pass needs no atomics. The bin where the cumulative weight crosses
-//     top_p * W is usually narrow: a second pass copies its tokens' keys
-//     into LDS (ballot-compacted, one slot reservation per wave), and key
-//     passes over them cut their key range into 2048 sub-ranges until one
-//     key is left. A bin with more tokens than LDS holds (nearly flat
-//     logits) runs the key passes over the row instead.
-//   * The row's cut is the larger of z* and the min-p cut. A last pass sums
-//     the kept weight of every 1024-logit sub-slice (four waves a sub-slice,
-//     added in a fixed order); a scan finds the sub-slice the draw
+//     The coarse step is spread over the grid: every sub-slice's weight in
+//     each of 32 bins, a power of two of weight each below the maximum (the
+//     last bin takes everything further down). One workgroup a row adds
+//     them up and finds the bin where the cumulative weight crosses
+//     top_p * W, which is usually narrow; its tokens' keys and ids go to a
+//     per-row list, again over the grid. Key passes over the list (in LDS)
+//     cut its key range into 2048 sub-ranges until one key is left. A bin
+//     with more tokens than the list holds (nearly flat logits) runs the key
+//     passes over the row instead.
+//   * The row's cut is the larger of z* and the min-p cut. The kept weight of
+//     every 1024-logit sub-slice: when the cut is z* and the crossing bin's
+//     tokens are all listed, its bins above the crossing one plus its listed
+//     tokens at or above z*; else a pass over the row (four waves a
+//     sub-slice, added in a fixed order). A scan finds the sub-slice the draw
 //     u * (kept weight) falls in, and a scan over its 1024 tokens the token.
 // Every pass over the row loads a thread's next eight 4-token groups before
 // using any (a group past the row reloads the last one and is masked). The
-// weights are summed in fp32 in an unspecified order, so a cut within
-// rounding of a cumulative boundary may come out one value either side.
+// list's order and the key passes' LDS sums follow the order in which
+// atomics land, so a cut within rounding of a cumulative boundary may come
+// out one value either side, and may differ between calls.
 constexpr int kToppThreads = 1024;
 constexpr int kToppWaves = kToppThreads / kWave;
 constexpr int kToppBins = 2048;           // key-pass bins
-constexpr int kToppCoarse = 32;           // pass-0 bins: powers of two of weight
-constexpr int kToppCand = 16384;          // keys of the crossing bin held in LDS
+constexpr int kToppCoarse = kToppCoarseBins;   // pass-0 bins: powers of two of weight
+constexpr int kToppCand = kToppCandMax;   // keys (and token ids) of the crossing bin held in LDS
 constexpr int kToppBatch = 8;             // 4-token groups a thread loads at once
 
 __device__ __forceinline__ uint32_t topp_key(float f) {
@@ -731,22 +743,39 @@ __device__ __forceinline__ void topp_visit(int V, float theta, float inv_theta, 
 }
 
 struct ToppLds {
-  union {
-    float ph[kToppThreads][kToppCoarse + 1];   // pass 0: each thread's bins (padded row)
-    struct {
-      float hw[kToppBins];                   // key passes: weight per bin
-      uint32_t kmn[kToppBins], kmx[kToppBins];   // smallest and largest key per bin (none: ~0 and 0)
-      uint32_t cand[kToppCand];              // keys of the crossing bin
-    } k;
-    float part[4 * kSampleMaxSubs];        // kept weight of each sub-slice, per wave quarter
-  } u;
-  float coarse[kToppWaves][kToppCoarse];
+  float hw[kToppBins];                   // key passes: weight per bin
+  uint32_t kmn[kToppBins], kmx[kToppBins];   // smallest and largest key per bin (none: ~0 and 0)
+  uint32_t cand[kToppCand];              // keys of the crossing bin
+  int32_t cid[kToppCand];                // and their token ids
+  float part[4 * kSampleMaxSubs];        // kept weight of each sub-slice, in four parts
   float red[kToppWaves];
   float above;                           // weight above the current range
-  uint32_t lo, hi;                       // the current key range
-  int sel, last, ncand;
+  uint32_t lo, hi;                       // the crossing bin's key range
+  int sel, last;
   int win, lastk;
 };
+
+// Coarse bin of z below the row maximum Z: whole powers of two of weight
+// (the last bin takes everything further down). Every kernel bins with this.
+__device__ __forceinline__ int topp_coarse(float z, float Z, float s2) {
+  const float d = (Z - z) * s2;
+  return d < (float)(kToppCoarse - 1) ? (int)d : kToppCoarse - 1;
+}
+
+// The lane's 16 penalised logits of sub-slice b of row r, with the window
+// bits the scan stored.
+template <typename Tin, bool kVec>
+__device__ __forceinline__ void topp_sub_z(const SampleArgs& a, int r, int b, int lane, float (&z)[kPL]) {
+  const Tin* row = static_cast<const Tin*>(a.logits) + (int64_t)r * a.V;
+  const int base = b * kSampleSub;
+  const uint32_t* bits = a.wbits + ((int64_t)r * a.nb + b) * (kSampleSub / 32);
+  SubRaw<Tin> raw;
+  fetch_sub<Tin, kVec>(row, base, a.V, lane, raw);
+  if (base + kSampleSub <= a.V)
+    sub_values<Tin, kVec, true>(row, base, base, a, lane, raw, bits, z);
+  else
+    sub_values<Tin, kVec, false>(row, base, base, a, lane, raw, bits, z);
+}
 
 // Among the 2048 key bins (in order of decreasing z), the first whose
 // cumulative weight (after s.above) reaches `target`, else the last non-empty
@@ -759,10 +788,10 @@ __device__ int topp_select(ToppLds& s, float target) {
   }
   const float above0 = s.above;
   const int b0 = 2 * tid, b1 = 2 * tid + 1;
-  const float c0 = s.u.k.hw[b0], c1 = s.u.k.hw[b1];
+  const float c0 = s.hw[b0], c1 = s.hw[b1];
   // a bin holds tokens iff its smallest key is set (every token of the
   // crossing coarse bin has a positive weight: they are within a factor 2)
-  const bool n0 = s.u.k.kmn[b0] != 0xFFFFFFFFu, n1 = s.u.k.kmn[b1] != 0xFFFFFFFFu;
+  const bool n0 = s.kmn[b0] != 0xFFFFFFFFu, n1 = s.kmn[b1] != 0xFFFFFFFFu;
   float tot;
   const float run = above0 + topp_scan(c0 + c1, s.red, tot);   // its barriers order the init above
   float my_above = 0.0f;
@@ -788,9 +817,9 @@ __device__ int topp_select(ToppLds& s, float target) {
 
 __device__ __forceinline__ void topp_clear_keys(ToppLds& s) {
   for (int b = threadIdx.x; b < kToppBins; b += kToppThreads) {
-    s.u.k.hw[b] = 0.0f;
-    s.u.k.kmn[b] = 0xFFFFFFFFu;
-    s.u.k.kmx[b] = 0u;
+    s.hw[b] = 0.0f;
+    s.kmn[b] = 0xFFFFFFFFu;
+    s.kmx[b] = 0u;
   }
 }
 
@@ -800,122 +829,223 @@ __device__ __forceinline__ void topp_key_bin(ToppLds& s, uint32_t key, float Z, 
                                              int shift) {
   if (key < lo || key > hi) return;
   const int b = kToppBins - 1 - (int)((key - lo) >> shift);
-  atomicAdd(&s.u.k.hw[b], __builtin_amdgcn_exp2f((topp_value(key) - Z) * s2));
-  atomicMin(&s.u.k.kmn[b], key);
-  atomicMax(&s.u.k.kmx[b], key);
+  atomicAdd(&s.hw[b], __builtin_amdgcn_exp2f((topp_value(key) - Z) * s2));
+  atomicMin(&s.kmn[b], key);
+  atomicMax(&s.kmx[b], key);
 }
 
-template <typename Tin, bool kVec>
-__global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a) {
-  __shared__ ToppLds s;
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const Tin* row = static_cast<const Tin*>(a.logits) + (int64_t)r * a.V;
-  const uint32_t* bits = a.wbits + (int64_t)r * a.nb * (kSampleSub / 32);
-  const int V = a.V;
-  const int ngroups = (V + 3) / 4;
-  const float th = a.theta, ith = a.inv_theta;
+// H: each sub-slice's weight in every coarse bin, one sub-slice a wave. A
+// lane adds its tokens' weights 2^((z - Z) s2) into its own LDS row of bins
+// (plain read-modify-write: LDS float atomics run about a lane a cycle); the
+// wave then adds each column over the 64 rows in a fixed order.
+constexpr int kHistWaves = 4;
 
-  // the row maximum and total weight from the sub-slice summaries (nb <= 1024)
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kHistWaves * kWave) void sample_topp_hist_kernel(SampleArgs a) {
+  __shared__ float ph[kHistWaves][kWave][kToppCoarse + 1];
+  __shared__ float red[kHistWaves];
+  const int r = blockIdx.y, lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int b = blockIdx.x * kHistWaves + wave;
+  // the row maximum Z from the sub-slice summaries
+  float m = -INFINITY;
+  for (int q = threadIdx.x; q < a.nb; q += kHistWaves * kWave) m = fmaxf(m, a.sub[(int64_t)r * a.nb + q].m);
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  float Z = red[0];
+#pragma unroll
+  for (int w = 1; w < kHistWaves; ++w) Z = fmaxf(Z, red[w]);
+  if (b >= a.nb) return;                 // past the only barrier
+  float* mine = ph[wave][lane];
+#pragma unroll
+  for (int c = 0; c < kToppCoarse; ++c) mine[c] = 0.0f;
+  if (Z > -INFINITY) {
+    float z[kPL];
+    topp_sub_z<Tin, kVec>(a, r, b, lane, z);
+#pragma unroll
+    for (int e = 0; e < kPL; ++e)
+      if (z[e] > -INFINITY) mine[topp_coarse(z[e], Z, a.s2)] += __builtin_amdgcn_exp2f((z[e] - Z) * a.s2);
+  }
+  // the wave's own rows only: its LDS operations complete in order
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // column c = lane % 32 over rows 32h .. 32h + 31 (h = lane / 32), then the halves
+  const int c = lane & (kToppCoarse - 1), h = lane >> 5;
+  float t = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) t += ph[wave][32 * h + j][c];
+  t += __shfl_xor(t, 32, kWave);
+  if (lane < kToppCoarse) a.topp_hist[((int64_t)r * a.nb + b) * kToppCoarse + lane] = t;
+}
+
+// C: one workgroup a row. Z and the total weight W from the sub-slice
+// summaries; the coarse bin totals (each wave adds its 64 sub-slices, then
+// the waves in order); the crossing bin bc, the first whose cumulative weight
+// reaches top_p * W (else the last non-empty one), and the weight above it;
+// each sub-slice's weight in the bins above bc. Also resets the row's
+// candidate count for the extract kernel.
+__global__ __launch_bounds__(kToppThreads) void sample_topp_coarse_kernel(SampleArgs a) {
+  __shared__ float ph[kToppThreads][kToppCoarse + 1];
+  __shared__ float coarse[kToppWaves][kToppCoarse];
+  __shared__ float red[kToppWaves];
+  __shared__ int sel;
+  __shared__ float above;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   SampleSub sb = SampleSub{-INFINITY, 0.0f, 0, 0.0f};
   if (tid < a.nb) sb = a.sub[(int64_t)r * a.nb + tid];
   const float vmax = wave_max(sb.m);
-  if (lane == 0) s.red[wave] = vmax;
+  if (lane == 0) red[wave] = vmax;
   __syncthreads();
-  float Z = s.red[0];
+  float Z = red[0];
 #pragma unroll
-  for (int w = 1; w < kToppWaves; ++w) Z = fmaxf(Z, s.red[w]);
+  for (int w = 1; w < kToppWaves; ++w) Z = fmaxf(Z, red[w]);
   __syncthreads();
   float W;
-  topp_scan(sb.m > -INFINITY ? sb.wall * __builtin_amdgcn_exp2f((sb.m - Z) * a.s2) : 0.0f, s.red, W);
+  topp_scan(sb.m > -INFINITY ? sb.wall * __builtin_amdgcn_exp2f((sb.m - Z) * a.s2) : 0.0f, red, W);
+  ToppRow* row = a.topp_row + r;
   if (!(Z > -INFINITY)) {                // no finite logit in the row (outside the contract)
-    if (tid == 0) a.tok[r] = -1;
+    if (tid == 0) *row = ToppRow{Z, 0.0f, 0.0f, -1, 0, {}};
     return;
   }
   const float target = a.top_p * W;
-  auto coarse_of = [&](float z) -> int {   // pass-0 bin: whole powers of two below the maximum
-    const float d = (Z - z) * a.s2;
-    return d < (float)(kToppCoarse - 1) ? (int)d : kToppCoarse - 1;
-  };
-
-  // ---- pass 0: each thread's own coarse bins ---------------------------------
+  // this thread's sub-slice's bins, kept for the weight above bc
+  float hb[kToppCoarse];
+  if (tid < a.nb) {
+    const float4* src = reinterpret_cast<const float4*>(a.topp_hist + ((int64_t)r * a.nb + tid) * kToppCoarse);
 #pragma unroll
-  for (int b = 0; b < kToppCoarse; ++b) s.u.ph[tid][b] = 0.0f;
-  if (tid == 0) {
-    s.above = 0.0f;
-    s.ncand = 0;
+    for (int q = 0; q < kToppCoarse / 4; ++q) {
+      const float4 v = src[q];
+      hb[4 * q] = v.x; hb[4 * q + 1] = v.y; hb[4 * q + 2] = v.z; hb[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kToppCoarse; ++q) hb[q] = 0.0f;
   }
-  topp_visit<Tin, kVec>(V, th, ith, row, bits, ngroups, [&](int, const float (&z)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (z[i] > -INFINITY) s.u.ph[tid][coarse_of(z[i])] += __builtin_amdgcn_exp2f((z[i] - Z) * a.s2);
-  });
+  for (int q = 0; q < kToppCoarse; ++q) ph[tid][q] = hb[q];
+  if (tid == 0) above = 0.0f;
   __syncthreads();
-  // bin totals: lane b < 32 of each wave adds its wave's 64 rows, then wave 0 the 16 waves
   if (lane < kToppCoarse) {
     float t = 0.0f;
-    for (int j = 0; j < kWave; ++j) t += s.u.ph[wave * kWave + j][lane];
-    s.coarse[wave][lane] = t;
+#pragma unroll 16
+    for (int j = 0; j < kWave; ++j) t += ph[wave * kWave + j][lane];
+    coarse[wave][lane] = t;
   }
   __syncthreads();
-  int bc = -1;                           // the crossing coarse bin
   if (wave == 0) {
     float c = 0.0f;
     if (lane < kToppCoarse)
-      for (int w = 0; w < kToppWaves; ++w) c += s.coarse[w][lane];
+      for (int w = 0; w < kToppWaves; ++w) c += coarse[w][lane];
     const float incl = wave_incl_scan(c);
     const float excl = incl - c;
     const uint64_t hit = __ballot(lane < kToppCoarse && c > 0.0f && incl >= target);
     const uint64_t any = __ballot(lane < kToppCoarse && c > 0.0f);
     const int src = hit ? __ffsll((unsigned long long)hit) - 1 : (any ? 63 - __clzll((unsigned long long)any) : -1);
-    if (lane == 0) s.sel = src;
-    if (src >= 0 && lane == src) s.above = excl;
+    if (lane == 0) sel = src;
+    if (src >= 0 && lane == src) above = excl;
   }
   __syncthreads();
-  bc = s.sel;
-  __syncthreads();
-  if (bc < 0) {                          // nothing finite (cannot happen past the check above)
+  const int bc = sel;
+  if (tid < a.nb) {
+    float w = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kToppCoarse; ++q) w += q < bc ? hb[q] : 0.0f;
+    a.topp_above[(int64_t)r * a.nb + tid] = w;
+  }
+  if (tid == 0) *row = ToppRow{Z, target, above, bc, 0, {}};
+}
+
+// E: the tokens of the crossing bin, one sub-slice a wave: their keys and ids
+// into the row's candidate list (one slot reservation a wave, ballot-
+// compacted; slots past the list's capacity are counted, not stored). A
+// sub-slice whose maximum lies in a lower bin (less weight) has none of them
+// and is not read.
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kHistWaves * kWave) void sample_topp_extract_kernel(SampleArgs a) {
+  const int r = blockIdx.y, lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int b = blockIdx.x * kHistWaves + wave;
+  ToppRow* row = a.topp_row + r;
+  const int bc = row->bc;
+  if (b >= a.nb || bc < 0) return;
+  const float Z = row->Z;
+  const float mb = a.sub[(int64_t)r * a.nb + b].m;
+  if (!(mb > -INFINITY) || topp_coarse(mb, Z, a.s2) > bc) return;
+  float z[kPL];
+  topp_sub_z<Tin, kVec>(a, r, b, lane, z);
+  uint64_t in[kPL];
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < kPL; ++e) {
+    in[e] = __ballot(z[e] > -INFINITY && topp_coarse(z[e], Z, a.s2) == bc);
+    cnt += __popcll(in[e]);
+  }
+  if (cnt == 0) return;                  // uniform across the wave
+  int base = 0;
+  if (lane == 0) base = atomicAdd(&row->n, cnt);
+  base = __builtin_amdgcn_readfirstlane(base);
+  uint32_t* keys = a.topp_key + (int64_t)r * kToppCand;
+  int32_t* ids = a.topp_id + (int64_t)r * kToppCand;
+  int off = 0;
+#pragma unroll
+  for (int e = 0; e < kPL; ++e) {
+    const uint64_t m = in[e];
+    if (m == 0ull) continue;
+    if ((m >> lane) & 1ull) {
+      const int slot = base + off + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (slot < kToppCand) {
+        keys[slot] = topp_key(z[e]);
+        ids[slot] = token_of<Tin>(b * kSampleSub, e, lane);
+      }
+    }
+    off += __popcll(m);
+  }
+}
+
+// T: one 1024-thread workgroup a row: the crossing bin's candidates into LDS,
+// the key passes down to z*, the kept weight of every sub-slice, the draw.
+template <typename Tin, bool kVec>
+__global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a) {
+  __shared__ ToppLds s;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const Tin* row = static_cast<const Tin*>(a.logits) + (int64_t)r * a.V;
+  const uint32_t* bits = a.wbits + (int64_t)r * a.nb * (kSampleSub / 32);
+  const int V = a.V;
+  const int ngroups = (V + 3) / 4;
+  const float th = a.theta, ith = a.inv_theta;
+  const ToppRow rw = a.topp_row[r];
+  // no finite logit, or (cannot happen: the crossing bin has weight) no token in it
+  if (rw.bc < 0 || rw.n == 0) {
     if (tid == 0) a.tok[r] = -1;
     return;
   }
-
-  // ---- the crossing bin's keys into LDS, ballot-compacted --------------------
+  const float Z = rw.Z, target = rw.target;
+  const int bc = rw.bc, n = rw.n;
+  // the held candidates and their key range; a crowded bin starts from the
+  // whole key range (three 11-bit passes still end on one key)
   if (tid == 0) {
-    s.lo = 0xFFFFFFFFu;
-    s.hi = 0u;
+    s.above = rw.above;
+    s.lo = n <= kToppCand ? 0xFFFFFFFFu : 0u;
+    s.hi = n <= kToppCand ? 0u : 0xFFFFFFFFu;
   }
   __syncthreads();
-  uint32_t kmin_own = 0xFFFFFFFFu, kmax_own = 0u;
-  topp_visit<Tin, kVec>(V, th, ith, row, bits, ngroups, [&](int, const float (&z)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool in = z[i] > -INFINITY && coarse_of(z[i]) == bc;
-      const uint64_t m = __ballot(in);
-      if (m == 0ull) continue;
-      const int l0 = __ffsll((unsigned long long)m) - 1;
-      int base = 0;
-      if (lane == l0) base = atomicAdd(&s.ncand, __popcll(m));
-      base = __builtin_amdgcn_readlane(base, l0);
-      const int slot = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint32_t key = topp_key(z[i]);
-      if (in) {
-        if (slot < kToppCand) s.u.k.cand[slot] = key;
-        kmin_own = min(kmin_own, key);
-        kmax_own = max(kmax_own, key);
-      }
+  if (n <= kToppCand) {
+    const uint32_t* keys = a.topp_key + (int64_t)r * kToppCand;
+    const int32_t* ids = a.topp_id + (int64_t)r * kToppCand;
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    for (int i = tid; i < n; i += kToppThreads) {
+      const uint32_t key = keys[i];
+      s.cand[i] = key;
+      s.cid[i] = ids[i];
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
     }
-  });
-  // the crossing bin's key range: the key passes start from it
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmin_own = min(kmin_own, (uint32_t)__shfl_xor((int)kmin_own, o, kWave));
-    kmax_own = max(kmax_own, (uint32_t)__shfl_xor((int)kmax_own, o, kWave));
-  }
-  if (lane == 0) {
-    atomicMin(&s.lo, kmin_own);
-    atomicMax(&s.hi, kmax_own);
+    kmin = wave_all(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+    kmax = wave_all(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
+    if ((tid & (kWave - 1)) == 0) {
+      atomicMin(&s.lo, kmin);
+      atomicMax(&s.hi, kmax);
+    }
   }
   __syncthreads();
-  const int n = s.ncand;
   uint32_t lo = s.lo, hi = s.hi;
   bool done = lo == hi;
   for (int pass = 0; pass < 3 && !done; ++pass) {
@@ -924,19 +1054,19 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
     topp_clear_keys(s);
     __syncthreads();
     if (n <= kToppCand) {
-      for (int i = tid; i < n; i += kToppThreads) topp_key_bin(s, s.u.k.cand[i], Z, a.s2, lo, hi, shift);
+      for (int i = tid; i < n; i += kToppThreads) topp_key_bin(s, s.cand[i], Z, a.s2, lo, hi, shift);
     } else {
       // a crowded bin (nearly flat logits): the key passes read the row
       topp_visit<Tin, kVec>(V, th, ith, row, bits, ngroups, [&](int, const float (&z)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (z[i] > -INFINITY && coarse_of(z[i]) == bc) topp_key_bin(s, topp_key(z[i]), Z, a.s2, lo, hi, shift);
+          if (z[i] > -INFINITY && topp_coarse(z[i], Z, a.s2) == bc) topp_key_bin(s, topp_key(z[i]), Z, a.s2, lo, hi, shift);
       });
     }
     __syncthreads();
     const int d = topp_select(s, target);
-    lo = s.u.k.kmn[d];
-    hi = s.u.k.kmx[d];
+    lo = s.kmn[d];
+    hi = s.kmx[d];
     done = lo == hi;
     __syncthreads();
   }
@@ -945,7 +1075,7 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
   if (tid == 0) a.topp_cut[r] = zstar;
 
   // ---- the kept weight of every sub-slice at the row's cut ------------------
-  for (int q = tid; q < 4 * a.nb; q += kToppThreads) s.u.part[q] = 0.0f;
+  for (int q = tid; q < 4 * a.nb; q += kToppThreads) s.part[q] = 0.0f;
   if (tid == 0) {
     s.win = INT32_MAX;
     s.lastk = -1;
@@ -953,19 +1083,33 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
     s.last = -1;
   }
   __syncthreads();
-  topp_visit<Tin, kVec>(V, th, ith, row, bits, ngroups, [&](int k, const float (&z)[4]) {
-    float acc = 0.0f;
+  if (thr == zstar && n <= kToppCand) {
+    // the cut is z* (min-p does not bind) and every token of the crossing bin
+    // is a held candidate: a sub-slice keeps its weight in the bins above the
+    // crossing one and its candidates at or above z* (keys are
+    // order-preserving: key >= lo)
+    for (int q = tid; q < a.nb; q += kToppThreads) s.part[4 * q] = a.topp_above[(int64_t)r * a.nb + q];
+    for (int i = tid; i < n; i += kToppThreads) {
+      const uint32_t key = s.cand[i];
+      if (key >= lo)
+        atomicAdd(&s.part[4 * (s.cid[i] / kSampleSub) + 1], __builtin_amdgcn_exp2f((topp_value(key) - Z) * a.s2));
+    }
+  } else {
+    const int wave = tid >> 6, lane = tid & (kWave - 1);
+    topp_visit<Tin, kVec>(V, th, ith, row, bits, ngroups, [&](int k, const float (&z)[4]) {
+      float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (z[i] > -INFINITY && z[i] >= thr) acc += __builtin_amdgcn_exp2f((z[i] - Z) * a.s2);
-    acc = wave_sum(acc);
-    // a wave's 64 groups are 256 tokens of sub-slice 4k + wave/4
-    const int q = 4 * k + (wave >> 2);
-    if (lane == 0 && q < a.nb) s.u.part[4 * q + (wave & 3)] = acc;
-  });
+      for (int i = 0; i < 4; ++i)
+        if (z[i] > -INFINITY && z[i] >= thr) acc += __builtin_amdgcn_exp2f((z[i] - Z) * a.s2);
+      acc = wave_sum(acc);
+      // a wave's 64 groups are 256 tokens of sub-slice 4k + wave/4
+      const int q = 4 * k + (wave >> 2);
+      if (lane == 0 && q < a.nb) s.part[4 * q + (wave & 3)] = acc;
+    });
+  }
   __syncthreads();
   float c = 0.0f;
-  if (tid < a.nb) c = (s.u.part[4 * tid] + s.u.part[4 * tid + 1]) + (s.u.part[4 * tid + 2] + s.u.part[4 * tid + 3]);
+  if (tid < a.nb) c = (s.part[4 * tid] + s.part[4 * tid + 1]) + (s.part[4 * tid + 2] + s.part[4 * tid + 3]);
   float total;
   const float excl = topp_scan(c, s.red, total);
   const float target2 = a.u[r] * total;
@@ -1013,7 +1157,18 @@ hipError_t launch_t(const SampleArgs& a, hipStream_t st) {
   else
     sample_scan_kernel<Tin, kNT, kPW, false><<<grid, kNT, 0, st>>>(a);
   if (a.topp_cut != nullptr) {
-    // top-p rows: the cut and the draw in one kernel
+    // top-p rows: the coarse bins over the grid, the crossing bin per row,
+    // its tokens over the grid, then the cut and the draw per row
+    const dim3 hgrid((a.nb + kHistWaves - 1) / kHistWaves, a.R);
+    if (vec)
+      sample_topp_hist_kernel<Tin, true><<<hgrid, kHistWaves * kWave, 0, st>>>(a);
+    else
+      sample_topp_hist_kernel<Tin, false><<<hgrid, kHistWaves * kWave, 0, st>>>(a);
+    sample_topp_coarse_kernel<<<a.R, kToppThreads, 0, st>>>(a);
+    if (vec)
+      sample_topp_extract_kernel<Tin, true><<<hgrid, kHistWaves * kWave, 0, st>>>(a);
+    else
+      sample_topp_extract_kernel<Tin, false><<<hgrid, kHistWaves * kWave, 0, st>>>(a);
     if (vec)
       sample_topp_kernel<Tin, true><<<a.R, kToppThreads, 0, st>>>(a);
     else
@@ -1033,7 +1188,8 @@ int sample_subslices(int V) { return V < 1 ? 1 : (V + kSampleSub - 1) / kSampleS
 size_t sample_workspace_bytes(int R, int V) {
   const size_t n = (size_t)R * sample_subslices(V);
   return n * sizeof(SampleSub) + n * kSampleList * sizeof(SampleCand) + n * (kSampleSub / 32) * sizeof(uint32_t) +
-         (size_t)R * sizeof(float);
+         (size_t)R * sizeof(float) + n * (kToppCoarse + 1) * sizeof(float) +
+         (size_t)R * kToppCand * (sizeof(uint32_t) + sizeof(int32_t)) + (size_t)R * sizeof(ToppRow);
 }
 
 hipError_t launch_sample(const SampleArgs& a, ts_dtype dtype, hipStream_t s) {
