@@ -28,15 +28,13 @@
 //      ballots: the maximum m, the kept weight relative to m at the
 //      sub-slice's own cut m + cut, and the kept tokens themselves while there
 //      are at most 32 (weights and list entries only for those).
-//   H. (top-p only) grid (workgroups per row, rows), one sub-slice a wave: the
-//      weight of the sub-slice's tokens in each of 32 coarse bins below the
-//      row maximum (powers of two of weight);
+//   (top-p rows: the scan also bins each sub-slice's weight into 32 coarse
+//   bins on a fixed lattice of levels, powers of two of weight)
 //   C. (top-p only) grid (rows): the bin totals in a fixed order, the bin where
 //      the cumulative weight crosses top_p * W, and each sub-slice's weight
 //      above it;
 //   E. (top-p only) grid (workgroups per row, rows): the crossing bin's tokens
-//      into a per-row list (sub-slices whose maximum lies below it are not
-//      read);
+//      into a per-row list (sub-slices with no weight in it are not read);
 //   T. (top-p only) grid (rows): z* by key passes over that list, the kept
 //      weight of every sub-slice and the draw, in place of B;
 //   B. grid (rows): the row maximum Z gives the row's cut Z + cut >= m + cut,
@@ -60,12 +58,19 @@ constexpr int kPT = kSampleSub / kThreads;              // logits a thread per s
 constexpr int kMaxScanSubs = 64;                        // sub-slices a scanning workgroup, at most
 constexpr int kPerT = kSampleMaxSubs / kThreads;        // sub-slices a picking thread, at most
 
-template <int kWords>
+template <int kWords, int kBinWaves = 0>
 struct Lds {
   uint32_t bits[kWords];                    // windowed tokens of [i0, i1)
-  int par[TS_MAX_DRAFT], dtok[TS_MAX_DRAFT];
-  int path[TS_MAX_DRAFT];                   // draft tokens on the root path, leaf first
-  int path_len;
+  // the window's forest and path are dead once the bitmap is built (a barrier
+  // ends the marking), so top-p rows' coarse bins reuse their space
+  union {
+    struct {
+      int par[TS_MAX_DRAFT], dtok[TS_MAX_DRAFT];
+      int path[TS_MAX_DRAFT];               // draft tokens on the root path, leaf first
+      int path_len;
+    };
+    float bins[kBinWaves][kWave][kToppCoarseBins + 1];   // top-p: each lane's coarse bins (padded row)
+  };
 };
 
 struct BlockRed {
@@ -263,11 +268,27 @@ __device__ __forceinline__ T wave_all(T v, Op op) {
 __device__ __forceinline__ float wave_all_max(float v) { return wave_all(v, [](float x, float y) { return fmaxf(x, y); }); }
 __device__ __forceinline__ float wave_all_sum(float v) { return wave_all(v, [](float x, float y) { return x + y; }); }
 
+// Top-p coarse bins lie on a fixed lattice: token z is on level floor(-z s2)
+// (clamped to +-2^29, so that differences fit an int), and its bin below a
+// maximum on level l is min(level - l, 31) -- whole powers of two of weight,
+// the last bin taking everything further down. A sub-slice bins its tokens
+// below its own maximum; since levels are absolute, shifting its bins by the
+// level difference to the row maximum gives exactly the row's binning.
+__device__ __forceinline__ int topp_level(float z, float s2) {
+  return (int)floorf(fminf(fmaxf(-z * s2, -536870912.0f), 536870912.0f));
+}
+__device__ __forceinline__ int topp_bin(float z, int top_level, float s2) {
+  return min(topp_level(z, s2) - top_level, kToppCoarseBins - 1);
+}
+
 // Summary of sub-slice b (at `base`) by one wave: m, the kept weight relative
 // to m at the cut m + cut, the count n, and the kept tokens when n <= 32.
-template <typename Tin, bool kVec, bool kFull, typename L>
+// Top-p rows instead: m, the weight of every finite token relative to m, and
+// the sub-slice's coarse bins (each lane adds its tokens' weights into its own
+// LDS row; the wave adds the columns in a fixed order).
+template <typename Tin, bool kVec, bool kFull, bool kTopp, typename L>
 __device__ __forceinline__ void summarise(const SampleArgs& a, const Tin* row, int r, int b, int i0, int lane,
-                                          SubRaw<Tin>& raw, const L& s) {
+                                          SubRaw<Tin>& raw, L& s) {
   const int base = b * kSampleSub;
   float z[kPL];
   sub_values<Tin, kVec, kFull>(row, base, i0, a, lane, raw, s.bits, z);
@@ -275,6 +296,35 @@ __device__ __forceinline__ void summarise(const SampleArgs& a, const Tin* row, i
 #pragma unroll
   for (int e = 1; e < kPL; ++e) m = fmaxf(m, z[e]);
   m = wave_all_max(m);
+  if constexpr (kTopp) {
+    float* mine = s.bins[threadIdx.x >> 6][lane];
+#pragma unroll
+    for (int c = 0; c < kToppCoarseBins; ++c) mine[c] = 0.0f;
+    float wall = 0.0f;
+    if (m > -INFINITY) {
+      const int lm = topp_level(m, a.s2);
+#pragma unroll
+      for (int e = 0; e < kPL; ++e) {
+        // no branch: -inf adds 0 to bin 0, which changes nothing
+        const bool fin = z[e] > -INFINITY;
+        const float w = fin ? __builtin_amdgcn_exp2f((z[e] - m) * a.s2) : 0.0f;
+        wall += w;
+        mine[fin ? topp_bin(z[e], lm, a.s2) : 0] += w;
+      }
+    }
+    wall = wave_all_sum(wall);
+    // the wave's own rows only: its LDS operations complete in order
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // column c = lane % 32 over rows 32h .. 32h + 31 (h = lane / 32), then the halves
+    const int c = lane & (kToppCoarseBins - 1), h = lane >> 5;
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) t += s.bins[threadIdx.x >> 6][32 * h + j][c];
+    t += __shfl_xor(t, 32, kWave);
+    if (lane < kToppCoarseBins) a.topp_hist[((int64_t)r * a.nb + b) * kToppCoarseBins + lane] = t;
+    if (lane == 0) a.sub[r * a.nb + b] = SampleSub{m, 0.0f, 0, wall};
+    return;
+  }
   // kept: z >= m + cut, never -inf (the floor -FLT_MAX stands in for cut = -inf)
   const float thr = fmaxf(m + a.cut, -FLT_MAX);
   uint64_t kept[kPL];
@@ -350,11 +400,12 @@ __device__ T block_excl_scan(T v, T* red, T& total) {
   return off + excl;
 }
 
-template <typename Tin, int kNT, int kPW, bool kVec>
-__global__ __launch_bounds__(kNT) void sample_scan_kernel(SampleArgs a) {
+// (top-p: at most 128 VGPRs, so that four workgroups of 256 fit a CU, as their LDS does)
+template <typename Tin, int kNT, int kPW, bool kVec, bool kTopp>
+__global__ __launch_bounds__(kNT, kTopp ? 4 : 1) void sample_scan_kernel(SampleArgs a) {
   constexpr int kW = kNT / kWave;
   static_assert(kW * kPW <= kMaxScanSubs, "sub-slices a workgroup");
-  __shared__ Lds<kW * kPW * kSampleSub / 32> s;
+  __shared__ Lds<kW * kPW * kSampleSub / 32, kTopp ? kW : 0> s;
   const int r = blockIdx.y, lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int b0 = blockIdx.x * (kW * kPW), b1 = min(a.nb, b0 + kW * kPW);
   const int i0 = b0 * kSampleSub, i1 = min(a.V, b1 * kSampleSub);
@@ -377,9 +428,9 @@ __global__ __launch_bounds__(kNT) void sample_scan_kernel(SampleArgs a) {
     const int b = b0 + wave + kW * k;
     if (b >= b1) break;
     if ((b + 1) * kSampleSub <= a.V)
-      summarise<Tin, kVec, true>(a, row, r, b, i0, lane, raw[k], s);
+      summarise<Tin, kVec, true, kTopp>(a, row, r, b, i0, lane, raw[k], s);
     else
-      summarise<Tin, kVec, false>(a, row, r, b, i0, lane, raw[k], s);
+      summarise<Tin, kVec, false, kTopp>(a, row, r, b, i0, lane, raw[k], s);
   }
 }
 
@@ -608,14 +659,15 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-p rows (top_p < 1, tau > 0): four launches after the scan find each
+// Top-p rows (top_p < 1, tau > 0): three launches after the scan find each
 // row's cut and draw the token, in place of the pick kernel.
 //   * Z and the total weight W = sum 2^((z - Z) s2) come from the scan's
 //     sub-slice summaries.
 //   * The cut z* -- the value at which the weight at or above it first
 //     reaches top_p * W -- by a weighted select from the largest z down.
-//     The coarse step is spread over the grid: every sub-slice's weight in
-//     each of 32 bins, a power of two of weight each below the maximum (the
+//     The coarse step is spread over the grid: the scan bins every
+//     sub-slice's weight into 32 bins, a power of two of weight each (on a
+//     fixed lattice, so that sub-slice bins shift exactly into the row's; the
 //     last bin takes everything further down). One workgroup a row adds
 //     them up and finds the bin where the cumulative weight crosses
 //     top_p * W, which is usually narrow; its tokens' keys and ids go to a
@@ -755,28 +807,6 @@ struct ToppLds {
   int win, lastk;
 };
 
-// Coarse bin of z below the row maximum Z: whole powers of two of weight
-// (the last bin takes everything further down). Every kernel bins with this.
-__device__ __forceinline__ int topp_coarse(float z, float Z, float s2) {
-  const float d = (Z - z) * s2;
-  return d < (float)(kToppCoarse - 1) ? (int)d : kToppCoarse - 1;
-}
-
-// The lane's 16 penalised logits of sub-slice b of row r, with the window
-// bits the scan stored.
-template <typename Tin, bool kVec>
-__device__ __forceinline__ void topp_sub_z(const SampleArgs& a, int r, int b, int lane, float (&z)[kPL]) {
-  const Tin* row = static_cast<const Tin*>(a.logits) + (int64_t)r * a.V;
-  const int base = b * kSampleSub;
-  const uint32_t* bits = a.wbits + ((int64_t)r * a.nb + b) * (kSampleSub / 32);
-  SubRaw<Tin> raw;
-  fetch_sub<Tin, kVec>(row, base, a.V, lane, raw);
-  if (base + kSampleSub <= a.V)
-    sub_values<Tin, kVec, true>(row, base, base, a, lane, raw, bits, z);
-  else
-    sub_values<Tin, kVec, false>(row, base, base, a, lane, raw, bits, z);
-}
-
 // Among the 2048 key bins (in order of decreasing z), the first whose
 // cumulative weight (after s.above) reaches `target`, else the last non-empty
 // one; sets s.above to the weight before it and returns it.
@@ -834,55 +864,15 @@ __device__ __forceinline__ void topp_key_bin(ToppLds& s, uint32_t key, float Z, 
   atomicMax(&s.kmx[b], key);
 }
 
-// H: each sub-slice's weight in every coarse bin, one sub-slice a wave. A
-// lane adds its tokens' weights 2^((z - Z) s2) into its own LDS row of bins
-// (plain read-modify-write: LDS float atomics run about a lane a cycle); the
-// wave then adds each column over the 64 rows in a fixed order.
-constexpr int kHistWaves = 4;
-
-template <typename Tin, bool kVec>
-__global__ __launch_bounds__(kHistWaves * kWave) void sample_topp_hist_kernel(SampleArgs a) {
-  __shared__ float ph[kHistWaves][kWave][kToppCoarse + 1];
-  __shared__ float red[kHistWaves];
-  const int r = blockIdx.y, lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int b = blockIdx.x * kHistWaves + wave;
-  // the row maximum Z from the sub-slice summaries
-  float m = -INFINITY;
-  for (int q = threadIdx.x; q < a.nb; q += kHistWaves * kWave) m = fmaxf(m, a.sub[(int64_t)r * a.nb + q].m);
-  m = wave_max(m);
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  float Z = red[0];
-#pragma unroll
-  for (int w = 1; w < kHistWaves; ++w) Z = fmaxf(Z, red[w]);
-  if (b >= a.nb) return;                 // past the only barrier
-  float* mine = ph[wave][lane];
-#pragma unroll
-  for (int c = 0; c < kToppCoarse; ++c) mine[c] = 0.0f;
-  if (Z > -INFINITY) {
-    float z[kPL];
-    topp_sub_z<Tin, kVec>(a, r, b, lane, z);
-#pragma unroll
-    for (int e = 0; e < kPL; ++e)
-      if (z[e] > -INFINITY) mine[topp_coarse(z[e], Z, a.s2)] += __builtin_amdgcn_exp2f((z[e] - Z) * a.s2);
-  }
-  // the wave's own rows only: its LDS operations complete in order
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  // column c = lane % 32 over rows 32h .. 32h + 31 (h = lane / 32), then the halves
-  const int c = lane & (kToppCoarse - 1), h = lane >> 5;
-  float t = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) t += ph[wave][32 * h + j][c];
-  t += __shfl_xor(t, 32, kWave);
-  if (lane < kToppCoarse) a.topp_hist[((int64_t)r * a.nb + b) * kToppCoarse + lane] = t;
-}
+constexpr int kExtractWaves = 4;
 
 // C: one workgroup a row. Z and the total weight W from the sub-slice
-// summaries; the coarse bin totals (each wave adds its 64 sub-slices, then
-// the waves in order); the crossing bin bc, the first whose cumulative weight
-// reaches top_p * W (else the last non-empty one), and the weight above it;
-// each sub-slice's weight in the bins above bc. Also resets the row's
-// candidate count for the extract kernel.
+// summaries; each sub-slice's bins shifted by its level difference to Z and
+// scaled by 2^((m - Z) s2) into the row's bins; the bin totals (each wave adds
+// its 64 sub-slices, then the waves in order); the crossing bin bc, the first
+// whose cumulative weight reaches top_p * W (else the last non-empty one), and
+// the weight above it; each sub-slice's weight in the bins above bc. Also
+// resets the row's candidate count for the extract kernel.
 __global__ __launch_bounds__(kToppThreads) void sample_topp_coarse_kernel(SampleArgs a) {
   __shared__ float ph[kToppThreads][kToppCoarse + 1];
   __shared__ float coarse[kToppWaves][kToppCoarse];
@@ -890,8 +880,21 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_coarse_kernel(Sample
   __shared__ int sel;
   __shared__ float above;
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  // this thread's sub-slice: its summary and its bins (below its own maximum)
   SampleSub sb = SampleSub{-INFINITY, 0.0f, 0, 0.0f};
-  if (tid < a.nb) sb = a.sub[(int64_t)r * a.nb + tid];
+  float hb[kToppCoarse];
+  if (tid < a.nb) {
+    sb = a.sub[(int64_t)r * a.nb + tid];
+    const float4* src = reinterpret_cast<const float4*>(a.topp_hist + ((int64_t)r * a.nb + tid) * kToppCoarse);
+#pragma unroll
+    for (int q = 0; q < kToppCoarse / 4; ++q) {
+      const float4 v = src[q];
+      hb[4 * q] = v.x; hb[4 * q + 1] = v.y; hb[4 * q + 2] = v.z; hb[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kToppCoarse; ++q) hb[q] = 0.0f;
+  }
   const float vmax = wave_max(sb.m);
   if (lane == 0) red[wave] = vmax;
   __syncthreads();
@@ -907,21 +910,23 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_coarse_kernel(Sample
     return;
   }
   const float target = a.top_p * W;
-  // this thread's sub-slice's bins, kept for the weight above bc
-  float hb[kToppCoarse];
-  if (tid < a.nb) {
-    const float4* src = reinterpret_cast<const float4*>(a.topp_hist + ((int64_t)r * a.nb + tid) * kToppCoarse);
+  // the bins scaled to Z, kept for the weight above bc; bin j is the row's
+  // bin min(j + dl, 31)
+  int dl = kToppCoarse;
+  const float sc = sb.m > -INFINITY ? __builtin_amdgcn_exp2f((sb.m - Z) * a.s2) : 0.0f;
+  if (sb.m > -INFINITY) dl = min(topp_level(sb.m, a.s2) - topp_level(Z, a.s2), kToppCoarse);
 #pragma unroll
-    for (int q = 0; q < kToppCoarse / 4; ++q) {
-      const float4 v = src[q];
-      hb[4 * q] = v.x; hb[4 * q + 1] = v.y; hb[4 * q + 2] = v.z; hb[4 * q + 3] = v.w;
-    }
-  } else {
+  for (int q = 0; q < kToppCoarse; ++q) hb[q] *= sc;
+  float tail = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kToppCoarse; ++q) hb[q] = 0.0f;
+  for (int c = 0; c < kToppCoarse - 1; ++c)
+    if (c < dl) ph[tid][c] = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kToppCoarse; ++q) {
+    if (q + dl < kToppCoarse - 1) ph[tid][q + dl] = hb[q];
+    else tail += hb[q];
   }
-#pragma unroll
-  for (int q = 0; q < kToppCoarse; ++q) ph[tid][q] = hb[q];
+  ph[tid][kToppCoarse - 1] = tail;
   if (tid == 0) above = 0.0f;
   __syncthreads();
   if (lane < kToppCoarse) {
@@ -948,7 +953,7 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_coarse_kernel(Sample
   if (tid < a.nb) {
     float w = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kToppCoarse; ++q) w += q < bc ? hb[q] : 0.0f;
+    for (int q = 0; q < kToppCoarse; ++q) w += q + dl < bc ? hb[q] : 0.0f;
     a.topp_above[(int64_t)r * a.nb + tid] = w;
   }
   if (tid == 0) *row = ToppRow{Z, target, above, bc, 0, {}};
@@ -957,25 +962,39 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_coarse_kernel(Sample
 // E: the tokens of the crossing bin, one sub-slice a wave: their keys and ids
 // into the row's candidate list (one slot reservation a wave, ballot-
 // compacted; slots past the list's capacity are counted, not stored). A
-// sub-slice whose maximum lies in a lower bin (less weight) has none of them
-// and is not read.
+// sub-slice with no weight in the crossing bin has none of its tokens (a bin
+// above the last holds weights of at least 2^-32 of its maximum's) and is
+// not read.
 template <typename Tin, bool kVec>
-__global__ __launch_bounds__(kHistWaves * kWave) void sample_topp_extract_kernel(SampleArgs a) {
+__global__ __launch_bounds__(kExtractWaves * kWave) void sample_topp_extract_kernel(SampleArgs a) {
   const int r = blockIdx.y, lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int b = blockIdx.x * kHistWaves + wave;
+  const int b = blockIdx.x * kExtractWaves + wave;
   ToppRow* row = a.topp_row + r;
   const int bc = row->bc;
   if (b >= a.nb || bc < 0) return;
-  const float Z = row->Z;
   const float mb = a.sub[(int64_t)r * a.nb + b].m;
-  if (!(mb > -INFINITY) || topp_coarse(mb, Z, a.s2) > bc) return;
+  if (!(mb > -INFINITY)) return;
+  const int lz = topp_level(row->Z, a.s2);
+  const int dl = topp_level(mb, a.s2) - lz;   // the sub-slice's bin j is the row's min(j + dl, 31)
+  if (dl > bc) return;
+  if (bc < kToppCoarse - 1 && !(a.topp_hist[((int64_t)r * a.nb + b) * kToppCoarse + (bc - dl)] > 0.0f)) return;
   float z[kPL];
-  topp_sub_z<Tin, kVec>(a, r, b, lane, z);
+  {
+    const Tin* lrow = static_cast<const Tin*>(a.logits) + (int64_t)r * a.V;
+    const int base = b * kSampleSub;
+    const uint32_t* bits = a.wbits + ((int64_t)r * a.nb + b) * (kSampleSub / 32);
+    SubRaw<Tin> raw;
+    fetch_sub<Tin, kVec>(lrow, base, a.V, lane, raw);
+    if (base + kSampleSub <= a.V)
+      sub_values<Tin, kVec, true>(lrow, base, base, a, lane, raw, bits, z);
+    else
+      sub_values<Tin, kVec, false>(lrow, base, base, a, lane, raw, bits, z);
+  }
   uint64_t in[kPL];
   int cnt = 0;
 #pragma unroll
   for (int e = 0; e < kPL; ++e) {
-    in[e] = __ballot(z[e] > -INFINITY && topp_coarse(z[e], Z, a.s2) == bc);
+    in[e] = __ballot(z[e] > -INFINITY && topp_bin(z[e], lz, a.s2) == bc);
     cnt += __popcll(in[e]);
   }
   if (cnt == 0) return;                  // uniform across the wave
@@ -1012,6 +1031,10 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
   const int ngroups = (V + 3) / 4;
   const float th = a.theta, ith = a.inv_theta;
   const ToppRow rw = a.topp_row[r];
+  // loads that depend on nothing here: the draw's uniform, this thread's
+  // sub-slice's weight above the crossing bin
+  const float u_r = a.u[r];
+  const float above_q = tid < a.nb ? a.topp_above[(int64_t)r * a.nb + tid] : 0.0f;
   // no finite logit, or (cannot happen: the crossing bin has weight) no token in it
   if (rw.bc < 0 || rw.n == 0) {
     if (tid == 0) a.tok[r] = -1;
@@ -1019,6 +1042,7 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
   }
   const float Z = rw.Z, target = rw.target;
   const int bc = rw.bc, n = rw.n;
+  const int lz = topp_level(Z, a.s2);
   // the held candidates and their key range; a crowded bin starts from the
   // whole key range (three 11-bit passes still end on one key)
   if (tid == 0) {
@@ -1060,7 +1084,7 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
       topp_visit<Tin, kVec>(V, th, ith, row, bits, ngroups, [&](int, const float (&z)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (z[i] > -INFINITY && topp_coarse(z[i], Z, a.s2) == bc) topp_key_bin(s, topp_key(z[i]), Z, a.s2, lo, hi, shift);
+          if (z[i] > -INFINITY && topp_bin(z[i], lz, a.s2) == bc) topp_key_bin(s, topp_key(z[i]), Z, a.s2, lo, hi, shift);
       });
     }
     __syncthreads();
@@ -1088,7 +1112,7 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
     // is a held candidate: a sub-slice keeps its weight in the bins above the
     // crossing one and its candidates at or above z* (keys are
     // order-preserving: key >= lo)
-    for (int q = tid; q < a.nb; q += kToppThreads) s.part[4 * q] = a.topp_above[(int64_t)r * a.nb + q];
+    if (tid < a.nb) s.part[4 * tid] = above_q;
     for (int i = tid; i < n; i += kToppThreads) {
       const uint32_t key = s.cand[i];
       if (key >= lo)
@@ -1112,7 +1136,7 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
   if (tid < a.nb) c = (s.part[4 * tid] + s.part[4 * tid + 1]) + (s.part[4 * tid + 2] + s.part[4 * tid + 3]);
   float total;
   const float excl = topp_scan(c, s.red, total);
-  const float target2 = a.u[r] * total;
+  const float target2 = u_r * total;
   if (c > 0.0f && excl + c > target2) atomicMin(&s.sel, tid);
   if (c > 0.0f) atomicMax(&s.last, tid);
   __syncthreads();
@@ -1152,23 +1176,24 @@ hipError_t launch_t(const SampleArgs& a, hipStream_t st) {
   constexpr int kPer = 16 / sizeof(Tin);
   // 16-byte loads when every row is whole 16-byte groups from an aligned base
   const bool vec = (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0 && a.V % kPer == 0;
-  if (vec)
-    sample_scan_kernel<Tin, kNT, kPW, true><<<grid, kNT, 0, st>>>(a);
+  const bool topp = a.topp_cut != nullptr;
+  if (vec && topp)
+    sample_scan_kernel<Tin, kNT, kPW, true, true><<<grid, kNT, 0, st>>>(a);
+  else if (vec)
+    sample_scan_kernel<Tin, kNT, kPW, true, false><<<grid, kNT, 0, st>>>(a);
+  else if (topp)
+    sample_scan_kernel<Tin, kNT, kPW, false, true><<<grid, kNT, 0, st>>>(a);
   else
-    sample_scan_kernel<Tin, kNT, kPW, false><<<grid, kNT, 0, st>>>(a);
-  if (a.topp_cut != nullptr) {
-    // top-p rows: the coarse bins over the grid, the crossing bin per row,
-    // its tokens over the grid, then the cut and the draw per row
-    const dim3 hgrid((a.nb + kHistWaves - 1) / kHistWaves, a.R);
-    if (vec)
-      sample_topp_hist_kernel<Tin, true><<<hgrid, kHistWaves * kWave, 0, st>>>(a);
-    else
-      sample_topp_hist_kernel<Tin, false><<<hgrid, kHistWaves * kWave, 0, st>>>(a);
+    sample_scan_kernel<Tin, kNT, kPW, false, false><<<grid, kNT, 0, st>>>(a);
+  if (topp) {
+    // top-p rows (the scan also binned them): the crossing bin per row, its
+    // tokens over the grid, then the cut and the draw per row
     sample_topp_coarse_kernel<<<a.R, kToppThreads, 0, st>>>(a);
+    const dim3 egrid((a.nb + kExtractWaves - 1) / kExtractWaves, a.R);
     if (vec)
-      sample_topp_extract_kernel<Tin, true><<<hgrid, kHistWaves * kWave, 0, st>>>(a);
+      sample_topp_extract_kernel<Tin, true><<<egrid, kExtractWaves * kWave, 0, st>>>(a);
     else
-      sample_topp_extract_kernel<Tin, false><<<hgrid, kHistWaves * kWave, 0, st>>>(a);
+      sample_topp_extract_kernel<Tin, false><<<egrid, kExtractWaves * kWave, 0, st>>>(a);
     if (vec)
       sample_topp_kernel<Tin, true><<<a.R, kToppThreads, 0, st>>>(a);
     else
