@@ -252,6 +252,22 @@ def test_top_p_flat_and_tied_logits(top_p):
             min_p=0.0, top_p=top_p, u=u, label=f"tied tau={tau} top_p={top_p}")
 
 
+@pytest.mark.parametrize("temperature,top_p", [
+    (1e-8, 0.9),                  # near-greedy: z * log2e / tau passes the coarse levels' clamp
+    (1e-3, 0.5),
+    (0.3, 0.9999999),             # the nucleus nearly the whole mass: the cut lies in the deepest bins
+    (5.0, 0.999),                 # hot: weight spread over most of the vocabulary
+])
+def test_top_p_extreme_temperatures_and_deep_cuts(temperature, top_p):
+    """16 rows over the 128,256-token vocabulary (logits N(0, 3^2) with 64 hot
+    tokens, the pages' penalty) at temperatures and nuclei that put the cut at
+    the ends of the coarse binning."""
+    c = inputs.make_sample(dtype="f32", parent=np.arange(-1, 14, dtype=np.int32), seed=41)
+    run(c.logits, "f32", c.hist, c.parent, c.draft_tok, window=inputs.PENALTY_WINDOW, penalty=inputs.PENALTY,
+        temperature=temperature, min_p=0.0, top_p=top_p, u=c.u,
+        label=f"top-p 16x128256 tau={temperature} top_p={top_p}")
+
+
 @pytest.mark.parametrize("V", [7, 1025, 4097, 128257])
 def test_top_p_ragged_vocabularies(V):
     rng = np.random.default_rng(V + 1)
