@@ -683,9 +683,10 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(SampleArgs a) {
 //     u * (kept weight) falls in, and a scan over its 1024 tokens the token.
 // Every pass over the row loads a thread's next eight 4-token groups before
 // using any (a group past the row reloads the last one and is masked). The
-// list's order and the key passes' LDS sums follow the order in which
-// atomics land, so a cut within rounding of a cumulative boundary may come
-// out one value either side, and may differ between calls.
+// list's order follows the order in which its slot reservations land, but
+// the key passes and the kept weights add the crossing bin's weights as
+// integers, so the cut and the draw do not depend on it. All other sums run
+// in a fixed order: every call gives the same tokens.
 constexpr int kToppThreads = 1024;
 constexpr int kToppWaves = kToppThreads / kWave;
 constexpr int kToppBins = 2048;           // key-pass bins
@@ -795,11 +796,12 @@ __device__ __forceinline__ void topp_visit(int V, float theta, float inv_theta, 
 }
 
 struct ToppLds {
-  float hw[kToppBins];                   // key passes: weight per bin
+  unsigned long long hw[kToppBins];      // key passes: weight per bin, fixed point
   uint32_t kmn[kToppBins], kmx[kToppBins];   // smallest and largest key per bin (none: ~0 and 0)
   uint32_t cand[kToppCand];              // keys of the crossing bin
   int32_t cid[kToppCand];                // and their token ids
   float part[4 * kSampleMaxSubs];        // kept weight of each sub-slice, in four parts
+  unsigned long long partq[kSampleMaxSubs];   // its listed tokens' share, fixed point
   float red[kToppWaves];
   float above;                           // weight above the current range
   uint32_t lo, hi;                       // the crossing bin's key range
@@ -810,7 +812,7 @@ struct ToppLds {
 // Among the 2048 key bins (in order of decreasing z), the first whose
 // cumulative weight (after s.above) reaches `target`, else the last non-empty
 // one; sets s.above to the weight before it and returns it.
-__device__ int topp_select(ToppLds& s, float target) {
+__device__ int topp_select(ToppLds& s, float target, float inv_fx) {
   const int tid = threadIdx.x;
   if (tid == 0) {
     s.sel = INT32_MAX;
@@ -818,7 +820,7 @@ __device__ int topp_select(ToppLds& s, float target) {
   }
   const float above0 = s.above;
   const int b0 = 2 * tid, b1 = 2 * tid + 1;
-  const float c0 = s.hw[b0], c1 = s.hw[b1];
+  const float c0 = (float)s.hw[b0] * inv_fx, c1 = (float)s.hw[b1] * inv_fx;
   // a bin holds tokens iff its smallest key is set (every token of the
   // crossing coarse bin has a positive weight: they are within a factor 2)
   const bool n0 = s.kmn[b0] != 0xFFFFFFFFu, n1 = s.kmn[b1] != 0xFFFFFFFFu;
@@ -847,19 +849,28 @@ __device__ int topp_select(ToppLds& s, float target) {
 
 __device__ __forceinline__ void topp_clear_keys(ToppLds& s) {
   for (int b = threadIdx.x; b < kToppBins; b += kToppThreads) {
-    s.hw[b] = 0.0f;
+    s.hw[b] = 0ull;
     s.kmn[b] = 0xFFFFFFFFu;
     s.kmx[b] = 0u;
   }
 }
 
+// Weights of the crossing bin's tokens are added as 64-bit integers, each
+// the fp32 weight times fx = 2^(bc + 41): a token of coarse bin bc weighs
+// less than 2^(1 - bc) (at most 1 in bin 0), so each term is below 2^42 and a
+// row's sum below 2^62. Integer sums do not depend on the order in which the
+// atomics land, so the cut and the draw are the same on every call.
+__device__ __forceinline__ unsigned long long topp_fixed(float w, float fx) {
+  return (unsigned long long)(w * fx);
+}
+
 // One key pass: the tokens with keys in [lo, hi] into bins of (key - lo) >> shift,
 // in order of decreasing key.
 __device__ __forceinline__ void topp_key_bin(ToppLds& s, uint32_t key, float Z, float s2, uint32_t lo, uint32_t hi,
-                                             int shift) {
+                                             int shift, float fx) {
   if (key < lo || key > hi) return;
   const int b = kToppBins - 1 - (int)((key - lo) >> shift);
-  atomicAdd(&s.hw[b], __builtin_amdgcn_exp2f((topp_value(key) - Z) * s2));
+  atomicAdd(&s.hw[b], topp_fixed(__builtin_amdgcn_exp2f((topp_value(key) - Z) * s2), fx));
   atomicMin(&s.kmn[b], key);
   atomicMax(&s.kmx[b], key);
 }
@@ -1043,6 +1054,7 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
   const float Z = rw.Z, target = rw.target;
   const int bc = rw.bc, n = rw.n;
   const int lz = topp_level(Z, a.s2);
+  const float fx = ldexpf(1.0f, bc + 41), inv_fx = ldexpf(1.0f, -(bc + 41));
   // the held candidates and their key range; a crowded bin starts from the
   // whole key range (three 11-bit passes still end on one key)
   if (tid == 0) {
@@ -1078,17 +1090,18 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
     topp_clear_keys(s);
     __syncthreads();
     if (n <= kToppCand) {
-      for (int i = tid; i < n; i += kToppThreads) topp_key_bin(s, s.cand[i], Z, a.s2, lo, hi, shift);
+      for (int i = tid; i < n; i += kToppThreads) topp_key_bin(s, s.cand[i], Z, a.s2, lo, hi, shift, fx);
     } else {
       // a crowded bin (nearly flat logits): the key passes read the row
       topp_visit<Tin, kVec>(V, th, ith, row, bits, ngroups, [&](int, const float (&z)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (z[i] > -INFINITY && topp_bin(z[i], lz, a.s2) == bc) topp_key_bin(s, topp_key(z[i]), Z, a.s2, lo, hi, shift);
+          if (z[i] > -INFINITY && topp_bin(z[i], lz, a.s2) == bc)
+            topp_key_bin(s, topp_key(z[i]), Z, a.s2, lo, hi, shift, fx);
       });
     }
     __syncthreads();
-    const int d = topp_select(s, target);
+    const int d = topp_select(s, target, inv_fx);
     lo = s.kmn[d];
     hi = s.kmx[d];
     done = lo == hi;
@@ -1100,6 +1113,7 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
 
   // ---- the kept weight of every sub-slice at the row's cut ------------------
   for (int q = tid; q < 4 * a.nb; q += kToppThreads) s.part[q] = 0.0f;
+  for (int q = tid; q < a.nb; q += kToppThreads) s.partq[q] = 0ull;
   if (tid == 0) {
     s.win = INT32_MAX;
     s.lastk = -1;
@@ -1112,11 +1126,15 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
     // is a held candidate: a sub-slice keeps its weight in the bins above the
     // crossing one and its candidates at or above z* (keys are
     // order-preserving: key >= lo)
-    if (tid < a.nb) s.part[4 * tid] = above_q;
     for (int i = tid; i < n; i += kToppThreads) {
       const uint32_t key = s.cand[i];
       if (key >= lo)
-        atomicAdd(&s.part[4 * (s.cid[i] / kSampleSub) + 1], __builtin_amdgcn_exp2f((topp_value(key) - Z) * a.s2));
+        atomicAdd(&s.partq[s.cid[i] / kSampleSub], topp_fixed(__builtin_amdgcn_exp2f((topp_value(key) - Z) * a.s2), fx));
+    }
+    __syncthreads();
+    if (tid < a.nb) {
+      s.part[4 * tid] = above_q;
+      s.part[4 * tid + 1] = (float)s.partq[tid] * inv_fx;
     }
   } else {
     const int wave = tid >> 6, lane = tid & (kWave - 1);

@@ -286,3 +286,18 @@ def test_top_p_ragged_vocabularies(V):
         for tau, mp, tp in ((1.0, 0.0, 0.8), (0.6, 0.05, 0.7)):
             run(xx, dtype, hist, parent, draft, window=64, penalty=1.3, temperature=tau, min_p=mp, top_p=tp,
                 u=u, label=f"top-p V={V} {dtype} tau={tau} min_p={mp} top_p={tp}")
+
+
+def test_top_p_same_tokens_on_every_call():
+    """The top-p path lists the crossing bin's tokens in the order their slot
+    reservations land, but adds their weights as integers: ten calls on the
+    same rows (fp32 and bf16, with and without min-p) give the same tokens."""
+    for dtype, min_p in (("f32", 0.0), ("bf16", 0.05)):
+        c = inputs.make_sample(dtype=dtype, seed=43)
+        kw = dict(hist=_i32(c.hist), parent=_i32(c.parent), draft_tok=_i32(c.draft_tok), window=inputs.PENALTY_WINDOW,
+                  penalty=inputs.PENALTY, temperature=0.8, min_p=min_p, top_p=0.9, u=to_dev(c.u, "f32"))
+        x = to_dev(c.logits, dtype)
+        first = ops.sample_tokens(x, **kw).cpu()
+        for _ in range(9):
+            assert torch.equal(ops.sample_tokens(x, **kw).cpu(), first), f"{dtype} min_p={min_p}"
+        say(f"  top-p {dtype} min_p={min_p}: 10 calls, identical tokens {first[:6].tolist()}...")
