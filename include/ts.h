@@ -88,10 +88,12 @@ int ts_abi_version(void);
  *   scale    softmax scale (usually 1/sqrt(D)); finite and > 0, else
  *            TS_ERR_INVALID_ARG
  *   num_splits  0 = library choice; otherwise the number of key ranges the
- *            work is split into (results agree across choices up to fp32
- *            rounding). Must match the value given to the size query.
+ *            work is split into (results agree across choices up to rounding).
+ *            Must match the value given to the size query.
  *   workspace   >= ts_tree_verify_attn_workspace(...) bytes, 256-byte aligned;
- *            contents on entry are ignored.
+ *            contents on entry are ignored. It holds the split partials: each
+ *            split's normalised output in the input dtype (bf16 inputs: bf16,
+ *            rounded to nearest even; fp32 inputs: fp32) and its fp32 lse.
  * Supported: T in [1, 1024], Hq in [1, 4096], Hq % Hkv == 0, Hq/Hkv <= 16,
  *            D in {64, 128}, 0 <= L <= 2^30, and one launch's worth of
  *            (split, KV head, row group) units (TS_ERR_UNSUPPORTED beyond).

@@ -109,13 +109,18 @@ int ts_tree_verify_attn_num_splits(int T, int Hq, int Hkv, int D, int64_t L, ts_
   return plan_attention(T, Hq, Hkv, D, L, dtype, num_splits).n_splits;
 }
 
+// A call that merges its own splits keeps the O partials in bf16 when the
+// inputs are bf16 (the output is bf16 too): half the bytes for the merge to
+// read. The partials of ts_tree_verify_attn_partials stay fp32.
+static size_t own_part_elem_bytes(ts_dtype dtype) { return dtype == TS_BF16 ? sizeof(bf16_t) : sizeof(float); }
+
 size_t ts_tree_verify_attn_workspace(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype,
                                      int num_splits) {
   if (check_attn_shape("ts_tree_verify_attn_workspace", T, Hq, Hkv, D, L, dtype, num_splits) != TS_OK)
     return 0;
   const AttnPlan p = plan_attention(T, Hq, Hkv, D, L, dtype, num_splits);
   const size_t rows = (size_t)T * Hq;
-  return align_up((size_t)p.n_splits * rows * D * sizeof(float)) +
+  return align_up((size_t)p.n_splits * rows * D * own_part_elem_bytes(dtype)) +
          align_up((size_t)p.n_splits * rows * sizeof(float));
 }
 
@@ -141,7 +146,8 @@ static ts_status attn_common(const char* fn, const void* q, const void* kc, cons
                              const int32_t* parent, bool need_parent, float* o_part, float* l_part,
                              int T, int Hq, int Hkv, int D, int64_t L, float scale,
                              ts_dtype dtype, int num_splits, hipStream_t stream,
-                             const ImpFusion* imp = nullptr, const GatherFusion* gf = nullptr) {
+                             const ImpFusion* imp = nullptr, const GatherFusion* gf = nullptr,
+                             bf16_t* o_part_h = nullptr) {
   ts_status st = check_attn_shape(fn, T, Hq, Hkv, D, L, dtype, num_splits);
   if (st != TS_OK) return st;
   if (!q || !kd || !vd || !o_part || !l_part) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
@@ -166,7 +172,7 @@ static ts_status attn_common(const char* fn, const void* q, const void* kc, cons
 
   AttnArgs a{};
   a.q = q; a.kc = kc; a.vc = vc; a.cache_stride = cache_stride; a.kd = kd; a.vd = vd;
-  a.parent = parent; a.o_part = o_part; a.l_part = l_part;
+  a.parent = parent; a.o_part = o_part; a.o_part_h = o_part_h; a.l_part = l_part;
   a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D; a.L = L;
   a.scale_log2 = scale * kLog2e;
   a.plan = plan;
@@ -282,13 +288,18 @@ static ts_status verify_like(const char* fn, const void* q, const void* kc, cons
     return fail(TS_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
   const AttnPlan p = plan_attention(T, Hq, Hkv, D, L, dtype, num_splits);
   const size_t rows = (size_t)T * Hq;
+  // the O partials at the front of the workspace (bf16 for bf16 inputs), then l_part
   float* o_part = static_cast<float*>(workspace);
+  bf16_t* o_part_h = dtype == TS_BF16 ? static_cast<bf16_t*>(workspace) : nullptr;
   float* l_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                           align_up((size_t)p.n_splits * rows * D * sizeof(float)));
+                                           align_up((size_t)p.n_splits * rows * D * own_part_elem_bytes(dtype)));
   st = attn_common(fn, q, kc, vc, cache_stride, kd, vd, parent, need_parent, o_part, l_part, T,
-                   Hq, Hkv, D, L, scale, dtype, num_splits, stream, nullptr, gf);
+                   Hq, Hkv, D, L, scale, dtype, num_splits, stream, nullptr, gf, o_part_h);
   if (st != TS_OK) return st;
-  return from_hip(launch_attn_merge(o_part, l_part, p.n_splits, (int)rows, D, out, lse, dtype, stream), fn);
+  const hipError_t e = o_part_h != nullptr
+                           ? launch_attn_merge_h(o_part_h, l_part, p.n_splits, (int)rows, D, out, lse, dtype, stream)
+                           : launch_attn_merge(o_part, l_part, p.n_splits, (int)rows, D, out, lse, dtype, stream);
+  return from_hip(e, fn);
 }
 
 ts_status ts_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,

@@ -1,29 +1,29 @@
-// Cross-split log-sum-exp merge of partial attention results: the kernel and
-// its launch shape; the per-workgroup body (and the formula) is in
-// merge_block.h.
+// Cross-split log-sum-exp merge of partial attention results (fp32 partials,
+// or the bf16 ones a call keeps in its own workspace): the kernel and its
+// launch shape; the per-workgroup body (and the formula) is in merge_block.h.
 #include "merge_block.h"
 
 namespace ts {
 namespace {
 
-template <typename Tout, int D, int WPR>
+template <typename Tout, int D, int WPR, typename Tin>
 __global__ __launch_bounds__(MergeShape<WPR>::block) void attn_merge_kernel(
-    const float* __restrict__ o_part, const float* __restrict__ l_part, int S, int rows,
+    const Tin* __restrict__ o_part, const float* __restrict__ l_part, int S, int rows,
     Tout* __restrict__ out, float* __restrict__ lse) {
-  merge_block<Tout, D, WPR>(o_part, l_part, S, rows, out, lse, blockIdx.x);
+  merge_block<Tout, D, WPR, Tin>(o_part, l_part, S, rows, out, lse, blockIdx.x);
 }
 
-template <typename Tout, int D, int WPR>
-void launch_one(const float* o_part, const float* l_part, int S, int rows, void* out, float* lse,
+template <typename Tout, int D, int WPR, typename Tin>
+void launch_one(const Tin* o_part, const float* l_part, int S, int rows, void* out, float* lse,
                 hipStream_t s) {
   using Sh = MergeShape<WPR>;
   const int grid = (rows + Sh::rows - 1) / Sh::rows;
-  attn_merge_kernel<Tout, D, WPR><<<grid, Sh::block, 0, s>>>(o_part, l_part, S, rows,
-                                                             static_cast<Tout*>(out), lse);
+  attn_merge_kernel<Tout, D, WPR, Tin><<<grid, Sh::block, 0, s>>>(o_part, l_part, S, rows,
+                                                                  static_cast<Tout*>(out), lse);
 }
 
-template <typename Tout, int D>
-void launch_d(const float* o_part, const float* l_part, int S, int rows, void* out, float* lse,
+template <typename Tout, int D, typename Tin>
+void launch_d(const Tin* o_part, const float* l_part, int S, int rows, void* out, float* lse,
               hipStream_t s) {
   // lanes needed so that each lane holds at most one batch of splits
   const int need = ((S + kMergeBatch - 1) / kMergeBatch) * (D / 4);
@@ -34,10 +34,9 @@ void launch_d(const float* o_part, const float* l_part, int S, int rows, void* o
   else launch_one<Tout, D, 16>(o_part, l_part, S, rows, out, lse, s);
 }
 
-}  // namespace
-
-hipError_t launch_attn_merge(const float* o_part, const float* l_part, int n_parts, int rows,
-                             int D, void* out, float* lse, ts_dtype dtype, hipStream_t s) {
+template <typename Tin>
+hipError_t launch_t(const Tin* o_part, const float* l_part, int n_parts, int rows, int D, void* out,
+                    float* lse, ts_dtype dtype, hipStream_t s) {
   if (dtype == TS_BF16) {
     if (D == 128) launch_d<bf16_t, 128>(o_part, l_part, n_parts, rows, out, lse, s);
     else launch_d<bf16_t, 64>(o_part, l_part, n_parts, rows, out, lse, s);
@@ -46,6 +45,18 @@ hipError_t launch_attn_merge(const float* o_part, const float* l_part, int n_par
     else launch_d<float, 64>(o_part, l_part, n_parts, rows, out, lse, s);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_merge(const float* o_part, const float* l_part, int n_parts, int rows,
+                             int D, void* out, float* lse, ts_dtype dtype, hipStream_t s) {
+  return launch_t(o_part, l_part, n_parts, rows, D, out, lse, dtype, s);
+}
+
+hipError_t launch_attn_merge_h(const bf16_t* o_part, const float* l_part, int n_parts, int rows,
+                               int D, void* out, float* lse, ts_dtype dtype, hipStream_t s) {
+  return launch_t(o_part, l_part, n_parts, rows, D, out, lse, dtype, s);
 }
 
 }  // namespace ts

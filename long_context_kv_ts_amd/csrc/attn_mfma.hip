@@ -681,16 +681,30 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void attn_split_mfma_kerne
   if (row_ok) {
     const int64_t orow = ((int64_t)split * T + row_t) * Hq + row_h;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    float* op = a.o_part + orow * D;
+    if (a.o_part_h != nullptr) {
+      // a call's own bf16 partials: half the bytes for its merge to read
+      bf16_t* op = a.o_part_h + orow * D;
 #pragma unroll
-    for (int db = 0; db < Ly::DB; ++db)
+      for (int db = 0; db < Ly::DB; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * db + 8 * q4 + 4 * half;
-        float4 v = make_float4(O[db][4 * q4] * inv, O[db][4 * q4 + 1] * inv,
-                               O[db][4 * q4 + 2] * inv, O[db][4 * q4 + 3] * inv);
-        *reinterpret_cast<float4*>(op + d) = v;
-      }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * db + 8 * q4 + 4 * half;
+          *reinterpret_cast<uint2*>(op + d) =
+              pack_bf16x4(O[db][4 * q4] * inv, O[db][4 * q4 + 1] * inv, O[db][4 * q4 + 2] * inv,
+                          O[db][4 * q4 + 3] * inv);
+        }
+    } else {
+      float* op = a.o_part + orow * D;
+#pragma unroll
+      for (int db = 0; db < Ly::DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * db + 8 * q4 + 4 * half;
+          float4 v = make_float4(O[db][4 * q4] * inv, O[db][4 * q4 + 1] * inv,
+                                 O[db][4 * q4 + 2] * inv, O[db][4 * q4 + 3] * inv);
+          *reinterpret_cast<float4*>(op + d) = v;
+        }
+    }
     if (half == 0) a.l_part[orow] = ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
   }
 }

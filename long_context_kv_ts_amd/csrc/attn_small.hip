@@ -262,11 +262,21 @@ __global__ __launch_bounds__(kThreads) void attn_split_small_kernel(AttnArgs a) 
   if (row_ok) {
     const int64_t orow = ((int64_t)split * T + row_t) * Hq + row_h;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    float* op = a.o_part + orow * D;
+    if (a.o_part_h != nullptr) {
+      // a call's own bf16 partials: half the bytes for its merge to read
+      bf16_t* op = a.o_part_h + orow * D;
 #pragma unroll
-    for (int db = 0; db < Ly::DB; ++db) {
-      const f32x4_t v = O[db] * inv;
-      *reinterpret_cast<float4*>(op + 16 * db + 4 * grp) = make_float4(v[0], v[1], v[2], v[3]);
+      for (int db = 0; db < Ly::DB; ++db) {
+        const f32x4_t v = O[db] * inv;
+        *reinterpret_cast<uint2*>(op + 16 * db + 4 * grp) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+      float* op = a.o_part + orow * D;
+#pragma unroll
+      for (int db = 0; db < Ly::DB; ++db) {
+        const f32x4_t v = O[db] * inv;
+        *reinterpret_cast<float4*>(op + 16 * db + 4 * grp) = make_float4(v[0], v[1], v[2], v[3]);
+      }
     }
     if (grp == 0) a.l_part[orow] = ltot > 0.f ? (m + log2f(ltot)) * kLn2 : -INFINITY;
   }

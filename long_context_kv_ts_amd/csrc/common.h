@@ -31,6 +31,12 @@ template <> struct Elem<float> {
   __device__ static float load(const float* p) { return *p; }
   __device__ static void store(float* p, float v) { *p = v; }
 };
+// four values rounded to bf16 (to nearest even) and packed, lowest first
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  return make_uint2((uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
+                    (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16));
+}
+
 template <> struct Elem<bf16_t> {
   __device__ static float load(const bf16_t* p) { return bf16_to_f32(*p); }
   __device__ static void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
@@ -180,6 +186,7 @@ struct AttnArgs {
   const void* vd;
   const int32_t* parent;    // [T] or nullptr = causal chain
   float* o_part;            // [S][T][Hq][D]
+  bf16_t* o_part_h;         // or, when set, the same partials in bf16 (a call's own workspace)
   float* l_part;            // [S][T][Hq]
   int T, Hq, Hkv, G, D;
   int64_t L;
@@ -230,6 +237,9 @@ hipError_t launch_attn_split_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_split_small(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const float* o_part, const float* l_part, int n_parts, int rows,
                              int D, void* out, float* lse, ts_dtype dtype, hipStream_t s);
+// the same merge of bf16 partials (those a call keeps in its own workspace)
+hipError_t launch_attn_merge_h(const bf16_t* o_part, const float* l_part, int n_parts, int rows,
+                               int D, void* out, float* lse, ts_dtype dtype, hipStream_t s);
 hipError_t launch_importance(const void* q, const void* kc, int64_t stride, float* scores,
                              int R, int Hq, int Hkv, int D, int64_t L, int chunk, float scale,
                              ts_dtype dtype, hipStream_t s);

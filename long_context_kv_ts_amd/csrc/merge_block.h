@@ -36,8 +36,16 @@ template <int WPR> struct MergeShape {
   static constexpr int rows = block / lanes;                   // rows per workgroup
 };
 
-template <typename Tout, int D, int WPR>
-__device__ __forceinline__ void merge_block(const float* __restrict__ o_part, const float* __restrict__ l_part,
+// 4 consecutive partial values: fp32, or bf16 widened exactly
+__device__ __forceinline__ float4 load_part4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load_part4(const bf16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+
+template <typename Tout, int D, int WPR, typename Tin = float>
+__device__ __forceinline__ void merge_block(const Tin* __restrict__ o_part, const float* __restrict__ l_part,
                                             int S, int rows, Tout* __restrict__ out, float* __restrict__ lse,
                                             int bx) {
   using Sh = MergeShape<WPR>;
@@ -65,7 +73,7 @@ __device__ __forceinline__ void merge_block(const float* __restrict__ o_part, co
         if (sp < S) {
           const int64_t pr = (int64_t)sp * rows + row;
           lb[b] = l_part[pr];
-          ob[b] = *reinterpret_cast<const float4*>(o_part + pr * D + 4 * c);
+          ob[b] = load_part4(o_part + pr * D + 4 * c);
         }
       }
 #pragma unroll

@@ -111,9 +111,14 @@ def test_workspace_query():
             assert S >= 1
             if ns:
                 assert S <= ns
+            # bf16 inputs: bf16 O partials and fp32 lse per split and row
             w = lib.ts_tree_verify_attn_workspace(120, 32, 8, 128, L, B, ns)
-            assert w >= S * 120 * 32 * 129 * 4
+            assert w >= S * 120 * 32 * (128 * 2 + 4)
             assert w % 256 == 0
+            # fp32 inputs: fp32 O partials
+            Sf = lib.ts_tree_verify_attn_num_splits(120, 32, 8, 128, L, ops.TS_F32, ns)
+            wf = lib.ts_tree_verify_attn_workspace(120, 32, 8, 128, L, ops.TS_F32, ns)
+            assert wf >= Sf * 120 * 32 * 129 * 4 and wf % 256 == 0
     assert lib.ts_tree_verify_attn_workspace(0, 32, 8, 128, 10, B, 0) == 0
     assert lib.ts_tree_verify_attn_num_splits(0, 32, 8, 128, 10, B, 0) == -1
     assert lib.ts_partial_draft_attn_workspace(4, 32, 8, 128, 4096, B, 0) > 0
@@ -390,9 +395,10 @@ def test_noalloc_rejects_before_any_hip_call():
         return lib.ts_tree_verify_attn_noalloc(a["q"], a["kc"], a["vc"], a["stride"], a["kd"], a["vd"], a["parent"],
                                                a["out"], a["lse"], a["T"], a["Hq"], a["Hkv"], a["D"], a["L"],
                                                a["scale"], a["dtype"], a["ns"], None)
-    # 40 splits of 120 x 32 rows of 128 fp32 is 78.6 MB of partials: more than 64 MiB
-    assert lib.ts_tree_verify_attn_workspace(120, 32, 8, 128, 102400, B, 40) > 64 << 20
-    assert call(ns=40) == ops.TS_ERR_UNSUPPORTED
+    # 77 splits (80 asked) of 120 x 32 rows of 128 bf16 + an fp32 lse is 76.9 MB of
+    # partials: more than 64 MiB
+    assert lib.ts_tree_verify_attn_workspace(120, 32, 8, 128, 102400, B, 80) > 64 << 20
+    assert call(ns=80) == ops.TS_ERR_UNSUPPORTED
     assert "static scratch" in _err() and "ts_tree_verify_attn_noalloc" in _err()
     assert call(T=0) == ops.TS_ERR_UNSUPPORTED and "ts_tree_verify_attn_noalloc" in _err()
     assert call(Hq=30) == ops.TS_ERR_INVALID_ARG
