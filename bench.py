@@ -227,7 +227,8 @@ def main():
     parent = to_dev(vc.parent, "i32", dev)
     T, Hq, Hkv, D, L = vc.T, vc.Hq, vc.Hkv, vc.D, vc.L
     S = ops.num_splits(T, Hq, Hkv, D, L, torch.bfloat16)
-    o_part = torch.empty((S, T, Hq, D), dtype=torch.float32, device=dev)
+    # the split partials in bf16 (the output is bf16): half the bytes for the merge
+    o_part = torch.empty((S, T, Hq, D), dtype=torch.bfloat16, device=dev)
     l_part = torch.empty((S, T, Hq), dtype=torch.float32, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)

@@ -61,7 +61,7 @@ const char* ts_last_error(void);
 /* ABI version of this header (bumped on any signature change). */
 int ts_abi_version(void);
 
-#define TS_ABI_VERSION 2
+#define TS_ABI_VERSION 3
 #define TS_MAX_DRAFT 1024 /* max draft tokens T of one verify call */
 
 /* ------------------------------------------------------------------------
@@ -133,8 +133,10 @@ ts_status ts_tree_verify_attn_noalloc(const void* q, const void* k_cache, const 
  * exp rule as merging across splits).
  *
  * ts_tree_verify_attn_partials writes, for every split s in [0, n_splits):
- *   o_part [n_splits][T][Hq][D] fp32   softmax(s restricted to split s) . v
- *   l_part [n_splits][T][Hq]    fp32   ln sum exp(s) over split s (-inf if empty)
+ *   o_part [n_splits][T][Hq][D]  part_dtype   softmax(s restricted to split s) . v
+ *   l_part [n_splits][T][Hq]     fp32         ln sum exp(s) over split s (-inf if empty)
+ * part_dtype is TS_F32, or TS_BF16 (rounded to nearest even: half the bytes
+ * for the merge to read) when dtype is TS_BF16; else TS_ERR_UNSUPPORTED.
  * with n_splits = ts_tree_verify_attn_num_splits(...). Split s covers a
  * contiguous range of cached tokens; the draft tokens belong to the last split.
  * ts_attn_merge combines `n_parts` such partials:
@@ -145,11 +147,12 @@ int ts_tree_verify_attn_num_splits(int T, int Hq, int Hkv, int D, int64_t L,
 ts_status ts_tree_verify_attn_partials(const void* q, const void* k_cache, const void* v_cache,
                                        int64_t cache_stride, const void* k_draft,
                                        const void* v_draft, const int32_t* parent,
-                                       float* o_part, float* l_part,
+                                       void* o_part, ts_dtype part_dtype, float* l_part,
                                        int T, int Hq, int Hkv, int D, int64_t L, float scale,
                                        ts_dtype dtype, int num_splits, hipStream_t stream);
 
-ts_status ts_attn_merge(const float* o_part, const float* l_part, int n_parts,
+/* o_part in part_dtype (TS_F32 or TS_BF16); out in dtype. */
+ts_status ts_attn_merge(const void* o_part, ts_dtype part_dtype, const float* l_part, int n_parts,
                         int rows, int D, void* out, float* lse, ts_dtype dtype,
                         hipStream_t stream);
 
@@ -169,8 +172,8 @@ ts_status ts_attn_merge(const float* o_part, const float* l_part, int n_parts,
  * last 256-row group empty (e.g. 480 rows); otherwise the two launches. */
 ts_status ts_tree_verify_attn_partials_and_importance(
     const void* q, const void* k_cache, const void* v_cache, int64_t cache_stride, const void* k_draft,
-    const void* v_draft, const int32_t* parent, float* o_part, float* l_part, int T, int Hq, int Hkv, int D,
-    int64_t L, float scale, ts_dtype dtype, int num_splits, const void* q_recent, int R, int chunk,
+    const void* v_draft, const int32_t* parent, void* o_part, ts_dtype part_dtype, float* l_part, int T, int Hq,
+    int Hkv, int D, int64_t L, float scale, ts_dtype dtype, int num_splits, const void* q_recent, int R, int chunk,
     float imp_scale, float* scores, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
@@ -209,8 +212,8 @@ ts_status ts_kv_importance_score(const void* q_recent, const void* k_cache, int6
  * chunk = 64 and R*(Hq/Hkv) <= 64; otherwise the two launches of the separate
  * calls, merge first, on the same stream.
  * ---------------------------------------------------------------------- */
-ts_status ts_attn_merge_and_importance(const float* o_part, const float* l_part, int n_parts, int rows, int Dv,
-                                       void* out, float* lse, ts_dtype out_dtype, const void* q_recent,
+ts_status ts_attn_merge_and_importance(const void* o_part, ts_dtype part_dtype, const float* l_part, int n_parts,
+                                       int rows, int Dv, void* out, float* lse, ts_dtype out_dtype, const void* q_recent,
                                        const void* k_cache, int64_t cache_stride, float* scores, int R, int Hq,
                                        int Hkv, int D, int64_t L, int chunk, float scale, ts_dtype dtype,
                                        hipStream_t stream);
@@ -237,8 +240,8 @@ ts_status ts_kv_topk_select(const float* scores, int Hkv, int n_chunks, int k,
  * operations' buffers must not overlap. Results are bit-identical to the two
  * calls. One launch when Dv = 128 and n_parts <= 16; otherwise the two
  * launches, merge first. */
-ts_status ts_attn_merge_and_topk(const float* o_part, const float* l_part, int n_parts, int rows, int Dv,
-                                 void* out, float* lse, ts_dtype out_dtype, const float* scores, int Hkv,
+ts_status ts_attn_merge_and_topk(const void* o_part, ts_dtype part_dtype, const float* l_part, int n_parts,
+                                 int rows, int Dv, void* out, float* lse, ts_dtype out_dtype, const float* scores, int Hkv,
                                  int n_chunks, int k, int32_t* chunk_idx, float* chunk_score,
                                  hipStream_t stream);
 

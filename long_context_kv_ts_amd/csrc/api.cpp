@@ -109,9 +109,9 @@ int ts_tree_verify_attn_num_splits(int T, int Hq, int Hkv, int D, int64_t L, ts_
   return plan_attention(T, Hq, Hkv, D, L, dtype, num_splits).n_splits;
 }
 
-// A call that merges its own splits keeps the O partials in bf16 when the
-// inputs are bf16 (the output is bf16 too): half the bytes for the merge to
-// read. The partials of ts_tree_verify_attn_partials stay fp32.
+// A call that merges its own splits keeps the O partials in its input dtype:
+// bf16 for bf16 inputs (the output is bf16 too), half the bytes for the merge
+// to read.
 static size_t own_part_elem_bytes(ts_dtype dtype) { return dtype == TS_BF16 ? sizeof(bf16_t) : sizeof(float); }
 
 size_t ts_tree_verify_attn_workspace(int T, int Hq, int Hkv, int D, int64_t L, ts_dtype dtype,
@@ -141,14 +141,25 @@ struct GatherFusion {
   void* v_part;
 };
 
+// Partials in fp32, or in bf16 for bf16 inputs (the split kernels of fp32
+// inputs write fp32 only).
+static ts_status check_part_dtype(const char* fn, ts_dtype part_dtype, ts_dtype dtype) {
+  if (part_dtype != TS_F32 && part_dtype != TS_BF16)
+    return fail(TS_ERR_INVALID_ARG, "%s: unknown part_dtype %d", fn, (int)part_dtype);
+  if (part_dtype == TS_BF16 && dtype != TS_BF16)
+    return fail(TS_ERR_UNSUPPORTED, "%s: bf16 partials need bf16 inputs", fn);
+  return TS_OK;
+}
+
 static ts_status attn_common(const char* fn, const void* q, const void* kc, const void* vc,
                              int64_t cache_stride, const void* kd, const void* vd,
-                             const int32_t* parent, bool need_parent, float* o_part, float* l_part,
-                             int T, int Hq, int Hkv, int D, int64_t L, float scale,
+                             const int32_t* parent, bool need_parent, void* o_part, ts_dtype part_dtype,
+                             float* l_part, int T, int Hq, int Hkv, int D, int64_t L, float scale,
                              ts_dtype dtype, int num_splits, hipStream_t stream,
-                             const ImpFusion* imp = nullptr, const GatherFusion* gf = nullptr,
-                             bf16_t* o_part_h = nullptr) {
+                             const ImpFusion* imp = nullptr, const GatherFusion* gf = nullptr) {
   ts_status st = check_attn_shape(fn, T, Hq, Hkv, D, L, dtype, num_splits);
+  if (st != TS_OK) return st;
+  st = check_part_dtype(fn, part_dtype, dtype);
   if (st != TS_OK) return st;
   if (!q || !kd || !vd || !o_part || !l_part) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (L > 0 && (!kc || !vc)) return fail(TS_ERR_INVALID_ARG, "%s: null cache pointer with L=%lld", fn, (long long)L);
@@ -172,7 +183,9 @@ static ts_status attn_common(const char* fn, const void* q, const void* kc, cons
 
   AttnArgs a{};
   a.q = q; a.kc = kc; a.vc = vc; a.cache_stride = cache_stride; a.kd = kd; a.vd = vd;
-  a.parent = parent; a.o_part = o_part; a.o_part_h = o_part_h; a.l_part = l_part;
+  a.parent = parent; a.l_part = l_part;
+  if (part_dtype == TS_BF16) a.o_part_h = static_cast<bf16_t*>(o_part);
+  else a.o_part = static_cast<float*>(o_part);
   a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D; a.L = L;
   a.scale_log2 = scale * kLog2e;
   a.plan = plan;
@@ -197,11 +210,11 @@ static ts_status attn_common(const char* fn, const void* q, const void* kc, cons
 ts_status ts_tree_verify_attn_partials(const void* q, const void* k_cache, const void* v_cache,
                                        int64_t cache_stride, const void* k_draft,
                                        const void* v_draft, const int32_t* parent,
-                                       float* o_part, float* l_part, int T, int Hq, int Hkv,
-                                       int D, int64_t L, float scale, ts_dtype dtype,
+                                       void* o_part, ts_dtype part_dtype, float* l_part, int T, int Hq,
+                                       int Hkv, int D, int64_t L, float scale, ts_dtype dtype,
                                        int num_splits, hipStream_t stream) {
   return attn_common("ts_tree_verify_attn_partials", q, k_cache, v_cache, cache_stride, k_draft,
-                     v_draft, parent, true, o_part, l_part, T, Hq, Hkv, D, L, scale, dtype,
+                     v_draft, parent, true, o_part, part_dtype, l_part, T, Hq, Hkv, D, L, scale, dtype,
                      num_splits, stream);
 }
 
@@ -211,8 +224,8 @@ static ts_status check_importance(const char* fn, const void* q_recent, const vo
 
 ts_status ts_tree_verify_attn_partials_and_importance(
     const void* q, const void* k_cache, const void* v_cache, int64_t cache_stride, const void* k_draft,
-    const void* v_draft, const int32_t* parent, float* o_part, float* l_part, int T, int Hq, int Hkv, int D,
-    int64_t L, float scale, ts_dtype dtype, int num_splits, const void* q_recent, int R, int chunk,
+    const void* v_draft, const int32_t* parent, void* o_part, ts_dtype part_dtype, float* l_part, int T, int Hq,
+    int Hkv, int D, int64_t L, float scale, ts_dtype dtype, int num_splits, const void* q_recent, int R, int chunk,
     float imp_scale, float* scores, hipStream_t stream) {
   const char* fn = "ts_tree_verify_attn_partials_and_importance";
   ts_status st = check_importance(fn, q_recent, k_cache, cache_stride, scores, R, Hq, Hkv, D, L, chunk,
@@ -220,25 +233,29 @@ ts_status ts_tree_verify_attn_partials_and_importance(
   if (st != TS_OK) return st;
   st = check_attn_shape(fn, T, Hq, Hkv, D, L, dtype, num_splits);
   if (st != TS_OK) return st;
+  st = check_part_dtype(fn, part_dtype, dtype);
+  if (st != TS_OK) return st;
   const AttnPlan plan = plan_attention(T, Hq, Hkv, D, L, dtype, num_splits);
   const bool fused = dtype == TS_BF16 && chunk == 64 &&
                      attn_mfma_importance_fusable(plan, T, Hq / Hkv, D, L, R);
   if (!fused) {
     // two launches: the split kernel, then the importance kernel
-    st = attn_common(fn, q, k_cache, v_cache, cache_stride, k_draft, v_draft, parent, true, o_part, l_part, T, Hq,
-                     Hkv, D, L, scale, dtype, num_splits, stream);
+    st = attn_common(fn, q, k_cache, v_cache, cache_stride, k_draft, v_draft, parent, true, o_part, part_dtype,
+                     l_part, T, Hq, Hkv, D, L, scale, dtype, num_splits, stream);
     if (st != TS_OK) return st;
     return from_hip(launch_importance(q_recent, k_cache, cache_stride, scores, R, Hq, Hkv, D, L, chunk, imp_scale,
                                       dtype, stream), fn);
   }
   ImpFusion f{q_recent, scores, R, imp_scale};
-  return attn_common(fn, q, k_cache, v_cache, cache_stride, k_draft, v_draft, parent, true, o_part, l_part, T, Hq,
-                     Hkv, D, L, scale, dtype, num_splits, stream, &f);
+  return attn_common(fn, q, k_cache, v_cache, cache_stride, k_draft, v_draft, parent, true, o_part, part_dtype,
+                     l_part, T, Hq, Hkv, D, L, scale, dtype, num_splits, stream, &f);
 }
 
-static ts_status check_merge(const char* fn, const float* o_part, const float* l_part, int n_parts, int rows,
-                             int D, const void* out, ts_dtype dtype) {
+static ts_status check_merge(const char* fn, const void* o_part, ts_dtype part_dtype, const float* l_part,
+                             int n_parts, int rows, int D, const void* out, ts_dtype dtype) {
   if (dtype != TS_F32 && dtype != TS_BF16) return fail(TS_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (part_dtype != TS_F32 && part_dtype != TS_BF16)
+    return fail(TS_ERR_INVALID_ARG, "%s: unknown part_dtype %d", fn, (int)part_dtype);
   if (!o_part || !l_part || !out) return fail(TS_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (n_parts < 1 || rows < 1) return fail(TS_ERR_INVALID_ARG, "%s: n_parts=%d rows=%d must be >= 1", fn, n_parts, rows);
   if (D != 64 && D != 128) return fail(TS_ERR_UNSUPPORTED, "%s: D=%d (supported: 64, 128)", fn, D);
@@ -247,12 +264,13 @@ static ts_status check_merge(const char* fn, const float* o_part, const float* l
   return TS_OK;
 }
 
-ts_status ts_attn_merge(const float* o_part, const float* l_part, int n_parts, int rows, int D,
+ts_status ts_attn_merge(const void* o_part, ts_dtype part_dtype, const float* l_part, int n_parts, int rows, int D,
                         void* out, float* lse, ts_dtype dtype, hipStream_t stream) {
   const char* fn = "ts_attn_merge";
-  const ts_status st = check_merge(fn, o_part, l_part, n_parts, rows, D, out, dtype);
+  const ts_status st = check_merge(fn, o_part, part_dtype, l_part, n_parts, rows, D, out, dtype);
   if (st != TS_OK) return st;
-  return from_hip(launch_attn_merge(o_part, l_part, n_parts, rows, D, out, lse, dtype, stream), fn);
+  return from_hip(launch_attn_merge(o_part, part_dtype == TS_BF16, l_part, n_parts, rows, D, out, lse, dtype, stream),
+                  fn);
 }
 
 }  // extern "C"
@@ -288,18 +306,15 @@ static ts_status verify_like(const char* fn, const void* q, const void* kc, cons
     return fail(TS_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
   const AttnPlan p = plan_attention(T, Hq, Hkv, D, L, dtype, num_splits);
   const size_t rows = (size_t)T * Hq;
-  // the O partials at the front of the workspace (bf16 for bf16 inputs), then l_part
-  float* o_part = static_cast<float*>(workspace);
-  bf16_t* o_part_h = dtype == TS_BF16 ? static_cast<bf16_t*>(workspace) : nullptr;
+  // the O partials at the front of the workspace (in the input dtype), then l_part
+  void* o_part = workspace;
   float* l_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                            align_up((size_t)p.n_splits * rows * D * own_part_elem_bytes(dtype)));
-  st = attn_common(fn, q, kc, vc, cache_stride, kd, vd, parent, need_parent, o_part, l_part, T,
-                   Hq, Hkv, D, L, scale, dtype, num_splits, stream, nullptr, gf, o_part_h);
+  st = attn_common(fn, q, kc, vc, cache_stride, kd, vd, parent, need_parent, o_part, dtype, l_part, T,
+                   Hq, Hkv, D, L, scale, dtype, num_splits, stream, nullptr, gf);
   if (st != TS_OK) return st;
-  const hipError_t e = o_part_h != nullptr
-                           ? launch_attn_merge_h(o_part_h, l_part, p.n_splits, (int)rows, D, out, lse, dtype, stream)
-                           : launch_attn_merge(o_part, l_part, p.n_splits, (int)rows, D, out, lse, dtype, stream);
-  return from_hip(e, fn);
+  return from_hip(launch_attn_merge(o_part, dtype == TS_BF16, l_part, p.n_splits, (int)rows, D, out, lse, dtype,
+                                    stream), fn);
 }
 
 ts_status ts_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
@@ -377,20 +392,22 @@ ts_status ts_kv_importance_score(const void* q_recent, const void* k_cache, int6
                                     chunk, scale, dtype, stream), fn);
 }
 
-ts_status ts_attn_merge_and_importance(const float* o_part, const float* l_part, int n_parts, int rows, int Dv,
-                                       void* out, float* lse, ts_dtype out_dtype, const void* q_recent,
-                                       const void* k_cache, int64_t cache_stride, float* scores, int R, int Hq,
-                                       int Hkv, int D, int64_t L, int chunk, float scale, ts_dtype dtype,
-                                       hipStream_t stream) {
+ts_status ts_attn_merge_and_importance(const void* o_part, ts_dtype part_dtype, const float* l_part, int n_parts,
+                                       int rows, int Dv, void* out, float* lse, ts_dtype out_dtype,
+                                       const void* q_recent, const void* k_cache, int64_t cache_stride, float* scores,
+                                       int R, int Hq, int Hkv, int D, int64_t L, int chunk, float scale,
+                                       ts_dtype dtype, hipStream_t stream) {
   const char* fn = "ts_attn_merge_and_importance";
-  ts_status st = check_merge(fn, o_part, l_part, n_parts, rows, Dv, out, out_dtype);
+  ts_status st = check_merge(fn, o_part, part_dtype, l_part, n_parts, rows, Dv, out, out_dtype);
   if (st != TS_OK) return st;
   st = check_importance(fn, q_recent, k_cache, cache_stride, scores, R, Hq, Hkv, D, L, chunk, scale, dtype);
   if (st != TS_OK) return st;
   if (L > 0 && merge_importance_fusable(n_parts, Dv, D, R, Hq, Hkv, chunk, dtype))
-    return from_hip(launch_merge_importance(o_part, l_part, n_parts, rows, out, lse, out_dtype, q_recent, k_cache,
-                                            cache_stride, scores, R, Hq, Hkv, L, scale, stream), fn);
-  st = from_hip(launch_attn_merge(o_part, l_part, n_parts, rows, Dv, out, lse, out_dtype, stream), fn);
+    return from_hip(launch_merge_importance(o_part, part_dtype == TS_BF16, l_part, n_parts, rows, out, lse, out_dtype,
+                                            q_recent, k_cache, cache_stride, scores, R, Hq, Hkv, L, scale, stream),
+                    fn);
+  st = from_hip(launch_attn_merge(o_part, part_dtype == TS_BF16, l_part, n_parts, rows, Dv, out, lse, out_dtype,
+                                  stream), fn);
   if (st != TS_OK) return st;
   return from_hip(launch_importance(q_recent, k_cache, cache_stride, scores, R, Hq, Hkv, D, L, chunk, scale, dtype,
                                     stream), fn);
@@ -415,18 +432,19 @@ ts_status ts_kv_topk_select(const float* scores, int Hkv, int n_chunks, int k,
   return from_hip(launch_topk(scores, Hkv, n_chunks, k, chunk_idx, chunk_score, stream), fn);
 }
 
-ts_status ts_attn_merge_and_topk(const float* o_part, const float* l_part, int n_parts, int rows, int Dv, void* out,
-                                 float* lse, ts_dtype out_dtype, const float* scores, int Hkv, int n_chunks, int k,
-                                 int32_t* chunk_idx, float* chunk_score, hipStream_t stream) {
+ts_status ts_attn_merge_and_topk(const void* o_part, ts_dtype part_dtype, const float* l_part, int n_parts, int rows,
+                                 int Dv, void* out, float* lse, ts_dtype out_dtype, const float* scores, int Hkv,
+                                 int n_chunks, int k, int32_t* chunk_idx, float* chunk_score, hipStream_t stream) {
   const char* fn = "ts_attn_merge_and_topk";
-  ts_status st = check_merge(fn, o_part, l_part, n_parts, rows, Dv, out, out_dtype);
+  ts_status st = check_merge(fn, o_part, part_dtype, l_part, n_parts, rows, Dv, out, out_dtype);
   if (st != TS_OK) return st;
   st = check_topk(fn, scores, Hkv, n_chunks, k, chunk_idx, chunk_score);
   if (st != TS_OK) return st;
   if (merge_topk_fusable(n_parts, Dv))
-    return from_hip(launch_merge_topk(o_part, l_part, n_parts, rows, out, lse, out_dtype, scores, Hkv, n_chunks, k,
-                                      chunk_idx, chunk_score, stream), fn);
-  st = from_hip(launch_attn_merge(o_part, l_part, n_parts, rows, Dv, out, lse, out_dtype, stream), fn);
+    return from_hip(launch_merge_topk(o_part, part_dtype == TS_BF16, l_part, n_parts, rows, out, lse, out_dtype,
+                                      scores, Hkv, n_chunks, k, chunk_idx, chunk_score, stream), fn);
+  st = from_hip(launch_attn_merge(o_part, part_dtype == TS_BF16, l_part, n_parts, rows, Dv, out, lse, out_dtype,
+                                  stream), fn);
   if (st != TS_OK) return st;
   return from_hip(launch_topk(scores, Hkv, n_chunks, k, chunk_idx, chunk_score, stream), fn);
 }

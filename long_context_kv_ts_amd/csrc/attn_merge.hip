@@ -1,6 +1,6 @@
-// Cross-split log-sum-exp merge of partial attention results (fp32 partials,
-// or the bf16 ones a call keeps in its own workspace): the kernel and its
-// launch shape; the per-workgroup body (and the formula) is in merge_block.h.
+// Cross-split log-sum-exp merge of partial attention results (fp32 or bf16
+// partials): the kernel and its launch shape; the per-workgroup body (and the
+// formula) is in merge_block.h.
 #include "merge_block.h"
 
 namespace ts {
@@ -49,14 +49,10 @@ hipError_t launch_t(const Tin* o_part, const float* l_part, int n_parts, int row
 
 }  // namespace
 
-hipError_t launch_attn_merge(const float* o_part, const float* l_part, int n_parts, int rows,
+hipError_t launch_attn_merge(const void* o_part, bool part_bf16, const float* l_part, int n_parts, int rows,
                              int D, void* out, float* lse, ts_dtype dtype, hipStream_t s) {
-  return launch_t(o_part, l_part, n_parts, rows, D, out, lse, dtype, s);
-}
-
-hipError_t launch_attn_merge_h(const bf16_t* o_part, const float* l_part, int n_parts, int rows,
-                               int D, void* out, float* lse, ts_dtype dtype, hipStream_t s) {
-  return launch_t(o_part, l_part, n_parts, rows, D, out, lse, dtype, s);
+  return part_bf16 ? launch_t(static_cast<const bf16_t*>(o_part), l_part, n_parts, rows, D, out, lse, dtype, s)
+                   : launch_t(static_cast<const float*>(o_part), l_part, n_parts, rows, D, out, lse, dtype, s);
 }
 
 }  // namespace ts

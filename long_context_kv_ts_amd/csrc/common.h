@@ -235,18 +235,16 @@ int mfma_tile_keys();
 hipError_t launch_attn_split_valu(const AttnArgs& a, ts_dtype dtype, hipStream_t s);
 hipError_t launch_attn_split_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_split_small(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attn_merge(const float* o_part, const float* l_part, int n_parts, int rows,
+// o_part: fp32, or bf16 when part_bf16
+hipError_t launch_attn_merge(const void* o_part, bool part_bf16, const float* l_part, int n_parts, int rows,
                              int D, void* out, float* lse, ts_dtype dtype, hipStream_t s);
-// the same merge of bf16 partials (those a call keeps in its own workspace)
-hipError_t launch_attn_merge_h(const bf16_t* o_part, const float* l_part, int n_parts, int rows,
-                               int D, void* out, float* lse, ts_dtype dtype, hipStream_t s);
 hipError_t launch_importance(const void* q, const void* kc, int64_t stride, float* scores,
                              int R, int Hq, int Hkv, int D, int64_t L, int chunk, float scale,
                              ts_dtype dtype, hipStream_t s);
 // The merge and the 64-token chunk importance in one grid (fused.hip), for the
 // shapes merge_importance_fusable accepts.
 bool merge_importance_fusable(int n_parts, int Dm, int Di, int R, int Hq, int Hkv, int chunk, ts_dtype dtype);
-hipError_t launch_merge_importance(const float* o_part, const float* l_part, int n_parts, int rows, void* out,
+hipError_t launch_merge_importance(const void* o_part, bool part_bf16, const float* l_part, int n_parts, int rows, void* out,
                                    float* lse, ts_dtype out_dtype, const void* q, const void* kc,
                                    int64_t stride, float* scores, int R, int Hq, int Hkv, int64_t L,
                                    float scale, hipStream_t s);
@@ -255,7 +253,7 @@ hipError_t launch_topk(const float* scores, int Hkv, int n, int k, int32_t* idx,
 // The merge and the top-k selection in one grid (fused.hip), for the merges
 // merge_topk_fusable accepts.
 bool merge_topk_fusable(int n_parts, int Dm);
-hipError_t launch_merge_topk(const float* o_part, const float* l_part, int n_parts, int rows, void* out, float* lse,
+hipError_t launch_merge_topk(const void* o_part, bool part_bf16, const float* l_part, int n_parts, int rows, void* out, float* lse,
                              ts_dtype out_dtype, const float* scores, int Hkv, int n, int k, int32_t* idx, float* val,
                              hipStream_t s);
 hipError_t launch_gather(const void* kc, const void* vc, int64_t stride, const int32_t* idx,

@@ -18,7 +18,7 @@ namespace ts {
 namespace {
 
 struct MergePart {
-  const float* o_part;
+  const void* o_part;        // fp32, or bf16 (the kernels' Tin)
   const float* l_part;
   int S, rows;
   void* out;
@@ -34,7 +34,7 @@ struct ImportancePart {
   float scale;
 };
 
-template <typename Tout, int NRB, bool kPow2>
+template <typename Tout, typename Tin, int NRB, bool kPow2>
 __global__ __launch_bounds__(256) void merge_importance_kernel(MergePart m, ImportancePart p, int imp_bx) {
   static_assert(MergeShape<1>::block == 256, "a merge workgroup is the launch's 256 threads");
   // chunk scoring first, merged rows last: the merge's short workgroups fill
@@ -45,19 +45,27 @@ __global__ __launch_bounds__(256) void merge_importance_kernel(MergePart m, Impo
                                         b % imp_bx, b / imp_bx, imp_bx);
     return;
   }
-  merge_block<Tout, 128, 1>(m.o_part, m.l_part, m.S, m.rows, static_cast<Tout*>(m.out), m.lse, b - imp_blocks);
+  merge_block<Tout, 128, 1, Tin>(static_cast<const Tin*>(m.o_part), m.l_part, m.S, m.rows,
+                                 static_cast<Tout*>(m.out), m.lse, b - imp_blocks);
 }
 
-template <typename Tout, bool kPow2>
+template <typename Tout, typename Tin, bool kPow2>
 hipError_t launch_rows(const MergePart& m, const ImportancePart& p, int imp_bx, int blocks, int rows_i,
                        hipStream_t s) {
   if (rows_i <= 16)
-    merge_importance_kernel<Tout, 1, kPow2><<<blocks, 256, 0, s>>>(m, p, imp_bx);
+    merge_importance_kernel<Tout, Tin, 1, kPow2><<<blocks, 256, 0, s>>>(m, p, imp_bx);
   else if (rows_i <= 32)
-    merge_importance_kernel<Tout, 2, kPow2><<<blocks, 256, 0, s>>>(m, p, imp_bx);
+    merge_importance_kernel<Tout, Tin, 2, kPow2><<<blocks, 256, 0, s>>>(m, p, imp_bx);
   else
-    merge_importance_kernel<Tout, 4, kPow2><<<blocks, 256, 0, s>>>(m, p, imp_bx);
+    merge_importance_kernel<Tout, Tin, 4, kPow2><<<blocks, 256, 0, s>>>(m, p, imp_bx);
   return hipGetLastError();
+}
+
+template <typename Tout, typename Tin>
+hipError_t launch_rows_t(const MergePart& m, const ImportancePart& p, int imp_bx, int blocks, int rows_i,
+                         bool pow2, hipStream_t s) {
+  return pow2 ? launch_rows<Tout, Tin, true>(m, p, imp_bx, blocks, rows_i, s)
+              : launch_rows<Tout, Tin, false>(m, p, imp_bx, blocks, rows_i, s);
 }
 
 // The verify merge and the top-k chunk selection in one launch: the first Hkv
@@ -70,14 +78,21 @@ struct TopkPart {
   float* val;
 };
 
-template <typename Tout, bool kResident>
+template <typename Tout, typename Tin, bool kResident>
 __global__ __launch_bounds__(256) void merge_topk_kernel(MergePart m, TopkPart t, int Hkv) {
   const int b = blockIdx.x;
   if (b < Hkv) {
     topk_block<256, 8, kResident>(t.scores, t.n, t.k, t.idx, t.val, b);
     return;
   }
-  merge_block<Tout, 128, 1>(m.o_part, m.l_part, m.S, m.rows, static_cast<Tout*>(m.out), m.lse, b - Hkv);
+  merge_block<Tout, 128, 1, Tin>(static_cast<const Tin*>(m.o_part), m.l_part, m.S, m.rows,
+                                 static_cast<Tout*>(m.out), m.lse, b - Hkv);
+}
+
+template <typename Tout, typename Tin>
+void launch_merge_topk_t(const MergePart& m, const TopkPart& t, int Hkv, int blocks, bool resident, hipStream_t s) {
+  if (resident) merge_topk_kernel<Tout, Tin, true><<<blocks, 256, 0, s>>>(m, t, Hkv);
+  else merge_topk_kernel<Tout, Tin, false><<<blocks, 256, 0, s>>>(m, t, Hkv);
 }
 
 }  // namespace
@@ -87,9 +102,9 @@ bool merge_topk_fusable(int n_parts, int Dm) {
   return Dm == 128 && need <= kWave;
 }
 
-hipError_t launch_merge_topk(const float* o_part, const float* l_part, int n_parts, int rows, void* out, float* lse,
-                             ts_dtype out_dtype, const float* scores, int Hkv, int n, int k, int32_t* idx, float* val,
-                             hipStream_t s) {
+hipError_t launch_merge_topk(const void* o_part, bool part_bf16, const float* l_part, int n_parts, int rows, void* out,
+                             float* lse, ts_dtype out_dtype, const float* scores, int Hkv, int n, int k, int32_t* idx,
+                             float* val, hipStream_t s) {
   const int merge_blocks = (rows + MergeShape<1>::rows - 1) / MergeShape<1>::rows;
   const int64_t blocks = (int64_t)merge_blocks + Hkv;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
@@ -97,11 +112,11 @@ hipError_t launch_merge_topk(const float* o_part, const float* l_part, int n_par
   const TopkPart t{scores, n, k, idx, val};
   const bool resident = n <= 256 * 8;
   if (out_dtype == TS_BF16) {
-    if (resident) merge_topk_kernel<bf16_t, true><<<(int)blocks, 256, 0, s>>>(m, t, Hkv);
-    else merge_topk_kernel<bf16_t, false><<<(int)blocks, 256, 0, s>>>(m, t, Hkv);
+    if (part_bf16) launch_merge_topk_t<bf16_t, bf16_t>(m, t, Hkv, (int)blocks, resident, s);
+    else launch_merge_topk_t<bf16_t, float>(m, t, Hkv, (int)blocks, resident, s);
   } else {
-    if (resident) merge_topk_kernel<float, true><<<(int)blocks, 256, 0, s>>>(m, t, Hkv);
-    else merge_topk_kernel<float, false><<<(int)blocks, 256, 0, s>>>(m, t, Hkv);
+    if (part_bf16) launch_merge_topk_t<float, bf16_t>(m, t, Hkv, (int)blocks, resident, s);
+    else launch_merge_topk_t<float, float>(m, t, Hkv, (int)blocks, resident, s);
   }
   return hipGetLastError();
 }
@@ -111,7 +126,7 @@ bool merge_importance_fusable(int n_parts, int Dm, int Di, int R, int Hq, int Hk
   return Dm == 128 && Di == 128 && need <= kWave && dtype == TS_BF16 && chunk == 64 && R * (Hq / Hkv) <= 64;
 }
 
-hipError_t launch_merge_importance(const float* o_part, const float* l_part, int n_parts, int rows, void* out,
+hipError_t launch_merge_importance(const void* o_part, bool part_bf16, const float* l_part, int n_parts, int rows, void* out,
                                    float* lse, ts_dtype out_dtype, const void* q, const void* kc,
                                    int64_t stride, float* scores, int R, int Hq, int Hkv, int64_t L,
                                    float scale, hipStream_t s) {
@@ -126,10 +141,10 @@ hipError_t launch_merge_importance(const float* o_part, const float* l_part, int
   const int G = Hq / Hkv, rows_i = R * G;
   const bool pow2 = (G & (G - 1)) == 0;
   if (out_dtype == TS_BF16)
-    return pow2 ? launch_rows<bf16_t, true>(m, p, imp_bx, (int)blocks, rows_i, s)
-                : launch_rows<bf16_t, false>(m, p, imp_bx, (int)blocks, rows_i, s);
-  return pow2 ? launch_rows<float, true>(m, p, imp_bx, (int)blocks, rows_i, s)
-              : launch_rows<float, false>(m, p, imp_bx, (int)blocks, rows_i, s);
+    return part_bf16 ? launch_rows_t<bf16_t, bf16_t>(m, p, imp_bx, (int)blocks, rows_i, pow2, s)
+                     : launch_rows_t<bf16_t, float>(m, p, imp_bx, (int)blocks, rows_i, pow2, s);
+  return part_bf16 ? launch_rows_t<float, bf16_t>(m, p, imp_bx, (int)blocks, rows_i, pow2, s)
+                   : launch_rows_t<float, float>(m, p, imp_bx, (int)blocks, rows_i, pow2, s);
 }
 
 }  // namespace ts

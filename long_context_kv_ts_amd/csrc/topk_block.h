@@ -10,12 +10,17 @@
 // Scores map to order-preserving 32-bit keys (larger score -> larger key; -0
 // and +0 share a key). Ties go to the lower chunk index and the chosen chunks
 // are written in ascending index order, so no sort is needed:
-//   1. four 8-bit radix passes over an LDS histogram find the exact key `thr`
-//      of the k-th largest element and how many (`need`) of the elements equal
-//      to it are kept -- the lowest-indexed ones;
-//   2. an exclusive count, in index order, of elements above `thr` and of
-//      elements equal to it gives every kept element its output slot
-//      (slot = above_before + min(equal_before, need)).
+//   1. up to four 8-bit radix passes over an LDS histogram find the prefix
+//      `thr` (the bits `mask` covers) of the k-th largest element's offset
+//      d = key - (smallest key) and how many (`need`) of the elements with
+//      that prefix are kept -- the lowest-indexed ones. Digits are taken from
+//      the top of d's range, so the first pass already spreads the keys over
+//      the bins (scores of one magnitude share their top key bits, and would
+//      crowd one bin's atomics). The passes stop early once the bin of the k-th
+//      element holds exactly `need` elements: all of them are kept;
+//   2. an exclusive count, in index order, of elements whose prefix is above
+//      `thr` and of elements equal to it gives every kept element its output
+//      slot (slot = above_before + min(equal_before, need)).
 // Thread t of kNT owns elements t, t + kNT, t + 2 kNT, ... (coalesced loads).
 // With n <= kNT * kPer the keys stay in registers across all passes; larger n
 // re-reads the scores (L2-resident) in every pass. Per-wave counts come from ballots,
@@ -43,7 +48,7 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ scores, int
   static_assert(kPer * kWaves <= kWave, "one scan lane per (round element, wave)");
   __shared__ uint32_t hist[2][256];
   __shared__ uint32_t cnt_gt[kPer * kWaves], cnt_eq[kPer * kWaves];
-  __shared__ uint32_t sh_digit, sh_need;
+  __shared__ uint32_t sh_digit, sh_need, sh_whole, sh_kmin, sh_kmax;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const float* s = scores + (int64_t)g * n;
   const int n_rounds = (n + kRound - 1) / kRound;
@@ -65,20 +70,55 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ scores, int
   };
 
   if (tid < 512) (&hist[0][0])[tid] = 0u;
+  if (tid == 0) {
+    sh_kmin = 0xFFFFFFFFu;
+    sh_kmax = 0u;
+  }
   __syncthreads();
 
-  // 1. radix select of the k-th largest key
+  // the keys' range
+  {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int r = 0; r < n_rounds; ++r)
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = (r * kPer + j) * kThreads + tid;
+        if (i < n) {
+          lo = min(lo, key_at(r, j));
+          hi = max(hi, key_at(r, j));
+        }
+      }
+    lo = __float_as_uint(wave_reduce(__uint_as_float(lo), [](float a, float b) {
+      return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
+    }));
+    hi = __float_as_uint(wave_reduce(__uint_as_float(hi), [](float a, float b) {
+      return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
+    }));
+    if (lane == 0) {
+      atomicMin(&sh_kmin, lo);
+      atomicMax(&sh_kmax, hi);
+    }
+  }
+  __syncthreads();
+  const uint32_t kmin = sh_kmin;
+  const int nbits = sh_kmax == kmin ? 0 : 32 - __clz((int)(sh_kmax - kmin));
+  const int n_passes = (nbits + 7) / 8;  // 8-bit digits from the top of d's range
+
+  // 1. radix select of the k-th largest offset
   uint32_t prefix = 0u, mask = 0u, need = (uint32_t)k;
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+    if (pass >= n_passes || (pass > 0 && sh_whole)) break;   // uniform (read after the last barrier)
+    // the next 8 bits below those already decided (the last pass may overlap
+    // decided bits, which all candidates share)
+    const int shift = max(nbits - 8 * (pass + 1), 0);
     uint32_t* h = hist[pass & 1];
     for (int r = 0; r < n_rounds; ++r)
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         const int i = (r * kPer + j) * kThreads + tid;
-        const uint32_t key = key_at(r, j);
-        if (i < n && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+        const uint32_t d = key_at(r, j) - kmin;
+        if (i < n && (d & mask) == prefix) atomicAdd(&h[(d >> shift) & 255u], 1u);
       }
     __syncthreads();
     if (wave == 0) {
@@ -95,6 +135,7 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ scores, int
         if (above < need && above + c[j] >= need) {
           sh_digit = 255u - 4u * lane - j;
           sh_need = need - above;
+          sh_whole = above + c[j] == need;   // the whole bin is kept
         }
         above += c[j];
       }
@@ -109,7 +150,7 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ scores, int
     mask |= 255u << shift;
     need = sh_need;
   }
-  const uint32_t thr = prefix;
+  const uint32_t thr = prefix;             // the k-th element's offset on the bits of `mask`
 
   // 2. index-order compaction
   uint32_t base_gt = 0u, base_eq = 0u;          // wave 0: counts of earlier rounds
@@ -119,9 +160,9 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ scores, int
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int i = (r * kPer + j) * kThreads + tid;
-      key[j] = key_at(r, j);
-      gt[j] = i < n && key[j] > thr;
-      eq[j] = i < n && key[j] == thr;
+      key[j] = key_at(r, j) - kmin;
+      gt[j] = i < n && (key[j] & mask) > thr;
+      eq[j] = i < n && (key[j] & mask) == thr;
       const uint64_t bg = __ballot(gt[j]), be = __ballot(eq[j]);
       pg[j] = popc_below(bg, lane);
       pe[j] = popc_below(be, lane);

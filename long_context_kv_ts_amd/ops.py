@@ -47,22 +47,23 @@ SIGNATURES = {
                                              _c_i64, _c_f, _c_int, _c_int, _c_void_p]),
     "ts_tree_verify_attn_num_splits": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_i64, _c_int, _c_int]),
     "ts_tree_verify_attn_partials": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_void_p,
-                                              _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                              _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_int,
                                               _c_int, _c_int, _c_int, _c_i64, _c_f, _c_int, _c_int,
                                               _c_void_p]),
     "ts_tree_verify_attn_partials_and_importance": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_i64, _c_void_p,
-                                                             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
-                                                             _c_int, _c_int, _c_int, _c_i64, _c_f, _c_int, _c_int,
-                                                             _c_void_p, _c_int, _c_int, _c_f, _c_void_p, _c_void_p]),
-    "ts_attn_merge": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                                             _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p,
+                                                             _c_int, _c_int, _c_int, _c_int, _c_i64, _c_f, _c_int,
+                                                             _c_int, _c_void_p, _c_int, _c_int, _c_f, _c_void_p,
+                                                             _c_void_p]),
+    "ts_attn_merge": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                _c_int, _c_void_p]),
     "ts_kv_importance_score": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int,
                                         _c_int, _c_int, _c_i64, _c_int, _c_f, _c_int, _c_void_p]),
-    "ts_attn_merge_and_importance": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
-                                              _c_int, _c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int,
-                                              _c_int, _c_int, _c_i64, _c_int, _c_f, _c_int, _c_void_p]),
-    "ts_attn_merge_and_topk": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_int,
-                                        _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
+    "ts_attn_merge_and_importance": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
+                                              _c_void_p, _c_int, _c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int,
+                                              _c_int, _c_int, _c_int, _c_i64, _c_int, _c_f, _c_int, _c_void_p]),
+    "ts_attn_merge_and_topk": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                        _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "ts_kv_topk_select": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "ts_kv_gather": (_c_int, [_c_void_p, _c_void_p, _c_i64, _c_void_p, _c_int, _c_int, _c_int, _c_int,
                               _c_i64, _c_void_p, _c_void_p, _c_int, _c_void_p]),
@@ -200,11 +201,25 @@ def _workspace(t: Optional[torch.Tensor], name: str, need: int, device) -> Optio
 
 
 def _parts(o_part, l_part, device=None) -> None:
-    """Split partials: o_part [S][..][D] and l_part [S][..], fp32 on one GPU."""
+    """Split partials: o_part [S][..][D] (fp32 or bf16) and l_part [S][..] fp32 on one GPU."""
     if not isinstance(o_part, torch.Tensor) or o_part.dim() < 2:
         raise ValueError("o_part must be a [S][..][D] tensor")
-    _need(o_part, "o_part", o_part.dim(), torch.float32, device)
+    if o_part.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"o_part: dtype {o_part.dtype}, expected float32 or bfloat16")
+    _need(o_part, "o_part", o_part.dim(), o_part.dtype, device)
     _need(l_part, "l_part", o_part.dim() - 1, torch.float32, o_part.device)
+
+
+def _part_code(o_part: torch.Tensor) -> int:
+    return TS_BF16 if o_part.dtype == torch.bfloat16 else TS_F32
+
+
+def _part_dtype(o_part, part_dtype) -> torch.dtype:
+    """The partials' dtype: the given o_part's, else part_dtype (float32 or bfloat16)."""
+    dt = o_part.dtype if o_part is not None else part_dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"o_part: dtype {dt}, expected float32 or bfloat16")
+    return dt
 
 
 def _nbytes(t: torch.Tensor) -> int:
@@ -327,8 +342,9 @@ def tree_verify_attn_noalloc(q, k_cache, v_cache, k_draft, v_draft, parent, *, s
 
 
 def tree_verify_attn_partials(q, k_cache, v_cache, k_draft, v_draft, parent, *, scale=None,
-                              o_part=None, l_part=None, num_splits: int = 0):
-    """ts_tree_verify_attn_partials -> (o_part [S][T][Hq][D] fp32, l_part [S][T][Hq] fp32)."""
+                              o_part=None, l_part=None, num_splits: int = 0, part_dtype=torch.float32):
+    """ts_tree_verify_attn_partials -> (o_part [S][T][Hq][D] in part_dtype (float32, or
+    bfloat16 for bf16 inputs; a given o_part's dtype wins), l_part [S][T][Hq] fp32)."""
     _need(q, "q", 3)
     dev = q.device
     T, Hq, D = q.shape
@@ -350,15 +366,16 @@ def tree_verify_attn_partials(q, k_cache, v_cache, k_draft, v_draft, parent, *, 
     if _cache_stride(v_cache, "v_cache") != stride:
         raise ValueError("k_cache and v_cache must share the row stride")
     S = globals()["num_splits"](T, Hq, Hkv, D, L, q.dtype, num_splits)
-    _out(o_part, "o_part", (S, T, Hq, D), torch.float32, dev)
+    pdt = _part_dtype(o_part, part_dtype)
+    _out(o_part, "o_part", (S, T, Hq, D), pdt, dev)
     _out(l_part, "l_part", (S, T, Hq), torch.float32, dev)
     if o_part is None:
-        o_part = torch.empty((S, T, Hq, D), dtype=torch.float32, device=dev)
+        o_part = torch.empty((S, T, Hq, D), dtype=pdt, device=dev)
     if l_part is None:
         l_part = torch.empty((S, T, Hq), dtype=torch.float32, device=dev)
     _check(lib().ts_tree_verify_attn_partials(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stride, k_draft.data_ptr(),
-        v_draft.data_ptr(), parent.data_ptr(), o_part.data_ptr(), l_part.data_ptr(), T, Hq, Hkv,
+        v_draft.data_ptr(), parent.data_ptr(), o_part.data_ptr(), _part_code(o_part), l_part.data_ptr(), T, Hq, Hkv,
         D, L, float(1.0 / math.sqrt(D) if scale is None else scale), _dtype_code(q), num_splits,
         _stream(dev)))
     return o_part, l_part
@@ -366,10 +383,11 @@ def tree_verify_attn_partials(q, k_cache, v_cache, k_draft, v_draft, parent, *, 
 
 def tree_verify_attn_partials_and_importance(q, k_cache, v_cache, k_draft, v_draft, parent, q_recent, chunk: int,
                                              *, scale=None, imp_scale=None, o_part=None, l_part=None, scores=None,
-                                             num_splits: int = 0):
+                                             num_splits: int = 0, part_dtype=torch.float32):
     """ts_tree_verify_attn_partials_and_importance: the verify split partials
-    and the chunk importance of the same cache for the recent queries q_recent
-    [R][Hq][D], in one launch where the shapes allow -> (o_part, l_part, scores)."""
+    (o_part in part_dtype, as tree_verify_attn_partials) and the chunk
+    importance of the same cache for the recent queries q_recent [R][Hq][D], in
+    one launch where the shapes allow -> (o_part, l_part, scores)."""
     _need(q, "q", 3)
     dev = q.device
     T, Hq, D = q.shape
@@ -393,11 +411,12 @@ def tree_verify_attn_partials_and_importance(q, k_cache, v_cache, k_draft, v_dra
     if _cache_stride(v_cache, "v_cache") != stride:
         raise ValueError("k_cache and v_cache must share the row stride")
     S = globals()["num_splits"](T, Hq, Hkv, D, L, q.dtype, num_splits)
-    _out(o_part, "o_part", (S, T, Hq, D), torch.float32, dev)
+    pdt = _part_dtype(o_part, part_dtype)
+    _out(o_part, "o_part", (S, T, Hq, D), pdt, dev)
     _out(l_part, "l_part", (S, T, Hq), torch.float32, dev)
     _out(scores, "scores", (Hkv, L // max(int(chunk), 1)), torch.float32, dev)
     if o_part is None:
-        o_part = torch.empty((S, T, Hq, D), dtype=torch.float32, device=dev)
+        o_part = torch.empty((S, T, Hq, D), dtype=pdt, device=dev)
     if l_part is None:
         l_part = torch.empty((S, T, Hq), dtype=torch.float32, device=dev)
     if scores is None:
@@ -406,13 +425,14 @@ def tree_verify_attn_partials_and_importance(q, k_cache, v_cache, k_draft, v_dra
     isc = float(1.0 / math.sqrt(D) if imp_scale is None else imp_scale)
     _check(lib().ts_tree_verify_attn_partials_and_importance(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stride, k_draft.data_ptr(), v_draft.data_ptr(),
-        parent.data_ptr(), o_part.data_ptr(), l_part.data_ptr(), T, Hq, Hkv, D, L, sc, _dtype_code(q), num_splits,
+        parent.data_ptr(), o_part.data_ptr(), _part_code(o_part), l_part.data_ptr(), T, Hq, Hkv, D, L, sc,
+        _dtype_code(q), num_splits,
         q_recent.data_ptr(), R, int(chunk), isc, scores.data_ptr(), _stream(dev)))
     return o_part, l_part, scores
 
 
 def attn_merge(o_part, l_part, *, out_dtype=torch.bfloat16, out=None, lse=None):
-    """ts_attn_merge over the leading (parts) dim: o_part [S][..][D], l_part [S][..]."""
+    """ts_attn_merge over the leading (parts) dim: o_part [S][..][D] (fp32 or bf16), l_part [S][..]."""
     _parts(o_part, l_part)
     dev = o_part.device
     _contig(o_part, "o_part")
@@ -428,7 +448,7 @@ def attn_merge(o_part, l_part, *, out_dtype=torch.bfloat16, out=None, lse=None):
         out = torch.empty(o_part.shape[1:], dtype=out_dtype, device=dev)
     if lse is None:
         lse = torch.empty(l_part.shape[1:], dtype=torch.float32, device=dev)
-    _check(lib().ts_attn_merge(o_part.data_ptr(), l_part.data_ptr(), S, rows, D, out.data_ptr(),
+    _check(lib().ts_attn_merge(o_part.data_ptr(), _part_code(o_part), l_part.data_ptr(), S, rows, D, out.data_ptr(),
                                lse.data_ptr(), _dtype_code(out), _stream(dev)))
     return out, lse
 
@@ -481,8 +501,8 @@ def attn_merge_and_importance(o_part, l_part, q_recent, k_cache, chunk: int, *, 
     if scores is None:
         scores = torch.empty((Hkv, L // chunk), dtype=torch.float32, device=dev)
     _check(lib().ts_attn_merge_and_importance(
-        o_part.data_ptr(), l_part.data_ptr(), S, rows, Dv, out.data_ptr(), lse.data_ptr(), _dtype_code(out),
-        q_recent.data_ptr(), k_cache.data_ptr(), stride, scores.data_ptr(), R, Hq, Hkv, D, L, chunk,
+        o_part.data_ptr(), _part_code(o_part), l_part.data_ptr(), S, rows, Dv, out.data_ptr(), lse.data_ptr(),
+        _dtype_code(out), q_recent.data_ptr(), k_cache.data_ptr(), stride, scores.data_ptr(), R, Hq, Hkv, D, L, chunk,
         float(1.0 / math.sqrt(D) if scale is None else scale), _dtype_code(q_recent), _stream(dev)))
     return out, lse, scores
 
@@ -515,7 +535,8 @@ def attn_merge_and_topk(o_part, l_part, scores, k: int, *, out_dtype=torch.bfloa
         chunk_idx = torch.empty((Hkv, k), dtype=torch.int32, device=dev)
     if chunk_score is None and want_scores:
         chunk_score = torch.empty((Hkv, k), dtype=torch.float32, device=dev)
-    _check(lib().ts_attn_merge_and_topk(o_part.data_ptr(), l_part.data_ptr(), S, rows, Dv, out.data_ptr(),
+    _check(lib().ts_attn_merge_and_topk(o_part.data_ptr(), _part_code(o_part), l_part.data_ptr(), S, rows, Dv,
+                                        out.data_ptr(),
                                         lse.data_ptr(), _dtype_code(out), scores.data_ptr(), Hkv, n, k,
                                         chunk_idx.data_ptr(),
                                         chunk_score.data_ptr() if chunk_score is not None else None, _stream(dev)))

@@ -40,7 +40,7 @@ def test_every_declared_function_is_exported_and_bound():
         assert name in ops.SIGNATURES, f"{name} not bound in ops.py"
         assert len(ops.SIGNATURES[name][1]) == nargs, f"{name}: binding has wrong arg count"
     assert set(ops.SIGNATURES) == set(protos)
-    assert lib.ts_abi_version() == 2
+    assert lib.ts_abi_version() == 3
 
 
 def test_every_probe_function_is_exported_and_bound():
@@ -126,17 +126,24 @@ def test_workspace_query():
 
 def test_partials_and_merge_reject():
     lib = ops.lib()
-    st = lib.ts_tree_verify_attn_partials(P, P, P, 64, P, P, None, P, P, 4, 4, 1, 64, 64, 0.1, F, 0, None)
+    st = lib.ts_tree_verify_attn_partials(P, P, P, 64, P, P, None, P, F, P, 4, 4, 1, 64, 64, 0.1, F, 0, None)
     assert st == ops.TS_ERR_INVALID_ARG and "parent" in _err()
+    # partial dtypes: fp32 always, bf16 only for bf16 inputs, nothing else
+    st = lib.ts_tree_verify_attn_partials(P, P, P, 64, P, P, P, P, B, P, 4, 4, 1, 64, 64, 0.1, F, 0, None)
+    assert st == ops.TS_ERR_UNSUPPORTED and "bf16 partials" in _err(), _err()
+    st = lib.ts_tree_verify_attn_partials(P, P, P, 64, P, P, P, P, 7, P, 4, 4, 1, 64, 64, 0.1, B, 0, None)
+    assert st == ops.TS_ERR_INVALID_ARG and "part_dtype" in _err(), _err()
     # fp32 rows go 16 to a workgroup: 65535 splits x 256 KV heads x 1024 row groups is
     # more workgroups than one launch holds
-    st = lib.ts_tree_verify_attn_partials(P, P, P, 1 << 30, P, P, P, P, P, 1024, 4096, 256, 128, 1 << 30,
+    st = lib.ts_tree_verify_attn_partials(P, P, P, 1 << 30, P, P, P, P, F, P, 1024, 4096, 256, 128, 1 << 30,
                                           0.1, F, 65535, None)
     assert st == ops.TS_ERR_UNSUPPORTED and "one launch" in _err(), _err()
-    assert lib.ts_attn_merge(P, P, 0, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
-    assert lib.ts_attn_merge(P, P, 2, 10, 100, P, P, B, None) == ops.TS_ERR_UNSUPPORTED
-    assert lib.ts_attn_merge(None, P, 2, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
-    assert lib.ts_attn_merge(MIS, P, 2, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_attn_merge(P, F, P, 0, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_attn_merge(P, F, P, 2, 10, 100, P, P, B, None) == ops.TS_ERR_UNSUPPORTED
+    assert lib.ts_attn_merge(None, F, P, 2, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_attn_merge(MIS, B, P, 2, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
+    assert lib.ts_attn_merge(P, 7, P, 2, 10, 128, P, P, B, None) == ops.TS_ERR_INVALID_ARG
+    assert "part_dtype" in _err()
 
 
 def test_merge_and_importance_rejects():
@@ -145,10 +152,11 @@ def test_merge_and_importance_rejects():
     lib = ops.lib()
 
     def call(**kw):
-        a = dict(o=P, l=P, S=16, rows=3840, Dv=128, out=P, lse=P, odt=B, q=P, k=P, stride=4096, scores=P,
+        a = dict(o=P, pdt=F, l=P, S=16, rows=3840, Dv=128, out=P, lse=P, odt=B, q=P, k=P, stride=4096, scores=P,
                  R=4, Hq=32, Hkv=8, D=128, L=4096, chunk=64, scale=0.1, dt=B)
         a.update(kw)
-        return lib.ts_attn_merge_and_importance(a["o"], a["l"], a["S"], a["rows"], a["Dv"], a["out"], a["lse"],
+        return lib.ts_attn_merge_and_importance(a["o"], a["pdt"], a["l"], a["S"], a["rows"], a["Dv"], a["out"],
+                                                a["lse"],
                                                 a["odt"], a["q"], a["k"], a["stride"], a["scores"], a["R"],
                                                 a["Hq"], a["Hkv"], a["D"], a["L"], a["chunk"], a["scale"],
                                                 a["dt"], None)
@@ -161,6 +169,7 @@ def test_merge_and_importance_rejects():
     assert call(R=8, Hq=128) == ops.TS_ERR_UNSUPPORTED     # R*G = 128 > 64
     assert call(q=None) == ops.TS_ERR_INVALID_ARG
     assert call(dt=7) == ops.TS_ERR_INVALID_ARG
+    assert call(pdt=7) == ops.TS_ERR_INVALID_ARG and "part_dtype" in _err()
 
 
 def test_merge_and_topk_rejects():
@@ -169,10 +178,10 @@ def test_merge_and_topk_rejects():
     lib = ops.lib()
 
     def call(**kw):
-        a = dict(o=P, l=P, S=16, rows=3840, Dv=128, out=P, lse=P, odt=B, scores=P, Hkv=8, n=1600, k=64,
+        a = dict(o=P, pdt=F, l=P, S=16, rows=3840, Dv=128, out=P, lse=P, odt=B, scores=P, Hkv=8, n=1600, k=64,
                  idx=P, val=P)
         a.update(kw)
-        return lib.ts_attn_merge_and_topk(a["o"], a["l"], a["S"], a["rows"], a["Dv"], a["out"], a["lse"],
+        return lib.ts_attn_merge_and_topk(a["o"], a["pdt"], a["l"], a["S"], a["rows"], a["Dv"], a["out"], a["lse"],
                                           a["odt"], a["scores"], a["Hkv"], a["n"], a["k"], a["idx"], a["val"],
                                           None)
     assert call(S=0) == ops.TS_ERR_INVALID_ARG
@@ -186,6 +195,7 @@ def test_merge_and_topk_rejects():
     assert call(n=65537, k=4) == ops.TS_ERR_UNSUPPORTED
     assert call(Hkv=0) == ops.TS_ERR_INVALID_ARG
     assert call(odt=7) == ops.TS_ERR_INVALID_ARG
+    assert call(pdt=7) == ops.TS_ERR_INVALID_ARG and "part_dtype" in _err()
 
 
 def test_gather_and_draft_attn_rejects():
@@ -227,7 +237,7 @@ def test_draft_attn_rejects():
     # -inf logits into +inf): rejected before any launch
     st = lib.ts_partial_draft_attn(P, P, P, P, P, P, P, 4, 32, 8, 128, 4096, -0.1, B, 0, P, 1 << 30, None)
     assert st == ops.TS_ERR_INVALID_ARG and "> 0" in _err()
-    st = lib.ts_tree_verify_attn_partials(P, P, P, 64, P, P, P, P, P, 4, 4, 1, 64, 64, -0.1, F, 0, None)
+    st = lib.ts_tree_verify_attn_partials(P, P, P, 64, P, P, P, P, F, P, 4, 4, 1, 64, 64, -0.1, F, 0, None)
     assert st == ops.TS_ERR_INVALID_ARG and "> 0" in _err()
 
 
@@ -410,11 +420,12 @@ def test_partials_and_importance_rejects():
     lib = ops.lib()
 
     def call(**kw):
-        a = dict(q=P, kc=P, vc=P, stride=4096, kd=P, vd=P, parent=P, o=P, l=P, T=120, Hq=32, Hkv=8, D=128, L=4096,
-                 scale=0.088, dt=B, ns=0, qr=P, R=4, chunk=64, isc=0.088, scores=P)
+        a = dict(q=P, kc=P, vc=P, stride=4096, kd=P, vd=P, parent=P, o=P, pdt=B, l=P, T=120, Hq=32, Hkv=8, D=128,
+                 L=4096, scale=0.088, dt=B, ns=0, qr=P, R=4, chunk=64, isc=0.088, scores=P)
         a.update(kw)
         return lib.ts_tree_verify_attn_partials_and_importance(
-            a["q"], a["kc"], a["vc"], a["stride"], a["kd"], a["vd"], a["parent"], a["o"], a["l"], a["T"], a["Hq"],
+            a["q"], a["kc"], a["vc"], a["stride"], a["kd"], a["vd"], a["parent"], a["o"], a["pdt"], a["l"], a["T"],
+            a["Hq"],
             a["Hkv"], a["D"], a["L"], a["scale"], a["dt"], a["ns"], a["qr"], a["R"], a["chunk"], a["isc"],
             a["scores"], None)
     name = "ts_tree_verify_attn_partials_and_importance"
@@ -425,3 +436,5 @@ def test_partials_and_importance_rejects():
     assert call(parent=None) == ops.TS_ERR_INVALID_ARG
     assert call(scale=-1.0) == ops.TS_ERR_INVALID_ARG and "> 0" in _err()
     assert call(o=MIS) == ops.TS_ERR_INVALID_ARG
+    assert call(pdt=7) == ops.TS_ERR_INVALID_ARG and "part_dtype" in _err()
+    assert call(dt=F) == ops.TS_ERR_UNSUPPORTED and "bf16 partials" in _err()

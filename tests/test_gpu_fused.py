@@ -39,11 +39,13 @@ def _inputs(seed, S, T, Hq_v, Dv, R, Hq, Hkv, D, L, empty_splits=False):
     dict(S=16, T=120, Hq_v=32, Dv=64, R=4, Hq=32, Hkv=8, D=64, L=64 * 50, chunk=64, odt=torch.bfloat16),
     dict(S=16, T=120, Hq_v=32, Dv=128, R=4, Hq=32, Hkv=8, D=128, L=32 * 77, chunk=32, odt=torch.bfloat16),
 ], ids=["bench-shape", "G7", "rows64-f32", "S20-two-launches", "D64-two-launches", "chunk32-two-launches"])
-def test_bit_identical_to_separate_calls(case):
+@pytest.mark.parametrize("pdt", [torch.float32, torch.bfloat16], ids=["f32-partials", "bf16-partials"])
+def test_bit_identical_to_separate_calls(case, pdt):
     c = dict(case)
     odt, chunk = c.pop("odt"), c.pop("chunk")
-    say(f"fused merge+importance {case}")
+    say(f"fused merge+importance {case} partials {pdt}")
     o_part, l_part, q, k = _inputs(5, **c, empty_splits=True)
+    o_part = o_part.to(pdt)
     out_a, lse_a = ops.attn_merge(o_part, l_part, out_dtype=odt)
     scores_a = ops.kv_importance_score(q, k, chunk, scale=0.09)
     out_b, lse_b, scores_b = ops.attn_merge_and_importance(o_part, l_part, q, k, chunk, out_dtype=odt, scale=0.09)
@@ -110,14 +112,14 @@ def _dev(a, dt):
     return to_dev(a, dt)
 
 
-def _partials_and_scores(c, q_rec, chunk, imp_scale, num_splits=0):
+def _partials_and_scores(c, q_rec, chunk, imp_scale, num_splits=0, part_dtype=torch.float32):
     dt = c.dtype
     args = (_dev(c.q, dt), _dev(c.k_cache, dt), _dev(c.v_cache, dt), _dev(c.k_draft, dt), _dev(c.v_draft, dt),
             _dev(c.parent, "i32"))
     qr = _dev(q_rec, dt)
     o1, l1, s1 = ops.tree_verify_attn_partials_and_importance(*args, qr, chunk, scale=c.scale, imp_scale=imp_scale,
-                                                             num_splits=num_splits)
-    o2, l2 = ops.tree_verify_attn_partials(*args, scale=c.scale, num_splits=num_splits)
+                                                             num_splits=num_splits, part_dtype=part_dtype)
+    o2, l2 = ops.tree_verify_attn_partials(*args, scale=c.scale, num_splits=num_splits, part_dtype=part_dtype)
     s2 = ops.kv_importance_score(qr, args[1], chunk, scale=imp_scale)
     torch.cuda.synchronize()
     return (o1, l1, s1), (o2, l2, s2)
@@ -125,7 +127,8 @@ def _partials_and_scores(c, q_rec, chunk, imp_scale, num_splits=0):
 
 def _check_same(fused, sep, label, imp_rel=1e-5):
     (o1, l1, s1), (o2, l2, s2) = fused, sep
-    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32)), f"{label}: partials differ"
+    iv = torch.int16 if o1.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(o1.view(iv), o2.view(iv)), f"{label}: partials differ"
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), f"{label}: partial lse differ"
     a, b = s1.cpu().numpy().astype(np.float64), s2.cpu().numpy().astype(np.float64)
     err = np.abs(a - b).max()
@@ -174,15 +177,16 @@ def test_partials_and_importance_full_size_against_the_oracle():
     dict(Hq=28, Hkv=4, T=40, L=64 * 33, R=4),       # G = 7 -> two launches
     dict(Hq=32, Hkv=8, T=300, L=64 * 20, R=4),      # more than 256 drafts -> two launches
 ])
-def test_partials_and_importance_shapes(case):
+@pytest.mark.parametrize("pdt", [torch.float32, torch.bfloat16], ids=["f32-partials", "bf16-partials"])
+def test_partials_and_importance_shapes(case, pdt):
     from long_context_kv_ts_amd import inputs
     c = inputs.make_verify("vi", dtype="bf16", Hq=case["Hq"], Hkv=case["Hkv"], D=128, L=case["L"], seed=31,
                            with_chains=False,
                            parent=np.array([-1 if t % 7 == 0 else t - 1 for t in range(case["T"])], np.int32))
     rng = np.random.default_rng(32)
     q_rec = inputs.f32_to_bf16_bits(rng.standard_normal((case["R"], case["Hq"], 128)).astype(np.float32))
-    say(f"[verify+importance] {case}")
-    fused, sep = _partials_and_scores(c, q_rec, 64, 0.0884)
+    say(f"[verify+importance] {case} partials {pdt}")
+    fused, sep = _partials_and_scores(c, q_rec, 64, 0.0884, part_dtype=pdt)
     _check_same(fused, sep, str(case))
 
 
@@ -221,10 +225,12 @@ def _scores(seed, Hkv, n, ties=False):
     dict(S=16, T=120, Hq_v=32, Dv=64, Hkv=8, n=1600, k=64, odt=torch.bfloat16),
 ], ids=["bench-shape", "k-equals-n", "streamed-f32", "tiny", "n20000", "S20-two-launches", "D64-two-launches"])
 @pytest.mark.parametrize("ties", [False, True], ids=["distinct", "ties"])
-def test_merge_topk_bit_identical_to_separate_calls(case, ties):
+@pytest.mark.parametrize("pdt", [torch.float32, torch.bfloat16], ids=["f32-partials", "bf16-partials"])
+def test_merge_topk_bit_identical_to_separate_calls(case, ties, pdt):
     c = dict(case)
-    say(f"fused merge+topk {case} ties={ties}")
+    say(f"fused merge+topk {case} ties={ties} partials {pdt}")
     o_part, l_part, _, _ = _inputs(7, c["S"], c["T"], c["Hq_v"], c["Dv"], 1, 1, 1, 64, 64, empty_splits=True)
+    o_part = o_part.to(pdt)
     scores = _scores(8, c["Hkv"], c["n"], ties)
     out_a, lse_a = ops.attn_merge(o_part, l_part, out_dtype=c["odt"])
     idx_a, val_a = ops.kv_topk_select(scores, c["k"])
@@ -327,7 +333,7 @@ def test_gather_draft_full_size_against_the_oracle():
 
 def test_bench_step_at_full_size_against_the_oracle():
     """The decode step exactly as the benchmark times it -- four kernels through
-    the three combined calls, on the 102,400-token LLaMA3.1-8B cache with its 4
+    the three combined calls (bf16 split partials), on the 102,400-token LLaMA3.1-8B cache with its 4
     recent queries and the 120-draft forest -- against the oracle: verify output
     and lse element by element, chunk scores within 1e-5, the top-64 bit-exact on
     the GPU's own scores and within the near-tie rule on the oracle's, the partial
@@ -344,7 +350,7 @@ def test_bench_step_at_full_size_against_the_oracle():
     parent = torch.from_numpy(vc.parent).to(DEV)
     pq = to_dev(pc.q, "bf16")
     o_part, l_part, scores = ops.tree_verify_attn_partials_and_importance(
-        q, kc, v_c, kd, vd, parent, pq, pc.chunk, scale=vc.scale, imp_scale=pc.scale)
+        q, kc, v_c, kd, vd, parent, pq, pc.chunk, scale=vc.scale, imp_scale=pc.scale, part_dtype=torch.bfloat16)
     out, lse, idx, _ = ops.attn_merge_and_topk(o_part, l_part, scores, pc.k)
     kp, vp, dout, dlse = ops.kv_gather_and_draft_attn(kc, v_c, idx, pc.chunk, pq, to_dev(pc.k_new, "bf16"),
                                                       to_dev(pc.v_new, "bf16"), scale=pc.scale)

@@ -248,3 +248,27 @@ def test_partials_then_merge_equal_single_call():
     out2, lse2 = ops.attn_merge(torch.stack([a_o, b_o]), torch.stack([a_l, b_l]), out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     check_attn(out2, lse2, ro, rl, "bf16", "merge of merges")
+
+
+def test_bf16_partials_then_merge_equal_single_call_bit_for_bit():
+    """ts_tree_verify_attn keeps its split partials in bf16 for bf16 inputs:
+    the exported partials in bf16 followed by ts_attn_merge are the same two
+    launches, so out and lse agree bit for bit; against the oracle both meet
+    the contract, and the fp32-partial form differs only by that rounding."""
+    say("[phases] bf16 partials + merge")
+    c, (ro, rl) = workload_with_ref("llama8b_20k", L=5000)
+    dt = c.dtype
+    args = (to_dev(c.q, dt), to_dev(c.k_cache, dt), to_dev(c.v_cache, dt), to_dev(c.k_draft, dt),
+            to_dev(c.v_draft, dt), to_dev(c.parent, "i32"))
+    o_part, l_part = ops.tree_verify_attn_partials(*args, scale=c.scale, num_splits=5, part_dtype=torch.bfloat16)
+    assert o_part.dtype == torch.bfloat16
+    out, lse = ops.attn_merge(o_part, l_part, out_dtype=torch.bfloat16)
+    out1, lse1 = ops.tree_verify_attn(*args, scale=c.scale, num_splits=5)
+    o32, l32 = ops.tree_verify_attn_partials(*args, scale=c.scale, num_splits=5)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse1.view(torch.int32))
+    assert torch.equal(l_part.view(torch.int32), l32.view(torch.int32))   # the lse partials stay fp32
+    # the bf16 partials are the fp32 ones rounded to nearest even
+    assert torch.equal(o_part.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16))
+    check_attn(out, lse, ro, rl, "bf16", "bf16 partials + merge")
