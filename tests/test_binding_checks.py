@@ -49,3 +49,15 @@ def test_partials_must_be_fp32_on_the_gpu():
         ops._parts(None, None)
     with pytest.raises(ValueError, match="GPU"):
         ops._parts(torch.empty((2, 3, 128)), torch.empty((2, 3)))
+
+
+def test_partials_take_fp32_or_bf16_only():
+    with pytest.raises(TypeError, match="float32 or bfloat16"):
+        ops._parts(torch.empty((2, 3, 128), dtype=torch.float16), torch.empty((2, 3)))
+    with pytest.raises(TypeError, match="float32 or bfloat16"):
+        ops._part_dtype(None, torch.float16)
+    # a given o_part decides the form; the keyword only sizes a new one
+    assert ops._part_dtype(torch.empty(1, dtype=torch.bfloat16), torch.float32) == torch.bfloat16
+    assert ops._part_dtype(None, torch.bfloat16) == torch.bfloat16
+    assert ops._part_code(torch.empty(1, dtype=torch.bfloat16)) == ops.TS_BF16
+    assert ops._part_code(torch.empty(1, dtype=torch.float32)) == ops.TS_F32
