@@ -54,6 +54,9 @@ template <int D> __device__ __forceinline__ int vs_chunk(int r, int c) {
   return c ^ ((2 * (r & 7)) & (SLayout<D>::CH - 1));
 }
 
+// M0 carries the wave-uniform LDS destination, set right before its one
+// reader; the compiler emits no M0 access of its own in this kernel, so the
+// clobber it does not honour for a reserved register leaves nothing unsaved.
 __device__ __forceinline__ void lds_dma16(const bf16_t* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
