@@ -802,6 +802,8 @@ struct ToppLds {
   int32_t cid[kToppCand];                // and their token ids
   float part[4 * kSampleMaxSubs];        // kept weight of each sub-slice, in four parts
   unsigned long long partq[kSampleMaxSubs];   // its listed tokens' share, fixed point
+  int32_t qlist[kSampleMaxSubs];         // sub-slices whose maximum reaches a binding min-p cut
+  int nq;
   float red[kToppWaves];
   float above;                           // weight above the current range
   uint32_t lo, hi;                       // the crossing bin's key range
@@ -876,6 +878,8 @@ __device__ __forceinline__ void topp_key_bin(ToppLds& s, uint32_t key, float Z, 
 }
 
 constexpr int kExtractWaves = 4;
+// ToppRow::bc of a row whose min-p cut clearly binds: no crossing bin is sought
+constexpr int kToppMinpBinds = -2;
 
 // C: one workgroup a row. Z and the total weight W from the sub-slice
 // summaries; each sub-slice's bins shifted by its level difference to Z and
@@ -884,6 +888,11 @@ constexpr int kExtractWaves = 4;
 // whose cumulative weight reaches top_p * W (else the last non-empty one), and
 // the weight above it; each sub-slice's weight in the bins above bc. Also
 // resets the row's candidate count for the extract kernel.
+// Every token above the min-p cut Z + cut lies in the cut's bin or above it,
+// so when those bins hold clearly less than top_p * W (by 2^-10 of it, far
+// beyond the sums' rounding), the top-p cut z* lies below the min-p cut and
+// the row's cut is the min-p one whatever z* is: bc = kToppMinpBinds, and the
+// extract and the key passes are skipped.
 __global__ __launch_bounds__(kToppThreads) void sample_topp_coarse_kernel(SampleArgs a) {
   __shared__ float ph[kToppThreads][kToppCoarse + 1];
   __shared__ float coarse[kToppWaves][kToppCoarse];
@@ -956,7 +965,10 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_coarse_kernel(Sample
     const uint64_t hit = __ballot(lane < kToppCoarse && c > 0.0f && incl >= target);
     const uint64_t any = __ballot(lane < kToppCoarse && c > 0.0f);
     const int src = hit ? __ffsll((unsigned long long)hit) - 1 : (any ? 63 - __clzll((unsigned long long)any) : -1);
-    if (lane == 0) sel = src;
+    // (min-p off: cut = -inf sits in the last bin, whose inclusive sum is W)
+    const int bm = topp_bin(Z + a.cut, topp_level(Z, a.s2), a.s2);
+    const bool minp = __shfl(incl, bm, kWave) < target * (1.0f - 0x1p-10f);
+    if (lane == 0) sel = minp ? kToppMinpBinds : src;
     if (src >= 0 && lane == src) above = excl;
   }
   __syncthreads();
@@ -1046,13 +1058,15 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
   // sub-slice's weight above the crossing bin
   const float u_r = a.u[r];
   const float above_q = tid < a.nb ? a.topp_above[(int64_t)r * a.nb + tid] : 0.0f;
+  // the min-p cut binds (the coarse kernel saw it): no crossing bin, no key passes
+  const bool minp_only = rw.bc == kToppMinpBinds;
   // no finite logit, or (cannot happen: the crossing bin has weight) no token in it
-  if (rw.bc < 0 || rw.n == 0) {
+  if (!minp_only && (rw.bc < 0 || rw.n == 0)) {
     if (tid == 0) a.tok[r] = -1;
     return;
   }
   const float Z = rw.Z, target = rw.target;
-  const int bc = rw.bc, n = rw.n;
+  const int bc = minp_only ? kToppCoarse - 1 : rw.bc, n = minp_only ? 0 : rw.n;
   const int lz = topp_level(Z, a.s2);
   const float fx = ldexpf(1.0f, bc + 41), inv_fx = ldexpf(1.0f, -(bc + 41));
   // the held candidates and their key range; a crowded bin starts from the
@@ -1083,7 +1097,7 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
   }
   __syncthreads();
   uint32_t lo = s.lo, hi = s.hi;
-  bool done = lo == hi;
+  bool done = lo == hi || minp_only;
   for (int pass = 0; pass < 3 && !done; ++pass) {
     const int nbits = 32 - __clz((int)(hi - lo));
     const int shift = nbits > 11 ? nbits - 11 : 0;
@@ -1107,7 +1121,7 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
     done = lo == hi;
     __syncthreads();
   }
-  const float zstar = topp_value(lo);
+  const float zstar = minp_only ? -INFINITY : topp_value(lo);
   const float thr = fmaxf(Z + a.cut, zstar);
   if (tid == 0) a.topp_cut[r] = zstar;
 
@@ -1136,7 +1150,32 @@ __global__ __launch_bounds__(kToppThreads) void sample_topp_kernel(SampleArgs a)
       s.part[4 * tid] = above_q;
       s.part[4 * tid + 1] = (float)s.partq[tid] * inv_fx;
     }
+  } else if (thr > zstar) {
+    // min-p binds: a sub-slice whose maximum is below the cut keeps nothing,
+    // so only the others are read, each as four 256-token quarters with the
+    // lanes, sums and slots of the pass over the row below (the same weights)
+    const int wave = tid >> 6, lane = tid & (kWave - 1);
+    if (tid == 0) s.nq = 0;
+    __syncthreads();
+    if (tid < a.nb && a.sub[(int64_t)r * a.nb + tid].m >= thr) s.qlist[atomicAdd(&s.nq, 1)] = tid;
+    __syncthreads();
+    const int items = 4 * s.nq;
+    for (int it = wave; it < items; it += kToppWaves) {
+      const int q = s.qlist[it >> 2], j = it & 3;
+      const int g = q * (kSampleSub / 4) + kWave * j + lane;
+      ToppRaw<Tin, kVec> raw;
+      topp_fetch<Tin, kVec>(V, row, bits, 4 * min(g, ngroups - 1), raw);
+      float z[4];
+      topp_values<Tin, kVec>(V, th, ith, 4 * g, g < ngroups, raw, z);
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (z[i] > -INFINITY && z[i] >= thr) acc += __builtin_amdgcn_exp2f((z[i] - Z) * a.s2);
+      acc = wave_sum(acc);
+      if (lane == 0) s.part[4 * q + j] = acc;
+    }
   } else {
+    // a crowded crossing bin at the cut z*: the pass over the row
     const int wave = tid >> 6, lane = tid & (kWave - 1);
     topp_visit<Tin, kVec>(V, th, ith, row, bits, ngroups, [&](int k, const float (&z)[4]) {
       float acc = 0.0f;

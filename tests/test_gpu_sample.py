@@ -221,7 +221,8 @@ def test_top_p_hand_worked_example():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("temperature,min_p,top_p", [
-    (1.0, 0.1, 0.9),              # the CLI's min-p with a nucleus on top
+    (1.0, 0.1, 0.9),              # the CLI's min-p with a nucleus on top (min-p binds: no crossing bin sought)
+    (1.0, 0.001, 0.5),            # both filters, the nucleus binding (the crossing bin's key passes)
     (0.4, 0.0, 0.9),              # the temperature ablation's range, top-p alone
     (0.8, 0.0, 0.95),
     (1.2, 0.0, 0.9),
