@@ -96,6 +96,12 @@ template <int D> __device__ __forceinline__ int v_chunk(int r, int c) { return c
 // The base address and the LDS destination are wave-uniform; they are passed
 // through readfirstlane so that they stay scalar operands even where the
 // compiler cannot prove it (free when they already live in scalar registers).
+// M0 carries the LDS destination: the statement sets it right before its one
+// reader. The compiler does not save a reserved register named as clobbered
+// (it warns so); in these kernels it emits no M0 access of its own, so there
+// is nothing of its to save. Written as asm, not as the compiler's builtin for
+// this load, because the compiler would then put a wait for every DMA in
+// flight before each LDS read it cannot tell apart from the ring's stages.
 __device__ __forceinline__ void lds_dma16(const bf16_t* base, uint32_t voff, uint32_t lds) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
   const uint64_t bs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32) |
