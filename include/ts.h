@@ -135,9 +135,9 @@ ts_status ts_tree_verify_attn_noalloc(const void* q, const void* k_cache, const 
  * ts_tree_verify_attn_partials writes, for every split s in [0, n_splits):
  *   o_part [n_splits][T][Hq][D]  part_dtype   softmax(s restricted to split s) . v
  *   l_part [n_splits][T][Hq]     fp32         ln sum exp(s) over split s (-inf if empty)
- * part_dtype is TS_F32, or TS_BF16 (rounded to nearest even: half the bytes
- * for the merge to read) when dtype is TS_BF16; else TS_ERR_UNSUPPORTED.
- * with n_splits = ts_tree_verify_attn_num_splits(...). Split s covers a
+ * with n_splits = ts_tree_verify_attn_num_splits(...). part_dtype is TS_F32,
+ * or TS_BF16 (rounded to nearest even: half the bytes for the merge to read)
+ * when dtype is TS_BF16; else TS_ERR_UNSUPPORTED. Split s covers a
  * contiguous range of cached tokens; the draft tokens belong to the last split.
  * ts_attn_merge combines `n_parts` such partials:
  *   lse = ln sum_s exp(l_part[s]);  out = sum_s exp(l_part[s] - lse) * o_part[s]. */
