@@ -272,3 +272,33 @@ def test_bf16_partials_then_merge_equal_single_call_bit_for_bit():
     # the bf16 partials are the fp32 ones rounded to nearest even
     assert torch.equal(o_part.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16))
     check_attn(out, lse, ro, rl, "bf16", "bf16 partials + merge")
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,D,L", [
+    (3, 4, 1, 128, 3000),      # 12 rows a KV head: the wave-per-split kernel
+    (4, 4, 2, 64, 777),        # the same kernel at head_dim 64, a ragged cache
+    (40, 8, 8, 64, 2500),      # one query head per KV head: the 128-row matrix-core form
+    (100, 8, 2, 64, 1500),     # 400 rows a KV head: two 256-row groups at head_dim 64
+])
+def test_bf16_partials_every_kernel_form(T, Hq, Hkv, D, L):
+    """bf16 partials from each split kernel's epilogue: the fp32 partials
+    rounded to nearest even, and the merge of them equal to the single call
+    bit for bit."""
+    say(f"[phases] bf16 partials T={T} Hq={Hq} Hkv={Hkv} D={D} L={L}")
+    rng = np.random.default_rng(T * 7 + D)
+    parent = np.array([-1 if t == 0 else int(rng.integers(max(0, t - 5), t)) for t in range(T)], np.int32)
+    c = inputs.make_verify("bf16 partials", dtype="bf16", Hq=Hq, Hkv=Hkv, D=D, L=L, seed=T + L,
+                           with_chains=False, parent=parent)
+    args = (to_dev(c.q, "bf16"), to_dev(c.k_cache, "bf16"), to_dev(c.v_cache, "bf16"), to_dev(c.k_draft, "bf16"),
+            to_dev(c.v_draft, "bf16"), to_dev(c.parent, "i32"))
+    o16, l16 = ops.tree_verify_attn_partials(*args, scale=c.scale, num_splits=3, part_dtype=torch.bfloat16)
+    o32, l32 = ops.tree_verify_attn_partials(*args, scale=c.scale, num_splits=3)
+    out, lse = ops.attn_merge(o16, l16, out_dtype=torch.bfloat16)
+    out1, lse1 = ops.tree_verify_attn(*args, scale=c.scale, num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(l16.view(torch.int32), l32.view(torch.int32))
+    assert torch.equal(o16.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(out.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse1.view(torch.int32))
+    ro, rl = oracle.verify_attn_ref(c.q, c.k_cache, c.v_cache, c.k_draft, c.v_draft, c.parent, c.scale, c.dtype)
+    check_attn(out, lse, ro, rl, "bf16", "bf16 partials, every kernel form")
