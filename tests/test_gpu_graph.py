@@ -94,6 +94,7 @@ def test_graph_fused_step_and_sampling_replays_match_eager():
     sws = ops.alloc_workspace(int(ops.lib().ts_sample_workspace(s.R, s.V)), dev)
     tok_minp = torch.empty(s.R, dtype=torch.int32, device=dev)
     tok_topp = torch.empty(s.R, dtype=torch.int32, device=dev)
+    tok_both = torch.empty(s.R, dtype=torch.int32, device=dev)
     kw = dict(hist=hist, parent=sp, draft_tok=dtok, window=inputs.PENALTY_WINDOW, penalty=inputs.PENALTY, u=u,
               workspace=sws)
 
@@ -105,9 +106,10 @@ def test_graph_fused_step_and_sampling_replays_match_eager():
                                      out=dout, lse=dlse, workspace=dws)
         ops.sample_tokens(logits, temperature=1.0, min_p=0.1, tok=tok_minp, **kw)
         ops.sample_tokens(logits, temperature=0.8, min_p=0.0, top_p=0.9, tok=tok_topp, **kw)
+        ops.sample_tokens(logits, temperature=1.0, min_p=0.1, top_p=0.9, tok=tok_both, **kw)   # min-p binds
 
-    names = ("out", "lse", "scores", "idx", "val", "kp", "vp", "dout", "dlse", "tok_minp", "tok_topp")
-    results = (out, lse, scores, idx, val, kp, vp, dout, dlse, tok_minp, tok_topp)
+    names = ("out", "lse", "scores", "idx", "val", "kp", "vp", "dout", "dlse", "tok_minp", "tok_topp", "tok_both")
+    results = (out, lse, scores, idx, val, kp, vp, dout, dlse, tok_minp, tok_topp, tok_both)
     step()
     torch.cuda.synchronize()
     eager = [r.clone() for r in results]
